@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized KV cache on one MI355X.
+
+One step = kvq_quantize_append of the new token of every sequence into one
+layer, then kvq_decode_attention over that layer (every cached token, the new
+one included). The default workload is the Llama-2-7B-shaped cache (16
+sequences, 32 heads of 128 channels, 4096 cached tokens, fp16, 2-bit K
+per-channel / V per-token, groups of 32), one layer per step. Independent
+layer caches are rotated so that each step reads memory that is not resident
+in the 256 MB last-level cache.
+
+Prints one JSON line: metric/value (decode-step GB/s of algorithmic bytes),
+tokens/s, the decode kernel's roofline (HIP events on the launch stream) and
+the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+LLC_BYTES = 256 << 20  # MI355X Infinity Cache
+
+METRIC = "quantized decode-attention HBM GB/s (% of peak) and tokens/s; quantize GB/s"
+
+
+def algorithmic_head_bytes(T, D, axis_k, axis_v, Gk, Gv, bk, bv, ib):
+    """Bytes decode attention must read for one (seq, kv head) at length T:
+    packed codes + 4-byte (step, zero) pairs + residual rows in the input dtype."""
+    tot = 0
+    for axis, G, B in ((axis_k, Gk, bk), (axis_v, Gv, bv)):
+        if axis == 0:
+            tq = T // G * G
+            tot += tq * D * B // 8 + (tq // G) * D * 4 + (T - tq) * D * ib
+        else:
+            tot += T * D * B // 8 + T * (D // G) * 4
+    return tot
+
+
+def rotation_for(step_bytes):
+    return max(1, math.ceil(4 * LLC_BYTES / max(step_bytes, 1)))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2-7b",
+                    choices=["tiny", "gpt2-small", "llama2-7b", "long-gqa", "mixed"])
+    ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_kv_cache_groupwise_amd import kvq
+    from bit_kv_cache_groupwise_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.get(args.workload)
+    ib = 4 if w.in_dtype == "f32" else 2
+    S, H, D = w.num_seqs, w.kv_heads, w.head_dim
+    n_new = w.new_tokens
+    model_layers = w.layers  # layers attended per step (12 for the GPT-2 shape, else 1)
+    step_lens = [L + n_new for L in w.lengths]
+    step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
+                     for T, (bk, bv) in zip(step_lens, w.bits)) * model_layers
+    rot = args.rotate or rotation_for(step_bytes)
+    total_steps = args.warmup + args.steps
+    appends_per_layer = math.ceil(total_steps / rot) + 1
+    layers = rot * model_layers
+    cap = [L + n_new * appends_per_layer for L in w.lengths]
+    geom = kvq.geometry(layers=layers, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D, group_k=w.group_k,
+                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype)
+    cache = kvq.Cache(geom, cap, [b[0] for b in w.bits], [b[1] for b in w.bits], device=dev)
+
+    # ---- bulk prefill = quantize-append into an empty cache (timed: quantize GB/s)
+    qz_ms = []
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for l in range(layers):
+        k, v = W.draw_kv(w, l % model_layers if rot == 1 else l, w.lengths, device=dev, stream=0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        cache.append(l, k, v, list(w.lengths))
+        e1.record()
+        torch.cuda.synchronize()
+        qz_ms.append(e0.elapsed_time(e1))
+        del k, v
+    prefill_tokens = sum(w.lengths)
+    qz_bytes = 0
+    for T, (bk, bv) in zip(w.lengths, w.bits):
+        qz_bytes += H * (2 * T * D * ib + algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v,
+                                                                 bk, bv, ib))
+    quantize_gbps = qz_bytes / (np.median(qz_ms) * 1e-3) / 1e9
+
+    # ---- per-step inputs, drawn up front
+    new_k, new_v, qs = [], [], []
+    for st in range(total_steps):
+        k, v = W.draw_kv(w, 0, [n_new] * S, device=dev, stream=1 + st)
+        new_k.append(k)
+        new_v.append(v)
+        qs.append(W.draw_q(w, 0, device=dev, step=st))
+    out = torch.empty((S, w.q_heads, D), dtype=torch.float32, device=dev)
+    ws = cache.workspace()
+    counts = [n_new] * S
+    scale = w.softmax_scale
+
+    def step(st, events=None):
+        base = (st % rot) * model_layers
+        for m in range(model_layers):
+            l = base + m
+            if events is not None:
+                events[m][0].record()
+            cache.append(l, new_k[st], new_v[st], counts)
+            if events is not None:
+                events[m][1].record()
+            kvq.kvq_decode_attention(cache.handle, l, qs[st], scale, out, ws, ws.numel())
+            if events is not None:
+                events[m][2].record()
+
+    for st in range(args.warmup):
+        step(st)
+    torch.cuda.synchronize()
+    evs = [[[ev(), ev(), ev()] for _ in range(model_layers)] for _ in range(args.steps)]
+    # bytes attended in the timed steps (lengths grow by one token per append)
+    lens0 = {l: cache.lengths(l) for l in range(layers)}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    dec_ms = [evs[i][m][1].elapsed_time(evs[i][m][2]) for i in range(args.steps) for m in range(model_layers)]
+    app_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(model_layers)]
+    # algorithmic bytes of every timed decode launch, from the lengths each saw
+    lens = {l: list(v) for l, v in lens0.items()}
+    dec_bytes = []
+    for i in range(args.steps):
+        base = ((args.warmup + i) % rot) * model_layers
+        for m in range(model_layers):
+            l = base + m
+            lens[l] = [x + n_new for x in lens[l]]
+            dec_bytes.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
+                                 for T, (bk, bv) in zip(lens[l], w.bits)))
+    app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
+    ms_per_step = wall_s * 1e3 / args.steps
+    step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
+    value = step_total_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_gbps = float(np.mean(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
+    tokens_per_s = S * n_new / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": S, "kv_heads": H, "q_heads": w.q_heads, "head_dim": D,
+                   "cached_tokens": list(sorted(set(w.lengths)))[:4] if len(set(w.lengths)) > 1 else w.lengths[0],
+                   "layers_per_step": model_layers, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
+                   "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "decode_attention_GBps": round(dec_gbps, 2),
+        "decode_attention_us": round(dec_avg_ms * 1e3, 3),
+        "append_us": round(float(np.mean(app_ms)) * 1e3, 3),
+        "quantize_GBps": round(quantize_gbps, 2),
+        "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
+        "prefill_tokens": prefill_tokens,
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "kvq_decode_attention (split + merge)",
+                     "bytes_per_launch": int(np.mean(dec_bytes))},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU oracle, untuned, on a bounded sample of the same decode step:
+    for a few sequences it encodes each kv head's cache (quantize + pack),
+    dequantizes in float64 and runs the attention of the head's queries. The
+    rate is the same algorithmic decode bytes per second as the GPU figure."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from bit_kv_cache_groupwise_amd import workloads as W
+    from oracle import kvq_oracle as o
+
+    ib = 4 if w.in_dtype == "f32" else 2
+    R = w.q_heads // w.kv_heads
+    done_bytes = 0
+    heads = 0
+    t_cpu = 0.0
+    with threadpool_limits(limits=1):
+        s = 0
+        while t_cpu < budget_s and s < w.num_seqs:
+            T = w.lengths[s] + w.new_tokens
+            bk, bv = w.bits[s]
+            counts = [0] * w.num_seqs
+            counts[s] = T
+            k, v = W.draw_kv(w, 0, counts, stream=0)
+            q = W.draw_q(w, 0)[s].double().numpy()
+            k = k.float().numpy()
+            v = v.float().numpy()
+            for h in range(w.kv_heads):
+                t0 = time.perf_counter()
+                e = o.encode_head(k[:, h], v[:, h], group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k,
+                                  axis_v=w.axis_v, bits_k=bk, bits_v=bv)
+                o.attend(q[h * R:(h + 1) * R], e["k_hat"], e["v_hat"], w.softmax_scale)
+                t_cpu += time.perf_counter() - t0
+                done_bytes += algorithmic_head_bytes(T, w.head_dim, w.axis_k, w.axis_v, w.group_k, w.group_v,
+                                                     bk, bv, ib)
+                heads += 1
+                if t_cpu >= budget_s:
+                    break
+            s += 1
+    return {"value": round(done_bytes / t_cpu / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} (seq, kv head) caches of {w.name}: quantize+pack, fp64 dequantize, fp64 attention",
+            "seconds": round(t_cpu, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,62 @@
+"""Build libkvq.so (HIP kernels for gfx950 + the C-ABI host library) in-tree.
+
+    python -m bit_kv_cache_groupwise_amd.build
+
+Every call recompiles. Flags that matter for the numerics: no FP contraction
+(the quantizer's subtract and divide must not fuse), correctly rounded fp32
+division, fp32 denormals kept; packed fp32 VALU ops are disabled.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libkvq.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    return os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    jobs = [
+        [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kvq_kernels.hip"), "-o", os.path.join(BUILD, "kvq_kernels.o")],
+        [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", os.path.join(BUILD, "kvq_api.o")],
+    ]
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        for r in ex.map(_run, jobs):
+            if verbose and (r.stdout or r.stderr):
+                print(r.stdout, r.stderr, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+          os.path.join(BUILD, "kvq_kernels.o"), os.path.join(BUILD, "kvq_api.o")])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,460 @@
+// Host side of libkvq: argument validation, pool layout, the per-layer length
+// state and kernel launches behind the C ABI declared in include/kvq.h.
+#include "kvq.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+size_t decode_lds_bytes(int R, int D, int C);
+}
+
+using kvq::SeqEntry;
+
+struct kvq_cache {
+    kvq_geometry g{};
+    std::vector<int32_t> cap;
+    std::vector<uint8_t> bits_k, bits_v;
+    uint8_t* codes = nullptr;
+    uint8_t* meta = nullptr;
+    uint8_t* resid = nullptr;
+    uint8_t* table = nullptr;
+    kvq::TableLayout tl{};
+    std::vector<SeqEntry> entries;  // [layers][num_seqs]
+    std::vector<int32_t> lens;      // host mirror of the current lengths [layers][num_seqs]
+    std::vector<uint8_t> parity;    // which length buffer is current, per layer
+    std::vector<int32_t> args;      // staging for the call-argument area
+    int32_t max_cap = 0;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+    return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int in_bytes(int dt) { return dt == KVQ_F32 ? 4 : 2; }
+
+bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 6 || b == 8; }
+
+bool aligned(const void* p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+kvq_status check_geometry(const kvq_geometry* g) {
+    if (!g) return fail(KVQ_ERR_ARG, "geometry is NULL");
+    if (g->layers < 1 || g->num_seqs < 1 || g->kv_heads < 1 || g->q_heads < 1)
+        return fail(KVQ_ERR_ARG, "layers, num_seqs, kv_heads and q_heads must be >= 1");
+    if (g->q_heads % g->kv_heads)
+        return fail(KVQ_ERR_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", g->q_heads, g->kv_heads);
+    if (g->head_dim < 32 || g->head_dim % 32 || g->head_dim > kvq::kMaxHeadDim)
+        return fail(KVQ_ERR_ARG, "head_dim (%d) must be a multiple of 32 in [32, 256]", g->head_dim);
+    const int groups[2] = {g->group_k, g->group_v};
+    const int axes[2] = {g->axis_k, g->axis_v};
+    for (int t = 0; t < 2; ++t) {
+        const int G = groups[t];
+        if (G != 32 && G != 64 && G != 128 && G != 256)
+            return fail(KVQ_ERR_ARG, "group_%c (%d) must be 32, 64, 128 or 256", "kv"[t], G);
+        if (axes[t] != KVQ_AXIS_CHANNEL && axes[t] != KVQ_AXIS_TOKEN)
+            return fail(KVQ_ERR_ARG, "axis_%c (%d) is not a kvq axis", "kv"[t], axes[t]);
+        if (axes[t] == KVQ_AXIS_TOKEN && g->head_dim % G)
+            return fail(KVQ_ERR_ARG, "token-axis group_%c (%d) must divide head_dim (%d)", "kv"[t], G, g->head_dim);
+    }
+    if (g->in_dtype != KVQ_F32 && g->in_dtype != KVQ_F16 && g->in_dtype != KVQ_BF16)
+        return fail(KVQ_ERR_ARG, "in_dtype (%d) is not a kvq dtype", g->in_dtype);
+    if (g->meta_dtype == KVQ_F32 || g->meta_dtype == KVQ_BF16)
+        return fail(KVQ_ERR_UNSUPPORTED, "only fp16 step/zero metadata is stored by this build");
+    if (g->meta_dtype != KVQ_F16) return fail(KVQ_ERR_ARG, "meta_dtype (%d) is not a kvq dtype", g->meta_dtype);
+    return KVQ_OK;
+}
+
+kvq_status check_seqs(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv) {
+    if (!cap || !bk || !bv) return fail(KVQ_ERR_ARG, "capacity, bits_k and bits_v must be non-NULL");
+    for (int s = 0; s < g->num_seqs; ++s) {
+        if (cap[s] < 0 || cap[s] > (1 << 28)) return fail(KVQ_ERR_ARG, "capacity[%d] = %d out of range", s, cap[s]);
+        if (!valid_bits(bk[s]) || !valid_bits(bv[s]))
+            return fail(KVQ_ERR_ARG, "bits of sequence %d (%d, %d) must be in {2,3,4,6,8}", s, bk[s], bv[s]);
+    }
+    return KVQ_OK;
+}
+
+// Pool layout: layer -> seq -> tensor (K, V) -> head, each head region 256-byte aligned.
+void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
+            std::vector<SeqEntry>* entries, kvq_sizes* sz, kvq::TableLayout* tl) {
+    const uint64_t D = g->head_dim, H = g->kv_heads, ib = in_bytes(g->in_dtype);
+    const int groups[2] = {g->group_k, g->group_v};
+    const int axes[2] = {g->axis_k, g->axis_v};
+    uint64_t oc = 0, om = 0, orr = 0, fc = 0, fm = 0, fr = 0;
+    if (entries) entries->assign((size_t)g->layers * g->num_seqs, SeqEntry{});
+    for (int l = 0; l < g->layers; ++l) {
+        for (int s = 0; s < g->num_seqs; ++s) {
+            SeqEntry e{};
+            const int bits[2] = {bk[s], bv[s]};
+            for (int t = 0; t < 2; ++t) {
+                const uint64_t G = groups[t], B = bits[t], c = cap[s];
+                const bool ch = axes[t] == KVQ_AXIS_CHANNEL;
+                const uint64_t rows = ch ? (c / G) * G : c;
+                const uint64_t code_b = rows * D * B / 8;
+                const uint64_t meta_b = (ch ? (c / G) * D : c * (D / G)) * 4;
+                const uint64_t res_b = ch ? G * D * ib : 0;
+                e.codes[t] = oc;
+                e.codes_hs[t] = align_up(code_b, kvq::kAlign);
+                oc += e.codes_hs[t] * H;
+                e.meta[t] = om;
+                e.meta_hs[t] = align_up(meta_b, kvq::kAlign);
+                om += e.meta_hs[t] * H;
+                e.resid[t] = orr;
+                e.resid_hs[t] = align_up(res_b, kvq::kAlign);
+                orr += e.resid_hs[t] * H;
+                fc += code_b * H;
+                fm += meta_b * H;
+                fr += res_b * H;
+                e.bits[t] = bits[t];
+            }
+            e.cap = cap[s];
+            if (entries) (*entries)[(size_t)l * g->num_seqs + s] = e;
+        }
+    }
+    const uint64_t LS = (uint64_t)g->layers * g->num_seqs;
+    tl->entries_bytes = align_up(LS * sizeof(SeqEntry), kvq::kAlign);
+    tl->len_off = tl->entries_bytes;
+    tl->args_off = tl->len_off + align_up(2 * LS * 4, kvq::kAlign);
+    tl->total = tl->args_off + align_up(2 * (uint64_t)g->num_seqs * 4, kvq::kAlign);
+    sz->codes_bytes = std::max<uint64_t>(oc, kvq::kAlign);
+    sz->meta_bytes = std::max<uint64_t>(om, kvq::kAlign);
+    sz->residual_bytes = std::max<uint64_t>(orr, kvq::kAlign);
+    sz->table_bytes = tl->total;
+    sz->formula_codes_bytes = fc;
+    sz->formula_meta_bytes = fm;
+    sz->formula_residual_bytes = fr;
+}
+
+int group_size(const kvq_cache* c) { return c->g.q_heads / c->g.kv_heads; }
+
+// Tokens per decode split: a multiple of the key block, grown while the grid
+// stays above ~8 workgroups per compute unit, shrunk to fit 64 KB of LDS.
+int choose_chunk(const kvq_cache* c, int max_len) {
+    const kvq_geometry& g = c->g;
+    const int kmin = g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, g.group_k) : 64;
+    const long pairs = (long)g.num_seqs * g.kv_heads;
+    if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
+        const int v = std::atoi(env);
+        if (v >= kmin && v <= 1024 && v % kmin == 0 && (v & (v - 1)) == 0 &&
+            kvq::decode_lds_bytes(group_size(c), g.head_dim, v) <= 65536)
+            return v;
+    }
+    int C = kmin;
+    while (C < 1024 && pairs * ((max_len + 2L * C - 1) / (2L * C)) >= 2048) C *= 2;
+    while (C > kmin && kvq::decode_lds_bytes(group_size(c), g.head_dim, C) > 65536) C /= 2;
+    return C;
+}
+
+int min_chunk(const kvq_cache* c) {
+    return c->g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, c->g.group_k) : 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_version(void) { return "0.1.0"; }
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_ARG: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported by this build";
+        case KVQ_ERR_CAPACITY: return "capacity exceeded";
+        case KVQ_ERR_ALIGN: return "misaligned device pointer";
+        case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_plan(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv, kvq_sizes* out) {
+    g_last_error.clear();
+    kvq_status st = check_geometry(g);
+    if (st) return st;
+    if ((st = check_seqs(g, cap, bk, bv))) return st;
+    if (!out) return fail(KVQ_ERR_ARG, "out is NULL");
+    kvq::TableLayout tl;
+    layout(g, cap, bk, bv, nullptr, out, &tl);
+    return KVQ_OK;
+}
+
+kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
+                            void* d_codes, void* d_meta, void* d_residual, void* d_table, void* stream,
+                            kvq_cache** out) {
+    g_last_error.clear();
+    kvq_status st = check_geometry(g);
+    if (st) return st;
+    if ((st = check_seqs(g, cap, bk, bv))) return st;
+    if (!out) return fail(KVQ_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (!d_codes || !d_meta || !d_residual || !d_table) return fail(KVQ_ERR_ARG, "a device pool is NULL");
+    if (!aligned(d_codes, kvq::kAlign) || !aligned(d_meta, kvq::kAlign) || !aligned(d_residual, kvq::kAlign) ||
+        !aligned(d_table, kvq::kAlign))
+        return fail(KVQ_ERR_ALIGN, "device pools must be 256-byte aligned");
+    kvq_cache* c = new (std::nothrow) kvq_cache;
+    if (!c) return fail(KVQ_ERR_ARG, "out of host memory");
+    c->g = *g;
+    c->cap.assign(cap, cap + g->num_seqs);
+    c->bits_k.assign(bk, bk + g->num_seqs);
+    c->bits_v.assign(bv, bv + g->num_seqs);
+    c->codes = (uint8_t*)d_codes;
+    c->meta = (uint8_t*)d_meta;
+    c->resid = (uint8_t*)d_residual;
+    c->table = (uint8_t*)d_table;
+    kvq_sizes sz;
+    layout(g, cap, bk, bv, &c->entries, &sz, &c->tl);
+    c->lens.assign((size_t)g->layers * g->num_seqs, 0);
+    c->parity.assign(g->layers, 0);
+    c->args.assign(2 * (size_t)g->num_seqs, 0);
+    c->max_cap = *std::max_element(cap, cap + g->num_seqs);
+    std::vector<uint8_t> img(c->tl.total, 0);
+    std::memcpy(img.data(), c->entries.data(), c->entries.size() * sizeof(SeqEntry));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(d_table, img.data(), img.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "writing the cache table");
+    }
+    *out = c;
+    return KVQ_OK;
+}
+
+void kvq_cache_destroy(kvq_cache* c) { delete c; }
+
+kvq_status kvq_seq_lengths(const kvq_cache* c, int32_t layer, int32_t* out) {
+    g_last_error.clear();
+    if (!c || !out) return fail(KVQ_ERR_ARG, "cache or out is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    std::memcpy(out, &c->lens[(size_t)layer * c->g.num_seqs], sizeof(int32_t) * c->g.num_seqs);
+    return KVQ_OK;
+}
+
+kvq_status kvq_get_region(const kvq_cache* c, int32_t layer, int32_t seq, kvq_region* out) {
+    g_last_error.clear();
+    if (!c || !out) return fail(KVQ_ERR_ARG, "cache or out is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    if (seq < 0 || seq >= c->g.num_seqs) return fail(KVQ_ERR_ARG, "seq %d out of range", seq);
+    const SeqEntry& e = c->entries[(size_t)layer * c->g.num_seqs + seq];
+    out->k_codes = e.codes[0];
+    out->v_codes = e.codes[1];
+    out->k_meta = e.meta[0];
+    out->v_meta = e.meta[1];
+    out->k_resid = e.resid[0];
+    out->v_resid = e.resid[1];
+    out->k_codes_head_stride = e.codes_hs[0];
+    out->v_codes_head_stride = e.codes_hs[1];
+    out->k_meta_head_stride = e.meta_hs[0];
+    out->v_meta_head_stride = e.meta_hs[1];
+    out->k_resid_head_stride = e.resid_hs[0];
+    out->v_resid_head_stride = e.resid_hs[1];
+    out->bits_k = e.bits[0];
+    out->bits_v = e.bits[1];
+    out->capacity = e.cap;
+    out->length = c->lens[(size_t)layer * c->g.num_seqs + seq];
+    return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                               const int32_t* n_new, void* stream) {
+    g_last_error.clear();
+    if (!c || !n_new) return fail(KVQ_ERR_ARG, "cache or n_new is NULL");
+    const kvq_geometry& g = c->g;
+    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    const int S = g.num_seqs;
+    int32_t* lens = &c->lens[(size_t)layer * S];
+    long total = 0;
+    int max_n = 0;
+    bool uniform = true;
+    for (int s = 0; s < S; ++s) {
+        if (n_new[s] < 0) return fail(KVQ_ERR_ARG, "n_new[%d] = %d is negative", s, n_new[s]);
+        if ((long)lens[s] + n_new[s] > c->cap[s])
+            return fail(KVQ_ERR_CAPACITY, "sequence %d: length %d + %d exceeds capacity %d", s, lens[s], n_new[s], c->cap[s]);
+        total += n_new[s];
+        max_n = std::max(max_n, n_new[s]);
+        uniform = uniform && n_new[s] == n_new[0];
+    }
+    if (total == 0) return KVQ_OK;
+    if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new and v_new must be non-NULL when tokens are appended");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVQ_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
+    if (total > (1L << 30)) return fail(KVQ_ERR_ARG, "too many tokens in one append");
+
+    hipStream_t hs = (hipStream_t)stream;
+    const int32_t* d_n = nullptr;
+    const int32_t* d_start = nullptr;
+    int32_t* args_dev = (int32_t*)(c->table + c->tl.args_off);
+    if (!uniform) {
+        int32_t acc = 0;
+        for (int s = 0; s < S; ++s) {
+            c->args[s] = n_new[s];
+            c->args[S + s] = acc;
+            acc += n_new[s];
+        }
+        hipError_t e = hipMemcpyAsync(args_dev, c->args.data(), sizeof(int32_t) * 2 * S, hipMemcpyHostToDevice, hs);
+        if (e != hipSuccess) return hip_fail(e, "uploading append counts");
+        d_n = args_dev;
+        d_start = args_dev + S;
+    }
+    int32_t* len_base = (int32_t*)(c->table + c->tl.len_off);
+    const int p = c->parity[layer];
+    const SeqEntry* entries = (const SeqEntry*)c->table + (size_t)layer * S;
+
+    const void* srcs[2] = {k_new, v_new};
+    const int groups[2] = {g.group_k, g.group_v};
+    const int axes[2] = {g.axis_k, g.axis_v};
+    for (int t = 0; t < 2; ++t) {
+        kvq::TensorArgs a{};
+        a.src = srcs[t];
+        a.codes = c->codes;
+        a.meta = c->meta;
+        a.resid = c->resid;
+        a.table = entries;
+        a.len_in = len_base + ((size_t)p * g.layers + layer) * S;
+        a.len_out = t == 0 ? len_base + ((size_t)(1 - p) * g.layers + layer) * S : nullptr;
+        a.n_new = d_n;
+        a.row_start = d_start;
+        a.n_uniform = uniform ? n_new[0] : 0;
+        a.tensor = t;
+        a.num_seqs = S;
+        a.kv_heads = g.kv_heads;
+        a.head_dim = g.head_dim;
+        a.group = groups[t];
+        a.in_dtype = g.in_dtype;
+        hipError_t e;
+        if (axes[t] == KVQ_AXIS_TOKEN) {
+            a.rows_per_block = kvq::kThreads / (g.head_dim / 32);
+            const int gx = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
+            e = kvq::launch_quant_token_axis(a, gx, hs);
+        } else {
+            int gx = 1;
+            for (int s = 0; s < S; ++s)
+                gx = std::max(gx, (lens[s] + n_new[s]) / groups[t] - lens[s] / groups[t]);
+            e = kvq::launch_quant_channel_axis(a, gx, hs);
+        }
+        if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
+    }
+    for (int s = 0; s < S; ++s) lens[s] += n_new[s];
+    c->parity[layer] ^= 1;
+    return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_size(const kvq_cache* c) {
+    if (!c) return 0;
+    const kvq_geometry& g = c->g;
+    const uint64_t chunks = std::max<uint64_t>(1, (c->max_cap + min_chunk(c) - 1) / min_chunk(c));
+    const uint64_t slots = (uint64_t)g.num_seqs * g.q_heads * chunks;
+    return align_up(slots * 2 * 4, kvq::kAlign) + align_up(slots * g.head_dim * 4, kvq::kAlign);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
+    const kvq_geometry& g = c->g;
+    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    if (group_size(c) > kvq::kMaxQueryGroup)
+        return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d", group_size(c), kvq::kMaxQueryGroup);
+    if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
+    if (!(softmax_scale == softmax_scale)) return fail(KVQ_ERR_ARG, "softmax_scale is NaN");
+    if (!aligned(q, in_bytes(g.in_dtype)) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "q or out misaligned");
+    const int S = g.num_seqs;
+    const int32_t* lens = &c->lens[(size_t)layer * S];
+    const int max_len = *std::max_element(lens, lens + S);
+    const int C = choose_chunk(c, max_len);
+    const int max_chunks = std::max(1, (max_len + C - 1) / C);
+    const uint64_t slots = (uint64_t)S * g.q_heads * max_chunks;
+    const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
+    const uint64_t need = ml_bytes + align_up(slots * g.head_dim * 4, kvq::kAlign);
+    if (!workspace || workspace_bytes < need)
+        return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %llu needed", workspace_bytes, (unsigned long long)need);
+    if (!aligned(workspace, kvq::kAlign)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    kvq::DecodeArgs a{};
+    a.q = q;
+    a.out = out;
+    a.ws_ml = (float*)workspace;
+    a.ws_o = (float*)((uint8_t*)workspace + ml_bytes);
+    a.codes = c->codes;
+    a.meta = c->meta;
+    a.resid = c->resid;
+    a.table = (const SeqEntry*)c->table + (size_t)layer * S;
+    a.len = (const int32_t*)(c->table + c->tl.len_off) + ((size_t)c->parity[layer] * g.layers + layer) * S;
+    a.qscale = softmax_scale * 1.4426950408889634f;
+    a.num_seqs = S;
+    a.kv_heads = g.kv_heads;
+    a.q_heads = g.q_heads;
+    a.head_dim = g.head_dim;
+    a.group_k = g.group_k;
+    a.group_v = g.group_v;
+    a.axis_k = g.axis_k;
+    a.axis_v = g.axis_v;
+    a.in_dtype = g.in_dtype;
+    a.chunk = C;
+    a.max_chunks = max_chunks;
+    hipError_t e = kvq::launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+    return KVQ_OK;
+}
+
+kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float* k_out, float* v_out, void* stream) {
+    g_last_error.clear();
+    if (!c) return fail(KVQ_ERR_ARG, "cache is NULL");
+    const kvq_geometry& g = c->g;
+    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    if (seq < 0 || seq >= g.num_seqs) return fail(KVQ_ERR_ARG, "seq %d out of range", seq);
+    if ((k_out && !aligned(k_out, 4)) || (v_out && !aligned(v_out, 4))) return fail(KVQ_ERR_ALIGN, "outputs misaligned");
+    const int len = c->lens[(size_t)layer * g.num_seqs + seq];
+    float* outs[2] = {k_out, v_out};
+    const int groups[2] = {g.group_k, g.group_v};
+    const int axes[2] = {g.axis_k, g.axis_v};
+    for (int t = 0; t < 2; ++t) {
+        if (!outs[t]) continue;
+        kvq::DequantArgs a{};
+        a.out = outs[t];
+        a.codes = c->codes;
+        a.meta = c->meta;
+        a.resid = c->resid;
+        a.entry = c->entries[(size_t)layer * g.num_seqs + seq];
+        a.tensor = t;
+        a.len = len;
+        a.kv_heads = g.kv_heads;
+        a.head_dim = g.head_dim;
+        a.group = groups[t];
+        a.axis = axes[t];
+        a.in_dtype = g.in_dtype;
+        hipError_t e = kvq::launch_dequant(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "launching dequantize");
+    }
+    return KVQ_OK;
+}
+
+}  // extern "C"

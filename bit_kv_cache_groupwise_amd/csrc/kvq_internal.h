@@ -1,0 +1,88 @@
+// Internal declarations shared by the host side of libkvq (kvq_api.cpp) and
+// its HIP kernels (kvq_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace kvq {
+
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxQueryGroup = 16;  // q_heads / kv_heads handled by one decode workgroup
+constexpr int kThreads = 256;       // threads per workgroup of every kernel
+constexpr uint64_t kAlign = 256;    // alignment of every head region and pool
+
+// One (layer, seq) entry of the device table. Byte offsets into the codes,
+// metadata and residual pools of head 0 of each tensor, and per-head strides.
+struct SeqEntry {
+    uint64_t codes[2];        // [K, V]
+    uint64_t meta[2];
+    uint64_t resid[2];
+    uint64_t codes_hs[2];
+    uint64_t meta_hs[2];
+    uint64_t resid_hs[2];
+    int32_t bits[2];
+    int32_t cap;
+    int32_t pad_;
+};
+static_assert(sizeof(SeqEntry) == 112, "SeqEntry layout");
+
+// Table buffer layout (bytes from d_table):
+//   [0, entries_bytes)                 SeqEntry[layers][num_seqs]
+//   [len_off, +2*layers*num_seqs*4)    int32 lengths[2][layers][num_seqs] (double buffered)
+//   [args_off, +2*num_seqs*4)          int32 call args: n_new[num_seqs], row_start[num_seqs]
+struct TableLayout {
+    uint64_t entries_bytes, len_off, args_off, total;
+};
+
+// Per-launch description of one tensor (K = 0 or V = 1) of one layer.
+struct TensorArgs {
+    const void* src;            // new rows [sum n][Hkv][D], input dtype
+    uint8_t* codes;             // codes pool
+    uint8_t* meta;              // metadata pool
+    uint8_t* resid;             // residual pool
+    const SeqEntry* table;      // entries of this layer: table[seq]
+    const int32_t* len_in;      // lengths of this layer before the call [num_seqs]
+    int32_t* len_out;           // lengths after the call (other buffer), or nullptr
+    const int32_t* n_new;       // device [num_seqs] or nullptr when uniform
+    const int32_t* row_start;   // device [num_seqs] or nullptr when uniform
+    int32_t n_uniform;
+    int32_t tensor;             // 0 = K, 1 = V
+    int32_t num_seqs, kv_heads, head_dim, group, in_dtype;
+    int32_t rows_per_block;     // token-axis kernel: rows per workgroup
+};
+
+struct DecodeArgs {
+    const void* q;              // [S][Hq][D], input dtype
+    float* out;                 // [S][Hq][D]
+    float* ws_ml;               // [S][Hq][max_chunks][2]
+    float* ws_o;                // [S][Hq][max_chunks][D]
+    const uint8_t* codes;
+    const uint8_t* meta;
+    const uint8_t* resid;
+    const SeqEntry* table;      // entries of this layer
+    const int32_t* len;         // lengths of this layer [num_seqs]
+    float qscale;               // softmax scale * log2(e)
+    int32_t num_seqs, kv_heads, q_heads, head_dim;
+    int32_t group_k, group_v, axis_k, axis_v, in_dtype;
+    int32_t chunk;              // tokens per split (multiple of group_k when axis_k is channel)
+    int32_t max_chunks;         // chunks per (seq, head) the workspace is laid out for
+};
+
+struct DequantArgs {
+    float* out;                 // [Hkv][len][D]
+    const uint8_t* codes;
+    const uint8_t* meta;
+    const uint8_t* resid;
+    SeqEntry entry;
+    int32_t tensor, len, kv_heads, head_dim, group, axis, in_dtype;
+};
+
+hipError_t launch_quant_token_axis(const TensorArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+
+}  // namespace kvq

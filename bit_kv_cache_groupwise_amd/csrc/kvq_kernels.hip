@@ -1,0 +1,648 @@
+// HIP kernels of libkvq for CDNA4 (gfx950): groupwise asymmetric quantization
+// of KV-cache rows into bit-packed uint32 words, the fused split-K decode
+// attention that reads them, the split merge, and the unfused dequantizer.
+//
+// Sources, by page title and section:
+//   [N] nalar.dev, "Kuantisasi KV cache untuk mengurangi memory inferensi long-context"
+//   [U] unite.ai (pt), "O Seu Cache KV Nao Tem um Problema de Bits. Tem um Problema de Geometria."
+//
+// Numerics of the quantizer (must match the published definition bit for
+// bit, so this file is compiled with -ffp-contract=off, correctly rounded
+// fp32 division and fp32 denormals kept):
+//   zero = group min; step = (max - min) / (2^B - 1) as an fp32 subtract then
+//   an fp32 divide ([U] "O Que o Erro de Quantizacao E Realmente Feito");
+//   both rounded to fp16 (v_cvt_f16_f32, nearest-even); code =
+//   clamp(rint((x - z) / s), 0, 2^B - 1) against the stored z, s
+//   (v_rndne_f32: ties to even); stored step 0 -> code 0.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float((bits16 & 0xffffu) << 16);
+}
+
+// Input dtype tags: 0 = f32, 1 = f16, 2 = bf16.
+template <int DT> struct In;
+template <> struct In<0> { static constexpr int bytes = 4; };
+template <> struct In<1> { static constexpr int bytes = 2; };
+template <> struct In<2> { static constexpr int bytes = 2; };
+
+template <int DT>
+__device__ __forceinline__ float load_in(const void* p, size_t i) {
+    if constexpr (DT == 0) {
+        return ((const float*)p)[i];
+    } else if constexpr (DT == 1) {
+        return f16_to_f32(((const uint16_t*)p)[i]);
+    } else {
+        return bf16_to_f32(((const uint16_t*)p)[i]);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+    if constexpr (DT == 1) return f16_to_f32(h);
+    else return bf16_to_f32(h);
+}
+
+// 32 consecutive input elements starting at element `off` (16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void load32(const void* base, size_t off, float (&x)[32]) {
+    if constexpr (DT == 0) {
+        const uint4* p = (const uint4*)((const float*)base + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 v = p[i];
+            x[4 * i + 0] = __uint_as_float(v.x);
+            x[4 * i + 1] = __uint_as_float(v.y);
+            x[4 * i + 2] = __uint_as_float(v.z);
+            x[4 * i + 3] = __uint_as_float(v.w);
+        }
+    } else {
+        const uint4* p = (const uint4*)((const uint16_t*)base + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = p[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[8 * i + 2 * k + 0] = half_to_f32<DT>(w[k]);
+                x[8 * i + 2 * k + 1] = half_to_f32<DT>(w[k] >> 16);
+            }
+        }
+    }
+}
+
+// Code of one value against the stored grid (step s, zero z), L = 2^B - 1.
+__device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float L) {
+    if (s == 0.0f) return 0u;
+    float t = rintf((x - z) / s);
+    t = fminf(fmaxf(t, 0.0f), L);
+    return (uint32_t)t;
+}
+
+// Pack 32 codes into the B words of one unit: code j at stream bits [jB, jB+B).
+template <int B>
+__device__ __forceinline__ void pack32(const uint32_t (&c)[32], uint32_t (&w)[B]) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+        w[wi] |= c[j] << sh;
+        if (sh + B > 32) w[wi + 1] |= c[j] >> (32 - sh);
+    }
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[B], int j) {
+    const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+    uint32_t v = w[wi] >> sh;
+    if (sh + B > 32) v |= w[wi + 1] << (32 - sh);
+    return v & ((1u << B) - 1u);
+}
+
+template <int B>
+__device__ __forceinline__ void load_unit(const uint32_t* p, uint32_t (&w)[B]) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = p[k];
+}
+
+template <int B>
+__device__ __forceinline__ void store_codes(const uint32_t (&c)[32], uint32_t* dst) {
+    uint32_t w[B];
+    pack32<B>(c, w);
+#pragma unroll
+    for (int k = 0; k < B; ++k) dst[k] = w[k];
+}
+
+__device__ __forceinline__ void store_codes_rt(int B, const uint32_t (&c)[32], uint32_t* dst) {
+    switch (B) {
+        case 2: store_codes<2>(c, dst); break;
+        case 3: store_codes<3>(c, dst); break;
+        case 4: store_codes<4>(c, dst); break;
+        case 6: store_codes<6>(c, dst); break;
+        default: store_codes<8>(c, dst); break;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Workgroup-wide reductions over 256 threads (4 waves); `scratch` holds 4 floats.
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+    v = wave_sum(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+}
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
+}
+
+// ---------------------------------------------------------------------------
+// Quantize, token axis: one group = G consecutive channels of one token
+// ([U] "Valores: Onde a Intuicao Quebra"; [U] "O Imposto dos Sistemas ...":
+// such groups are complete when their token arrives). One thread per
+// 32-channel unit; a group spans G/32 adjacent lanes and its min/max is a
+// butterfly over those lanes.
+// grid = (row tiles, kv_heads, num_seqs)
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_token_axis_kernel(TensorArgs a) {
+    const int seq = blockIdx.z, head = blockIdx.y;
+    const int D = a.head_dim, UPR = D >> 5;
+    const int len0 = a.len_in[seq];
+    const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
+    if (a.len_out && blockIdx.x == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len0 + n;
+    const int r = blockIdx.x * a.rows_per_block + (int)threadIdx.x / UPR;
+    const int u = (int)threadIdx.x % UPR;
+    if (r >= n) return;  // whole rows (and so whole groups) leave together
+    const int row_start = a.row_start ? a.row_start[seq] : seq * a.n_uniform;
+    const SeqEntry& e = a.table[seq];
+    const int T = a.tensor, B = e.bits[T], G = a.group, UG = G >> 5;
+    const int t = len0 + r;
+
+    float x[32];
+    load32<DT>(a.src, ((size_t)(row_start + r) * a.kv_heads + head) * D + 32 * u, x);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        mn = fminf(mn, x[j]);
+        mx = fmaxf(mx, x[j]);
+    }
+    for (int off = 1; off < UG; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    const float L = (float)((1 << B) - 1);
+    const float s32 = (mx - mn) / L;
+    const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
+    const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+    uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
+    if ((u & (UG - 1)) == 0) meta[(size_t)t * (D / G) + u / UG] = sb | (zb << 16);
+    uint32_t c[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = quant_code(x[j], s, z, L);
+    uint32_t* dst = (uint32_t*)(a.codes + e.codes[T] + (size_t)head * e.codes_hs[T] + (size_t)t * (D * B / 8)) + u * B;
+    store_codes_rt(B, c, dst);
+}
+
+// ---------------------------------------------------------------------------
+// Quantize, channel axis: one group = one channel over a block of G tokens
+// ([U] "Chaves: Os Valores Extremos Vivem em Canais Fixos"). A block is
+// quantized when its G-th token arrives; until then its tokens wait in the
+// residual rows ([U] "O Imposto dos Sistemas ..."). Workgroup item 0 also
+// moves the new tail tokens into the residual, after it has read the old
+// residual rows of its own block, so the two never race.
+// grid = (items, kv_heads, num_seqs); dynamic LDS = G * D bytes of codes.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_channel_axis_kernel(TensorArgs a) {
+    extern __shared__ uint32_t lds_codes_w[];
+    uint8_t* lds_codes = (uint8_t*)lds_codes_w;
+    const int seq = blockIdx.z, head = blockIdx.y, item = blockIdx.x;
+    const int D = a.head_dim, UPR = D >> 5, G = a.group;
+    const int len0 = a.len_in[seq];
+    const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
+    const int len1 = len0 + n;
+    if (a.len_out && item == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len1;
+    const int b_first = len0 / G, b_end = len1 / G, nb = b_end - b_first;
+    if (item >= (nb > 0 ? nb : 1)) return;
+    const int row_start = a.row_start ? a.row_start[seq] : seq * a.n_uniform;
+    const SeqEntry& e = a.table[seq];
+    const int T = a.tensor, B = e.bits[T];
+    const uint8_t* resid = a.resid + e.resid[T] + (size_t)head * e.resid_hs[T];
+    constexpr int IB = In<DT>::bytes;
+
+    if (item < nb) {
+        const int b = b_first + item;
+        const float L = (float)((1 << B) - 1);
+        for (int ch = threadIdx.x; ch < D; ch += kThreads) {
+            float mn = 0.f, mx = 0.f;
+            for (int i = 0; i < G; ++i) {
+                const int t = b * G + i;
+                const float x = t < len0 ? load_in<DT>(resid, (size_t)(t % G) * D + ch)
+                                         : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch);
+                mn = i == 0 ? x : fminf(mn, x);
+                mx = i == 0 ? x : fmaxf(mx, x);
+            }
+            const float s32 = (mx - mn) / L;
+            const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
+            const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+            uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
+            meta[(size_t)b * D + ch] = sb | (zb << 16);
+            for (int i = 0; i < G; ++i) {
+                const int t = b * G + i;
+                const float x = t < len0 ? load_in<DT>(resid, (size_t)(t % G) * D + ch)
+                                         : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch);
+                lds_codes[i * D + ch] = (uint8_t)quant_code(x, s, z, L);
+            }
+        }
+        __syncthreads();
+        uint8_t* codes = a.codes + e.codes[T] + (size_t)head * e.codes_hs[T];
+        for (int idx = threadIdx.x; idx < G * UPR; idx += kThreads) {
+            const int i = idx / UPR, u = idx % UPR;
+            const uint32_t* src = lds_codes_w + (i * D + 32 * u) / 4;
+            uint32_t c[32];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t v = src[k];
+                c[4 * k + 0] = v & 0xffu;
+                c[4 * k + 1] = (v >> 8) & 0xffu;
+                c[4 * k + 2] = (v >> 16) & 0xffu;
+                c[4 * k + 3] = v >> 24;
+            }
+            uint32_t* dst = (uint32_t*)(codes + (size_t)(b * G + i) * (D * B / 8)) + u * B;
+            store_codes_rt(B, c, dst);
+        }
+    }
+    if (item == 0) {
+        __syncthreads();  // this block's reads of the old residual rows are done
+        const int start = b_end * G > len0 ? b_end * G : len0;
+        uint8_t* rw = a.resid + e.resid[T] + (size_t)head * e.resid_hs[T];
+        const int count = (len1 - start) * D;
+        for (int idx = threadIdx.x; idx < count; idx += kThreads) {
+            const int i = idx / D, ch = idx % D;
+            const int t = start + i;
+            const size_t so = ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch;
+            const size_t dof = (size_t)(t % G) * D + ch;
+            if constexpr (IB == 4) ((uint32_t*)rw)[dof] = ((const uint32_t*)a.src)[so];
+            else ((uint16_t*)rw)[dof] = ((const uint16_t*)a.src)[so];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention, one split: workgroup = (chunk of C tokens, kv head, seq).
+// Keys on the channel axis use the rewrite score_t = q.z_b + sum_c (q_c s_bc)
+// code_tc, so each quantized key element costs one multiply-add; values on the
+// token axis accumulate sum_t (p_t s_tg) code_tc plus sum_t p_t z_tg per group
+// ([N] "Kuantisasi dapat memindahkan pekerjaan ke decode path": unpacking and
+// scale application inside the attention kernel). Query heads sharing the kv
+// head are processed one after the other. Each split writes (m, l, o) in the
+// log2 domain for the merge.
+// ---------------------------------------------------------------------------
+
+// acc += sum_j q[j] * code_j over one unit.
+template <int B>
+__device__ __forceinline__ float dot_unit(const uint32_t* unit, const float* q, float acc) {
+    uint32_t w[B];
+    load_unit<B>(unit, w);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc = fmaf(q[j], (float)code_at<B>(w, j), acc);
+    return acc;
+}
+
+template <int B>
+__device__ __forceinline__ void axpy_unit(const uint32_t* unit, float wgt, float (&acc)[32]) {
+    uint32_t w[B];
+    load_unit<B>(unit, w);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = fmaf(wgt, (float)code_at<B>(w, j), acc[j]);
+}
+
+template <int BK>
+__device__ __forceinline__ float key_score_channel(const uint32_t* row, const float* qb, int UPR, float acc) {
+    for (int u = 0; u < UPR; ++u) acc = dot_unit<BK>(row + u * BK, qb + 32 * u, acc);
+    return acc;
+}
+
+template <int BK>
+__device__ __forceinline__ float key_score_token(const uint32_t* row, const uint32_t* meta_row, const float* qr,
+                                                 const float* qsum, int UPR, int UG) {
+    float acc = 0.f;
+    for (int g = 0; g < UPR / UG; ++g) {
+        float part = 0.f;
+        for (int u = g * UG; u < (g + 1) * UG; ++u) part = dot_unit<BK>(row + u * BK, qr + 32 * u, part);
+        const uint32_t w = meta_row[g];
+        acc = fmaf(f16_to_f32(w), part, acc);
+        acc = fmaf(f16_to_f32(w >> 16), qsum[g], acc);
+    }
+    return acc;
+}
+
+template <int BV>
+__device__ __forceinline__ void value_pass(const uint8_t* vc, const uint32_t* vm, const float* sc, int t0, int t1,
+                                           int tl, int TL, int u, int D, int Gv, float (&acc)[32], float& zacc) {
+    const int g = (32 * u) / Gv, gpr = D / Gv;
+    for (int t = t0 + tl; t < t1; t += TL) {
+        const float p = sc[t - t0];
+        const uint32_t w = vm[(size_t)t * gpr + g];
+        zacc = fmaf(p, f16_to_f32(w >> 16), zacc);
+        const uint32_t* unit = (const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + u * BV;
+        axpy_unit<BV>(unit, p * f16_to_f32(w), acc);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+    extern __shared__ float smem[];
+    const int seq = blockIdx.z, kvh = blockIdx.y, chunk = blockIdx.x;
+    const int len = a.len[seq];
+    const int C = a.chunk, t0 = chunk * C;
+    if (t0 >= len) return;
+    const int t1 = min(t0 + C, len), nt = t1 - t0;
+    const int D = a.head_dim, UPR = D >> 5, R = a.q_heads / a.kv_heads;
+    const int Gk = a.group_k, Gv = a.group_v;
+    const bool kch = a.axis_k == 0;
+    const SeqEntry& e = a.table[seq];
+    const int BK = e.bits[0], BV = e.bits[1];
+    const int nqk = kch ? (len / Gk) * Gk : len;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    constexpr int IB = In<DT>::bytes;
+
+    // LDS carve-up (floats): q[R][D] | scores[C] | qk[8][256] | small[64] | red[256*32]
+    float* q_s = smem;
+    float* sc = q_s + R * D;
+    float* qk = sc + C;
+    float* small = qk + 8 * 256;  // [0,8) bias, [8,16) qsum, [16,20) reduction scratch
+    float* red = small + 64;
+
+    const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
+    const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
+    const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
+    const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
+    const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
+
+    for (int i = tid; i < R * D; i += kThreads) {
+        const int r = i / D, ch = i % D;
+        q_s[i] = load_in<DT>(a.q, ((size_t)seq * a.q_heads + kvh * R + r) * D + ch) * a.qscale;
+    }
+    __syncthreads();
+
+    for (int r = 0; r < R; ++r) {
+        const float* qr = q_s + r * D;
+        const int hq = kvh * R + r;
+        // ---- keys -------------------------------------------------------
+        if (kch) {
+            const int kend = min(t1, nqk);
+            for (int tile0 = t0; tile0 < kend; tile0 += kThreads) {
+                const int tile_end = min(tile0 + kThreads, kend);
+                const int b0 = tile0 / Gk;
+                const int nbl = (tile_end - tile0 + Gk - 1) / Gk;
+                for (int idx = tid; idx < nbl * D; idx += kThreads) {
+                    const int bl = idx / D, ch = idx % D;
+                    qk[idx] = qr[ch] * f16_to_f32(km[(size_t)(b0 + bl) * D + ch]);
+                }
+                for (int bl = wave; bl < nbl; bl += 4) {
+                    float p = 0.f;
+                    for (int ch = lane; ch < D; ch += 64) p = fmaf(qr[ch], f16_to_f32(km[(size_t)(b0 + bl) * D + ch] >> 16), p);
+                    p = wave_sum(p);
+                    if (lane == 0) small[bl] = p;
+                }
+                __syncthreads();
+                const int t = tile0 + tid;
+                if (t < tile_end) {
+                    const int bl = t / Gk - b0;
+                    const uint32_t* row = (const uint32_t*)(kc + (size_t)t * (D * BK / 8));
+                    float acc = small[bl];
+                    const float* qb = qk + bl * D;
+                    switch (BK) {
+                        case 2: acc = key_score_channel<2>(row, qb, UPR, acc); break;
+                        case 3: acc = key_score_channel<3>(row, qb, UPR, acc); break;
+                        case 4: acc = key_score_channel<4>(row, qb, UPR, acc); break;
+                        case 6: acc = key_score_channel<6>(row, qb, UPR, acc); break;
+                        default: acc = key_score_channel<8>(row, qb, UPR, acc); break;
+                    }
+                    sc[t - t0] = acc;
+                }
+                __syncthreads();
+            }
+            // residual key rows (input dtype)
+            const int rs = max(t0, nqk);
+            for (int t = rs + tid; t < t1; t += kThreads) {
+                const uint8_t* rrow = kr + (size_t)(t % Gk) * D * IB;
+                float acc = 0.f;
+                for (int ch = 0; ch < D; ++ch) acc = fmaf(qr[ch], load_in<DT>(rrow, ch), acc);
+                sc[t - t0] = acc;
+            }
+        } else {
+            const int UG = Gk >> 5;
+            if (tid < D / Gk) {
+                float s = 0.f;
+                for (int ch = tid * Gk; ch < (tid + 1) * Gk; ++ch) s += qr[ch];
+                small[8 + tid] = s;
+            }
+            __syncthreads();
+            for (int t = t0 + tid; t < t1; t += kThreads) {
+                const uint32_t* row = (const uint32_t*)(kc + (size_t)t * (D * BK / 8));
+                const uint32_t* mrow = km + (size_t)t * (D / Gk);
+                float acc;
+                switch (BK) {
+                    case 2: acc = key_score_token<2>(row, mrow, qr, small + 8, UPR, UG); break;
+                    case 3: acc = key_score_token<3>(row, mrow, qr, small + 8, UPR, UG); break;
+                    case 4: acc = key_score_token<4>(row, mrow, qr, small + 8, UPR, UG); break;
+                    case 6: acc = key_score_token<6>(row, mrow, qr, small + 8, UPR, UG); break;
+                    default: acc = key_score_token<8>(row, mrow, qr, small + 8, UPR, UG); break;
+                }
+                sc[t - t0] = acc;
+            }
+        }
+        __syncthreads();
+        // ---- softmax over this split ------------------------------------
+        float m = -INFINITY;
+        for (int i = tid; i < nt; i += kThreads) m = fmaxf(m, sc[i]);
+        m = block_max(m, small + 16);
+        float l = 0.f;
+        for (int i = tid; i < nt; i += kThreads) {
+            const float p = exp2f(sc[i] - m);
+            sc[i] = p;
+            l += p;
+        }
+        l = block_sum(l, small + 16);  // its barriers also publish sc
+        // ---- values -----------------------------------------------------
+        const int TL = kThreads / UPR, tl = tid / UPR, u = tid % UPR;
+        float acc[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+        float zacc = 0.f;
+        switch (BV) {
+            case 2: value_pass<2>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 3: value_pass<3>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 4: value_pass<4>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 6: value_pass<6>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            default: value_pass<8>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) red[tl * D + 32 * u + j] = acc[j] + zacc;
+        __syncthreads();
+        const size_t slot = ((size_t)seq * a.q_heads + hq) * a.max_chunks + chunk;
+        for (int ch = tid; ch < D; ch += kThreads) {
+            float o = 0.f;
+            for (int i = 0; i < TL; ++i) o += red[i * D + ch];
+            a.ws_o[slot * D + ch] = o;
+        }
+        if (tid == 0) {
+            a.ws_ml[slot * 2 + 0] = m;
+            a.ws_ml[slot * 2 + 1] = l;
+        }
+        __syncthreads();  // red, sc and small are reused by the next query head
+    }
+}
+
+// Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
+// out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
+    const int hq = blockIdx.x, seq = blockIdx.y, D = a.head_dim;
+    const int len = a.len[seq];
+    const int nch = (len + a.chunk - 1) / a.chunk;
+    float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
+    if (nch == 0) {
+        for (int ch = threadIdx.x; ch < D; ch += kThreads) out[ch] = 0.f;
+        return;
+    }
+    const size_t base = ((size_t)seq * a.q_heads + hq) * a.max_chunks;
+    const float* ml = a.ws_ml + base * 2;
+    float M = -INFINITY;
+    for (int i = 0; i < nch; ++i) M = fmaxf(M, ml[2 * i]);
+    float L = 0.f;
+    for (int i = 0; i < nch; ++i) L += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
+    const float inv = 1.0f / L;
+    for (int ch = threadIdx.x; ch < D; ch += kThreads) {
+        float o = 0.f;
+        for (int i = 0; i < nch; ++i) o = fmaf(a.ws_o[(base + i) * D + ch], exp2f(ml[2 * i] - M), o);
+        out[ch] = o * inv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize one tensor of one sequence into float32 [Hkv][len][D]:
+// x_hat = fma(code, s, z), which is the correctly rounded value of the exact
+// z + code * s ([N] "Kuantisasi dapat memindahkan pekerjaan ke decode path":
+// the unfused alternative); residual rows are converted exactly.
+// grid = (ceil(len * D/32 / 256), kv_heads)
+// ---------------------------------------------------------------------------
+template <int B>
+__device__ __forceinline__ void dequant_unit(const uint32_t* unit, const uint32_t* meta, bool per_channel, float* out) {
+    uint32_t w[B];
+    load_unit<B>(unit, w);
+    if (per_channel) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const uint32_t m = meta[j];
+            out[j] = fmaf((float)code_at<B>(w, j), f16_to_f32(m), f16_to_f32(m >> 16));
+        }
+    } else {
+        const uint32_t m = meta[0];
+        const float s = f16_to_f32(m), z = f16_to_f32(m >> 16);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) out[j] = fmaf((float)code_at<B>(w, j), s, z);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
+    const int D = a.head_dim, UPR = D >> 5;
+    const int idx = blockIdx.x * kThreads + threadIdx.x;
+    const int t = idx / UPR, u = idx % UPR, head = blockIdx.y;
+    if (t >= a.len) return;
+    const int T = a.tensor, B = a.entry.bits[T], G = a.group;
+    const bool ch = a.axis == 0;
+    const int nq = ch ? (a.len / G) * G : a.len;
+    float* out = a.out + ((size_t)head * a.len + t) * D + 32 * u;
+    if (t < nq) {
+        const uint32_t* unit = (const uint32_t*)(a.codes + a.entry.codes[T] + (size_t)head * a.entry.codes_hs[T] +
+                                                 (size_t)t * (D * B / 8)) + u * B;
+        const uint32_t* meta = (const uint32_t*)(a.meta + a.entry.meta[T] + (size_t)head * a.entry.meta_hs[T]);
+        meta += ch ? (size_t)(t / G) * D + 32 * u : (size_t)t * (D / G) + (32 * u) / G;
+        float v[32];
+        switch (B) {
+            case 2: dequant_unit<2>(unit, meta, ch, v); break;
+            case 3: dequant_unit<3>(unit, meta, ch, v); break;
+            case 4: dequant_unit<4>(unit, meta, ch, v); break;
+            case 6: dequant_unit<6>(unit, meta, ch, v); break;
+            default: dequant_unit<8>(unit, meta, ch, v); break;
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) out[j] = v[j];
+    } else {
+        const uint8_t* rrow = a.resid + a.entry.resid[T] + (size_t)head * a.entry.resid_hs[T] +
+                              (size_t)(t % G) * D * In<DT>::bytes;
+        for (int j = 0; j < 32; ++j) out[j] = load_in<DT>(rrow, 32 * u + j);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+size_t decode_lds_bytes(int R, int D, int C) {
+    return sizeof(float) * ((size_t)R * D + C + 8 * 256 + 64 + 256 * 32);
+}
+
+hipError_t launch_quant_token_axis(const TensorArgs& a, int grid_x, hipStream_t s) {
+    dim3 grid(grid_x, a.kv_heads, a.num_seqs);
+    switch (a.in_dtype) {
+        case 0: hipLaunchKernelGGL(quant_token_axis_kernel<0>, grid, dim3(kThreads), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(quant_token_axis_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(quant_token_axis_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_t s) {
+    dim3 grid(grid_x, a.kv_heads, a.num_seqs);
+    const size_t lds = (size_t)a.group * a.head_dim;
+    switch (a.in_dtype) {
+        case 0: hipLaunchKernelGGL(quant_channel_axis_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
+        case 1: hipLaunchKernelGGL(quant_channel_axis_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
+        default: hipLaunchKernelGGL(quant_channel_axis_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    const int R = a.q_heads / a.kv_heads;
+    dim3 grid(a.max_chunks, a.kv_heads, a.num_seqs);
+    const size_t lds = decode_lds_bytes(R, a.head_dim, a.chunk);
+    switch (a.in_dtype) {
+        case 0: hipLaunchKernelGGL(decode_split_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
+        case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
+        default: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+    const int units = a.len * (a.head_dim >> 5);
+    if (units == 0) return hipSuccess;
+    dim3 grid((units + kThreads - 1) / kThreads, a.kv_heads);
+    switch (a.in_dtype) {
+        case 0: hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(kThreads), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(dequant_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL(dequant_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,205 @@
+/*
+ * kvq.h — C ABI of libkvq: groupwise asymmetric integer quantization of a
+ * transformer KV cache, bit-packed in HBM, and the decode-step attention that
+ * reads the packed cache directly (AMD Instinct MI355X, gfx950).
+ *
+ * Sources, cited by page title and section heading:
+ *   [N] nalar.dev, "Kuantisasi KV cache untuk mengurangi memory inferensi
+ *       long-context"
+ *   [U] unite.ai (pt), "O Seu Cache KV Nao Tem um Problema de Bits. Tem um
+ *       Problema de Geometria."
+ *   [H] hatterialabs.com (cs), "Asymetrie kvantizace KV cache"
+ *
+ * The quantizer ([U] "O Que o Erro de Quantizacao E Realmente Feito";
+ * [N] "Scale menentukan sistem koordinat kuantisasi"): for every group of
+ * values, zero z = group minimum, step s = (max - min) / (2^B - 1) computed in
+ * float32 (subtract, then a correctly rounded divide), both stored as fp16
+ * (round to nearest even); code = clamp(rint((x - z) / s), 0, 2^B - 1) against
+ * the stored z and s, with ties to even; a group whose stored step is 0 gets
+ * code 0. Reconstruction is x_hat = z + code * s.
+ *
+ * Grouping ([U] "Chaves: Os Valores Extremos Vivem em Canais Fixos",
+ * "Valores: Onde a Intuicao Quebra"): KVQ_AXIS_CHANNEL keeps one (s, z) per
+ * channel for each block of G consecutive tokens (the key default: outlier
+ * channels get their own steps); KVQ_AXIS_TOKEN keeps one (s, z) per token for
+ * each group of G consecutive channels (the value default: a token's error
+ * stays with that token). K and V have separate bit widths B in {2,3,4,6,8}
+ * ([N] "Key dan value dapat memiliki struktur numerik berbeda"; [H] "Vychozi
+ * zjisteni na GPT-2").
+ *
+ * Residual ([U] "O Imposto dos Sistemas e Por Que Nao E um Detalhe"; [N]
+ * "Pengecualian recent-token mengubah perhitungan memory"): a channel-axis
+ * step needs all G tokens of a block, so the last (len mod G) tokens of a
+ * channel-axis tensor stay in the input dtype and are quantized when their
+ * block completes. Results depend only on the token history, never on how
+ * appends were chunked.
+ *
+ * Storage (the pages leave the layout open: [N] "Scale menentukan ..."):
+ *   code row   one token of one head: D/32 units, unit u = B uint32 words
+ *              holding channels 32u..32u+31; channel 32u+j sits at bits
+ *              [jB, jB+B) of the unit's little-endian bitstream (3- and
+ *              6-bit codes straddle words). A row is D*B/8 bytes, no padding.
+ *   metadata   uint32 words, fp16 step in bits 0..15, fp16 zero in 16..31;
+ *              channel axis: [block][channel]; token axis: [token][group].
+ *   residual   channel-axis tensors only: G rows of D input-dtype values per
+ *              (layer, seq, head); token t lives in row t mod G.
+ *   pools      four caller-owned device buffers (codes, metadata, residual,
+ *              table) sized by kvq_plan; regions are ordered layer -> seq ->
+ *              tensor (K, V) -> head, each head region 256-byte aligned.
+ *
+ * Conventions
+ *   - Every call returns a kvq_status; nothing throws or aborts. On error
+ *     nothing is launched, nothing is written and lengths do not advance.
+ *     kvq_last_error() gives a detail message for the calling thread.
+ *   - The library never allocates device memory. All device buffers belong to
+ *     the caller and must stay alive while a cache handle uses them.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work on it and return. All calls on one cache must be ordered on one
+ *     stream, or synchronized by the caller between streams: the library keeps
+ *     the sequence lengths on the host and in the table, and reuses the
+ *     table's argument area from call to call.
+ *   - One decode step is kvq_quantize_append (the new token) followed by
+ *     kvq_decode_attention, which attends to every cached token including
+ *     the new one.
+ *   - Preconditions on data (not checked on the device): inputs finite and,
+ *     with fp16 metadata, |x| <= 65504.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+#define KVQ_OK               0
+#define KVQ_ERR_ARG         -1 /* null pointer, out-of-range index or shape, bad enum      */
+#define KVQ_ERR_UNSUPPORTED -2 /* valid request this build does not implement               */
+#define KVQ_ERR_CAPACITY    -3 /* an append would exceed a sequence's capacity              */
+#define KVQ_ERR_ALIGN       -4 /* a device pointer is not aligned as documented             */
+#define KVQ_ERR_WORKSPACE   -5 /* workspace null or smaller than kvq_decode_workspace_size */
+#define KVQ_ERR_HIP         -6 /* a HIP runtime call or kernel launch failed                */
+
+enum { KVQ_AXIS_CHANNEL = 0, KVQ_AXIS_TOKEN = 1 };
+enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 };
+
+/* The problem statement ([N] "Ukuran cache bertambah mengikuti token, layer,
+ * dan KV head": layers, cached tokens, kv heads, head_dim; [N] "Scale
+ * menentukan ...": group size, axis, precision of the scale). */
+typedef struct kvq_geometry {
+    int32_t layers;     /* >= 1                                                  */
+    int32_t num_seqs;   /* >= 1                                                  */
+    int32_t kv_heads;   /* >= 1                                                  */
+    int32_t q_heads;    /* multiple of kv_heads; head h reads kv head h/(q/kv)   */
+    int32_t head_dim;   /* D: multiple of 32, at most 256                        */
+    int32_t group_k;    /* G for K: 32, 64, 128 or 256 (token axis: divides D)   */
+    int32_t group_v;    /* G for V: same rules                                   */
+    int32_t axis_k;     /* KVQ_AXIS_CHANNEL (default for keys)                   */
+    int32_t axis_v;     /* KVQ_AXIS_TOKEN   (default for values)                 */
+    int32_t in_dtype;   /* KVQ_F32, KVQ_F16 or KVQ_BF16: K/V/q inputs, residual  */
+    int32_t meta_dtype; /* KVQ_F16 (the only metadata type this build stores)    */
+} kvq_geometry;
+
+/* Byte counts. The pool sizes include 256-byte alignment of every head
+ * region; the formula_* fields are the closed-form bytes at full capacity
+ * with no padding ([N] "Pengecualian recent-token ...": packed cache +
+ * scales/metadata + high-precision recent cache + workspace). */
+typedef struct kvq_sizes {
+    uint64_t codes_bytes;            /* codes pool                                   */
+    uint64_t meta_bytes;             /* metadata pool                                */
+    uint64_t residual_bytes;         /* residual pool                                */
+    uint64_t table_bytes;            /* table buffer (offsets, lengths, call args)   */
+    uint64_t formula_codes_bytes;    /* sum rows * kv_heads * D * B / 8              */
+    uint64_t formula_meta_bytes;     /* 4 bytes per group                            */
+    uint64_t formula_residual_bytes; /* G * D * in_bytes per channel-axis tensor head */
+} kvq_sizes;
+
+/* Byte offsets of one (layer, seq) in the pools, head 0, plus per-head
+ * strides; for serialization, inspection and tests. */
+typedef struct kvq_region {
+    uint64_t k_codes, v_codes, k_meta, v_meta, k_resid, v_resid;
+    uint64_t k_codes_head_stride, v_codes_head_stride;
+    uint64_t k_meta_head_stride, v_meta_head_stride;
+    uint64_t k_resid_head_stride, v_resid_head_stride;
+    int32_t bits_k, bits_v, capacity, length;
+} kvq_region;
+
+typedef struct kvq_cache kvq_cache;
+
+/* Pool sizes for a geometry. capacity, bits_k, bits_v: host arrays of
+ * num_seqs entries (capacity >= 0 tokens per sequence and layer; bits in
+ * {2,3,4,6,8}). Pure host computation. */
+kvq_status kvq_plan(const kvq_geometry* geometry, const int32_t* capacity,
+                    const uint8_t* bits_k, const uint8_t* bits_v, kvq_sizes* out);
+
+/* Create a cache handle over caller-owned device pools (each at least the
+ * size kvq_plan reports, 256-byte aligned). Writes the offset table and zero
+ * lengths into d_table with a blocking copy on `stream`; pool contents are
+ * not touched. The handle is a small host object freed by
+ * kvq_cache_destroy. */
+kvq_status kvq_cache_create(const kvq_geometry* geometry, const int32_t* capacity,
+                            const uint8_t* bits_k, const uint8_t* bits_v,
+                            void* d_codes, void* d_meta, void* d_residual, void* d_table,
+                            void* stream, kvq_cache** out);
+
+/* Free the host handle (the device pools stay with the caller). NULL is a no-op. */
+void kvq_cache_destroy(kvq_cache* cache);
+
+/* Append n_new[s] tokens to every sequence s of `layer` and quantize what
+ * becomes quantizable ([U] "O Imposto dos Sistemas ...": token-axis groups
+ * at once, channel-axis blocks when their G-th token arrives). k_new, v_new:
+ * device, in_dtype, [sum(n_new)][kv_heads][head_dim], sequences in order
+ * (element-aligned). n_new: host array of num_seqs counts >= 0. A bulk
+ * prefill is an append into an empty cache. Errors: KVQ_ERR_CAPACITY when
+ * length + n_new > capacity for any sequence (nothing is written). */
+kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                               const int32_t* n_new, void* stream);
+
+/* Bytes of workspace kvq_decode_attention needs for this cache at any
+ * length up to capacity (split partials; caller-owned, 256-byte aligned). */
+size_t kvq_decode_workspace_size(const kvq_cache* cache);
+
+/* Decode-step attention of one query per sequence and query head over every
+ * cached token of `layer`, reading the packed codes and fp16 metadata and
+ * dequantizing in registers ([N] "Kuantisasi dapat memindahkan pekerjaan ke
+ * decode path": the fused alternative to dequantizing into a temporary;
+ * [U] "Por Que o Cache KV E Onde Isso Morde": decode reads the whole cache
+ * once per generated token). out[s][h] = sum_t softmax_t(scale * q.k_hat_t) *
+ * v_hat_t, keys in the residual taken as stored. q: device, in_dtype,
+ * [num_seqs][q_heads][head_dim]; out: device float32, same shape; a sequence
+ * of length 0 gets zeros. This build: K on either axis, V on the token axis,
+ * q_heads/kv_heads <= 16 (else KVQ_ERR_UNSUPPORTED). */
+kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
+                                float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The unfused path ([N] "Kuantisasi dapat memindahkan pekerjaan ke decode
+ * path": dequantize into a temporary floating-point tensor): write x_hat =
+ * fma(code, s, z) in float32 for every cached token of one sequence, residual
+ * rows converted exactly from the input dtype. k_out, v_out: device float32
+ * [kv_heads][length][head_dim] (either may be NULL to skip it). */
+kvq_status kvq_dequantize(const kvq_cache* cache, int32_t layer, int32_t seq, float* k_out, float* v_out,
+                          void* stream);
+
+/* Current cached lengths of `layer`: host array of num_seqs entries. */
+kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t* out);
+
+/* Pool offsets of one (layer, seq). */
+kvq_status kvq_get_region(const kvq_cache* cache, int32_t layer, int32_t seq, kvq_region* out);
+
+/* Static description of a status code; never NULL. */
+const char* kvq_status_string(kvq_status status);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/kvq.h
+declares, sizes pools by the closed form, and rejects bad arguments before any
+HIP call is made. No kernel is launched here."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle import kvq_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+kvq = pytest.importorskip("bit_kv_cache_groupwise_amd.kvq", reason="libkvq.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    syms = declared_symbols()
+    for name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize", "kvq_plan",
+                 "kvq_cache_create", "kvq_cache_destroy", "kvq_decode_workspace_size", "kvq_status_string"):
+        assert name in syms
+    assert sorted(kvq.EXPORTED) == syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.raw()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", nm))
+    assert set(declared_symbols()) <= exported
+
+
+def test_status_strings_and_version():
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert kvq.kvq_status_string(st)
+    assert kvq.kvq_status_string(12345) == "unknown status"
+    assert re.match(r"\d+\.\d+\.\d+$", kvq.kvq_version())
+
+
+def _geom(**kw):
+    base = dict(layers=2, num_seqs=3, kv_heads=4, q_heads=8, head_dim=128, group_k=32, group_v=32)
+    base.update(kw)
+    return kvq.geometry(**base)
+
+
+@pytest.mark.parametrize("dt,ib", [("f32", 4), ("f16", 2), ("bf16", 2)])
+def test_plan_matches_closed_form(dt, ib):
+    caps = [0, 1000, 4097]
+    bk, bv = [2, 6, 4], [2, 4, 8]
+    g = _geom(in_dtype=dt)
+    sz = kvq.kvq_plan(g, caps, bk, bv)
+    codes = meta = resid = 0
+    for c, k, v in zip(caps, bk, bv):
+        hb = o.head_bytes(c, 128, group_k=32, group_v=32, axis_k=o.AXIS_CHANNEL, axis_v=o.AXIS_TOKEN,
+                          bits_k=k, bits_v=v, in_bytes=ib)
+        codes += hb["codes"]
+        meta += hb["meta"]
+        # the residual region is G rows per channel-axis head, whatever the length
+        resid += 32 * 128 * ib
+    assert sz.formula_codes_bytes == 2 * 4 * codes
+    assert sz.formula_meta_bytes == 2 * 4 * meta
+    assert sz.formula_residual_bytes == 2 * 4 * resid
+    assert sz.codes_bytes >= sz.formula_codes_bytes and sz.codes_bytes % 256 == 0
+    assert sz.meta_bytes >= sz.formula_meta_bytes and sz.residual_bytes >= sz.formula_residual_bytes
+    # padding is at most 255 bytes per head region
+    assert sz.codes_bytes - sz.formula_codes_bytes < 256 * 2 * 3 * 4 * 2
+
+
+def test_plan_gpt2_effective_bits():
+    """GPT-2-shaped cache (K6/V4, per-head 64-channel groups): 5.5 stored bits per
+    element at a length that is a multiple of G, as the hatterialabs.com page
+    prints for this configuration."""
+    g = kvq.geometry(layers=12, num_seqs=8, kv_heads=12, q_heads=12, head_dim=64, group_k=64, group_v=64)
+    sz = kvq.kvq_plan(g, [1024] * 8, [6] * 8, [4] * 8)
+    elems = o.cache_elements(12, 1024 * 8, 12, 64)
+    bits = (sz.formula_codes_bytes + sz.formula_meta_bytes) * 8 / elems
+    assert bits == 5.5
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), -1), (dict(head_dim=512), -1), (dict(q_heads=6), -1), (dict(group_k=16), -1),
+    (dict(group_v=96), -1), (dict(axis_v=2), -1), (dict(in_dtype=7), -1), (dict(layers=0), -1),
+    (dict(head_dim=64, group_v=128), -1), (dict(meta_dtype=0), -2),
+])
+def test_plan_rejects_bad_geometry(kw, status):
+    assert kvq.kvq_plan_status(_geom(**kw), [10, 10, 10], [2, 2, 2], [2, 2, 2]) == status
+    assert kvq.kvq_last_error()
+
+
+@pytest.mark.parametrize("bits", [1, 5, 7, 16, 0])
+def test_plan_rejects_bits(bits):
+    assert kvq.kvq_plan_status(_geom(), [10, 10, 10], [2, bits, 2], [2, 2, 2]) == kvq.KVQ_ERR_ARG
+    assert kvq.kvq_plan_status(_geom(), [10, 10, 10], [2, 2, 2], [bits, 2, 2]) == kvq.KVQ_ERR_ARG
+
+
+def test_plan_rejects_nulls_and_negative_capacity():
+    assert kvq.kvq_plan_status(None, [1, 1, 1], [2] * 3, [2] * 3) == kvq.KVQ_ERR_ARG
+    assert kvq.kvq_plan_status(_geom(), None, [2] * 3, [2] * 3) == kvq.KVQ_ERR_ARG
+    assert kvq.kvq_plan_status(_geom(), [1, -1, 1], [2] * 3, [2] * 3) == kvq.KVQ_ERR_ARG
+
+
+def test_create_validates_before_touching_the_device():
+    g = _geom()
+    args = ([10, 10, 10], [2] * 3, [2] * 3)
+    assert kvq.kvq_cache_create_status(g, *args, 0, 256, 256, 256) == kvq.KVQ_ERR_ARG
+    assert kvq.kvq_cache_create_status(g, *args, 256, 256, 256 + 4, 256) == kvq.KVQ_ERR_ALIGN
+    assert kvq.kvq_cache_create_status(_geom(group_k=7), *args, 256, 256, 256, 256) == kvq.KVQ_ERR_ARG
+
+
+def test_null_handle_calls_fail_cleanly():
+    lib = kvq.raw()
+    assert lib.kvq_quantize_append(None, 0, None, None, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_attention(None, 0, None, ctypes.c_float(1.0), None, None, 0, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_dequantize(None, 0, 0, None, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_workspace_size(None) == 0
+    lib.kvq_cache_destroy(None)

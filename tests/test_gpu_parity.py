@@ -1,0 +1,221 @@
+"""HIP path against the CPU oracle, through the C ABI, on seeded inputs small
+enough for the oracle: packed codes, metadata and residual rows bit-exact,
+dequantization bit-exact, decode attention within 2e-3 (max error of a row
+over the row's largest magnitude, against the fp64 oracle over the quantized
+cache)."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_groupwise_amd import workloads as W
+from oracle import kvq_oracle as o
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases():
+    mixed_lens = (0, 1, 31, 32, 33, 100, 512, 1000, 1500, 2047)
+    mixed_bits = tuple(W.BIT_PAIRS_MIXED[i % 5] for i in range(10))
+    return {
+        # all of the tiny configuration
+        "tiny": W.tiny(),
+        # GPT-2-shaped: 64-channel heads, K6/V4, G=64; a full length and a ragged one
+        "gpt2": W.gpt2_small().scaled(num_seqs=2, layers=2, kv_heads=3, q_heads=3, lengths=(1024, 777),
+                                      bits=((6, 4),) * 2),
+        # Llama-2-7B-shaped: 128-channel heads, 2-bit, G=32
+        "llama": W.llama2_7b().scaled(num_seqs=3, kv_heads=4, q_heads=4, lengths=(4096, 1000, 33),
+                                      bits=((2, 2),) * 3),
+        # long grouped-query shape: 32 query heads over 2 kv heads of 256 channels, bf16, K4/V8
+        "gqa": W.long_gqa().scaled(lengths=(20000,)),
+        # mixed batch: every bit pair, lengths around the block edges, 16-token append
+        "mixed": W.mixed_batch().scaled(num_seqs=10, lengths=mixed_lens, bits=mixed_bits),
+        # the per-token key reading of the long grouped-query configuration
+        "gqa_ktoken": W.long_gqa().scaled(lengths=(3000,), axis_k=o.AXIS_TOKEN),
+        # per-token keys over one 64-channel head
+        "gpt2_ktoken": W.gpt2_small().scaled(num_seqs=2, layers=1, kv_heads=2, q_heads=2, lengths=(300, 64),
+                                             bits=((6, 4),) * 2, axis_k=o.AXIS_TOKEN),
+        # head_dim 32 (one unit per row), 3-bit, fp32 input, groups of 32
+        "d32": W.tiny().scaled(head_dim=32, lengths=(95,), bits=((3, 3),)),
+        # groups of 128 and 256 tokens on the channel axis, G=128 channels on the token axis
+        "bigG": W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=4, lengths=(700, 256), group_k=256,
+                                     group_v=128, bits=((4, 6), (8, 3))),
+    }
+
+
+CASES = _cases()
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run_case(w, layer=0, chunks=None):
+    cache = H.make_cache(w)
+    prefix, new = H.history(w, layer)
+    H.append_chunks(cache, layer, prefix[0], prefix[1], prefix[2], chunks)
+    H.append_chunks(cache, layer, new[0], new[1], new[2])
+    torch.cuda.synchronize()
+    return cache, prefix, new
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity(name):
+    w = CASES[name]
+    _note(f"[parity] case={name} S={w.num_seqs} Hq={w.q_heads} Hkv={w.kv_heads} D={w.head_dim} lens={w.lengths}")
+    layer = w.layers - 1
+    cache, prefix, new = _run_case(w, layer)
+    assert cache.lengths(layer) == [L + w.new_tokens for L in w.lengths]
+    q = W.draw_q(w, layer)
+    out = cache.decode(layer, q.cuda(), w.softmax_scale)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    worst = 0.0
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.assert_head_bytes(cache, w, layer, s, h, k, v) for h in range(w.kv_heads)]
+        # unfused path: bit-exact float32 reconstruction
+        kd, vd = cache.dequantize(layer, s)
+        torch.cuda.synchronize()
+        for h in range(w.kv_heads):
+            np.testing.assert_array_equal(kd[h].cpu().numpy(), encs[h]["k_hat"].astype(np.float32))
+            np.testing.assert_array_equal(vd[h].cpu().numpy(), encs[h]["v_hat"].astype(np.float32))
+        ref = H.attn_ref(w, q[s].float().numpy(), encs)
+        err = H.row_rel_err(out[s], ref)
+        worst = max(worst, float(err.max()))
+        assert np.all(err <= H.ATTN_TOL), (name, s, err.max())
+    _note(f"[parity] case={name} worst row rel err {worst:.3e}")
+    cache.close()
+
+
+def test_chunked_appends_are_history_independent():
+    """Appending the same tokens in chunks of 1, 7, 33 and 100 stores the same
+    bytes as one bulk append (channel-axis blocks complete at the same tokens)."""
+    w = CASES["llama"]
+    for chunks in ([1, 7], [33], [100, 5, 1]):
+        w2 = w.scaled(lengths=(300, 97, 40))
+        cache, prefix, new = _run_case(w2, chunks=chunks)
+        for s in range(w2.num_seqs):
+            k, v = H.full_seq(prefix, new, s)
+            for h in range(w2.kv_heads):
+                H.assert_head_bytes(cache, w2, 0, s, h, k, v)
+        cache.close()
+
+
+def test_nonuniform_append_counts():
+    """One append with different counts per sequence (uploaded count table)."""
+    w = CASES["mixed"].scaled(lengths=(5, 40, 0, 64, 31, 33, 2, 90, 100, 17))
+    cache = H.make_cache(w)
+    prefix, new = H.history(w, 0)
+    H.append_chunks(cache, 0, prefix[0], prefix[1], prefix[2])
+    H.append_chunks(cache, 0, new[0], new[1], new[2])
+    torch.cuda.synchronize()
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        for h in range(w.kv_heads):
+            H.assert_head_bytes(cache, w, 0, s, h, k, v)
+    cache.close()
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256, 512, 1024])
+def test_split_count_invariance(chunk, monkeypatch):
+    """The decode output does not depend on how the tokens are split (up to
+    float32 summation order), and every split size meets the tolerance."""
+    w = CASES["llama"]
+    cache, prefix, new = _run_case(w)
+    q = W.draw_q(w, 0).cuda()
+    base = cache.decode(0, q, w.softmax_scale).cpu().numpy()
+    monkeypatch.setenv("KVQ_DECODE_CHUNK", str(chunk))
+    out = cache.decode(0, q, w.softmax_scale).cpu().numpy()
+    assert np.max(H.row_rel_err(out, base)) < 2e-5
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.encode(w, k, v, s, h) for h in range(w.kv_heads)]
+        ref = H.attn_ref(w, q[s].float().cpu().numpy(), encs)
+        assert np.all(H.row_rel_err(out[s], ref) <= H.ATTN_TOL)
+    cache.close()
+
+
+def test_decode_is_deterministic():
+    w = CASES["gqa"]
+    cache, _, _ = _run_case(w)
+    q = W.draw_q(w, 0).cuda()
+    a = cache.decode(0, q, w.softmax_scale).clone()
+    b = cache.decode(0, q, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    cache.close()
+
+
+def test_closed_forms_on_gpu():
+    """q = 0 gives the mean of the reconstructed values; an empty sequence gives
+    zeros; a single token gives its reconstructed value."""
+    w = CASES["mixed"].scaled(num_seqs=3, lengths=(0, 0, 200), bits=((4, 8),) * 3, new_tokens=1)
+    cache = H.make_cache(w)
+    prefix, new = H.history(w, 0)
+    # sequence 0 stays empty: append only to 1 and 2
+    H.append_chunks(cache, 0, prefix[0], prefix[1], prefix[2])
+    kn, vn, _ = new
+    cache.append(0, kn[1:].cuda().contiguous(), vn[1:].cuda().contiguous(), [0, 1, 1])
+    torch.cuda.synchronize()
+    assert cache.lengths(0) == [0, 1, 201]
+    q = torch.zeros((3, w.q_heads, w.head_dim), dtype=torch.float16, device="cuda")
+    out = cache.decode(0, q, w.softmax_scale).cpu().numpy()
+    assert np.all(out[0] == 0)
+    _, vd1 = cache.dequantize(0, 1)
+    _, vd2 = cache.dequantize(0, 2)
+    R = w.q_heads // w.kv_heads
+    for h in range(w.q_heads):
+        np.testing.assert_allclose(out[1, h], vd1[h // R, 0].cpu().numpy(), rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(out[2, h], vd2[h // R].double().mean(0).cpu().numpy(), rtol=1e-5, atol=1e-5)
+    q = W.draw_q(w, 0).cuda()
+    out = cache.decode(0, q, w.softmax_scale).cpu().numpy()
+    for h in range(w.q_heads):
+        np.testing.assert_allclose(out[1, h], vd1[h // R, 0].cpu().numpy(), rtol=1e-6, atol=1e-6)
+    cache.close()
+
+
+def test_error_paths_leave_the_cache_untouched():
+    k = H.kvq()
+    w = CASES["llama"].scaled(lengths=(10, 20, 30))
+    cache = H.make_cache(w, extra=0)  # capacity = length + 1
+    prefix, new = H.history(w, 0)
+    H.append_chunks(cache, 0, prefix[0], prefix[1], prefix[2])
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (cache.codes, cache.meta, cache.resid)]
+    kn, vn = W.draw_kv(w, 0, [2, 2, 2], stream=3)
+    with pytest.raises(k.KVQError) as ei:
+        cache.append(0, kn.cuda(), vn.cuda(), [2, 2, 2])  # 2 > remaining capacity 1
+    assert ei.value.status == k.KVQ_ERR_CAPACITY
+    with pytest.raises(k.KVQError) as ei:
+        cache.append(0, kn.cuda(), vn.cuda(), [1, -1, 1])
+    assert ei.value.status == k.KVQ_ERR_ARG
+    with pytest.raises(k.KVQError) as ei:
+        cache.append(1, kn.cuda(), vn.cuda(), [1, 1, 1])  # layer out of range
+    assert ei.value.status == k.KVQ_ERR_ARG
+    kb = torch.empty(kn.numel() + 8, dtype=kn.dtype, device="cuda")
+    with pytest.raises(k.KVQError) as ei:
+        cache.append(0, kb[1:1 + kn.numel()], vn.cuda(), [1, 1, 1])  # misaligned rows
+    assert ei.value.status == k.KVQ_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert cache.lengths(0) == [10, 20, 30]
+    for a, b in zip(before, (cache.codes, cache.meta, cache.resid)):
+        assert torch.equal(a, b)
+    q = W.draw_q(w, 0).cuda()
+    out = torch.empty((3, w.q_heads, w.head_dim), device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(k.KVQError) as ei:
+        k.kvq_decode_attention(cache.handle, 0, q, w.softmax_scale, out, ws, 16)
+    assert ei.value.status == k.KVQ_ERR_WORKSPACE
+    cache.close()
+    wide = W.mixed_batch().scaled(num_seqs=1, q_heads=64, kv_heads=2, lengths=(10,), bits=((2, 2),))
+    c2 = H.make_cache(wide)
+    with pytest.raises(k.KVQError) as ei:
+        c2.decode(0, torch.zeros((1, 64, 128), dtype=torch.float16, device="cuda"), 0.1)
+    assert ei.value.status == k.KVQ_ERR_UNSUPPORTED
+    c2.close()
