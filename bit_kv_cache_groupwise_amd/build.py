@@ -24,6 +24,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
+MHA_HEAD_DIMS = (64, 128, 256)
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -45,6 +46,8 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     jobs = [
         [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kvq_kernels.hip"), "-o", os.path.join(BUILD, "kvq_kernels.o")],
+        *[[cc, *COMMON, *DEVICE, f"-DKVQ_MHA_HEAD_DIM={d}", "-c", os.path.join(CSRC, "kvq_decode_mha.hip"), "-o",
+            os.path.join(BUILD, f"kvq_decode_mha_d{d}.o")] for d in MHA_HEAD_DIMS],
         [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", os.path.join(BUILD, "kvq_api.o")],
     ]
     with ThreadPoolExecutor(len(jobs)) as ex:
@@ -53,7 +56,8 @@ def build(verbose: bool = False) -> str:
                 print(r.stdout, r.stderr, file=sys.stderr)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-          os.path.join(BUILD, "kvq_kernels.o"), os.path.join(BUILD, "kvq_api.o")])
+          os.path.join(BUILD, "kvq_kernels.o"), *[os.path.join(BUILD, f"kvq_decode_mha_d{d}.o") for d in MHA_HEAD_DIMS],
+          os.path.join(BUILD, "kvq_api.o")])
     os.replace(tmp, LIB)
     return LIB
 

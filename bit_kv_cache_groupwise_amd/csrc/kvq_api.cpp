@@ -34,6 +34,8 @@ struct kvq_cache {
     std::vector<int32_t> lens;      // host mirror of the current lengths [layers][num_seqs]
     std::vector<uint8_t> parity;    // which length buffer is current, per layer
     std::vector<int32_t> args;      // staging for the call-argument area
+    struct Pair { int bk, bv, offset, count; };
+    std::vector<Pair> pairs;        // distinct (bits_k, bits_v) pairs and their slice of the table's seq list
     int32_t max_cap = 0;
 };
 
@@ -142,7 +144,9 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
     tl->entries_bytes = align_up(LS * sizeof(SeqEntry), kvq::kAlign);
     tl->len_off = tl->entries_bytes;
     tl->args_off = tl->len_off + align_up(2 * LS * 4, kvq::kAlign);
-    tl->total = tl->args_off + align_up(2 * (uint64_t)g->num_seqs * 4, kvq::kAlign);
+    tl->ctr_off = tl->args_off + align_up(2 * (uint64_t)g->num_seqs * 4, kvq::kAlign);
+    tl->pairs_off = tl->ctr_off + align_up((uint64_t)g->num_seqs * g->kv_heads * 4, kvq::kAlign);
+    tl->total = tl->pairs_off + align_up((uint64_t)g->num_seqs * 4, kvq::kAlign);
     sz->codes_bytes = std::max<uint64_t>(oc, kvq::kAlign);
     sz->meta_bytes = std::max<uint64_t>(om, kvq::kAlign);
     sz->residual_bytes = std::max<uint64_t>(orr, kvq::kAlign);
@@ -170,6 +174,22 @@ int choose_chunk(const kvq_cache* c, int max_len) {
     while (C < 1024 && pairs * ((max_len + 2L * C - 1) / (2L * C)) >= 2048) C *= 2;
     while (C > kmin && kvq::decode_lds_bytes(group_size(c), g.head_dim, C) > 65536) C /= 2;
     return C;
+}
+
+// Tokens per workgroup of the single-query kernel: a multiple of 64 and of the
+// key block, about 2048 workgroups in total; a sequence of length L gets
+// max(1, L / chunk) splits, the last one taking the remainder.
+int choose_split_mha(const kvq_cache* c, int max_len) {
+    const kvq_geometry& g = c->g;
+    const int unit = std::max(64, g.group_k);
+    if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
+        const int v = std::atoi(env);
+        if (v >= unit && v % unit == 0 && v <= (1 << 24)) return v;
+    }
+    const long pairs = (long)g.num_seqs * g.kv_heads;
+    const long nsplit = std::max(1L, 2048L / pairs);
+    const long cw = (max_len / nsplit) / unit * unit;
+    return (int)std::max<long>(unit, cw);
 }
 
 int min_chunk(const kvq_cache* c) {
@@ -239,6 +259,17 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
     c->max_cap = *std::max_element(cap, cap + g->num_seqs);
     std::vector<uint8_t> img(c->tl.total, 0);
     std::memcpy(img.data(), c->entries.data(), c->entries.size() * sizeof(SeqEntry));
+    {
+        int32_t* list = (int32_t*)(img.data() + c->tl.pairs_off);
+        int n = 0;
+        for (int bkk : {2, 3, 4, 6, 8})
+            for (int bvv : {2, 3, 4, 6, 8}) {
+                const int start = n;
+                for (int s2 = 0; s2 < g->num_seqs; ++s2)
+                    if (bk[s2] == bkk && bv[s2] == bvv) list[n++] = s2;
+                if (n > start) c->pairs.push_back({bkk, bvv, start, n - start});
+            }
+    }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(d_table, img.data(), img.size(), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -390,8 +421,9 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     const int S = g.num_seqs;
     const int32_t* lens = &c->lens[(size_t)layer * S];
     const int max_len = *std::max_element(lens, lens + S);
-    const int C = choose_chunk(c, max_len);
-    const int max_chunks = std::max(1, (max_len + C - 1) / C);
+    const bool mha = group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
+    const int C = mha ? choose_split_mha(c, max_len) : choose_chunk(c, max_len);
+    const int max_chunks = mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C);
     const uint64_t slots = (uint64_t)S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
     const uint64_t need = ml_bytes + align_up(slots * g.head_dim * 4, kvq::kAlign);
@@ -420,6 +452,22 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     a.in_dtype = g.in_dtype;
     a.chunk = C;
     a.max_chunks = max_chunks;
+    a.counters = (int32_t*)(c->table + c->tl.ctr_off);
+    a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
+    a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
+    if (mha) {
+        for (const auto& pr : c->pairs) {
+            a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
+            hipError_t e = kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+        }
+        if (max_chunks > 1) {
+            a.split_floor = 1;
+            hipError_t e = kvq::launch_merge(a, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+        }
+        return KVQ_OK;
+    }
     hipError_t e = kvq::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "launching decode attention");
     return KVQ_OK;

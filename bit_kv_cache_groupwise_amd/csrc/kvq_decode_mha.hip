@@ -1,0 +1,606 @@
+// Decode attention when every query head has its own kv head (q_heads ==
+// kv_heads), keys on the channel axis and values on the token axis: the
+// decode step is a matrix-vector product per head, so it stays on the VALU
+// and the kernel is organised around HBM streaming.
+//
+// Sources, by page title and section:
+//   [N] nalar.dev, "Kuantisasi KV cache untuk mengurangi memory inferensi
+//       long-context", "Kuantisasi dapat memindahkan pekerjaan ke decode path"
+//       (unpack and apply scales inside the attention kernel)
+//   [U] unite.ai (pt), "O Seu Cache KV Nao Tem um Problema de Bits...",
+//       "Por Que o Cache KV E Onde Isso Morde" (decode reads the whole cache
+//       once per generated token)
+//
+// Work decomposition: workgroup = (split of the token axis, kv head, seq);
+// its 4 waves take interleaved 64-token super-tiles and never synchronise
+// until the end. In a super-tile a lane owns one 32-channel unit (cg) of one
+// token per sub-tile, so a wave reads whole rows with consecutive lanes on
+// consecutive words.
+//
+// Keys: score_t = sum_u [ q.z_b over unit u ] + sum_c (q_c s_bc) code_tc. The
+// per-block vector q_c s_bc and the per-unit sums of q_c z_bc are built once
+// per block by the wave in LDS. Values: o_c = sum_t (p_t s_tg) code_tc +
+// sum_t p_t z_tg.
+//
+// Code application: a masked uint32 holds two codes in its fp16 halves as
+// integers code * 2^sh with sh + B <= 10, i.e. as fp16 subnormals of value
+// code * 2^(sh-24); v_fma_mix_f32 multiplies such a half by an fp32 operand
+// exactly, so one AND yields two products. The 2^(24-sh) factors are folded
+// into the key vector; on the value side the softmax weights carry 2^24 (the
+// reference maximum is lowered by 24) and the code shifts are undone at the end.
+//
+// Softmax: online in the log2 domain with a lazily moved reference maximum
+// (moved only when a score exceeds it by more than 2^8), so rescaling is
+// rare. Splits of one (seq, head) are merged by the last workgroup to finish
+// (agent-scope counter in the cache table, reset by that workgroup).
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ float mix_lo(uint32_t m, float b, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(m), "v"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float mix_hi(uint32_t m, float b, float c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(m), "v"(b), "v"(c));
+    return d;
+}
+
+// Bit position (within its fp16 half) at which channel j of a unit is applied.
+template <int B>
+__host__ __device__ constexpr int code_shift(int j) {
+    if (B == 2) {
+        const int r = j & 15;
+        return r < 5 ? 2 * r : r < 8 ? 2 * (r - 5) : r < 13 ? 2 * (r - 8) : 2 * (r - 13);
+    }
+    if (B == 4) {
+        const int r = j & 7;
+        return r < 2 ? 4 * r : r < 4 ? 4 * (r - 2) : r < 6 ? 4 * (r - 4) : 4 * (r - 6);
+    }
+    return 0;
+}
+
+// Visit the 32 codes of one unit: f.pair<JL, JH>(m) gets a word whose low half
+// holds code_JL << code_shift(JL) and high half code_JH << code_shift(JH);
+// f.one<J>(c) gets code_J in the low half.
+template <int B>
+struct Unit;
+
+template <>
+struct Unit<2> {
+    template <int Q, class F>
+    static __device__ __forceinline__ void word(uint32_t x, F& f) {
+        constexpr int J = 16 * Q;
+        f.template pair<J + 0, J + 8>(x & 0x00030003u);
+        f.template pair<J + 1, J + 9>(x & 0x000c000cu);
+        f.template pair<J + 2, J + 10>(x & 0x00300030u);
+        f.template pair<J + 3, J + 11>(x & 0x00c000c0u);
+        f.template pair<J + 4, J + 12>(x & 0x03000300u);
+        const uint32_t y = x >> 10;
+        f.template pair<J + 5, J + 13>(y & 0x00030003u);
+        f.template pair<J + 6, J + 14>(y & 0x000c000cu);
+        f.template pair<J + 7, J + 15>(y & 0x00300030u);
+    }
+    template <class F>
+    static __device__ __forceinline__ void visit(const uint32_t* w, F& f) {
+        word<0>(w[0], f);
+        word<1>(w[1], f);
+    }
+};
+
+template <>
+struct Unit<4> {
+    template <int Q, class F>
+    static __device__ __forceinline__ void word(uint32_t x, F& f) {
+        constexpr int J = 8 * Q;
+        f.template pair<J + 0, J + 4>(x & 0x000f000fu);
+        f.template pair<J + 1, J + 5>(x & 0x00f000f0u);
+        const uint32_t y = x >> 8;
+        f.template pair<J + 2, J + 6>(y & 0x000f000fu);
+        f.template pair<J + 3, J + 7>(y & 0x00f000f0u);
+    }
+    template <class F>
+    static __device__ __forceinline__ void visit(const uint32_t* w, F& f) {
+        word<0>(w[0], f);
+        word<1>(w[1], f);
+        word<2>(w[2], f);
+        word<3>(w[3], f);
+    }
+};
+
+template <>
+struct Unit<8> {
+    template <int Q, class F>
+    static __device__ __forceinline__ void word(uint32_t x, F& f) {
+        constexpr int J = 4 * Q;
+        f.template pair<J + 0, J + 2>(x & 0x00ff00ffu);
+        f.template pair<J + 1, J + 3>(__builtin_amdgcn_perm(x, x, 0x0c070c05u));
+    }
+    template <class F>
+    static __device__ __forceinline__ void visit(const uint32_t* w, F& f) {
+        word<0>(w[0], f);
+        word<1>(w[1], f);
+        word<2>(w[2], f);
+        word<3>(w[3], f);
+        word<4>(w[4], f);
+        word<5>(w[5], f);
+        word<6>(w[6], f);
+        word<7>(w[7], f);
+    }
+};
+
+// 3- and 6-bit codes straddle words: one bit-field extract per code.
+template <int B>
+struct UnitStraddle {
+    template <int J, class F>
+    static __device__ __forceinline__ void one(const uint32_t* w, F& f) {
+        constexpr int pos = J * B, wi = pos >> 5, sh = pos & 31;
+        uint32_t c;
+        if constexpr (sh + B <= 32) {
+            c = (w[wi] >> sh) & ((1u << B) - 1u);
+        } else {
+            c = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << B) - 1u);
+        }
+        f.template one<J>(c);
+    }
+    template <int J, class F>
+    static __device__ __forceinline__ void rec(const uint32_t* w, F& f) {
+        if constexpr (J < 32) {
+            one<J>(w, f);
+            rec<J + 1>(w, f);
+        }
+    }
+    template <class F>
+    static __device__ __forceinline__ void visit(const uint32_t* w, F& f) {
+        rec<0>(w, f);
+    }
+};
+template <>
+struct Unit<3> : UnitStraddle<3> {};
+template <>
+struct Unit<6> : UnitStraddle<6> {};
+
+// Dot product of one unit's codes with 32 prescaled key weights.
+struct KeyDot {
+    const float* qv;
+    float a0, a1;
+    template <int JL, int JH>
+    __device__ __forceinline__ void pair(uint32_t m) {
+        a0 = mix_lo(m, qv[JL], a0);
+        a1 = mix_hi(m, qv[JH], a1);
+    }
+    template <int J>
+    __device__ __forceinline__ void one(uint32_t c) {
+        if constexpr (J & 1) a1 = mix_lo(c, qv[J], a1);
+        else a0 = mix_lo(c, qv[J], a0);
+    }
+};
+
+// acc[j] += w * code_j * 2^code_shift(j)  (w carries the 2^24 factor).
+struct ValueAxpy {
+    float w;
+    float* acc;
+    template <int JL, int JH>
+    __device__ __forceinline__ void pair(uint32_t m) {
+        acc[JL] = mix_lo(m, w, acc[JL]);
+        acc[JH] = mix_hi(m, w, acc[JH]);
+    }
+    template <int J>
+    __device__ __forceinline__ void one(uint32_t c) {
+        acc[J] = mix_lo(c, w, acc[J]);
+    }
+};
+
+template <int B>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
+    if constexpr (B == 2) {
+        const uint2 v = *(const uint2*)p;
+        w[0] = v.x;
+        w[1] = v.y;
+    } else if constexpr (B == 4) {
+        const uint4 v = *(const uint4*)p;
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    } else if constexpr (B == 8) {
+        const uint4 v0 = *(const uint4*)p;
+        const uint4 v1 = *((const uint4*)p + 1);
+        w[0] = v0.x;
+        w[1] = v0.y;
+        w[2] = v0.z;
+        w[3] = v0.w;
+        w[4] = v1.x;
+        w[5] = v1.y;
+        w[6] = v1.z;
+        w[7] = v1.w;
+    } else if constexpr (B == 6) {
+        const uint2* q = (const uint2*)p;  // a 24-byte unit is 8-byte aligned
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const uint2 v = q[k];
+            w[2 * k] = v.x;
+            w[2 * k + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < B; ++k) w[k] = p[k];
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the N consecutive lanes (N = 2, 4, 8) that hold the units of one token.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f<0xb1>(v);  // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) v += dpp_f<0x4e>(v);  // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+    return v;
+}
+
+// Sum over the 32 lanes of each half-wave.
+__device__ __forceinline__ float half_wave_sum(float v) {
+    v += dpp_f<0xb1>(v);
+    v += dpp_f<0x4e>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);  // row_mirror
+    v += __shfl_xor(v, 16);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float load_in_rt(const void* p, size_t i, int dt) {
+    if (dt == 0) return load_in<0>(p, i);
+    if (dt == 1) return load_in<1>(p, i);
+    return load_in<2>(p, i);
+}
+
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kRescale = 8.0f;  // log2-domain slack before the reference maximum moves
+
+// Registers of one 64-token super-tile: the lane's key and value unit words,
+// value metadata, and the key metadata of the super-tile's blocks.
+template <int D, int BK, int BV>
+struct Stage {
+    static constexpr int UPR = D / 32, KPL = D / 64;
+    uint32_t kw[UPR][BK];
+    uint32_t vw[UPR][BV];
+    uint32_t vmw[UPR];
+    uint32_t kmw[2][KPL];
+};
+
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(kThreads) void decode_mha_kernel(DecodeArgs a) {
+    constexpr int UPR = D / 32;   // units per row = lanes per token
+    constexpr int TPW = 64 / UPR; // tokens per sub-tile
+    constexpr int KPL = D / 64;   // channels per lane in the per-block prologue
+    constexpr int HALF = UPR / 2; // sub-tiles per 32 tokens
+    using St = Stage<D, BK, BV>;
+
+    __shared__ float q_lds[D];
+    __shared__ float qs_lds[4][2][D];
+    __shared__ float bz_lds[4][2][UPR];
+    __shared__ float mrg_o[4][D];
+    __shared__ float mrg_ml[4][2];
+
+    const int seq = a.seq_list ? a.seq_list[blockIdx.z] : (int)blockIdx.z;
+    const int kvh = blockIdx.y, split = blockIdx.x;
+    const int len = a.len[seq];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    float* out = a.out + ((size_t)seq * a.q_heads + kvh) * D;
+    if (len == 0) {
+        if (split == 0)
+            for (int c = tid; c < D; c += kThreads) out[c] = 0.f;
+        return;
+    }
+    const int CW = a.chunk;
+    const int nsplit = max(1, len / CW);
+    if (split >= nsplit) return;
+    const int wa = split * CW, wb = split == nsplit - 1 ? len : wa + CW;
+    const int ts = lane / UPR, cg = lane % UPR;
+    const SeqEntry& e = a.table[seq];
+    const int lgk = a.log2_group_k;
+    const bool two_blocks = lgk == 5;  // a 64-token super-tile spans two 32-token key blocks
+    const int nqk = (len >> lgk) << lgk;
+    const int qend = min(wb, nqk);
+
+    const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
+    const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
+    const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
+    const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
+    const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
+    const int lgv = a.log2_group_v;
+    const int vgpr = D >> lgv;           // value groups per row
+    const int vg = (32 * cg) >> lgv;     // this lane's value group
+
+    for (int c = tid; c < D; c += kThreads)
+        q_lds[c] = load_in_rt(a.q, ((size_t)seq * a.q_heads + kvh) * D + c, a.in_dtype) * a.qscale;
+    __syncthreads();
+
+    // per-lane constants of the per-block prologue: q_c and q_c * 2^(24 - shift(c))
+    float qk[KPL], qks[KPL];
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+        const int c = lane + 64 * k;
+        qk[k] = q_lds[c];
+        qks[k] = qk[k] * (float)(1 << (24 - code_shift<BK>(c & 31)));
+    }
+
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+    // Every weight carries a 2^24 factor (the reference is m - 24), which the
+    // fp16-subnormal code products need; it cancels between o and l.
+    float zacc = 0.f, lsum = 0.f, m = -INFINITY;
+
+    auto load_stage = [&](int st, St& r) {
+        const bool full = st + 64 <= qend;
+#pragma unroll
+        for (int s = 0; s < UPR; ++s) {
+            const int t = st + s * TPW + ts;
+            if (full || t < qend) {
+                load_words<BK>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + cg * BK, r.kw[s]);
+                load_words<BV>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + cg * BV, r.vw[s]);
+                r.vmw[s] = vm[(size_t)t * vgpr + vg];
+            }
+        }
+        const int b0 = st >> lgk;
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl) {
+            if (bl == 0 || (two_blocks && ((b0 + 1) << lgk) < qend)) {
+#pragma unroll
+                for (int k = 0; k < KPL; ++k) r.kmw[bl][k] = km[(size_t)(b0 + bl) * D + lane + 64 * k];
+            }
+        }
+    };
+
+    // Online softmax over this lane's UPR scores (one per sub-tile), then the value rows.
+    auto softmax_and_values = [&](const float (&sc)[UPR], const uint32_t (&vw)[UPR][BV], const uint32_t (&vmw)[UPR],
+                                  const bool (&valid)[UPR]) {
+        float tmax = sc[0];
+#pragma unroll
+        for (int s = 1; s < UPR; ++s) tmax = fmaxf(tmax, sc[s]);
+        if (m == -INFINITY) {
+            m = wave_max_f(tmax);
+        } else if (__any(tmax > m + kRescale)) {
+            const float mn = wave_max_f(tmax);
+            const float alpha = exp2f(m - mn);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) acc[j] *= alpha;
+            zacc *= alpha;
+            lsum *= alpha;
+            m = mn;
+        }
+        const float m24 = m - 24.0f;
+#pragma unroll
+        for (int s = 0; s < UPR; ++s) {
+            if (valid[s]) {
+                const float p = exp2f(sc[s] - m24);
+                lsum += p;
+                zacc = mix_hi(vmw[s], p, zacc);
+                ValueAxpy f{mix_lo(vmw[s], p, 0.f), acc};
+                Unit<BV>::visit(vw[s], f);
+            }
+        }
+    };
+
+    // Key scores of one super-tile; `full` means every token is a quantized key.
+    auto key_scores = [&](int st, const St& r, bool full, float (&sc)[UPR], bool (&valid)[UPR]) {
+        const int b0 = st >> lgk;
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl) {
+            if (bl == 0 || (two_blocks && ((b0 + 1) << lgk) < qend)) {
+#pragma unroll
+                for (int k = 0; k < KPL; ++k) {
+                    const uint32_t w = r.kmw[bl][k];
+                    qs_lds[wave][bl][lane + 64 * k] = mix_lo(w, qks[k], 0.f);
+                    const float pz = half_wave_sum(mix_hi(w, qk[k], 0.f));
+                    if ((lane & 31) == 0) bz_lds[wave][bl][2 * k + (lane >> 5)] = pz;
+                }
+            }
+        }
+        wave_sync_lds();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int bl = two_blocks ? h : 0;
+            float qv[32];
+            const float4* src = (const float4*)&qs_lds[wave][bl][32 * cg];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = src[k];
+                qv[4 * k] = v.x;
+                qv[4 * k + 1] = v.y;
+                qv[4 * k + 2] = v.z;
+                qv[4 * k + 3] = v.w;
+            }
+            const float bzv = bz_lds[wave][bl][cg];
+#pragma unroll
+            for (int s = h * HALF; s < (h + 1) * HALF; ++s) {
+                valid[s] = full || st + s * TPW + ts < qend;
+                float part = 0.f;
+                if (valid[s]) {
+                    KeyDot f{qv, bzv, 0.f};
+                    Unit<BK>::visit(r.kw[s], f);
+                    part = f.a0 + f.a1;
+                }
+                part = group_sum<UPR>(part);
+                sc[s] = valid[s] ? part : -INFINITY;
+            }
+        }
+        wave_sync_lds();  // qs_lds is rewritten by the next super-tile
+    };
+
+    auto compute_stage = [&](int st, const St& r) {
+        float sc[UPR];
+        bool valid[UPR];
+        if (st + 64 <= qend) {
+            key_scores(st, r, true, sc, valid);
+        } else {
+            key_scores(st, r, false, sc, valid);
+        }
+        softmax_and_values(sc, r.vw, r.vmw, valid);
+    };
+
+    // ---- quantized keys: super-tiles of 64 tokens interleaved across waves,
+    // the next one's loads in flight while the current one is computed
+    {
+        St ra, rb;
+        int st = wa + 64 * wave;
+        if (st < qend) load_stage(st, ra);
+        while (st < qend) {
+            const int s1 = st + 4 * 64;
+            if (s1 < qend) load_stage(s1, rb);
+            compute_stage(st, ra);
+            st = s1;
+            if (st >= qend) break;
+            const int s2 = st + 4 * 64;
+            if (s2 < qend) load_stage(s2, ra);
+            compute_stage(st, rb);
+            st = s2;
+        }
+    }
+
+    // ---- residual keys (input dtype), fewer than G tokens, one wave
+    if (wave == 0) {
+        for (int st = max(wa, nqk); st < wb; st += 64) {
+            uint32_t vw[UPR][BV], vmw[UPR];
+            float sc[UPR];
+            bool valid[UPR];
+#pragma unroll
+            for (int s = 0; s < UPR; ++s) {
+                const int t = st + s * TPW + ts;
+                valid[s] = t < wb;
+                float part = 0.f;
+                if (valid[s]) {
+                    load_words<BV>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + cg * BV, vw[s]);
+                    vmw[s] = vm[(size_t)t * vgpr + vg];
+                    const size_t base = (size_t)(t & ((1 << lgk) - 1)) * D + 32 * cg;
+                    float x[32];
+                    if (a.in_dtype == 0) {
+#pragma unroll
+                        for (int j = 0; j < 32; ++j) x[j] = load_in<0>(kr, base + j);
+                    } else if (a.in_dtype == 1) {
+#pragma unroll
+                        for (int j = 0; j < 32; ++j) x[j] = load_in<1>(kr, base + j);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 32; ++j) x[j] = load_in<2>(kr, base + j);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                }
+                part = group_sum<UPR>(part);
+                sc[s] = valid[s] ? part : -INFINITY;
+            }
+            softmax_and_values(sc, vw, vmw, valid);
+        }
+    }
+
+    // ---- wave result: undo the code shifts, add the zero-point sums, reduce over tokens
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = acc[j] * (float)(1 << (24 - code_shift<BV>(j))) + zacc;
+#pragma unroll
+    for (int off = UPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[j] += __shfl_xor(acc[j], off);
+        lsum += __shfl_xor(lsum, off);
+    }
+    if (ts == 0) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) mrg_o[wave][32 * cg + j] = acc[j];
+    }
+    if (lane == 0) {
+        mrg_ml[wave][0] = m;
+        mrg_ml[wave][1] = lsum;
+    }
+    __syncthreads();
+
+    // ---- merge the 4 waves; several splits are merged by merge_kernel
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_ml[w][0]);
+    float L = 0.f, wgt[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        wgt[w] = mrg_ml[w][0] == -INFINITY ? 0.f : exp2f(mrg_ml[w][0] - M);
+        L = fmaf(mrg_ml[w][1], wgt[w], L);
+    }
+    if (nsplit == 1) {
+        const float inv = 1.0f / L;
+        for (int c = tid; c < D; c += kThreads) {
+            float o = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o = fmaf(mrg_o[w][c], wgt[w], o);
+            out[c] = o * inv;
+        }
+        return;
+    }
+    const size_t slot = ((size_t)seq * a.q_heads + kvh) * a.max_chunks + split;
+    for (int c = tid; c < D; c += kThreads) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o = fmaf(mrg_o[w][c], wgt[w], o);
+        a.ws_o[slot * D + c] = o;
+    }
+    if (tid == 0) {
+        a.ws_ml[slot * 2 + 0] = M;
+        a.ws_ml[slot * 2 + 1] = L;
+    }
+}
+
+template <int D, int BK>
+hipError_t launch_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
+    switch (bv) {
+        case 2: hipLaunchKernelGGL((decode_mha_kernel<D, BK, 2>), grid, dim3(kThreads), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_mha_kernel<D, BK, 3>), grid, dim3(kThreads), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_mha_kernel<D, BK, 4>), grid, dim3(kThreads), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((decode_mha_kernel<D, BK, 6>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_mha_kernel<D, BK, 8>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s) {
+    switch (bk) {
+        case 2: return launch_bv<D, 2>(a, bv, grid, s);
+        case 3: return launch_bv<D, 3>(a, bv, grid, s);
+        case 4: return launch_bv<D, 4>(a, bv, grid, s);
+        case 6: return launch_bv<D, 6>(a, bv, grid, s);
+        default: return launch_bv<D, 8>(a, bv, grid, s);
+    }
+}
+
+}  // namespace
+
+// This file is compiled once per head_dim (KVQ_MHA_HEAD_DIM = 64, 128, 256).
+#define KVQ_CAT2(a, b) a##b
+#define KVQ_CAT(a, b) KVQ_CAT2(a, b)
+hipError_t KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
+                                                          hipStream_t s) {
+    dim3 grid(a.max_chunks, a.kv_heads, nseqs);
+    return launch_bk<KVQ_MHA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
+}
+
+}  // namespace kvq

@@ -1,0 +1,155 @@
+// Device helpers shared by the HIP kernels of libkvq (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace dev {
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float((bits16 & 0xffffu) << 16);
+}
+
+// Input dtype tags: 0 = f32, 1 = f16, 2 = bf16.
+template <int DT> struct In;
+template <> struct In<0> { static constexpr int bytes = 4; };
+template <> struct In<1> { static constexpr int bytes = 2; };
+template <> struct In<2> { static constexpr int bytes = 2; };
+
+template <int DT>
+__device__ __forceinline__ float load_in(const void* p, size_t i) {
+    if constexpr (DT == 0) {
+        return ((const float*)p)[i];
+    } else if constexpr (DT == 1) {
+        return f16_to_f32(((const uint16_t*)p)[i]);
+    } else {
+        return bf16_to_f32(((const uint16_t*)p)[i]);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float half_to_f32(uint32_t h) {
+    if constexpr (DT == 1) return f16_to_f32(h);
+    else return bf16_to_f32(h);
+}
+
+// 32 consecutive input elements starting at element `off` (16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void load32(const void* base, size_t off, float (&x)[32]) {
+    if constexpr (DT == 0) {
+        const uint4* p = (const uint4*)((const float*)base + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 v = p[i];
+            x[4 * i + 0] = __uint_as_float(v.x);
+            x[4 * i + 1] = __uint_as_float(v.y);
+            x[4 * i + 2] = __uint_as_float(v.z);
+            x[4 * i + 3] = __uint_as_float(v.w);
+        }
+    } else {
+        const uint4* p = (const uint4*)((const uint16_t*)base + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = p[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[8 * i + 2 * k + 0] = half_to_f32<DT>(w[k]);
+                x[8 * i + 2 * k + 1] = half_to_f32<DT>(w[k] >> 16);
+            }
+        }
+    }
+}
+
+// Code of one value against the stored grid (step s, zero z), L = 2^B - 1.
+__device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float L) {
+    if (s == 0.0f) return 0u;
+    float t = rintf((x - z) / s);
+    t = fminf(fmaxf(t, 0.0f), L);
+    return (uint32_t)t;
+}
+
+// Pack 32 codes into the B words of one unit: code j at stream bits [jB, jB+B).
+template <int B>
+__device__ __forceinline__ void pack32(const uint32_t (&c)[32], uint32_t (&w)[B]) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+        w[wi] |= c[j] << sh;
+        if (sh + B > 32) w[wi + 1] |= c[j] >> (32 - sh);
+    }
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[B], int j) {
+    const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+    uint32_t v = w[wi] >> sh;
+    if (sh + B > 32) v |= w[wi + 1] << (32 - sh);
+    return v & ((1u << B) - 1u);
+}
+
+template <int B>
+__device__ __forceinline__ void load_unit(const uint32_t* p, uint32_t (&w)[B]) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = p[k];
+}
+
+template <int B>
+__device__ __forceinline__ void store_codes(const uint32_t (&c)[32], uint32_t* dst) {
+    uint32_t w[B];
+    pack32<B>(c, w);
+#pragma unroll
+    for (int k = 0; k < B; ++k) dst[k] = w[k];
+}
+
+__device__ __forceinline__ void store_codes_rt(int B, const uint32_t (&c)[32], uint32_t* dst) {
+    switch (B) {
+        case 2: store_codes<2>(c, dst); break;
+        case 3: store_codes<3>(c, dst); break;
+        case 4: store_codes<4>(c, dst); break;
+        case 6: store_codes<6>(c, dst); break;
+        default: store_codes<8>(c, dst); break;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Workgroup-wide reductions over 256 threads (4 waves); `scratch` holds 4 floats.
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+    v = wave_sum(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+}
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
+}
+
+}  // namespace dev
+}  // namespace kvq

@@ -33,8 +33,10 @@ static_assert(sizeof(SeqEntry) == 112, "SeqEntry layout");
 //   [0, entries_bytes)                 SeqEntry[layers][num_seqs]
 //   [len_off, +2*layers*num_seqs*4)    int32 lengths[2][layers][num_seqs] (double buffered)
 //   [args_off, +2*num_seqs*4)          int32 call args: n_new[num_seqs], row_start[num_seqs]
+//   [ctr_off, +num_seqs*kv_heads*4)    int32 split counters of the decode merge (zero between calls)
+//   [pairs_off, +num_seqs*4)           int32 sequence indices grouped by (bits_k, bits_v) pair
 struct TableLayout {
-    uint64_t entries_bytes, len_off, args_off, total;
+    uint64_t entries_bytes, len_off, args_off, ctr_off, pairs_off, total;
 };
 
 // Per-launch description of one tensor (K = 0 or V = 1) of one layer.
@@ -69,6 +71,10 @@ struct DecodeArgs {
     int32_t group_k, group_v, axis_k, axis_v, in_dtype;
     int32_t chunk;              // tokens per split (multiple of group_k when axis_k is channel)
     int32_t max_chunks;         // chunks per (seq, head) the workspace is laid out for
+    const int32_t* seq_list;    // blockIdx.z -> sequence (single-query kernel), or nullptr
+    int32_t* counters;          // [num_seqs][kv_heads] split counters (reserved)
+    int32_t split_floor;        // splits per seq: 0 -> ceil(len/chunk), 1 -> max(1, len/chunk)
+    int32_t log2_group_k, log2_group_v;
 };
 
 struct DequantArgs {
@@ -83,6 +89,16 @@ struct DequantArgs {
 hipError_t launch_quant_token_axis(const TensorArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mha_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_mha_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_mha_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+inline bool mha_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
+    return a.head_dim == 64    ? launch_decode_mha_d64(a, bits_k, bits_v, nseqs, s)
+           : a.head_dim == 128 ? launch_decode_mha_d128(a, bits_k, bits_v, nseqs, s)
+                               : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
+}
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -152,10 +152,11 @@ def test_decode_is_deterministic():
     cache.close()
 
 
-def test_closed_forms_on_gpu():
+@pytest.mark.parametrize("q_heads", [64, 8])
+def test_closed_forms_on_gpu(q_heads):
     """q = 0 gives the mean of the reconstructed values; an empty sequence gives
     zeros; a single token gives its reconstructed value."""
-    w = CASES["mixed"].scaled(num_seqs=3, lengths=(0, 0, 200), bits=((4, 8),) * 3, new_tokens=1)
+    w = CASES["mixed"].scaled(num_seqs=3, lengths=(0, 0, 200), bits=((4, 8),) * 3, new_tokens=1, q_heads=q_heads)
     cache = H.make_cache(w)
     prefix, new = H.history(w, 0)
     # sequence 0 stays empty: append only to 1 and 2
@@ -219,3 +220,44 @@ def test_error_paths_leave_the_cache_untouched():
         c2.decode(0, torch.zeros((1, 64, 128), dtype=torch.float16, device="cuda"), 0.1)
     assert ei.value.status == k.KVQ_ERR_UNSUPPORTED
     c2.close()
+
+
+MHA_BITS = ((2, 2), (3, 3), (4, 4), (6, 4), (4, 8), (8, 2), (2, 6), (3, 8), (6, 6), (8, 8))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("chunk", [None, "64"])
+def test_single_query_matrix(head_dim, chunk, monkeypatch):
+    """One query head per kv head: every bit width for K and V, several pairs
+    in one batch, ragged lengths around block edges, forced multi-split merges."""
+    if chunk:
+        monkeypatch.setenv("KVQ_DECODE_CHUNK", chunk)
+    lens = (1, 31, 33, 64, 300, 1031, 95, 2, 640, 129)
+    w = W.llama2_7b().scaled(num_seqs=10, kv_heads=2, q_heads=2, head_dim=head_dim, lengths=lens, bits=MHA_BITS,
+                             in_dtype="bf16" if head_dim == 256 else "f16")
+    _note(f"[mha] D={head_dim} chunk={chunk}")
+    cache, prefix, new = _run_case(w)
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.encode(w, k, v, s, h) for h in range(w.kv_heads)]
+        ref = H.attn_ref(w, q[s].float().numpy(), encs)
+        err = H.row_rel_err(out[s], ref)
+        assert np.all(err <= H.ATTN_TOL), (head_dim, chunk, s, w.bits[s], err.max())
+    cache.close()
+
+
+@pytest.mark.parametrize("group_k", [64, 128])
+def test_single_query_large_key_blocks(group_k):
+    w = W.llama2_7b().scaled(num_seqs=3, kv_heads=3, q_heads=3, lengths=(1000, 129, 4000), group_k=group_k,
+                             bits=((2, 4), (4, 2), (3, 3)))
+    cache, prefix, new = _run_case(w)
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.assert_head_bytes(cache, w, 0, s, h, k, v) for h in range(w.kv_heads)]
+        err = H.row_rel_err(out[s], H.attn_ref(w, q[s].float().numpy(), encs))
+        assert np.all(err <= H.ATTN_TOL), (group_k, s, err.max())
+    cache.close()
