@@ -177,7 +177,7 @@ int choose_chunk(const kvq_cache* c, int max_len) {
 }
 
 // Tokens per workgroup of the single-query kernel: a multiple of 64 and of the
-// key block, about 2048 workgroups in total; a sequence of length L gets
+// key block; a sequence of length L gets
 // max(1, L / chunk) splits, the last one taking the remainder.
 int choose_split_mha(const kvq_cache* c, int max_len) {
     const kvq_geometry& g = c->g;
@@ -186,8 +186,10 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
         const int v = std::atoi(env);
         if (v >= unit && v % unit == 0 && v <= (1 << 24)) return v;
     }
+    // Aim at ~512 workgroups (two 4-wave workgroups per compute unit, resident
+    // at once): long waves keep per-wave setup and the split merge small.
     const long pairs = (long)g.num_seqs * g.kv_heads;
-    const long nsplit = std::max(1L, 2048L / pairs);
+    const long nsplit = std::max(1L, 512L / pairs);
     const long cw = (max_len / nsplit) / unit * unit;
     return (int)std::max<long>(unit, cw);
 }
@@ -453,6 +455,7 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     a.chunk = C;
     a.max_chunks = max_chunks;
     a.counters = (int32_t*)(c->table + c->tl.ctr_off);
+    a.waves_per_group = 4;
     a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
     if (mha) {

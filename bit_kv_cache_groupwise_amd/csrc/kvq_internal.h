@@ -75,6 +75,7 @@ struct DecodeArgs {
     int32_t* counters;          // [num_seqs][kv_heads] split counters (reserved)
     int32_t split_floor;        // splits per seq: 0 -> ceil(len/chunk), 1 -> max(1, len/chunk)
     int32_t log2_group_k, log2_group_v;
+    int32_t waves_per_group;    // single-query kernel: waves per workgroup (4)
 };
 
 struct DequantArgs {

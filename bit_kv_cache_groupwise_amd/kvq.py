@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIBRARY selects another build of the same library (benchmarking variants).
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_kv_cache_groupwise_amd.build`")
 _lib = ctypes.CDLL(LIB_PATH)
