@@ -59,6 +59,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=256,
+                    help="plain device copy of this size before timing (calibrates HBM byte counters); 0 = none")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -108,6 +110,16 @@ def main():
         qz_bytes += H * (2 * T * D * ib + algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v,
                                                                  bk, bv, ib))
     quantize_gbps = qz_bytes / (np.median(qz_ms) * 1e-3) / 1e9
+
+    # ---- calibration copy: a plain device-to-device copy of known size whose
+    # FETCH_SIZE / WRITE_SIZE counters scale the decode kernel's (see profiles/)
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- per-step inputs, drawn up front
     new_k, new_v, qs = [], [], []
@@ -192,13 +204,39 @@ def main():
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
         "prefill_tokens": prefill_tokens,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "kvq_decode_attention (split + merge)",
-                     "bytes_per_launch": int(np.mean(dec_bytes))},
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "kvq_decode_attention", "bytes_per_launch": int(np.mean(dec_bytes))},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
     print(json.dumps(result), flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; a counter summary taken on other sources is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_kv_cache_groupwise_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary
+    (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE of the decode
+    kernel, each divided by the bytes-per-byte factor the same counter reads on
+    a plain copy of known size), or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(w, budget_s):
