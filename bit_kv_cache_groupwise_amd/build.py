@@ -48,15 +48,18 @@ def build(verbose: bool = False) -> str:
         [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kvq_kernels.hip"), "-o", os.path.join(BUILD, "kvq_kernels.o")],
         *[[cc, *COMMON, *DEVICE, f"-DKVQ_MHA_HEAD_DIM={d}", "-c", os.path.join(CSRC, "kvq_decode_mha.hip"), "-o",
             os.path.join(BUILD, f"kvq_decode_mha_d{d}.o")] for d in MHA_HEAD_DIMS],
+        *[[cc, *COMMON, *DEVICE, f"-DKVQ_GQA_HEAD_DIM={d}", "-c", os.path.join(CSRC, "kvq_decode_gqa.hip"), "-o",
+            os.path.join(BUILD, f"kvq_decode_gqa_d{d}.o")] for d in MHA_HEAD_DIMS],
         [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", os.path.join(BUILD, "kvq_api.o")],
     ]
-    with ThreadPoolExecutor(len(jobs)) as ex:
+    with ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 4)) as ex:
         for r in ex.map(_run, jobs):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout, r.stderr, file=sys.stderr)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
           os.path.join(BUILD, "kvq_kernels.o"), *[os.path.join(BUILD, f"kvq_decode_mha_d{d}.o") for d in MHA_HEAD_DIMS],
+          *[os.path.join(BUILD, f"kvq_decode_gqa_d{d}.o") for d in MHA_HEAD_DIMS],
           os.path.join(BUILD, "kvq_api.o")])
     os.replace(tmp, LIB)
     return LIB

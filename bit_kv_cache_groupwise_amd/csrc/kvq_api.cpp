@@ -194,6 +194,21 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
     return (int)std::max<long>(unit, cw);
 }
 
+// Tokens per workgroup of the query-group kernel: a multiple of 128 (4 waves x
+// 32-token tiles) and of the key block, about 1024 workgroups in total.
+int choose_split_gqa(const kvq_cache* c, int max_len) {
+    const kvq_geometry& g = c->g;
+    const int unit = std::max(128, g.group_k);
+    if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
+        const int v = std::atoi(env);
+        if (v >= unit && v % unit == 0 && v <= (1 << 24)) return v;
+    }
+    const long pairs = (long)g.num_seqs * g.kv_heads;
+    const long nsplit = std::max(1L, 1024L / pairs);
+    const long cw = (max_len + nsplit - 1) / nsplit;
+    return (int)std::max<long>(unit, (cw + unit - 1) / unit * unit);
+}
+
 int min_chunk(const kvq_cache* c) {
     return c->g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, c->g.group_k) : 64;
 }
@@ -424,7 +439,11 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     const int32_t* lens = &c->lens[(size_t)layer * S];
     const int max_len = *std::max_element(lens, lens + S);
     const bool mha = group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
-    const int C = mha ? choose_split_mha(c, max_len) : choose_chunk(c, max_len);
+    bool gqa = group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
+               kvq::mha_supported(g.head_dim);
+    for (const auto& pr : c->pairs)  // a lane's key channels must start on a word boundary
+        gqa = gqa && (g.head_dim * pr.bk) % 128 == 0;
+    const int C = mha ? choose_split_mha(c, max_len) : gqa ? choose_split_gqa(c, max_len) : choose_chunk(c, max_len);
     const int max_chunks = mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C);
     const uint64_t slots = (uint64_t)S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
@@ -469,6 +488,17 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
             hipError_t e = kvq::launch_merge(a, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching the split merge");
         }
+        return KVQ_OK;
+    }
+    if (gqa) {
+        for (const auto& pr : c->pairs) {
+            a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
+            hipError_t e = kvq::launch_decode_gqa(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+        }
+        a.split_floor = 0;
+        hipError_t e = kvq::launch_merge(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "launching the split merge");
         return KVQ_OK;
     }
     hipError_t e = kvq::launch_decode(a, (hipStream_t)stream);

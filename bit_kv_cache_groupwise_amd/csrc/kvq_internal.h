@@ -94,6 +94,14 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mha_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_mha_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_mha_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_gqa_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_gqa_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_gqa_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+inline hipError_t launch_decode_gqa(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
+    return a.head_dim == 64    ? launch_decode_gqa_d64(a, bits_k, bits_v, nseqs, s)
+           : a.head_dim == 128 ? launch_decode_gqa_d128(a, bits_k, bits_v, nseqs, s)
+                               : launch_decode_gqa_d256(a, bits_k, bits_v, nseqs, s);
+}
 inline bool mha_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     return a.head_dim == 64    ? launch_decode_mha_d64(a, bits_k, bits_v, nseqs, s)
