@@ -195,18 +195,21 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
 }
 
 // Tokens per workgroup of the query-group kernel: a multiple of 128 (4 waves x
-// 32-token tiles) and of the key block, about 1024 workgroups in total.
-int choose_split_gqa(const kvq_cache* c, int max_len) {
+// 32-token tiles), at least 512 (4 tiles per wave, so the register pipeline
+// and the per-workgroup setup pay off), and about 512 workgroups per launch
+// (two resident per compute unit): one launch per (bits_k, bits_v) pair.
+int choose_split_gqa(const kvq_cache* c, const int32_t* lens) {
     const kvq_geometry& g = c->g;
-    const int unit = std::max(128, g.group_k);
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
-        if (v >= unit && v % unit == 0 && v <= (1 << 24)) return v;
+        if (v >= 128 && v % 128 == 0 && v <= (1 << 24)) return v;
     }
-    const long pairs = (long)g.num_seqs * g.kv_heads;
-    const long nsplit = std::max(1L, 1024L / pairs);
-    const long cw = (max_len + nsplit - 1) / nsplit;
-    return (int)std::max<long>(unit, (cw + unit - 1) / unit * unit);
+    long total = 0;
+    for (int s = 0; s < g.num_seqs; ++s) total += lens[s];
+    const long per_launch = total * g.kv_heads / std::max<long>(1, (long)c->pairs.size());
+    long cw = (per_launch + 511) / 512;
+    cw = std::max(512L, (cw + 127) / 128 * 128);
+    return (int)std::min<long>(cw, 1L << 24);
 }
 
 int min_chunk(const kvq_cache* c) {
@@ -443,7 +446,7 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
                kvq::mha_supported(g.head_dim);
     for (const auto& pr : c->pairs)  // a lane's key channels must start on a word boundary
         gqa = gqa && (g.head_dim * pr.bk) % 128 == 0;
-    const int C = mha ? choose_split_mha(c, max_len) : gqa ? choose_split_gqa(c, max_len) : choose_chunk(c, max_len);
+    const int C = mha ? choose_split_mha(c, max_len) : gqa ? choose_split_gqa(c, lens) : choose_chunk(c, max_len);
     const int max_chunks = mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C);
     const uint64_t slots = (uint64_t)S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);

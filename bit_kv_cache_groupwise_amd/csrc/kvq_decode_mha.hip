@@ -31,8 +31,8 @@
 //
 // Softmax: online in the log2 domain with a lazily moved reference maximum
 // (moved only when a score exceeds it by more than 2^8), so rescaling is
-// rare. Splits of one (seq, head) are merged by the last workgroup to finish
-// (agent-scope counter in the cache table, reset by that workgroup).
+// rare. Splits of one (seq, head) are merged by merge_kernel; a sequence that
+// fits one split is written directly.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 

@@ -368,7 +368,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 // Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
 // out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
+    // grid = (q_heads, num_seqs, ceil(D / 64)): 64 channels per workgroup, its
+    // 4 waves take every 4th split and meet in LDS.
     const int hq = blockIdx.x, seq = blockIdx.y, D = a.head_dim;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = blockIdx.z * 64 + lane;
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
     if (a.split_floor) {
@@ -377,21 +381,35 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     }
     const int nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     if (nch == 0) {
-        for (int ch = threadIdx.x; ch < D; ch += kThreads) out[ch] = 0.f;
+        if (wave == 0 && c < D) out[c] = 0.f;
         return;
     }
     const size_t base = ((size_t)seq * a.q_heads + hq) * a.max_chunks;
     const float* ml = a.ws_ml + base * 2;
     float M = -INFINITY;
-    for (int i = 0; i < nch; ++i) M = fmaxf(M, ml[2 * i]);
+    for (int i = lane; i < nch; i += 64) M = fmaxf(M, ml[2 * i]);
+    M = wave_max(M);
     float L = 0.f;
-    for (int i = 0; i < nch; ++i) L += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
-    const float inv = 1.0f / L;
-    for (int ch = threadIdx.x; ch < D; ch += kThreads) {
-        float o = 0.f;
-        for (int i = 0; i < nch; ++i) o = fmaf(a.ws_o[(base + i) * D + ch], exp2f(ml[2 * i] - M), o);
-        out[ch] = o * inv;
+    for (int i = lane; i < nch; i += 64) L += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
+    L = wave_sum(L);
+    float o = 0.f;
+    if (c < D) {
+        const float* src = a.ws_o + base * D + c;
+        int i = wave;
+        for (; i + 12 < nch; i += 16) {
+            const float v0 = src[(size_t)i * D], v1 = src[(size_t)(i + 4) * D];
+            const float v2 = src[(size_t)(i + 8) * D], v3 = src[(size_t)(i + 12) * D];
+            o = fmaf(v0, exp2f(ml[2 * i] - M), o);
+            o = fmaf(v1, exp2f(ml[2 * (i + 4)] - M), o);
+            o = fmaf(v2, exp2f(ml[2 * (i + 8)] - M), o);
+            o = fmaf(v3, exp2f(ml[2 * (i + 12)] - M), o);
+        }
+        for (; i < nch; i += 4) o = fmaf(src[(size_t)i * D], exp2f(ml[2 * i] - M), o);
     }
+    __shared__ float part[4][64];
+    part[wave][lane] = o;
+    __syncthreads();
+    if (wave == 0 && c < D) out[c] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / L;
 }
 
 // ---------------------------------------------------------------------------
@@ -483,7 +501,7 @@ hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 63) / 64), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -498,7 +516,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 63) / 64), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
