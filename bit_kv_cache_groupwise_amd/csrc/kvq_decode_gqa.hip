@@ -92,6 +92,27 @@ __device__ __forceinline__ float rem_hi(uint32_t h, float x) {
 __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
+// a * half_S(b) - half_S(c), one rounding (S selects the low or high halves).
+__device__ __forceinline__ float mix3_lo(float a, uint32_t b, uint32_t c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float mix3_hi(float a, uint32_t b, uint32_t c) {
+    float d;
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
+}
+// (a0, a1) * (s0, s1) as hi + lo fp16 pairs: hi = fp16 product of the fp16
+// pair ah ~= (a0, a1) and s; lo = fp16 of the exact rest a * s - hi.
+__device__ __forceinline__ void mul_split(uint32_t ah, float a0, float a1, uint32_t sp, uint32_t& hi, uint32_t& lo) {
+    hi = pk_mul(ah, sp);
+    lo = pk_rtz(mix3_lo(a0, sp, hi), mix3_hi(a1, sp, hi));
+}
 // (x0, x1) ~= hi + lo with hi = fp16 truncation and lo = fp16 of the exact rest.
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     hi = pk_rtz(x0, x1);
@@ -255,16 +276,21 @@ __device__ __forceinline__ void store_lds_n(uint32_t* p, const uint32_t* w) {
 
 constexpr int pow2_align(int bytes) { return (bytes & 15) == 0 ? 16 : (bytes & 7) == 0 ? 8 : (bytes & 3) == 0 ? 4 : 1; }
 
-// Sums and maxima over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48).
+// Sums and maxima over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48),
+// with the row-swap permutes (no LDS round trip): after permlane16_swap(v, v)
+// the two results hold rows (0,0,2,2) and (1,1,3,3); after permlane32_swap(v, v)
+// they hold halves (lo, lo) and (hi, hi).
 __device__ __forceinline__ float col4_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float col4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -288,30 +314,48 @@ constexpr float kTwo16 = 65536.0f;
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kFarBelow = -1.0e30f;  // initial reference maximum: exp2(score - kFarBelow) never taken
 
+// Channels per wave: the workgroup's waves share each tile, wave w taking
+// channels [w*DW, (w+1)*DW) of the head. A lane group of a wave must own whole
+// key words, so 3-bit keys take 128 channels per wave.
+template <int BK>
+constexpr int wave_channels() { return BK == 3 ? 128 : 64; }
+
+__device__ __forceinline__ void wg_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D, int BK, int BV>
-__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
-    constexpr int NW = 4, NT = 256;
-    constexpr int DQ = D / 4;            // key channels of one lane group (lg)
-    constexpr int NCH = D / 32;          // 8-channel MFMA chunks per lane group
-    constexpr int NSUB = D / 16;         // 16-column output tiles
-    constexpr int KWL = DQ * BK / 32;    // key words of a lane per token
-    constexpr int VROW = D + 8;          // bytes per token row of the value tile
-    constexpr int UPL = D / 64;          // value units per lane per tile (32 tokens x D/32 units)
-    constexpr int UPR = D / 32;          // value units per token
-    constexpr int KM = D / 64;           // key metadata words per lane per block
+__global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kernel(DecodeArgs a) {
+    constexpr int DW = wave_channels<BK>();  // channels of this wave
+    constexpr int NWV = D / DW;               // waves per workgroup (they share every tile)
+    constexpr int NT = 64 * NWV;
+    constexpr int DQ = DW / 4;                // key channels of one lane group (lg)
+    constexpr int NCH = DQ / 8;               // 8-channel MFMA chunks per lane group
+    constexpr int NSUB = DW / 16;             // 16-column output tiles of the wave
+    constexpr int KWL = DQ * BK / 32;         // key words of a lane per token
+    constexpr int VROW = DW + 8;              // bytes per token row of the wave's value tile
+    constexpr int UPW = DW / 32;              // value units of the wave per token
+    constexpr int UPL = UPW / 2;              // value units per lane per tile (32 tokens)
+    constexpr int NVML = DW / 64;             // value metadata words per lane per tile
+    constexpr int ZROW = 40;                  // halves per row of the zero-point tile (padded)
     constexpr int KALIGN = pow2_align(D * BK / 8) < pow2_align(KWL * 4) ? pow2_align(D * BK / 8) : pow2_align(KWL * 4);
     constexpr int VALIGN = pow2_align(D * BV / 8) < pow2_align(BV * 4) ? pow2_align(D * BV / 8) : pow2_align(BV * 4);
     constexpr int NSH = BK == 2 ? 4 : BK == 4 ? 2 : 1;  // distinct code shifts of the key fragments
+    constexpr int XS = 2 * NWV * 64 * 8 > NWV * 16 * DW ? 2 * NWV * 64 * 8 : NWV * 16 * DW;
     using KF = KeyFrag<BK>;
     static_assert(KWL * 32 == DQ * BK, "lane key range must be whole words");
+    static_assert(UPL >= 1 && NVML >= 1, "wave tile shape");
 
-    __shared__ __align__(16) float q_lds[16][D + 4];         // q * scale * 2^(8 - shift); rows >= R zero
-    __shared__ __align__(16) uint32_t km_lds[NW][D];        // key metadata of the tile's block
-    __shared__ __align__(16) uint8_t vt_lds[NW][32 * VROW]; // value codes of the tile, one byte each
-    __shared__ __align__(16) uint16_t st_lds[NW][8][32];    // value scales [group][token]
-    __shared__ __align__(16) uint16_t zt_lds[NW][16][32];   // value zero points [group][token]; row G = 1.0
-    __shared__ float xm_lds[NW][16];                        // per-wave reference maxima
-    __shared__ float xz_lds[NW][16][16];                    // per-wave zero-point sums and denominators
+    // Key pairs follow the fragment order: dword 4w + jj of a wave row holds
+    // channels 8w + PERM[2jj] (low half) and 8w + PERM[2jj+1] (high half).
+    __shared__ __align__(16) float xbuf[XS];                   // partial scores [2][NWV][64][8]; output staging
+    __shared__ __align__(16) uint32_t sp_lds[NWV][DW / 2];     // key scales of the tile's block, fp16 pairs
+    __shared__ __align__(16) uint32_t zp_lds[NWV][DW / 2];     // key zero points, fp16 pairs
+    __shared__ __align__(16) uint8_t vt_lds[NWV][32 * VROW];  // value codes of the tile, one byte each
+    __shared__ __align__(16) uint16_t st_lds[NWV][4][32];     // value scales [group][token]
+    __shared__ __align__(16) uint16_t zt_lds[NWV][16][ZROW];  // value zero points [group][token]; row G = 1.0
 
     const int seq = a.seq_list ? a.seq_list[blockIdx.z] : (int)blockIdx.z;
     const int kvh = blockIdx.y, split = blockIdx.x;
@@ -322,14 +366,18 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     const int wb = min(wa + CW, len);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
+    const int cw0 = wave * DW;  // first channel of this wave
     const int R = a.q_heads / a.kv_heads;
     const SeqEntry& e = a.table[seq];
     const int lgk = a.log2_group_k, lgv = a.log2_group_v;
     const int Gk = 1 << lgk;
     const int nqk = (len >> lgk) << lgk;  // tokens with quantized keys
     const int qend = min(wb, nqk);
-    const int vgpr = D >> lgv;            // value groups per token (1..8)
-    const int tpg = lgv - 4;              // log2 of output tiles per value group
+    const int vgpr = D >> lgv;            // value groups per token
+    const int g0 = cw0 >> lgv;            // first value group of this wave
+    const int ngw = lgv <= 5 + __builtin_ctz(UPW) ? DW >> lgv : 1;  // value groups of this wave
+    const int lng = __builtin_ctz(ngw);
+    const int bpg = lgv - 5;              // log2 of 32-channel blocks per value group
 
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
     const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
@@ -337,62 +385,72 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
     const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
 
-    // ---- queries: q * scale * 2^(8 - chan_shift(c mod 8)), zero rows for r >= R
-    for (int i = tid; i < 16 * (D / 8); i += NT) {
-        const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-        float v[8];
-        if (r < R) {
-            load8_rt(a.q, ((size_t)seq * a.q_heads + kvh * R + r) * D + c, a.in_dtype, v);
-        } else {
+    // ---- query ln of this kv head, channels cw0 + lg*DQ + [0, DQ), in registers:
+    // q' = q * scale * 2^(8 - chan_shift(c mod 8)) and its fp16 pairs in fragment order
+    float qf[DQ];
+    uint32_t qh[DQ / 2];
+    {
+        const size_t qrow = ((size_t)seq * a.q_heads + kvh * R + min(ln, R - 1)) * D + cw0 + lg * DQ;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
+        for (int k = 0; k < NCH; ++k) load8_rt(a.q, qrow + 8 * k, a.in_dtype, qf + 8 * k);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) q_lds[r][c + j] = v[j] * a.qscale * (float)(1 << (8 - chan_shift<BK>(j)));
+        for (int j = 0; j < DQ; ++j) qf[j] = ln < R ? qf[j] * a.qscale * (float)(1 << (8 - chan_shift<BK>(j & 7))) : 0.f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                qh[4 * k + jj] = pk_rtz(qf[8 * k + KF::PERM[2 * jj]], qf[8 * k + KF::PERM[2 * jj + 1]]);
     }
-    // constant rows of the zero-point fragment: 1.0 in row vgpr, 0 above it
+    // constant rows of the zero-point fragment: 1.0 in row ngw, 0 above it
     for (int i = lane; i < 16 * 32; i += 64) {
         const int g = i >> 5;
-        if (g >= vgpr) zt_lds[wave][g][i & 31] = g == vgpr ? (uint16_t)0x3c00u : (uint16_t)0u;
+        if (g >= ngw) zt_lds[wave][g][i & 31] = g == ngw ? (uint16_t)0x3c00u : (uint16_t)0u;
     }
-    __syncthreads();
 
     f32x4 acc[NSUB];
 #pragma unroll
     for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4lg+i][col ln]: zero-point sums (ln < vgpr), denominator (ln == vgpr)
-    float m = kFarBelow;              // reference maximum of query ln
+    f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4lg+i][col ln]: zero-point sums (ln < ngw), denominator (ln == ngw)
+    float m = kFarBelow;              // reference maximum of query ln (the same in every wave)
 
     // ---- prefetch registers (the tile after the one being computed)
-    uint32_t kw[2][KWL];  // key words of token rows 8(ln>>2) + 4s + (ln&3), lane group lg
-    uint32_t kmw[KM];     // key metadata words lane*KM.. of the tile's block
-    uint32_t vw[UPL][BV]; // value units lane + 64u of the tile
-    uint32_t vmw[4];      // value metadata words lane + 64u of the tile
+    uint32_t kw[2][KWL];      // key words of token rows 8(ln>>2) + 4s + (ln&3), lane group lg
+    uint32_t kmw[2];          // the two key metadata words of this lane's fragment pair
+    uint32_t vw[UPL][BV];     // value units of the wave
+    uint32_t vmw[NVML];       // value metadata words
 
     auto load_keys = [&](int t0) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int t = min(t0 + 8 * (ln >> 2) + 4 * s + (ln & 3), nqk - 1);
-            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + lg * KWL, kw[s]);
+            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8) + (cw0 + lg * DQ) * BK / 8), kw[s]);
         }
     };
+    // Lane -> fragment pair (window kw8, pair kjj) of the wave's key channels.
+    const int kpair = lane % (DW / 2), kw8 = kpair >> 2, kjj = kpair & 3;
     auto load_kmeta = [&](int t0) {
-        load_n<KM, pow2_align(KM * 4)>(km + (size_t)(t0 >> lgk) * D + lane * KM, kmw);
+        const uint32_t* src = km + (size_t)(t0 >> lgk) * D + cw0 + 8 * kw8;
+        int c0 = 0, c1 = 0;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            if (kjj == jj) c0 = KF::PERM[2 * jj], c1 = KF::PERM[2 * jj + 1];
+        kmw[0] = src[c0];
+        kmw[1] = src[c1];
     };
     auto load_values = [&](int t0) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             const int f = lane + 64 * u;
-            const int t = min(t0 + f / UPR, wb - 1);
-            load_n<BV, VALIGN>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + (f % UPR) * BV, vw[u]);
+            const int t = min(t0 + f / UPW, wb - 1);
+            load_n<BV, VALIGN>((const uint32_t*)(vc + (size_t)t * (D * BV / 8) + (cw0 / 32 + f % UPW) * BV * 4), vw[u]);
         }
+        // a fixed count of loads (clamped indices), so the compiler's wait counts
+        // never have to assume a load was skipped
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int f = lane + 64 * u;
-            if (f < 32 * vgpr) {
-                const int t = min(t0 + f / vgpr, wb - 1);
-                vmw[u] = vm[(size_t)t * vgpr + f % vgpr];
-            }
+        for (int u = 0; u < NVML; ++u) {
+            const int f = min(lane + 64 * u, 32 * ngw - 1);
+            const int t = min(t0 + (f >> lng), wb - 1);
+            vmw[u] = vm[(size_t)t * vgpr + g0 + (f & (ngw - 1))];
         }
     };
     // Stage value bytes, value scales / zero points and key metadata of the tile in LDS.
@@ -402,49 +460,52 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
             const int f = lane + 64 * u;
             uint32_t by[8];
             unit_to_bytes<BV>(vw[u], by);
-            uint32_t* dst = (uint32_t*)&vt_lds[wave][(f / UPR) * VROW + (f % UPR) * 32];
+            uint32_t* dst = (uint32_t*)&vt_lds[wave][(f / UPW) * VROW + (f % UPW) * 32];
 #pragma unroll
             for (int k = 0; k < 4; ++k) ((uint2*)dst)[k] = make_uint2(by[2 * k], by[2 * k + 1]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NVML; ++u) {
             const int f = lane + 64 * u;
-            if (f < 32 * vgpr) {
-                const int tt = f / vgpr, g = f % vgpr;
+            if (f < 32 * ngw) {
+                const int tt = f >> lng, g = f & (ngw - 1);
                 st_lds[wave][g][tt] = (uint16_t)(vmw[u] & 0xffffu);
                 zt_lds[wave][g][tt] = (uint16_t)(vmw[u] >> 16);
             }
         }
-        if (with_keys) store_lds_n<KM>(&km_lds[wave][lane * KM], kmw);
+        if (with_keys && lane < DW / 2) {
+            sp_lds[wave][kpair] = __builtin_amdgcn_perm(kmw[1], kmw[0], 0x05040100u);
+            zp_lds[wave][kpair] = __builtin_amdgcn_perm(kmw[1], kmw[0], 0x07060302u);
+        }
     };
 
-    // Keys of a quantized tile -> scores sc[j] of query ln, token t0 + 8lg + j.
-    auto key_scores_quant = [&](int t0, float* sc) {
+    // Partial key scores over this wave's channels of a quantized tile:
+    // sc[j] for query ln, token t0 + 8lg + j.
+    auto key_scores_quant = [&](float* sc) {
         f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
         float bz[NSH];
 #pragma unroll
         for (int h = 0; h < NSH; ++h) bz[h] = 0.f;
+        uint4 spc = *(const uint4*)&sp_lds[wave][4 * (lg * NCH)];
+        uint4 zpc = *(const uint4*)&zp_lds[wave][4 * (lg * NCH)];
         static_for<NCH>([&](auto K) {
             constexpr int k = K;
-            const int cb = lg * DQ + 8 * k;
-            const float4 qa = *(const float4*)&q_lds[ln][cb];
-            const float4 qb = *(const float4*)&q_lds[ln][cb + 4];
-            const uint4 ma = *(const uint4*)&km_lds[wave][cb];
-            const uint4 mb = *(const uint4*)&km_lds[wave][cb + 4];
-            const float q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-            const uint32_t mw[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+            uint4 spn, zpn;
+            if constexpr (k + 1 < NCH) {  // one chunk of LDS reads in flight
+                spn = *(const uint4*)&sp_lds[wave][4 * (lg * NCH + k + 1)];
+                zpn = *(const uint4*)&zp_lds[wave][4 * (lg * NCH + k + 1)];
+            }
+            const uint32_t sp[4] = {spc.x, spc.y, spc.z, spc.w};
+            const uint32_t zp[4] = {zpc.x, zpc.y, zpc.z, zpc.w};
             Frag bh, bl;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int c0i = KF::PERM[2 * jj], c1i = KF::PERM[2 * jj + 1];
-                const float x0 = mix_lo(mw[c0i], q[c0i], 0.f);
-                const float x1 = mix_lo(mw[c1i], q[c1i], 0.f);
-                split2(x0, x1, bh.u[jj], bl.u[jj]);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int h = NSH == 4 ? (j & 3) : NSH == 2 ? (j & 1) : 0;
-                bz[h] = mix_hi(mw[j], q[j], bz[h]);
+                const int j0 = 8 * k + KF::PERM[2 * jj], j1 = 8 * k + KF::PERM[2 * jj + 1];
+                mul_split(qh[4 * k + jj], qf[j0], qf[j1], sp[jj], bh.u[jj], bl.u[jj]);
+                constexpr int step = BK == 2 ? 2 : BK == 4 ? 4 : 1;
+                const int h0 = KF::SHIFT[2 * jj] / step, h1 = KF::SHIFT[2 * jj + 1] / step;
+                bz[h0] = mix_lo(zp[jj], qf[j0], bz[h0]);
+                bz[h1] = mix_hi(zp[jj], qf[j1], bz[h1]);
             }
             Frag a0, a1;
             KF::template get<k>(kw[0], a0);
@@ -453,7 +514,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
             c0 = mfma(a0, bl, c0);
             c1 = mfma(a1, bh, c1);
             c1 = mfma(a1, bl, c1);
-            __builtin_amdgcn_sched_barrier(0);  // bound the live LDS operands to one chunk
+            if constexpr (k + 1 < NCH) spc = spn, zpc = zpn;
+            __builtin_amdgcn_sched_barrier(0);
         });
         float bias = 0.f;
 #pragma unroll
@@ -461,24 +523,23 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
         bias = col4_sum(bias);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 8 * lg + i;
-            sc[i] = t < qend ? fmaf(c0[i], kTwo16, bias) : -INFINITY;
-            sc[4 + i] = t + 4 < qend ? fmaf(c1[i], kTwo16, bias) : -INFINITY;
+            sc[i] = fmaf(c0[i], kTwo16, bias);
+            sc[4 + i] = fmaf(c1[i], kTwo16, bias);
         }
     };
 
-    // Keys of a residual tile (rows kept in the input dtype) -> scores, with
-    // keys and queries both split into fp16 hi + lo parts (three MFMAs).
+    // Partial scores of a residual tile (keys kept in the input dtype): keys and
+    // queries both split into fp16 hi + lo parts (three MFMAs).
     auto key_scores_resid = [&](int t0, float* sc) {
         f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         static_for<NCH>([&](auto K) {
             constexpr int k = K;
-            const int cb = lg * DQ + 8 * k;
+            const int cb = cw0 + lg * DQ + 8 * k;
             Frag bh, bl;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float x0 = q_lds[ln][cb + 2 * jj] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj))));
-                const float x1 = q_lds[ln][cb + 2 * jj + 1] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj + 1))));
+                const float x0 = qf[8 * k + 2 * jj] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj))));
+                const float x1 = qf[8 * k + 2 * jj + 1] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj + 1))));
                 split2(x0, x1, bh.u[jj], bl.u[jj]);
             }
 #pragma unroll
@@ -496,13 +557,34 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
         });
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 8 * lg + i;
-            sc[i] = t < wb ? c[0][i] : -INFINITY;
-            sc[4 + i] = t + 4 < wb ? c[1][i] : -INFINITY;
+            sc[i] = c[0][i];
+            sc[4 + i] = c[1][i];
         }
     };
 
-    // Softmax weights of the tile and the value products.
+    // Sum the waves' partial scores (fixed order: identical in every wave), mask.
+    auto full_scores = [&](float* sc, int buf, int t0, int lim) {
+        if constexpr (NWV > 1) {
+            float* xs = xbuf + (size_t)buf * NWV * 512;
+            *(float4*)&xs[(wave * 64 + lane) * 8] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            *(float4*)&xs[(wave * 64 + lane) * 8 + 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+            wg_lds_barrier();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sc[j] = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) {
+                const float4 u0 = *(const float4*)&xs[(w * 64 + lane) * 8];
+                const float4 u1 = *(const float4*)&xs[(w * 64 + lane) * 8 + 4];
+                sc[0] += u0.x, sc[1] += u0.y, sc[2] += u0.z, sc[3] += u0.w;
+                sc[4] += u1.x, sc[5] += u1.y, sc[6] += u1.z, sc[7] += u1.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (t0 + 8 * lg + j >= lim) sc[j] = -INFINITY;
+    };
+
+    // Softmax weights of the tile and the value products of this wave's channels.
     auto values = [&](const float* sc) {
         float tmax = sc[0];
 #pragma unroll
@@ -525,8 +607,9 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - m);
         // zero points and denominator
+        Frag ph, pl;
         {
-            Frag ph, pl, zf;
+            Frag zf;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj], p[2 * jj + 1], ph.u[jj], pl.u[jj]);
             const uint4 z4 = *(const uint4*)&zt_lds[wave][ln][8 * lg];
@@ -534,116 +617,122 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
             cz = mfma(ph, zf, cz);
             cz = mfma(pl, zf, cz);
         }
+        // Output tiles 2b, 2b+1 take columns 32b + 2ln and 32b + 2ln + 1 of the
+        // wave's value tile: one 16-bit LDS read per token row feeds both.
+        const uint8_t* vt = &vt_lds[wave][8 * lg * VROW + 2 * ln];
+        uint32_t vb[2][8];
+        uint4 sv[2];
+        auto read_v = [&](int b, uint32_t* w, uint4& s4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = *(const uint16_t*)&vt[j * VROW + 32 * b];
+            s4 = *(const uint4*)&st_lds[wave][(32 * b) >> lgv][8 * lg];
+        };
+        read_v(0, vb[0], sv[0]);
         Frag sh, sl;
-        const uint8_t* vt = &vt_lds[wave][8 * lg * VROW + ln];
-        static_for<NSUB>([&](auto N) {
-            constexpr int n = N;
-            if ((n & ((1 << tpg) - 1)) == 0) {
-                const uint4 s4 = *(const uint4*)&st_lds[wave][n >> tpg][8 * lg];
-                const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+        static_for<NSUB / 2>([&](auto B) {
+            constexpr int b = B;
+            if constexpr (b + 1 < NSUB / 2) read_v(b + 1, vb[(b + 1) & 1], sv[(b + 1) & 1]);
+            if ((b & ((1 << bpg) - 1)) == 0) {  // first block of a value group: P' = p * s
+                const uint32_t sw[4] = {sv[b & 1].x, sv[b & 1].y, sv[b & 1].z, sv[b & 1].w};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    split2(mix_lo(sw[jj], p[2 * jj], 0.f), mix_hi(sw[jj], p[2 * jj + 1], 0.f), sh.u[jj], sl.u[jj]);
+                for (int jj = 0; jj < 4; ++jj) mul_split(ph.u[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
             }
-            Frag bf;
+            const uint32_t* w = vb[b & 1];
+            Frag f0, f1;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                bf.u[jj] = (uint32_t)vt[(2 * jj) * VROW + 16 * n] | ((uint32_t)vt[(2 * jj + 1) * VROW + 16 * n] << 16);
-            acc[n] = mfma(sh, bf, acc[n]);
-            acc[n] = mfma(sl, bf, acc[n]);
+            for (int jj = 0; jj < 4; ++jj) {
+                f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c040c00u);
+                f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c050c01u);
+            }
+            acc[2 * b] = mfma(sh, f0, acc[2 * b]);
+            acc[2 * b] = mfma(sl, f0, acc[2 * b]);
+            acc[2 * b + 1] = mfma(sh, f1, acc[2 * b + 1]);
+            acc[2 * b + 1] = mfma(sl, f1, acc[2 * b + 1]);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
 
-    // ---- tiles of this wave: t0 = first + 128 i
-    const int first = wa + 32 * wave;
-    const int nq = first < qend ? (qend - first + 127) >> 7 : 0;
-    if (nq > 0) {
-        load_kmeta(first);
-        load_values(first);
-        load_keys(first);
+    // ---- tiles of the split, shared by all waves
+    const int ntile = (wb - wa + 31) >> 5;
+    const int nqt = qend > wa ? (qend - wa + 31) >> 5 : 0;
+    if (nqt > 0) {
+        load_kmeta(wa);
+        load_values(wa);
+        load_keys(wa);
     }
-    for (int i = 0; i < nq; ++i) {
-        const int t0 = first + 128 * i;
-        const int tn = i + 1 < nq ? t0 + 128 : t0;  // the last prefetch repeats the tile (cache hits)
+    wave_lds_sync();  // constant zero-point rows written
+    for (int i = 0; i < nqt; ++i) {
+        const int t0 = wa + 32 * i;
+        const int tn = i + 1 < nqt ? t0 + 32 : t0;  // the last prefetch repeats the tile (cache hits)
         stage(true);
         load_kmeta(tn);
         load_values(tn);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the key words
         wave_lds_sync();
         float sc[8];
-        key_scores_quant(t0, sc);
+        key_scores_quant(sc);
         load_keys(tn);
+        full_scores(sc, i & 1, t0, qend);
         values(sc);
         wave_lds_sync();  // the next stage rewrites this wave's LDS tiles
     }
-    for (int t0 = first + 128 * nq; t0 < wb; t0 += 128) {
+    for (int i = nqt; i < ntile; ++i) {
+        const int t0 = wa + 32 * i;
         load_values(t0);
         stage(false);
         wave_lds_sync();
         float sc[8];
         key_scores_resid(t0, sc);
+        full_scores(sc, i & 1, t0, wb);
         values(sc);
         wave_lds_sync();
     }
 
-    // ---- per-wave (m, zero-point sums, denominators) to LDS
-    if (lg == 0) xm_lds[wave][ln] = m;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xz_lds[wave][4 * lg + i][ln] = cz[i];
-    __syncthreads();
-    // ---- merge the waves into an LDS tile O[16][D] (fixed order), reusing vt_lds
-    float* o_lds = (float*)&vt_lds[0][0];  // 16 * D floats <= sizeof(vt_lds)
-    float wsc[4];
+    // ---- this split's partial (m, l, o) for the R real queries: o = 2^24 acc + zero-point sums
+    float* o_lds = xbuf + wave * 16 * DW;  // [16][DW] by value-tile position
+    if constexpr (NWV > 1) wg_lds_barrier();  // every wave is done reading the partial scores
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * lg + i;
-        float mm = kFarBelow;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) mm = fmaxf(mm, xm_lds[w][r]);
-        wsc[i] = __builtin_amdgcn_exp2f(xm_lds[wave][r] - mm);
+        for (int b = 0; b < NSUB / 2; ++b) {
+            const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv));  // zero-point sum of (r, group)
+            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], kTwo24, zs);
+            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], kTwo24, zs);
+        }
     }
-    for (int w = 0; w < NW; ++w) {
-        if (wave == w) {
+    wave_lds_sync();
+    for (int i = lane; i < R * DW; i += 64) {
+        const int r = i / DW, pos = i % DW;
+        const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
+        a.ws_o[slot * D + cw0 + val_chan<BV>(pos)] = o_lds[r * DW + pos];
+    }
+    if (wave == 0) {
+        // denominator of query 4lg + i sits in column ngw of cz
 #pragma unroll
-            for (int n = 0; n < NSUB; ++n) {
-                const int c = val_chan<BV>(16 * n + ln);
-                const int g = (16 * n) >> lgv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * lg + i;
-                    const float o = fmaf(acc[n][i], kTwo24, xz_lds[wave][r][g]) * wsc[i];
-                    o_lds[r * D + c] = w == 0 ? o : o_lds[r * D + c] + o;
-                }
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            if (ln == ngw && r < R) {
+                const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
+                a.ws_ml[slot * 2 + 1] = cz[i];
             }
         }
-        __syncthreads();
-    }
-    // ---- this split's partial (m, l, o) for the R real queries
-    for (int i = tid; i < R * D; i += NT) {
-        const int r = i / D, c = i % D;
-        const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
-        a.ws_o[slot * D + c] = o_lds[r * D + c];
-    }
-    if (tid < R) {
-        const int r = tid;
-        float mm = kFarBelow;
-        for (int w = 0; w < NW; ++w) mm = fmaxf(mm, xm_lds[w][r]);
-        float L = 0.f;
-        for (int w = 0; w < NW; ++w) L = fmaf(xz_lds[w][r][vgpr], __builtin_amdgcn_exp2f(xm_lds[w][r] - mm), L);
-        const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
-        a.ws_ml[slot * 2 + 0] = mm;
-        a.ws_ml[slot * 2 + 1] = L;
+        if (lg == 0 && ln < R) {
+            const size_t slot = ((size_t)seq * a.q_heads + kvh * R + ln) * a.max_chunks + split;
+            a.ws_ml[slot * 2 + 0] = m;
+        }
     }
 }
 
 template <int D, int BK>
 hipError_t gqa_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
+    const dim3 block(D / wave_channels<BK>() * 64);
     switch (bv) {
-        case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 3>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 4>), grid, dim3(256), 0, s, a); break;
-        case 6: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 6>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 8>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 4>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 6>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 8>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -653,12 +742,10 @@ hipError_t gqa_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s)
     switch (bk) {
         case 2: return gqa_bv<D, 2>(a, bv, grid, s);
         case 3:
-            if constexpr ((D / 4) * 3 % 32 == 0) return gqa_bv<D, 3>(a, bv, grid, s);
+            if constexpr (D >= 128) return gqa_bv<D, 3>(a, bv, grid, s);
             else return hipErrorInvalidValue;
         case 4: return gqa_bv<D, 4>(a, bv, grid, s);
-        case 6:
-            if constexpr ((D / 4) * 6 % 32 == 0) return gqa_bv<D, 6>(a, bv, grid, s);
-            else return hipErrorInvalidValue;
+        case 6: return gqa_bv<D, 6>(a, bv, grid, s);
         default: return gqa_bv<D, 8>(a, bv, grid, s);
     }
 }
