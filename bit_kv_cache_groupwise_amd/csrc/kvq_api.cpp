@@ -36,6 +36,7 @@ struct kvq_cache {
     std::vector<int32_t> args;      // staging for the call-argument area
     struct Pair { int bk, bv, offset, count; };
     std::vector<Pair> pairs;        // distinct (bits_k, bits_v) pairs and their slice of the table's seq list
+    std::vector<int32_t> pair_list; // host copy of that seq list
     int32_t max_cap = 0;
 };
 
@@ -194,22 +195,31 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
     return (int)std::max<long>(unit, cw);
 }
 
-// Tokens per workgroup of the query-group kernel: a multiple of 128 (4 waves x
-// 32-token tiles), at least 512 (4 tiles per wave, so the register pipeline
-// and the per-workgroup setup pay off), and about 512 workgroups per launch
-// (two resident per compute unit): one launch per (bits_k, bits_v) pair.
+// Tokens per workgroup of the query-group kernel (a multiple of 128, at least
+// 512). One launch per (bits_k, bits_v) pair; each launch runs its workgroups
+// in rounds of the resident count (three 64-channel waves per SIMD, head_dim/64
+// waves per workgroup). The choice minimises sum over launches of
+// rounds * (tokens per workgroup + a fixed per-workgroup cost of 128 tokens).
 int choose_split_gqa(const kvq_cache* c, const int32_t* lens) {
     const kvq_geometry& g = c->g;
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
         if (v >= 128 && v % 128 == 0 && v <= (1 << 24)) return v;
     }
-    long total = 0;
-    for (int s = 0; s < g.num_seqs; ++s) total += lens[s];
-    const long per_launch = total * g.kv_heads / std::max<long>(1, (long)c->pairs.size());
-    long cw = (per_launch + 511) / 512;
-    cw = std::max(512L, (cw + 127) / 128 * 128);
-    return (int)std::min<long>(cw, 1L << 24);
+    const long slots = 3L * 1024 / std::max(1, g.head_dim / 64);
+    long best_cost = -1;
+    int best = 512;
+    for (int cw : {512, 640, 768, 896, 1024, 1280, 1536, 2048, 3072, 4096}) {
+        long cost = 0;
+        for (const auto& pr : c->pairs) {
+            long wgs = 0;
+            for (int i = 0; i < pr.count; ++i) wgs += (lens[c->pair_list[pr.offset + i]] + cw - 1) / cw;
+            wgs *= g.kv_heads;
+            cost += (wgs + slots - 1) / slots * (cw + 128);
+        }
+        if (best_cost < 0 || cost < best_cost) best_cost = cost, best = cw;
+    }
+    return best;
 }
 
 int min_chunk(const kvq_cache* c) {
@@ -289,6 +299,7 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
                     if (bk[s2] == bkk && bv[s2] == bvv) list[n++] = s2;
                 if (n > start) c->pairs.push_back({bkk, bvv, start, n - start});
             }
+        c->pair_list.assign(list, list + n);
     }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipMemcpyAsync(d_table, img.data(), img.size(), hipMemcpyHostToDevice, s);

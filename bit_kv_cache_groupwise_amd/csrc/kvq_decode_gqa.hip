@@ -326,8 +326,11 @@ __device__ __forceinline__ void wg_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Three waves per SIMD for 64-channel waves (registers capped at 168, no
+// spills); 128-channel waves need more and run two.
 template <int D, int BK, int BV>
-__global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D / wave_channels<BK>() * 64)
+__attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void decode_gqa_kernel(DecodeArgs a) {
     constexpr int DW = wave_channels<BK>();  // channels of this wave
     constexpr int NWV = D / DW;               // waves per workgroup (they share every tile)
     constexpr int NT = 64 * NWV;
@@ -413,36 +416,39 @@ __global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kerne
     f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4lg+i][col ln]: zero-point sums (ln < ngw), denominator (ln == ngw)
     float m = kFarBelow;              // reference maximum of query ln (the same in every wave)
 
-    // ---- prefetch registers (the tile after the one being computed)
-    uint32_t kw[2][KWL];      // key words of token rows 8(ln>>2) + 4s + (ln&3), lane group lg
-    uint32_t kmw[2];          // the two key metadata words of this lane's fragment pair
-    uint32_t vw[UPL][BV];     // value units of the wave
-    uint32_t vmw[NVML];       // value metadata words
+    // ---- prefetch registers: two sets, so the tiles two ahead are in flight
+    struct Pref {
+        uint32_t kw[2][KWL];   // key words of token rows 8(ln>>2) + 4s + (ln&3), lane group lg
+        uint32_t kmw[2];       // the two key metadata words of this lane's fragment pair
+        uint32_t vw[UPL][BV];  // value units of the wave
+        uint32_t vmw[NVML];    // value metadata words
+    };
+    Pref pf[2];
 
-    auto load_keys = [&](int t0) {
+    auto load_keys = [&](Pref& P, int t0) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int t = min(t0 + 8 * (ln >> 2) + 4 * s + (ln & 3), nqk - 1);
-            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8) + (cw0 + lg * DQ) * BK / 8), kw[s]);
+            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8) + (cw0 + lg * DQ) * BK / 8), P.kw[s]);
         }
     };
     // Lane -> fragment pair (window kw8, pair kjj) of the wave's key channels.
     const int kpair = lane % (DW / 2), kw8 = kpair >> 2, kjj = kpair & 3;
-    auto load_kmeta = [&](int t0) {
+    auto load_kmeta = [&](Pref& P, int t0) {
         const uint32_t* src = km + (size_t)(t0 >> lgk) * D + cw0 + 8 * kw8;
         int c0 = 0, c1 = 0;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
             if (kjj == jj) c0 = KF::PERM[2 * jj], c1 = KF::PERM[2 * jj + 1];
-        kmw[0] = src[c0];
-        kmw[1] = src[c1];
+        P.kmw[0] = src[c0];
+        P.kmw[1] = src[c1];
     };
-    auto load_values = [&](int t0) {
+    auto load_values = [&](Pref& P, int t0) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             const int f = lane + 64 * u;
             const int t = min(t0 + f / UPW, wb - 1);
-            load_n<BV, VALIGN>((const uint32_t*)(vc + (size_t)t * (D * BV / 8) + (cw0 / 32 + f % UPW) * BV * 4), vw[u]);
+            load_n<BV, VALIGN>((const uint32_t*)(vc + (size_t)t * (D * BV / 8) + (cw0 / 32 + f % UPW) * BV * 4), P.vw[u]);
         }
         // a fixed count of loads (clamped indices), so the compiler's wait counts
         // never have to assume a load was skipped
@@ -450,16 +456,16 @@ __global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kerne
         for (int u = 0; u < NVML; ++u) {
             const int f = min(lane + 64 * u, 32 * ngw - 1);
             const int t = min(t0 + (f >> lng), wb - 1);
-            vmw[u] = vm[(size_t)t * vgpr + g0 + (f & (ngw - 1))];
+            P.vmw[u] = vm[(size_t)t * vgpr + g0 + (f & (ngw - 1))];
         }
     };
     // Stage value bytes, value scales / zero points and key metadata of the tile in LDS.
-    auto stage = [&](bool with_keys) {
+    auto stage = [&](Pref& P, bool with_keys) {
 #pragma unroll
         for (int u = 0; u < UPL; ++u) {
             const int f = lane + 64 * u;
             uint32_t by[8];
-            unit_to_bytes<BV>(vw[u], by);
+            unit_to_bytes<BV>(P.vw[u], by);
             uint32_t* dst = (uint32_t*)&vt_lds[wave][(f / UPW) * VROW + (f % UPW) * 32];
 #pragma unroll
             for (int k = 0; k < 4; ++k) ((uint2*)dst)[k] = make_uint2(by[2 * k], by[2 * k + 1]);
@@ -469,19 +475,19 @@ __global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kerne
             const int f = lane + 64 * u;
             if (f < 32 * ngw) {
                 const int tt = f >> lng, g = f & (ngw - 1);
-                st_lds[wave][g][tt] = (uint16_t)(vmw[u] & 0xffffu);
-                zt_lds[wave][g][tt] = (uint16_t)(vmw[u] >> 16);
+                st_lds[wave][g][tt] = (uint16_t)(P.vmw[u] & 0xffffu);
+                zt_lds[wave][g][tt] = (uint16_t)(P.vmw[u] >> 16);
             }
         }
         if (with_keys && lane < DW / 2) {
-            sp_lds[wave][kpair] = __builtin_amdgcn_perm(kmw[1], kmw[0], 0x05040100u);
-            zp_lds[wave][kpair] = __builtin_amdgcn_perm(kmw[1], kmw[0], 0x07060302u);
+            sp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x05040100u);
+            zp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x07060302u);
         }
     };
 
     // Partial key scores over this wave's channels of a quantized tile:
     // sc[j] for query ln, token t0 + 8lg + j.
-    auto key_scores_quant = [&](float* sc) {
+    auto key_scores_quant = [&](const Pref& P, float* sc) {
         f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
         float bz[NSH];
 #pragma unroll
@@ -508,8 +514,8 @@ __global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kerne
                 bz[h1] = mix_hi(zp[jj], qf[j1], bz[h1]);
             }
             Frag a0, a1;
-            KF::template get<k>(kw[0], a0);
-            KF::template get<k>(kw[1], a1);
+            KF::template get<k>(P.kw[0], a0);
+            KF::template get<k>(P.kw[1], a1);
             c0 = mfma(a0, bh, c0);
             c0 = mfma(a0, bl, c0);
             c1 = mfma(a1, bh, c1);
@@ -655,31 +661,40 @@ __global__ __launch_bounds__(D / wave_channels<BK>() * 64) void decode_gqa_kerne
     // ---- tiles of the split, shared by all waves
     const int ntile = (wb - wa + 31) >> 5;
     const int nqt = qend > wa ? (qend - wa + 31) >> 5 : 0;
-    if (nqt > 0) {
-        load_kmeta(wa);
-        load_values(wa);
-        load_keys(wa);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (b < nqt) {
+            load_kmeta(pf[b], wa + 32 * b);
+            load_values(pf[b], wa + 32 * b);
+            load_keys(pf[b], wa + 32 * b);
+        }
     }
     wave_lds_sync();  // constant zero-point rows written
-    for (int i = 0; i < nqt; ++i) {
+    // Tile i uses set i & 1 and refills it with tile i + 2 (the last tile is
+    // repeated past the end: cache hits).
+    auto quant_tile = [&](Pref& P, int i) {
         const int t0 = wa + 32 * i;
-        const int tn = i + 1 < nqt ? t0 + 32 : t0;  // the last prefetch repeats the tile (cache hits)
-        stage(true);
-        load_kmeta(tn);
-        load_values(tn);
+        const int tn = wa + 32 * min(i + 2, nqt - 1);
+        stage(P, true);
+        load_kmeta(P, tn);
+        load_values(P, tn);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the key words
         wave_lds_sync();
         float sc[8];
-        key_scores_quant(sc);
-        load_keys(tn);
+        key_scores_quant(P, sc);
+        load_keys(P, tn);
         full_scores(sc, i & 1, t0, qend);
         values(sc);
         wave_lds_sync();  // the next stage rewrites this wave's LDS tiles
+    };
+    for (int i = 0; i < nqt; i += 2) {
+        quant_tile(pf[0], i);
+        if (i + 1 < nqt) quant_tile(pf[1], i + 1);
     }
     for (int i = nqt; i < ntile; ++i) {
         const int t0 = wa + 32 * i;
-        load_values(t0);
-        stage(false);
+        load_values(pf[0], t0);
+        stage(pf[0], false);
         wave_lds_sync();
         float sc[8];
         key_scores_resid(t0, sc);
