@@ -394,8 +394,11 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, c
     const void* srcs[2] = {k_new, v_new};
     const int groups[2] = {g.group_k, g.group_v};
     const int axes[2] = {g.axis_k, g.axis_v};
+    kvq::TensorArgs ta[2];
+    int gx[2];
     for (int t = 0; t < 2; ++t) {
-        kvq::TensorArgs a{};
+        kvq::TensorArgs& a = ta[t];
+        a = kvq::TensorArgs{};
         a.src = srcs[t];
         a.codes = c->codes;
         a.meta = c->meta;
@@ -412,19 +415,19 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, c
         a.head_dim = g.head_dim;
         a.group = groups[t];
         a.in_dtype = g.in_dtype;
-        hipError_t e;
+        a.axis = axes[t];
+        a.rows_per_block = kvq::kThreads / (g.head_dim / 32);
         if (axes[t] == KVQ_AXIS_TOKEN) {
-            a.rows_per_block = kvq::kThreads / (g.head_dim / 32);
-            const int gx = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
-            e = kvq::launch_quant_token_axis(a, gx, hs);
+            gx[t] = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
         } else {
-            int gx = 1;
+            gx[t] = 1;
             for (int s = 0; s < S; ++s)
-                gx = std::max(gx, (lens[s] + n_new[s]) / groups[t] - lens[s] / groups[t]);
-            e = kvq::launch_quant_channel_axis(a, gx, hs);
+                gx[t] = std::max(gx[t], (lens[s] + n_new[s]) / groups[t] - lens[s] / groups[t]);
         }
-        if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
     }
+    if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");
+    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], hs);
+    if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
     for (int s = 0; s < S; ++s) lens[s] += n_new[s];
     c->parity[layer] ^= 1;
     return KVQ_OK;

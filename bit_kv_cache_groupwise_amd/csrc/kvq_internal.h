@@ -53,7 +53,8 @@ struct TensorArgs {
     int32_t n_uniform;
     int32_t tensor;             // 0 = K, 1 = V
     int32_t num_seqs, kv_heads, head_dim, group, in_dtype;
-    int32_t rows_per_block;     // token-axis kernel: rows per workgroup
+    int32_t rows_per_block;     // token axis: rows per workgroup
+    int32_t axis;               // KVQ_AXIS_CHANNEL (0) or KVQ_AXIS_TOKEN (1)
 };
 
 struct DecodeArgs {
@@ -87,8 +88,9 @@ struct DequantArgs {
     int32_t tensor, len, kv_heads, head_dim, group, axis, in_dtype;
 };
 
-hipError_t launch_quant_token_axis(const TensorArgs& a, int grid_x, hipStream_t s);
-hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_t s);
+// Keys and values of one append in one launch: gx_k workgroups per (head, seq)
+// for the keys, then gx_v for the values.
+hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mha_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);

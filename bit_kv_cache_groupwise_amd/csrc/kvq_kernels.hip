@@ -16,6 +16,8 @@
 //   (v_rndne_f32: ties to even); stored step 0 -> code 0.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -29,17 +31,15 @@ using namespace dev;
 // ([U] "Valores: Onde a Intuicao Quebra"; [U] "O Imposto dos Sistemas ...":
 // such groups are complete when their token arrives). One thread per
 // 32-channel unit; a group spans G/32 adjacent lanes and its min/max is a
-// butterfly over those lanes.
-// grid = (row tiles, kv_heads, num_seqs)
+// butterfly over those lanes. Workgroup `item` takes rows item*rows_per_block..
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quant_token_axis_kernel(TensorArgs a) {
-    const int seq = blockIdx.z, head = blockIdx.y;
+__device__ __forceinline__ void token_axis_part(const TensorArgs& a, int item, int head, int seq) {
     const int D = a.head_dim, UPR = D >> 5;
     const int len0 = a.len_in[seq];
     const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
-    if (a.len_out && blockIdx.x == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len0 + n;
-    const int r = blockIdx.x * a.rows_per_block + (int)threadIdx.x / UPR;
+    if (a.len_out && item == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len0 + n;
+    const int r = item * a.rows_per_block + (int)threadIdx.x / UPR;
     const int u = (int)threadIdx.x % UPR;
     if (r >= n) return;  // whole rows (and so whole groups) leave together
     const int row_start = a.row_start ? a.row_start[seq] : seq * a.n_uniform;
@@ -74,18 +74,26 @@ __global__ __launch_bounds__(kThreads) void quant_token_axis_kernel(TensorArgs a
 
 // ---------------------------------------------------------------------------
 // Quantize, channel axis: one group = one channel over a block of G tokens
-// ([U] "Chaves: Os Valores Extremos Vivem em Canais Fixos"). A block is
-// quantized when its G-th token arrives; until then its tokens wait in the
-// residual rows ([U] "O Imposto dos Sistemas ..."). Workgroup item 0 also
-// moves the new tail tokens into the residual, after it has read the old
-// residual rows of its own block, so the two never race.
-// grid = (items, kv_heads, num_seqs); dynamic LDS = G * D bytes of codes.
+// ([U] "Chaves: Outliers Tem Endereco Fixo"; [N] "Kuantisasi dapat memindahkan
+// pekerjaan ke decode path": rows wait in the residual until the block is
+// complete). Workgroup `item` < nb quantizes block b_first + item: the
+// workgroup's 256 threads are kThreads/D parts per channel, each over G*D/256
+// tokens; loads are issued 4 at a time, min/max meet in LDS, codes go through
+// an LDS [G][D] byte tile and are packed per 32-channel unit. Workgroup 0 also
+// copies the rows past the last complete block into the residual (after its
+// own reads of the old residual rows).
+// LDS: max(G*D bytes of codes, 2*kThreads floats of min/max exchange).
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quant_channel_axis_kernel(TensorArgs a) {
-    extern __shared__ uint32_t lds_codes_w[];
-    uint8_t* lds_codes = (uint8_t*)lds_codes_w;
-    const int seq = blockIdx.z, head = blockIdx.y, item = blockIdx.x;
+__device__ __forceinline__ float chan_value(const TensorArgs& a, const uint8_t* resid, int t, int len0, int row_start,
+                                            int head, int c) {
+    const int D = a.head_dim;
+    return t < len0 ? load_in<DT>(resid, (size_t)(t % a.group) * D + c)
+                    : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + c);
+}
+
+template <int DT>
+__device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item, int head, int seq, uint32_t* smem) {
     const int D = a.head_dim, UPR = D >> 5, G = a.group;
     const int len0 = a.len_in[seq];
     const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
@@ -100,45 +108,66 @@ __global__ __launch_bounds__(kThreads) void quant_channel_axis_kernel(TensorArgs
     constexpr int IB = In<DT>::bytes;
 
     if (item < nb) {
+        uint8_t* lds_codes = (uint8_t*)smem;
+        float* lmn = (float*)smem;  // min/max exchange, then reused by the code tile
+        float* lmx = lmn + kThreads;
         const int b = b_first + item;
         const float L = (float)((1 << B) - 1);
-        for (int ch = threadIdx.x; ch < D; ch += kThreads) {
-            float mn = 0.f, mx = 0.f;
-            for (int i = 0; i < G; ++i) {
-                const int t = b * G + i;
-                const float x = t < len0 ? load_in<DT>(resid, (size_t)(t % G) * D + ch)
-                                         : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch);
-                mn = i == 0 ? x : fminf(mn, x);
-                mx = i == 0 ? x : fmaxf(mx, x);
+        const int tpc = kThreads / D;  // threads per channel (head_dim <= 256)
+        const int c = threadIdx.x % D, part = threadIdx.x / D;
+        const bool active = part < tpc;  // head_dim not dividing 256 leaves threads idle
+        const int tpp = G / tpc;        // tokens per part, a multiple of 4
+        const int i_first = part * tpp;
+        const int t0 = b * G;
+        float mn = INFINITY, mx = -INFINITY;
+        for (int i = 0; active && i < tpp; i += 4) {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = chan_value<DT>(a, resid, t0 + i_first + i + j, len0, row_start, head, c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mn = fminf(mn, x[j]);
+                mx = fmaxf(mx, x[j]);
             }
-            const float s32 = (mx - mn) / L;
-            const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
-            const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+        }
+        lmn[threadIdx.x] = mn;
+        lmx[threadIdx.x] = mx;
+        __syncthreads();
+        for (int p = 0; p < tpc; ++p) {
+            mn = fminf(mn, lmn[p * D + c]);
+            mx = fmaxf(mx, lmx[p * D + c]);
+        }
+        __syncthreads();  // the code tile overwrites the exchange
+        const float s32 = (mx - mn) / L;
+        const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
+        const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+        if (active && part == 0) {
             uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
-            meta[(size_t)b * D + ch] = sb | (zb << 16);
-            for (int i = 0; i < G; ++i) {
-                const int t = b * G + i;
-                const float x = t < len0 ? load_in<DT>(resid, (size_t)(t % G) * D + ch)
-                                         : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch);
-                lds_codes[i * D + ch] = (uint8_t)quant_code(x, s, z, L);
-            }
+            meta[(size_t)b * D + c] = sb | (zb << 16);
+        }
+        for (int i = 0; active && i < tpp; i += 4) {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = chan_value<DT>(a, resid, t0 + i_first + i + j, len0, row_start, head, c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lds_codes[(i_first + i + j) * D + c] = (uint8_t)quant_code(x[j], s, z, L);
         }
         __syncthreads();
         uint8_t* codes = a.codes + e.codes[T] + (size_t)head * e.codes_hs[T];
         for (int idx = threadIdx.x; idx < G * UPR; idx += kThreads) {
             const int i = idx / UPR, u = idx % UPR;
-            const uint32_t* src = lds_codes_w + (i * D + 32 * u) / 4;
-            uint32_t c[32];
+            const uint32_t* src = smem + (i * D + 32 * u) / 4;
+            uint32_t cc[32];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t v = src[k];
-                c[4 * k + 0] = v & 0xffu;
-                c[4 * k + 1] = (v >> 8) & 0xffu;
-                c[4 * k + 2] = (v >> 16) & 0xffu;
-                c[4 * k + 3] = v >> 24;
+                cc[4 * k + 0] = v & 0xffu;
+                cc[4 * k + 1] = (v >> 8) & 0xffu;
+                cc[4 * k + 2] = (v >> 16) & 0xffu;
+                cc[4 * k + 3] = v >> 24;
             }
             uint32_t* dst = (uint32_t*)(codes + (size_t)(b * G + i) * (D * B / 8)) + u * B;
-            store_codes_rt(B, c, dst);
+            store_codes_rt(B, cc, dst);
         }
     }
     if (item == 0) {
@@ -150,10 +179,28 @@ __global__ __launch_bounds__(kThreads) void quant_channel_axis_kernel(TensorArgs
             const int i = idx / D, ch = idx % D;
             const int t = start + i;
             const size_t so = ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + ch;
-            const size_t dof = (size_t)(t % G) * D + ch;
+            const size_t dof = (size_t)(t % a.group) * D + ch;
             if constexpr (IB == 4) ((uint32_t*)rw)[dof] = ((const uint32_t*)a.src)[so];
             else ((uint16_t*)rw)[dof] = ((const uint16_t*)a.src)[so];
         }
+    }
+}
+
+// One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
+// keys, [gx_k, gx_k + gx_v) the values, each with its own axis.
+// grid = (gx_k + gx_v, kv_heads, num_seqs)
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k, TensorArgs v, int gx_k) {
+    extern __shared__ uint32_t quant_smem[];
+    const int seq = blockIdx.z, head = blockIdx.y;
+    uint32_t* smem = quant_smem;
+    if ((int)blockIdx.x < gx_k) {
+        if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
+        else channel_axis_part<DT>(k, blockIdx.x, head, seq, smem);
+    } else {
+        const int item = (int)blockIdx.x - gx_k;
+        if (v.axis == 1) token_axis_part<DT>(v, item, head, seq);
+        else channel_axis_part<DT>(v, item, head, seq, smem);
     }
 }
 
@@ -479,23 +526,15 @@ size_t decode_lds_bytes(int R, int D, int C) {
     return sizeof(float) * ((size_t)R * D + C + 8 * 256 + 64 + 256 * 32);
 }
 
-hipError_t launch_quant_token_axis(const TensorArgs& a, int grid_x, hipStream_t s) {
-    dim3 grid(grid_x, a.kv_heads, a.num_seqs);
-    switch (a.in_dtype) {
-        case 0: hipLaunchKernelGGL(quant_token_axis_kernel<0>, grid, dim3(kThreads), 0, s, a); break;
-        case 1: hipLaunchKernelGGL(quant_token_axis_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL(quant_token_axis_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_quant_channel_axis(const TensorArgs& a, int grid_x, hipStream_t s) {
-    dim3 grid(grid_x, a.kv_heads, a.num_seqs);
-    const size_t lds = (size_t)a.group * a.head_dim;
-    switch (a.in_dtype) {
-        case 0: hipLaunchKernelGGL(quant_channel_axis_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
-        case 1: hipLaunchKernelGGL(quant_channel_axis_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
-        default: hipLaunchKernelGGL(quant_channel_axis_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
+hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, hipStream_t s) {
+    dim3 grid(gx_k + gx_v, k.kv_heads, k.num_seqs);
+    size_t lds = 0;
+    for (const TensorArgs* t : {&k, &v})
+        if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, 2 * kThreads * sizeof(float)));
+    switch (k.in_dtype) {
+        case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
+        case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
+        default: hipLaunchKernelGGL(quant_append_kernel<2>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
     }
     return hipGetLastError();
 }
