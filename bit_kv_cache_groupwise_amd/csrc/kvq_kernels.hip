@@ -77,19 +77,30 @@ __device__ __forceinline__ void token_axis_part(const TensorArgs& a, int item, i
 // ([U] "Chaves: Outliers Tem Endereco Fixo"; [N] "Kuantisasi dapat memindahkan
 // pekerjaan ke decode path": rows wait in the residual until the block is
 // complete). Workgroup `item` < nb quantizes block b_first + item: the
-// workgroup's 256 threads are kThreads/D parts per channel, each over G*D/256
-// tokens; loads are issued 4 at a time, min/max meet in LDS, codes go through
+// workgroup's 256 threads are (token part, channel pair) with the parts a power
+// of two; loads are issued 2 tokens at a time, min/max meet in LDS, codes go through
 // an LDS [G][D] byte tile and are packed per 32-channel unit. Workgroup 0 also
 // copies the rows past the last complete block into the residual (after its
 // own reads of the old residual rows).
-// LDS: max(G*D bytes of codes, 2*kThreads floats of min/max exchange).
+// LDS: max(G*D bytes of codes, 4*kThreads floats of min/max exchange).
 // ---------------------------------------------------------------------------
+// Two consecutive channels c, c+1 of token t (even c), from the residual rows
+// (t < len0) or the new rows; f32 input takes one channel (the second is unused).
 template <int DT>
-__device__ __forceinline__ float chan_value(const TensorArgs& a, const uint8_t* resid, int t, int len0, int row_start,
-                                            int head, int c) {
+__device__ __forceinline__ void chan_pair(const TensorArgs& a, const uint8_t* resid, int t, int len0, int row_start,
+                                          int head, int c, float& x0, float& x1) {
     const int D = a.head_dim;
-    return t < len0 ? load_in<DT>(resid, (size_t)(t % a.group) * D + c)
-                    : load_in<DT>(a.src, ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + c);
+    const size_t i = t < len0 ? (size_t)(t % a.group) * D + c
+                              : ((size_t)(row_start + t - len0) * a.kv_heads + head) * D + c;
+    const void* base = t < len0 ? (const void*)resid : a.src;
+    if constexpr (DT == 0) {
+        x0 = ((const float*)base)[i];
+        x1 = x0;
+    } else {
+        const uint32_t w = *(const uint32_t*)((const uint16_t*)base + i);
+        x0 = half_to_f32<DT>(w & 0xffffu);
+        x1 = half_to_f32<DT>(w >> 16);
+    }
 }
 
 template <int DT>
@@ -108,49 +119,60 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     constexpr int IB = In<DT>::bytes;
 
     if (item < nb) {
+        // Thread = (token part, channel pair): a token row is D / CPT threads,
+        // with 2-byte inputs a 4-byte load per thread; parts = a power of two.
+        constexpr int CPT = IB == 4 ? 1 : 2;
         uint8_t* lds_codes = (uint8_t*)smem;
-        float* lmn = (float*)smem;  // min/max exchange, then reused by the code tile
-        float* lmx = lmn + kThreads;
+        const int rt = D / CPT;
+        const int parts = 1 << (31 - __builtin_clz(kThreads / rt));
+        const int part = threadIdx.x / rt, c = (threadIdx.x % rt) * CPT;
+        const bool active = part < parts;  // head_dim not dividing 256 leaves threads idle
+        const int tpp = G / parts;         // tokens per part, even
+        float* lmn = (float*)smem;         // [parts][D] min/max exchange, then reused by the code tile
+        float* lmx = lmn + parts * D;
         const int b = b_first + item;
         const float L = (float)((1 << B) - 1);
-        const int tpc = kThreads / D;  // threads per channel (head_dim <= 256)
-        const int c = threadIdx.x % D, part = threadIdx.x / D;
-        const bool active = part < tpc;  // head_dim not dividing 256 leaves threads idle
-        const int tpp = G / tpc;        // tokens per part, a multiple of 4
-        const int i_first = part * tpp;
-        const int t0 = b * G;
-        float mn = INFINITY, mx = -INFINITY;
-        for (int i = 0; active && i < tpp; i += 4) {
+        const int t0 = b * G + part * tpp;
+        float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+        for (int i = 0; active && i < tpp; i += 2) {
             float x[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = chan_value<DT>(a, resid, t0 + i_first + i + j, len0, row_start, head, c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                mn = fminf(mn, x[j]);
-                mx = fmaxf(mx, x[j]);
-            }
+            chan_pair<DT>(a, resid, t0 + i, len0, row_start, head, c, x[0], x[1]);
+            chan_pair<DT>(a, resid, t0 + i + 1, len0, row_start, head, c, x[2], x[3]);
+            mn0 = fminf(mn0, fminf(x[0], x[2]));
+            mx0 = fmaxf(mx0, fmaxf(x[0], x[2]));
+            mn1 = fminf(mn1, fminf(x[1], x[3]));
+            mx1 = fmaxf(mx1, fmaxf(x[1], x[3]));
         }
-        lmn[threadIdx.x] = mn;
-        lmx[threadIdx.x] = mx;
+        if (active) {
+            lmn[part * D + c] = mn0, lmx[part * D + c] = mx0;
+            if (CPT == 2) lmn[part * D + c + 1] = mn1, lmx[part * D + c + 1] = mx1;
+        }
         __syncthreads();
-        for (int p = 0; p < tpc; ++p) {
-            mn = fminf(mn, lmn[p * D + c]);
-            mx = fmaxf(mx, lmx[p * D + c]);
+        for (int p = 0; p < parts; ++p) {
+            mn0 = fminf(mn0, lmn[p * D + c]), mx0 = fmaxf(mx0, lmx[p * D + c]);
+            if (CPT == 2) mn1 = fminf(mn1, lmn[p * D + c + 1]), mx1 = fmaxf(mx1, lmx[p * D + c + 1]);
         }
         __syncthreads();  // the code tile overwrites the exchange
-        const float s32 = (mx - mn) / L;
-        const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
-        const float s = f16_to_f32(sb), z = f16_to_f32(zb);
+        const uint32_t sb0 = f32_to_f16_bits((mx0 - mn0) / L), zb0 = f32_to_f16_bits(mn0);
+        const uint32_t sb1 = f32_to_f16_bits((mx1 - mn1) / L), zb1 = f32_to_f16_bits(mn1);
+        const float s0 = f16_to_f32(sb0), z0 = f16_to_f32(zb0), s1 = f16_to_f32(sb1), z1 = f16_to_f32(zb1);
         if (active && part == 0) {
             uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
-            meta[(size_t)b * D + c] = sb | (zb << 16);
+            meta[(size_t)b * D + c] = sb0 | (zb0 << 16);
+            if (CPT == 2) meta[(size_t)b * D + c + 1] = sb1 | (zb1 << 16);
         }
-        for (int i = 0; active && i < tpp; i += 4) {
+        for (int i = 0; active && i < tpp; i += 2) {
             float x[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = chan_value<DT>(a, resid, t0 + i_first + i + j, len0, row_start, head, c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lds_codes[(i_first + i + j) * D + c] = (uint8_t)quant_code(x[j], s, z, L);
+            chan_pair<DT>(a, resid, t0 + i, len0, row_start, head, c, x[0], x[1]);
+            chan_pair<DT>(a, resid, t0 + i + 1, len0, row_start, head, c, x[2], x[3]);
+            const int r = part * tpp + i;
+            if constexpr (CPT == 2) {
+                *(uint16_t*)&lds_codes[r * D + c] = (uint16_t)(quant_code(x[0], s0, z0, L) | (quant_code(x[1], s1, z1, L) << 8));
+                *(uint16_t*)&lds_codes[(r + 1) * D + c] = (uint16_t)(quant_code(x[2], s0, z0, L) | (quant_code(x[3], s1, z1, L) << 8));
+            } else {
+                lds_codes[r * D + c] = (uint8_t)quant_code(x[0], s0, z0, L);
+                lds_codes[(r + 1) * D + c] = (uint8_t)quant_code(x[2], s0, z0, L);
+            }
         }
         __syncthreads();
         uint8_t* codes = a.codes + e.codes[T] + (size_t)head * e.codes_hs[T];
@@ -530,7 +552,7 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
     dim3 grid(gx_k + gx_v, k.kv_heads, k.num_seqs);
     size_t lds = 0;
     for (const TensorArgs* t : {&k, &v})
-        if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, 2 * kThreads * sizeof(float)));
+        if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));
     switch (k.in_dtype) {
         case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
         case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
