@@ -11,17 +11,18 @@
 //       (grouped-query attention shares kv heads among query heads)
 //
 // Work decomposition: workgroup = (split of the token axis, kv head, seq); its
-// 4 waves take interleaved 32-token tiles and meet only at the end. Per tile a
-// wave computes
-//   scores^T[t][r] = 2^16 * sum_c A[t][c] B[c][r] + bias[r],
+// waves share every 32-token tile, wave w owning 64 of the head's channels
+// (128 for 3-bit keys). Per tile a wave computes
+//   partial scores^T[t][r] = 2^16 * sum_c A[t][c] B[c][r] + bias[r] over its channels,
 //     A = key codes of token t as fp16 subnormals code * 2^(sh-24), unpacked
 //         from the lane's own row words (exact),
 //     B = q'_rc * s_c in fp16 hi + lo parts (two MFMAs), where q' carries the
 //         2^(8-sh) that undoes the code shift,
 //     bias[r] = sum_c q_rc z_c on the VALU;
-//   O[r][c]  += 2^24 * sum_t (p_rt s_t,g(c))[hi + lo] V[t][c],
-//     V = value codes as fp16 subnormals, read transposed from an LDS byte tile;
-//   Z[r][g]  += sum_t p_rt [hi + lo] * (z_t,g | 1),
+//   the waves' partial scores are summed through LDS (one barrier per tile);
+//   O[r][c]  += 2^(24-KB) * sum_t (2^KB p_rt s_t,g(c))[hi + lo] V[t][c],
+//     V = value codes as fp16 subnormals, read from an LDS byte tile;
+//   Z[r][g]  += 2^-KZ * sum_t (2^KZ p_rt)[hi + lo] * (z_t,g | 1),
 //     one MFMA against a [token][group] fragment of zero points whose column
 //     after the last group is 1, so it also yields the softmax denominator.
 // The score layout (lane: 1 query x 8 consecutive tokens) is the operand layout
@@ -32,9 +33,10 @@
 // LDS, key words after the score MFMAs), so every wave keeps one tile in
 // flight while it computes the current one.
 //
-// Softmax: online in the log2 domain with a lazily moved reference maximum
-// (moved when a score exceeds it by more than 2^8, so weights stay <= 256 and
-// P * s stays inside the fp16 range). Splits are merged by merge_kernel.
+// Softmax: online in the log2 domain with the exact running maximum, so
+// weights are <= 1; they enter the fp16 operands pre-scaled by powers of two
+// (2^(BV+2) for p * s, 2^14 for the zero-point / denominator product) so that
+// small weights keep full fp16 precision. Splits are merged by merge_kernel.
 #include <utility>
 
 #include "kvq_device.h"
@@ -346,6 +348,9 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     constexpr int KALIGN = pow2_align(D * BK / 8) < pow2_align(KWL * 4) ? pow2_align(D * BK / 8) : pow2_align(KWL * 4);
     constexpr int VALIGN = pow2_align(D * BV / 8) < pow2_align(BV * 4) ? pow2_align(D * BV / 8) : pow2_align(BV * 4);
     constexpr int NSH = BK == 2 ? 4 : BK == 4 ? 2 : 1;  // distinct code shifts of the key fragments
+    // Softmax weight scales (p <= 1): 2^KB p * s <= 2^(BV+2) * range / (2^BV - 1)
+    // stays far inside fp16 while small weights stay normal; 2^KZ p <= 16384.
+    constexpr int KB = BV + 2, KZ = 14;
     constexpr int XS = 2 * NWV * 64 * 8 > NWV * 16 * DW ? 2 * NWV * 64 * 8 : NWV * 16 * DW;
     using KF = KeyFrag<BK>;
     static_assert(KWL * 32 == DQ * BK, "lane key range must be whole words");
@@ -596,7 +601,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
 #pragma unroll
         for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
         tmax = col4_max(tmax);
-        if (__builtin_amdgcn_ballot_w64(tmax > m + 8.0f)) {
+        if (__builtin_amdgcn_ballot_w64(tmax > m)) {
             const float mnew = fmaxf(m, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m - mnew);
             // row 4lg + i of the accumulators belongs to query 4lg + i
@@ -609,15 +614,23 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             }
             m = mnew;
         }
+        // p <= 1 (exact running maximum), kept in fp16 range with power-of-two
+        // scales: 2^KB for the value product, 2^KZ for zero points / denominator
         float p[8];
+        const float mb = m - (float)KB;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - m);
-        // zero points and denominator
-        Frag ph, pl;
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
+        Frag ph, pl, pb;  // 2^KZ p as hi + lo; 2^KB p truncated to fp16 pairs
         {
             Frag zf;
+            float pz[8];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj], p[2 * jj + 1], ph.u[jj], pl.u[jj]);
+            for (int j = 0; j < 8; ++j) pz[j] = p[j] * (float)(1 << (KZ - KB));
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                split2(pz[2 * jj], pz[2 * jj + 1], ph.u[jj], pl.u[jj]);
+                pb.u[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
+            }
             const uint4 z4 = *(const uint4*)&zt_lds[wave][ln][8 * lg];
             zf.u[0] = z4.x, zf.u[1] = z4.y, zf.u[2] = z4.z, zf.u[3] = z4.w;
             cz = mfma(ph, zf, cz);
@@ -641,7 +654,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             if ((b & ((1 << bpg) - 1)) == 0) {  // first block of a value group: P' = p * s
                 const uint32_t sw[4] = {sv[b & 1].x, sv[b & 1].y, sv[b & 1].z, sv[b & 1].w};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) mul_split(ph.u[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
+                for (int jj = 0; jj < 4; ++jj) mul_split(pb.u[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
             }
             const uint32_t* w = vb[b & 1];
             Frag f0, f1;
@@ -711,9 +724,10 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
         const int r = 4 * lg + i;
 #pragma unroll
         for (int b = 0; b < NSUB / 2; ++b) {
-            const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv));  // zero-point sum of (r, group)
-            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], kTwo24, zs);
-            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], kTwo24, zs);
+            // zero-point sum of (r, group), carrying 2^KZ
+            const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv)) * (1.0f / (float)(1 << KZ));
+            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], kTwo24 / (float)(1 << KB), zs);
+            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], kTwo24 / (float)(1 << KB), zs);
         }
     }
     wave_lds_sync();
@@ -729,7 +743,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             const int r = 4 * lg + i;
             if (ln == ngw && r < R) {
                 const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
-                a.ws_ml[slot * 2 + 1] = cz[i];
+                a.ws_ml[slot * 2 + 1] = cz[i] * (1.0f / (float)(1 << KZ));
             }
         }
         if (lg == 0 && ln < R) {
