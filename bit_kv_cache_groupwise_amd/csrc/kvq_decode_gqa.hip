@@ -14,14 +14,14 @@
 // waves share every 32-token tile, wave w owning 64 of the head's channels
 // (128 for 3-bit keys). Per tile a wave computes
 //   partial scores^T[t][r] = 2^16 * sum_c A[t][c] B[c][r] + bias[r] over its channels,
-//     A = key codes of token t as fp16 subnormals code * 2^(sh-24), unpacked
+//     A = key codes of token t as fp16 values (code << sh) * 2^-24, unpacked
 //         from the lane's own row words (exact),
 //     B = q'_rc * s_c in fp16 hi + lo parts (two MFMAs), where q' carries the
 //         2^(8-sh) that undoes the code shift,
 //     bias[r] = sum_c q_rc z_c on the VALU;
 //   the waves' partial scores are summed through LDS (one barrier per tile);
-//   O[r][c]  += 2^(24-KB) * sum_t (2^KB p_rt s_t,g(c))[hi + lo] V[t][c],
-//     V = value codes as fp16 subnormals, read from an LDS byte tile;
+//   O[r][c]  += 2^(24-KB-sh) * sum_t (2^KB p_rt s_t,g(c))[hi + lo] V[t][c],
+//     V = value codes as fp16 values (code << sh) * 2^-24, from an LDS byte tile;
 //   Z[r][g]  += 2^-KZ * sum_t (2^KZ p_rt)[hi + lo] * (z_t,g | 1),
 //     one MFMA against a [token][group] fragment of zero points whose column
 //     after the last group is 1, so it also yields the softmax denominator.
@@ -121,53 +121,57 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
     lo = pk_rtz(rem_lo(hi, x0), rem_hi(hi, x1));
 }
 
+// Integer codes enter the MFMAs as fp16 values code * 2^(sh-24): subnormals,
+// or normals of exponent 1, where the value is still (code << sh) * 2^-24.
+// The MFMA's sum of products loses low bits of products whose subnormal
+// operand uses only the bottom of the mantissa, so every code is shifted until
+// its top bit reaches bit 9 or 10 (code << sh < 2048): sh = code_shift(B).
+__host__ __device__ constexpr int code_shift(int B) { return B == 2 ? 9 : B == 3 ? 8 : B == 4 ? 7 : B == 6 ? 5 : 3; }
+
 // Key-code fragments: chunk k of a lane's channel range (8 channels) as 8 fp16
 // halves. Half j of the fragment holds channel 8k + PERM[j] of the range as the
-// integer code << SHIFT[j], i.e. the fp16 subnormal code * 2^(SHIFT[j]-24).
+// integer code << code_shift(B).
 template <int B>
 struct KeyFrag;
 
 template <>
 struct KeyFrag<2> {
     static constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    static constexpr int SHIFT[8] = {0, 0, 2, 2, 4, 4, 6, 6};
     template <int K>
     static __device__ __forceinline__ void get(const uint32_t* w, Frag& f) {
+        // the chunk's two bytes (4 codes each) to the low byte of each half
         const uint32_t x = w[K / 2];
         const uint32_t y = (K & 1) ? __builtin_amdgcn_perm(x, x, 0x0c030c02u) : __builtin_amdgcn_perm(x, x, 0x0c010c00u);
-        f.u[0] = y & 0x00030003u;
-        f.u[1] = y & 0x000c000cu;
-        f.u[2] = y & 0x00300030u;
-        f.u[3] = y & 0x00c000c0u;
+        f.u[0] = (y << 9) & 0x06000600u;
+        f.u[1] = (y << 7) & 0x06000600u;
+        f.u[2] = (y << 5) & 0x06000600u;
+        f.u[3] = (y << 3) & 0x06000600u;
     }
 };
 
 template <>
 struct KeyFrag<4> {
     static constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    static constexpr int SHIFT[8] = {0, 0, 4, 4, 0, 0, 4, 4};
     template <int K>
     static __device__ __forceinline__ void get(const uint32_t* w, Frag& f) {
-        const uint32_t x = w[K];
-        const uint32_t y = x >> 8;
-        f.u[0] = x & 0x000f000fu;
-        f.u[1] = x & 0x00f000f0u;
-        f.u[2] = y & 0x000f000fu;
-        f.u[3] = y & 0x00f000f0u;
+        const uint32_t x = w[K];  // nibble i of each half to bits 7..10
+        f.u[0] = (x << 7) & 0x07800780u;
+        f.u[1] = (x << 3) & 0x07800780u;
+        f.u[2] = (x >> 1) & 0x07800780u;
+        f.u[3] = (x >> 5) & 0x07800780u;
     }
 };
 
 template <>
 struct KeyFrag<8> {
     static constexpr int PERM[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-    static constexpr int SHIFT[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     template <int K>
     static __device__ __forceinline__ void get(const uint32_t* w, Frag& f) {
-        const uint32_t x0 = w[2 * K], x1 = w[2 * K + 1];
-        f.u[0] = x0 & 0x00ff00ffu;
-        f.u[1] = __builtin_amdgcn_perm(x0, x0, 0x0c070c05u);
-        f.u[2] = x1 & 0x00ff00ffu;
-        f.u[3] = __builtin_amdgcn_perm(x1, x1, 0x0c070c05u);
+        const uint32_t x0 = w[2 * K], x1 = w[2 * K + 1];  // bytes to bits 3..10 of the halves
+        f.u[0] = (x0 << 3) & 0x07f807f8u;
+        f.u[1] = (x0 >> 5) & 0x07f807f8u;
+        f.u[2] = (x1 << 3) & 0x07f807f8u;
+        f.u[3] = (x1 >> 5) & 0x07f807f8u;
     }
 };
 
@@ -183,29 +187,22 @@ __device__ __forceinline__ uint32_t unit_code(const uint32_t* w) {
 template <int B>
 struct KeyFragStraddle {
     static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
-    static constexpr int SHIFT[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    static constexpr int SH = code_shift(B);
     template <int K>
     static __device__ __forceinline__ void get(const uint32_t* w, Frag& f) {
         // chunk K covers codes 8K..8K+7 of the lane's range; a 32-code unit is B words
         const uint32_t* u = w + (K / 4) * B;
         constexpr int j0 = 8 * (K % 4);
-        f.u[0] = unit_code<B, j0 + 0>(u) | (unit_code<B, j0 + 1>(u) << 16);
-        f.u[1] = unit_code<B, j0 + 2>(u) | (unit_code<B, j0 + 3>(u) << 16);
-        f.u[2] = unit_code<B, j0 + 4>(u) | (unit_code<B, j0 + 5>(u) << 16);
-        f.u[3] = unit_code<B, j0 + 6>(u) | (unit_code<B, j0 + 7>(u) << 16);
+        f.u[0] = (unit_code<B, j0 + 0>(u) << SH) | (unit_code<B, j0 + 1>(u) << (16 + SH));
+        f.u[1] = (unit_code<B, j0 + 2>(u) << SH) | (unit_code<B, j0 + 3>(u) << (16 + SH));
+        f.u[2] = (unit_code<B, j0 + 4>(u) << SH) | (unit_code<B, j0 + 5>(u) << (16 + SH));
+        f.u[3] = (unit_code<B, j0 + 6>(u) << SH) | (unit_code<B, j0 + 7>(u) << (16 + SH));
     }
 };
 template <>
 struct KeyFrag<3> : KeyFragStraddle<3> {};
 template <>
 struct KeyFrag<6> : KeyFragStraddle<6> {};
-
-// Shift at which channel offset j (0..7 within an 8-channel window) sits in its
-// key fragment half: SHIFT[PERM^-1[j]].
-template <int B>
-__host__ __device__ constexpr int chan_shift(int j) {
-    return B == 2 ? 2 * (j & 3) : B == 4 ? 4 * (j & 1) : 0;
-}
 
 // One 32-channel value unit as 32 bytes (8 words), one code per byte. Byte
 // position p of the unit holds channel val_chan<B>(p).
@@ -347,7 +344,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     constexpr int ZROW = 40;                  // halves per row of the zero-point tile (padded)
     constexpr int KALIGN = pow2_align(D * BK / 8) < pow2_align(KWL * 4) ? pow2_align(D * BK / 8) : pow2_align(KWL * 4);
     constexpr int VALIGN = pow2_align(D * BV / 8) < pow2_align(BV * 4) ? pow2_align(D * BV / 8) : pow2_align(BV * 4);
-    constexpr int NSH = BK == 2 ? 4 : BK == 4 ? 2 : 1;  // distinct code shifts of the key fragments
+    constexpr int KSH = code_shift(BK), VSH = code_shift(BV);
     // Softmax weight scales (p <= 1): 2^KB p * s <= 2^(BV+2) * range / (2^BV - 1)
     // stays far inside fp16 while small weights stay normal; 2^KZ p <= 16384.
     constexpr int KB = BV + 2, KZ = 14;
@@ -394,7 +391,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
 
     // ---- query ln of this kv head, channels cw0 + lg*DQ + [0, DQ), in registers:
-    // q' = q * scale * 2^(8 - chan_shift(c mod 8)) and its fp16 pairs in fragment order
+    // q' = q * scale * 2^(8 - KSH) and its fp16 pairs in fragment order
     float qf[DQ];
     uint32_t qh[DQ / 2];
     {
@@ -402,7 +399,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
 #pragma unroll
         for (int k = 0; k < NCH; ++k) load8_rt(a.q, qrow + 8 * k, a.in_dtype, qf + 8 * k);
 #pragma unroll
-        for (int j = 0; j < DQ; ++j) qf[j] = ln < R ? qf[j] * a.qscale * (float)(1 << (8 - chan_shift<BK>(j & 7))) : 0.f;
+        for (int j = 0; j < DQ; ++j) qf[j] = ln < R ? qf[j] * a.qscale * ((float)(1 << 8) / (float)(1 << KSH)) : 0.f;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
 #pragma unroll
@@ -494,9 +491,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     // sc[j] for query ln, token t0 + 8lg + j.
     auto key_scores_quant = [&](const Pref& P, float* sc) {
         f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-        float bz[NSH];
-#pragma unroll
-        for (int h = 0; h < NSH; ++h) bz[h] = 0.f;
+        float bz = 0.f;
         uint4 spc = *(const uint4*)&sp_lds[wave][4 * (lg * NCH)];
         uint4 zpc = *(const uint4*)&zp_lds[wave][4 * (lg * NCH)];
         static_for<NCH>([&](auto K) {
@@ -513,10 +508,8 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             for (int jj = 0; jj < 4; ++jj) {
                 const int j0 = 8 * k + KF::PERM[2 * jj], j1 = 8 * k + KF::PERM[2 * jj + 1];
                 mul_split(qh[4 * k + jj], qf[j0], qf[j1], sp[jj], bh.u[jj], bl.u[jj]);
-                constexpr int step = BK == 2 ? 2 : BK == 4 ? 4 : 1;
-                const int h0 = KF::SHIFT[2 * jj] / step, h1 = KF::SHIFT[2 * jj + 1] / step;
-                bz[h0] = mix_lo(zp[jj], qf[j0], bz[h0]);
-                bz[h1] = mix_hi(zp[jj], qf[j1], bz[h1]);
+                bz = mix_lo(zp[jj], qf[j0], bz);
+                bz = mix_hi(zp[jj], qf[j1], bz);
             }
             Frag a0, a1;
             KF::template get<k>(P.kw[0], a0);
@@ -528,10 +521,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             if constexpr (k + 1 < NCH) spc = spn, zpc = zpn;
             __builtin_amdgcn_sched_barrier(0);
         });
-        float bias = 0.f;
-#pragma unroll
-        for (int h = 0; h < NSH; ++h) bias = fmaf(bz[h], 1.0f / (float)(1 << (8 - chan_shift<BK>(h))), bias);
-        bias = col4_sum(bias);
+        const float bias = col4_sum(bz * ((float)(1 << KSH) / (float)(1 << 8)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sc[i] = fmaf(c0[i], kTwo16, bias);
@@ -549,8 +539,8 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             Frag bh, bl;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float x0 = qf[8 * k + 2 * jj] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj))));
-                const float x1 = qf[8 * k + 2 * jj + 1] * (1.0f / (float)(1 << (8 - chan_shift<BK>(2 * jj + 1))));
+                const float x0 = qf[8 * k + 2 * jj] * ((float)(1 << KSH) / (float)(1 << 8));
+                const float x1 = qf[8 * k + 2 * jj + 1] * ((float)(1 << KSH) / (float)(1 << 8));
                 split2(x0, x1, bh.u[jj], bl.u[jj]);
             }
 #pragma unroll
@@ -656,12 +646,19 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) mul_split(pb.u[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
             }
+            // code << VSH in each half: the high byte for 2- and 3-bit codes,
+            // else the low byte shifted
             const uint32_t* w = vb[b & 1];
             Frag f0, f1;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c040c00u);
-                f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c050c01u);
+                if constexpr (VSH == 8) {
+                    f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x040c000cu);
+                    f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x050c010cu);
+                } else {
+                    f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c040c00u) << VSH;
+                    f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c050c01u) << VSH;
+                }
             }
             acc[2 * b] = mfma(sh, f0, acc[2 * b]);
             acc[2 * b] = mfma(sl, f0, acc[2 * b]);
@@ -726,8 +723,9 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
         for (int b = 0; b < NSUB / 2; ++b) {
             // zero-point sum of (r, group), carrying 2^KZ
             const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv)) * (1.0f / (float)(1 << KZ));
-            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], kTwo24 / (float)(1 << KB), zs);
-            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], kTwo24 / (float)(1 << KB), zs);
+            constexpr float oscale = kTwo24 / (float)(1 << (KB + VSH));
+            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], oscale, zs);
+            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], oscale, zs);
         }
     }
     wave_lds_sync();

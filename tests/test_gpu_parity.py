@@ -261,3 +261,27 @@ def test_single_query_large_key_blocks(group_k):
         err = H.row_rel_err(out[s], H.attn_ref(w, q[s].float().numpy(), encs))
         assert np.all(err <= H.ATTN_TOL), (group_k, s, err.max())
     cache.close()
+
+
+@pytest.mark.parametrize("bits", [(2, 2), (8, 2), (2, 8), (8, 8)])
+def test_query_group_accuracy_at_low_bits(bits):
+    """Long, diffuse query-group attention at every extreme of the bit widths
+    stays two orders of magnitude inside the tolerance: the output is the small
+    difference of the code and zero-point sums, so any bias in the products of
+    small integer codes would show up here first."""
+    w = W.mixed_batch().scaled(num_seqs=1, lengths=(8192,), bits=(bits,))
+    R = w.q_heads // w.kv_heads
+    _note(f"[accuracy] bits={bits} T={w.lengths[0] + w.new_tokens}")
+    cache, prefix, new = _run_case(w)
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    k, v = H.full_seq(prefix, new, 0)
+    worst = 0.0
+    for h in (0, w.kv_heads - 1):
+        enc = H.encode(w, k, v, 0, h)
+        qs = q[0, h * R:(h + 1) * R].float().numpy().astype(np.float64)
+        ref = o.attend_heads(qs, [enc["k_hat"]], [enc["v_hat"]], w.softmax_scale)
+        worst = max(worst, float(H.row_rel_err(out[0, h * R:(h + 1) * R], ref).max()))
+    _note(f"[accuracy] bits={bits} worst row rel err {worst:.3e}")
+    assert worst <= 1e-4, (bits, worst)
+    cache.close()
