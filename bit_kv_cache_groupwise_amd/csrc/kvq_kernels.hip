@@ -437,11 +437,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 // Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
 // out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-    // grid = (q_heads, num_seqs, ceil(D / 64)): 64 channels per workgroup, its
-    // 4 waves take every 4th split and meet in LDS.
+    // grid = (q_heads, num_seqs, ceil(D / 16)): 16 channels per workgroup; its
+    // 256 threads are 16 split groups x 16 channels (split i goes to group
+    // i mod 16), meeting in LDS in a fixed order.
     const int hq = blockIdx.x, seq = blockIdx.y, D = a.head_dim;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int c = blockIdx.z * 64 + lane;
+    const int lane = threadIdx.x & 63, sg = threadIdx.x >> 4, cl = threadIdx.x & 15;
+    const int c = blockIdx.z * 16 + cl;
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
     if (a.split_floor) {
@@ -450,12 +451,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     }
     const int nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     if (nch == 0) {
-        if (wave == 0 && c < D) out[c] = 0.f;
+        if (sg == 0 && c < D) out[c] = 0.f;
         return;
     }
     const size_t base = ((size_t)seq * a.q_heads + hq) * a.max_chunks;
     const float* ml = a.ws_ml + base * 2;
-    float M = -INFINITY;
+    float M = -INFINITY;  // every wave computes the same maximum and denominator
     for (int i = lane; i < nch; i += 64) M = fmaxf(M, ml[2 * i]);
     M = wave_max(M);
     float L = 0.f;
@@ -464,21 +465,23 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
     float o = 0.f;
     if (c < D) {
         const float* src = a.ws_o + base * D + c;
-        int i = wave;
-        for (; i + 12 < nch; i += 16) {
-            const float v0 = src[(size_t)i * D], v1 = src[(size_t)(i + 4) * D];
-            const float v2 = src[(size_t)(i + 8) * D], v3 = src[(size_t)(i + 12) * D];
+        int i = sg;
+        for (; i + 16 < nch; i += 32) {
+            const float v0 = src[(size_t)i * D], v1 = src[(size_t)(i + 16) * D];
             o = fmaf(v0, exp2f(ml[2 * i] - M), o);
-            o = fmaf(v1, exp2f(ml[2 * (i + 4)] - M), o);
-            o = fmaf(v2, exp2f(ml[2 * (i + 8)] - M), o);
-            o = fmaf(v3, exp2f(ml[2 * (i + 12)] - M), o);
+            o = fmaf(v1, exp2f(ml[2 * (i + 16)] - M), o);
         }
-        for (; i < nch; i += 4) o = fmaf(src[(size_t)i * D], exp2f(ml[2 * i] - M), o);
+        if (i < nch) o = fmaf(src[(size_t)i * D], exp2f(ml[2 * i] - M), o);
     }
-    __shared__ float part[4][64];
-    part[wave][lane] = o;
+    __shared__ float part[16][16];
+    part[sg][cl] = o;
     __syncthreads();
-    if (wave == 0 && c < D) out[c] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / L;
+    if (sg == 0 && c < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) t += part[g][cl];
+        out[c] = t / L;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -562,7 +565,7 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 63) / 64), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 15) / 16), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -577,7 +580,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 63) / 64), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 15) / 16), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
