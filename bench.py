@@ -46,7 +46,10 @@ def algorithmic_head_bytes(T, D, axis_k, axis_v, Gk, Gv, bk, bv, ib):
 
 
 def rotation_for(step_bytes):
-    return max(1, math.ceil(4 * LLC_BYTES / max(step_bytes, 1)))
+    """Independent layer caches to cycle through so that a step never reads a
+    warm cache: 4x the last-level cache, capped where a step is too small for
+    HBM to matter (the small configurations are latency-bound)."""
+    return max(1, min(64, math.ceil(4 * LLC_BYTES / max(step_bytes, 1))))
 
 
 def main():
@@ -83,7 +86,8 @@ def main():
     step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
                      for T, (bk, bv) in zip(step_lens, w.bits)) * model_layers
     rot = args.rotate or rotation_for(step_bytes)
-    total_steps = args.warmup + args.steps
+    append_timing_steps = min(10, args.steps)  # after the timed region: events around the append alone
+    total_steps = args.warmup + args.steps + append_timing_steps
     appends_per_layer = math.ceil(total_steps / rot) + 1
     layers = rot * model_layers
     cap = [L + n_new * appends_per_layer for L in w.lengths]
@@ -133,33 +137,49 @@ def main():
     counts = [n_new] * S
     scale = w.softmax_scale
 
-    def step(st, events=None):
+    # arguments marshalled once, as a serving loop would
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    counts_c = kvq._i32(counts)
+    kp = [t.data_ptr() for t in new_k]
+    vp = [t.data_ptr() for t in new_v]
+    qp = [t.data_ptr() for t in qs]
+    out_p, ws_p, ws_b = out.data_ptr(), ws.data_ptr(), ws.numel()
+
+    def step(st, dec_events=None, app_events=None):
         base = (st % rot) * model_layers
         for m in range(model_layers):
             l = base + m
-            if events is not None:
-                events[m][0].record()
-            cache.append(l, new_k[st], new_v[st], counts)
-            if events is not None:
-                events[m][1].record()
-            kvq.kvq_decode_attention(cache.handle, l, qs[st], scale, out, ws, ws.numel())
-            if events is not None:
-                events[m][2].record()
+            if app_events is not None:
+                app_events[m][0].record()
+            kvq.kvq_quantize_append(cache.handle, l, kp[st], vp[st], counts_c, stream)
+            if dec_events is not None:
+                dec_events[m][0].record()
+            if app_events is not None:
+                app_events[m][1].record()
+            kvq.kvq_decode_attention(cache.handle, l, qp[st], scale, out_p, ws_p, ws_b, stream)
+            if dec_events is not None:
+                dec_events[m][1].record()
 
     for st in range(args.warmup):
         step(st)
     torch.cuda.synchronize()
-    evs = [[[ev(), ev(), ev()] for _ in range(model_layers)] for _ in range(args.steps)]
+    # the timed region carries one event pair per decode launch (its duration on
+    # the launch stream); the append alone is timed afterwards
+    evs = [[[ev(), ev()] for _ in range(model_layers)] for _ in range(args.steps)]
     # bytes attended in the timed steps (lengths grow by one token per append)
     lens0 = {l: cache.lengths(l) for l in range(layers)}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, dec_events=evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    dec_ms = [evs[i][m][1].elapsed_time(evs[i][m][2]) for i in range(args.steps) for m in range(model_layers)]
-    app_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(model_layers)]
+    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(model_layers)]
+    aevs = [[[ev(), ev()] for _ in range(model_layers)] for _ in range(append_timing_steps)]
+    for j in range(append_timing_steps):
+        step(args.warmup + args.steps + j, app_events=aevs[j])
+    torch.cuda.synchronize()
+    app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(model_layers)]
     # algorithmic bytes of every timed decode launch, from the lengths each saw
     lens = {l: list(v) for l, v in lens0.items()}
     dec_bytes = []

@@ -96,6 +96,8 @@ def _check(status: int, call: str):
 
 
 def _i32(seq):
+    if isinstance(seq, ctypes.Array):  # already marshalled (hot loops build it once)
+        return seq
     return (ctypes.c_int32 * len(seq))(*[int(v) for v in seq])
 
 
