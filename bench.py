@@ -232,12 +232,14 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources; a counter summary taken on other sources is stale."""
+def kernel_source_hash(sources=None):
+    """Hash of the named library sources (all of them when None); a counter
+    summary taken on other sources is stale."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_kv_cache_groupwise_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if sources is None else sorted(sources)
+    for name in names:
         if name.endswith((".hip", ".h", ".cpp")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + f.read())
@@ -248,13 +250,14 @@ def measured_traffic(workload):
     """HBM bytes per decode launch from the committed counter summary
     (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE of the decode
     kernel, each divided by the bytes-per-byte factor the same counter reads on
-    a plain copy of known size), or None when absent or taken on other sources."""
+    a plain copy of known size), or None when absent or when any source file of
+    the kernels it counted (listed in the summary) has changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(t.get("sources")):
         return None
     return t.get("traffic_bytes_per_launch")
 
