@@ -291,18 +291,18 @@ struct ValueAxpy {
 template <int B>
 __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
     if constexpr (B == 2) {
-        const uint2 v = *(const uint2*)p;
+        const uint2 v = ld_stream2(p);
         w[0] = v.x;
         w[1] = v.y;
     } else if constexpr (B == 4) {
-        const uint4 v = *(const uint4*)p;
+        const uint4 v = ld_stream4(p);
         w[0] = v.x;
         w[1] = v.y;
         w[2] = v.z;
         w[3] = v.w;
     } else if constexpr (B == 8) {
-        const uint4 v0 = *(const uint4*)p;
-        const uint4 v1 = *((const uint4*)p + 1);
+        const uint4 v0 = ld_stream4(p);
+        const uint4 v1 = ld_stream4(p + 4);
         w[0] = v0.x;
         w[1] = v0.y;
         w[2] = v0.z;
@@ -315,13 +315,13 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
         const uint2* q = (const uint2*)p;  // a 24-byte unit is 8-byte aligned
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const uint2 v = q[k];
+            const uint2 v = ld_stream2((const uint32_t*)(q + k));
             w[2 * k] = v.x;
             w[2 * k + 1] = v.y;
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < B; ++k) w[k] = p[k];
+        for (int k = 0; k < B; ++k) w[k] = ld_stream(p + k);
     }
 }
 
@@ -375,13 +375,13 @@ struct Stage {
 template <int N>
 __device__ __forceinline__ void load_words_n(const uint32_t* p, uint32_t* w) {
     if constexpr (N == 1) {
-        w[0] = p[0];
+        w[0] = ld_stream(p);
     } else if constexpr (N == 2) {
-        const uint2 v = *(const uint2*)p;
+        const uint2 v = ld_stream2(p);
         w[0] = v.x;
         w[1] = v.y;
     } else {
-        const uint4 v = *(const uint4*)p;
+        const uint4 v = ld_stream4(p);
         w[0] = v.x;
         w[1] = v.y;
         w[2] = v.z;
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
             const int t = min(t0 + s * TPW, tlast);
             load_words<BK>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + cg * BK, r.kw[s]);
             load_words<BV>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + cg * BV, r.vw[s]);
-            r.vmw[s] = vm[(size_t)t * vgpr + vg];
+            r.vmw[s] = ld_stream(vm + (size_t)t * vgpr + vg);
         }
         const int b0 = min(st, tlast) >> lgk;
         const int b1 = two_blocks ? min(b0 + 1, blast) : b0;
