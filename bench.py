@@ -62,6 +62,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="plain device copy of this size before timing (calibrates HBM byte counters); 0 = none")
     args = ap.parse_args()
@@ -195,6 +196,28 @@ def main():
     step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
     value = step_total_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = float(np.mean(dec_ms))
+    p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(dec_ms, [10, 50, 90]))
+
+    # ---- measured read ceiling: the library's plain streaming-read probe over
+    # the byte count of one decode call, timed the same way (one event pair on
+    # the launch stream) and kept cold by cycling through windows of a buffer
+    # at least 4x the last-level cache
+    probe_bytes = int(np.mean(dec_bytes)) // 16 * 16
+    win = (probe_bytes + 4095) // 4096 * 4096
+    nwin = max(8, math.ceil(4 * LLC_BYTES / win))
+    pbuf = torch.empty(win * nwin, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe_ms = []
+    for r in range(args.probe_reps + 2):
+        e0, e1 = ev(), ev()
+        e0.record()
+        kvq.kvq_read_probe(pbuf.data_ptr() + (r % nwin) * win, probe_bytes, sink.data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            probe_ms.append(e0.elapsed_time(e1))
+    del pbuf
+    ceiling_gbps = probe_bytes / (float(np.median(probe_ms)) * 1e-3) / 1e9
     dec_gbps = float(np.mean(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = S * n_new / (ms_per_step * 1e-3)
 
@@ -219,13 +242,18 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_attention_GBps": round(dec_gbps, 2),
         "decode_attention_us": round(dec_avg_ms * 1e3, 3),
+        "decode_attention_us_p10_p50_p90": [round(p10, 3), round(p50, 3), round(p90, 3)],
         "append_us": round(float(np.mean(app_ms)) * 1e3, 3),
         "quantize_GBps": round(quantize_gbps, 2),
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
         "prefill_tokens": prefill_tokens,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "kvq_decode_attention", "bytes_per_launch": int(np.mean(dec_bytes))},
+                     "kernel": "kvq_decode_attention", "bytes_per_launch": int(np.mean(dec_bytes)),
+                     "measured_ceiling": {"kernel": "kvq_read_probe", "bytes": probe_bytes,
+                                          "GBps": round(ceiling_gbps, 2),
+                                          "frac_of_peak": round(ceiling_gbps / HBM_PEAK_GBPS, 4),
+                                          "decode_frac_of_ceiling": round(dec_gbps / ceiling_gbps, 4)}},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)

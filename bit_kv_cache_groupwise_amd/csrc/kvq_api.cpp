@@ -555,4 +555,15 @@ kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float*
     return KVQ_OK;
 }
 
+kvq_status kvq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+    g_last_error.clear();
+    if (!buf || !sink) return fail(KVQ_ERR_ARG, "buffer or sink is NULL");
+    if (bytes % 16 != 0) return fail(KVQ_ERR_ARG, "bytes (%llu) is not a multiple of 16", (unsigned long long)bytes);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(KVQ_ERR_ALIGN, "buffer not 16-byte or sink not 4-byte aligned");
+    if (bytes == 0) return KVQ_OK;
+    hipError_t e = kvq::launch_read_probe(buf, bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the read probe");
+    return KVQ_OK;
+}
+
 }  // extern "C"

@@ -111,5 +111,6 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
                                : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
 }
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace kvq

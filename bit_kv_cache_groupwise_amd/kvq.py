@@ -33,7 +33,7 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
-            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version")
+            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -71,6 +71,7 @@ _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.kvq_dequantize.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
 _lib.kvq_seq_lengths.argtypes = [_P, ctypes.c_int32, _I32P]
+_lib.kvq_read_probe.argtypes = [_P, ctypes.c_uint64, _P, _P]
 _lib.kvq_get_region.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(kvq_region)]
 _lib.kvq_status_string.argtypes = [ctypes.c_int32]
 _lib.kvq_status_string.restype = ctypes.c_char_p
@@ -79,7 +80,7 @@ _lib.kvq_last_error.restype = ctypes.c_char_p
 _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
-           "kvq_seq_lengths", "kvq_get_region"):
+           "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -189,6 +190,11 @@ def kvq_decode_attention(handle, layer, q, softmax_scale, out, workspace, worksp
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.kvq_decode_attention(handle, layer, _ptr(q), ctypes.c_float(softmax_scale), _ptr(out),
                                      _ptr(workspace), workspace_bytes, _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_read_probe(buf, nbytes, sink, stream=None):
+    """Streaming read of nbytes of device memory at buf (measurement aid)."""
+    _check(_lib.kvq_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_read_probe")
 
 
 def kvq_dequantize(handle, layer, seq, k_out, v_out, stream=None):

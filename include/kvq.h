@@ -183,6 +183,14 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const voi
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t layer, int32_t seq, float* k_out, float* v_out,
                           void* stream);
 
+/* Measurement aid, not part of the method: read `bytes` (a multiple of 16)
+ * of device memory at `buf` (16-byte aligned) with the plainest streaming
+ * loop, so that a caller can time the HBM read ceiling the decode kernels are
+ * compared with. Nothing is written except possibly one word at `sink`
+ * (device, 4-byte aligned). bytes == 0 is a no-op. Errors: KVQ_ERR_ARG (NULL
+ * pointer, size not a multiple of 16), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+kvq_status kvq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
 /* Current cached lengths of `layer`: host array of num_seqs entries. */
 kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t* out);
 

@@ -285,3 +285,23 @@ def test_query_group_accuracy_at_low_bits(bits):
     _note(f"[accuracy] bits={bits} worst row rel err {worst:.3e}")
     assert worst <= 1e-4, (bits, worst)
     cache.close()
+
+
+def test_read_probe_reads_and_validates():
+    """The streaming-read probe bench.py times for the measured HBM ceiling:
+    it runs over a buffer of zeros without writing (the sink keeps its value)
+    and rejects sizes that are not whole 16-byte vectors and misaligned
+    pointers before launching anything."""
+    kvq = H.kvq()
+    buf = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    kvq.kvq_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr())
+    kvq.kvq_read_probe(buf.data_ptr(), 0, sink.data_ptr())
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_read_probe(buf.data_ptr(), 24, sink.data_ptr())
+    assert e.value.status == kvq.KVQ_ERR_ARG
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_read_probe(buf.data_ptr() + 8, 16, sink.data_ptr())
+    assert e.value.status == kvq.KVQ_ERR_ALIGN
