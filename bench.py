@@ -7,7 +7,9 @@ one included). The default workload is the Llama-2-7B-shaped cache (16
 sequences, 32 heads of 128 channels, 4096 cached tokens, fp16, 2-bit K
 per-channel / V per-token, groups of 32), one layer per step. Independent
 layer caches are rotated so that each step reads memory that is not resident
-in the 256 MB last-level cache.
+in the 256 MB last-level cache. A multi-layer workload (the GPT-2 shape, 12
+layers) appends into each layer and then decodes all of them in one
+kvq_decode_attention_layers call (--per-layer-decode: one call per layer).
 
 Prints one JSON line: metric/value (decode-step GB/s of algorithmic bytes),
 tokens/s, the decode kernel's roofline (HIP events on the launch stream) and
@@ -60,6 +62,8 @@ def main():
     ap.add_argument("--workload", default="llama2-7b",
                     choices=["tiny", "gpt2-small", "llama2-7b", "long-gqa", "mixed"])
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
+    ap.add_argument("--per-layer-decode", action="store_true",
+                    help="multi-layer workloads: one decode call per layer instead of one call for all layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -126,15 +130,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- per-step inputs, drawn up front
+    # ---- per-step inputs, drawn up front. A multi-layer step decodes all its
+    # layers in one kvq_decode_attention_layers call (one query per layer).
+    multi = model_layers > 1 and not args.per_layer_decode
+    dec_per_step = 1 if multi else model_layers
     new_k, new_v, qs = [], [], []
     for st in range(total_steps):
         k, v = W.draw_kv(w, 0, [n_new] * S, device=dev, stream=1 + st)
         new_k.append(k)
         new_v.append(v)
-        qs.append(W.draw_q(w, 0, device=dev, step=st))
-    out = torch.empty((S, w.q_heads, D), dtype=torch.float32, device=dev)
-    ws = cache.workspace()
+        if multi:
+            qs.append(torch.stack([W.draw_q(w, m, device=dev, step=st) for m in range(model_layers)]))
+        else:
+            qs.append(W.draw_q(w, 0, device=dev, step=st))
+    out = torch.empty(((model_layers,) if multi else ()) + (S, w.q_heads, D), dtype=torch.float32, device=dev)
+    ws = cache.workspace(model_layers if multi else 1)
     counts = [n_new] * S
     scale = w.softmax_scale
 
@@ -153,20 +163,27 @@ def main():
             if app_events is not None:
                 app_events[m][0].record()
             kvq.kvq_quantize_append(cache.handle, l, kp[st], vp[st], counts_c, stream)
-            if dec_events is not None:
-                dec_events[m][0].record()
             if app_events is not None:
                 app_events[m][1].record()
-            kvq.kvq_decode_attention(cache.handle, l, qp[st], scale, out_p, ws_p, ws_b, stream)
+            if not multi:
+                if dec_events is not None:
+                    dec_events[m][0].record()
+                kvq.kvq_decode_attention(cache.handle, l, qp[st], scale, out_p, ws_p, ws_b, stream)
+                if dec_events is not None:
+                    dec_events[m][1].record()
+        if multi:
             if dec_events is not None:
-                dec_events[m][1].record()
+                dec_events[0][0].record()
+            kvq.kvq_decode_attention_layers(cache.handle, base, model_layers, qp[st], scale, out_p, ws_p, ws_b, stream)
+            if dec_events is not None:
+                dec_events[0][1].record()
 
     for st in range(args.warmup):
         step(st)
     torch.cuda.synchronize()
     # the timed region carries one event pair per decode launch (its duration on
     # the launch stream); the append alone is timed afterwards
-    evs = [[[ev(), ev()] for _ in range(model_layers)] for _ in range(args.steps)]
+    evs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(args.steps)]
     # bytes attended in the timed steps (lengths grow by one token per append)
     lens0 = {l: cache.lengths(l) for l in range(layers)}
     t0 = time.perf_counter()
@@ -175,7 +192,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(model_layers)]
+    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(dec_per_step)]
     aevs = [[[ev(), ev()] for _ in range(model_layers)] for _ in range(append_timing_steps)]
     for j in range(append_timing_steps):
         step(args.warmup + args.steps + j, app_events=aevs[j])
@@ -183,14 +200,16 @@ def main():
     app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(model_layers)]
     # algorithmic bytes of every timed decode launch, from the lengths each saw
     lens = {l: list(v) for l, v in lens0.items()}
-    dec_bytes = []
+    dec_bytes = []  # per decode call (all model layers of a step when multi)
     for i in range(args.steps):
         base = ((args.warmup + i) % rot) * model_layers
+        per_layer = []
         for m in range(model_layers):
             l = base + m
             lens[l] = [x + n_new for x in lens[l]]
-            dec_bytes.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
-                                 for T, (bk, bv) in zip(lens[l], w.bits)))
+            per_layer.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib)
+                                 * H for T, (bk, bv) in zip(lens[l], w.bits)))
+        dec_bytes.extend([sum(per_layer)] if multi else per_layer)
     app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
     ms_per_step = wall_s * 1e3 / args.steps
     step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
@@ -236,7 +255,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": S, "kv_heads": H, "q_heads": w.q_heads, "head_dim": D,
                    "cached_tokens": list(sorted(set(w.lengths)))[:4] if len(set(w.lengths)) > 1 else w.lengths[0],
-                   "layers_per_step": model_layers, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
+                   "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
                    "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
@@ -249,7 +268,8 @@ def main():
         "prefill_tokens": prefill_tokens,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "kvq_decode_attention", "bytes_per_launch": int(np.mean(dec_bytes)),
+                     "kernel": "kvq_decode_attention_layers" if multi else "kvq_decode_attention",
+                     "bytes_per_launch": int(np.mean(dec_bytes)),
                      "measured_ceiling": {"kernel": "kvq_read_probe", "bytes": probe_bytes,
                                           "GBps": round(ceiling_gbps, 2),
                                           "frac_of_peak": round(ceiling_gbps / HBM_PEAK_GBPS, 4),

@@ -161,10 +161,10 @@ int group_size(const kvq_cache* c) { return c->g.q_heads / c->g.kv_heads; }
 
 // Tokens per decode split: a multiple of the key block, grown while the grid
 // stays above ~8 workgroups per compute unit, shrunk to fit 64 KB of LDS.
-int choose_chunk(const kvq_cache* c, int max_len) {
+int choose_chunk(const kvq_cache* c, int max_len, int n_layers) {
     const kvq_geometry& g = c->g;
     const int kmin = g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, g.group_k) : 64;
-    const long pairs = (long)g.num_seqs * g.kv_heads;
+    const long pairs = (long)g.num_seqs * g.kv_heads * n_layers;
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
         if (v >= kmin && v <= 1024 && v % kmin == 0 && (v & (v - 1)) == 0 &&
@@ -180,7 +180,7 @@ int choose_chunk(const kvq_cache* c, int max_len) {
 // Tokens per workgroup of the single-query kernel: a multiple of 64 and of the
 // key block; a sequence of length L gets
 // max(1, L / chunk) splits, the last one taking the remainder.
-int choose_split_mha(const kvq_cache* c, int max_len) {
+int choose_split_mha(const kvq_cache* c, int max_len, int n_layers) {
     const kvq_geometry& g = c->g;
     const int unit = std::max(64, g.group_k);
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
@@ -189,7 +189,7 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
     }
     // Aim at ~512 workgroups (two 4-wave workgroups per compute unit, resident
     // at once): long waves keep per-wave setup and the split merge small.
-    const long pairs = (long)g.num_seqs * g.kv_heads;
+    const long pairs = (long)g.num_seqs * g.kv_heads * n_layers;
     const long nsplit = std::max(1L, 512L / pairs);
     const long cw = (max_len / nsplit) / unit * unit;
     return (int)std::max<long>(unit, cw);
@@ -200,7 +200,8 @@ int choose_split_mha(const kvq_cache* c, int max_len) {
 // in rounds of the resident count (three 64-channel waves per SIMD, head_dim/64
 // waves per workgroup). The choice minimises sum over launches of
 // rounds * (tokens per workgroup + a fixed per-workgroup cost of 128 tokens).
-int choose_split_gqa(const kvq_cache* c, const int32_t* lens) {
+// lens: [n_layers][num_seqs], the layers of one launch.
+int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
     const kvq_geometry& g = c->g;
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
@@ -213,7 +214,9 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens) {
         long cost = 0;
         for (const auto& pr : c->pairs) {
             long wgs = 0;
-            for (int i = 0; i < pr.count; ++i) wgs += (lens[c->pair_list[pr.offset + i]] + cw - 1) / cw;
+            for (int l = 0; l < n_layers; ++l)
+                for (int i = 0; i < pr.count; ++i)
+                    wgs += (lens[(size_t)l * g.num_seqs + c->pair_list[pr.offset + i]] + cw - 1) / cw;
             wgs *= g.kv_heads;
             cost += (wgs + slots - 1) / slots * (cw + 128);
         }
@@ -441,12 +444,16 @@ size_t kvq_decode_workspace_size(const kvq_cache* c) {
     return align_up(slots * 2 * 4, kvq::kAlign) + align_up(slots * g.head_dim * 4, kvq::kAlign);
 }
 
-kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, float softmax_scale, float* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-    g_last_error.clear();
-    if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
+}  // extern "C"
+
+namespace {
+
+// Decode attention of layers [layer, layer + n_layers) in one launch per
+// kernel (1 <= n_layers <= 64, checked by the callers; the length-buffer
+// parities travel as a 64-bit mask). q, out: [n_layers][S][Hq][D].
+kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, const void* q, float softmax_scale,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
     const kvq_geometry& g = c->g;
-    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
     if (group_size(c) > kvq::kMaxQueryGroup)
         return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d", group_size(c), kvq::kMaxQueryGroup);
     if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
@@ -454,15 +461,17 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     if (!aligned(q, in_bytes(g.in_dtype)) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "q or out misaligned");
     const int S = g.num_seqs;
     const int32_t* lens = &c->lens[(size_t)layer * S];
-    const int max_len = *std::max_element(lens, lens + S);
+    const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     const bool mha = group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
     bool gqa = group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
                kvq::mha_supported(g.head_dim);
     for (const auto& pr : c->pairs)  // a lane's key channels must start on a word boundary
         gqa = gqa && (g.head_dim * pr.bk) % 128 == 0;
-    const int C = mha ? choose_split_mha(c, max_len) : gqa ? choose_split_gqa(c, lens) : choose_chunk(c, max_len);
+    const int C = mha   ? choose_split_mha(c, max_len, n_layers)
+                  : gqa ? choose_split_gqa(c, lens, n_layers)
+                        : choose_chunk(c, max_len, n_layers);
     const int max_chunks = mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C);
-    const uint64_t slots = (uint64_t)S * g.q_heads * max_chunks;
+    const uint64_t slots = (uint64_t)n_layers * S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
     const uint64_t need = ml_bytes + align_up(slots * g.head_dim * 4, kvq::kAlign);
     if (!workspace || workspace_bytes < need)
@@ -492,6 +501,11 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     a.max_chunks = max_chunks;
     a.counters = (int32_t*)(c->table + c->tl.ctr_off);
     a.waves_per_group = 4;
+    a.n_layers = n_layers;
+    a.layers_total = g.layers;
+    a.layer0 = layer;
+    a.len_base = (const int32_t*)(c->table + c->tl.len_off);
+    for (int i = 0; i < n_layers; ++i) a.len_parity |= (uint64_t)(c->parity[layer + i] & 1) << i;
     a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
     if (mha) {
@@ -521,6 +535,29 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     hipError_t e = kvq::launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "launching decode attention");
     return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    return decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_layers(const kvq_cache* c, int32_t layer0, int32_t n_layers, const void* q,
+                                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+    g_last_error.clear();
+    if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
+    if (n_layers < 1 || layer0 < 0 || layer0 > c->g.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    if (n_layers > 64) return fail(KVQ_ERR_UNSUPPORTED, "%d layers in one call (at most 64)", n_layers);
+    return decode_layers(c, layer0, n_layers, q, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float* k_out, float* v_out, void* stream) {

@@ -332,7 +332,9 @@ __device__ __forceinline__ void wg_lds_barrier() {
 // spills); 128-channel waves need more and run two.
 template <int D, int BK, int BV>
 __global__ __launch_bounds__(D / wave_channels<BK>() * 64)
-__attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void decode_gqa_kernel(DecodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void decode_gqa_kernel(DecodeArgs a0) {
+    int z = blockIdx.z;
+    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
     constexpr int DW = wave_channels<BK>();  // channels of this wave
     constexpr int NWV = D / DW;               // waves per workgroup (they share every tile)
     constexpr int NT = 64 * NWV;
@@ -365,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     __shared__ __align__(16) uint16_t st_lds[NWV][4][32];     // value scales [group][token]
     __shared__ __align__(16) uint16_t zt_lds[NWV][16][ZROW];  // value zero points [group][token]; row G = 1.0
 
-    const int seq = a.seq_list ? a.seq_list[blockIdx.z] : (int)blockIdx.z;
+    const int seq = a.seq_list ? a.seq_list[z] : z;
     const int kvh = blockIdx.y, split = blockIdx.x;
     const int len = a.len[seq];
     const int CW = a.chunk;
@@ -787,7 +789,7 @@ hipError_t gqa_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s)
 #define KVQ_GCAT(a, b) KVQ_GCAT2(a, b)
 hipError_t KVQ_GCAT(launch_decode_gqa_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                            hipStream_t s) {
-    dim3 grid(a.max_chunks, a.kv_heads, nseqs);
+    dim3 grid(a.max_chunks, a.kv_heads, nseqs * a.n_layers);
     return gqa_bk<KVQ_GQA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
 }
 

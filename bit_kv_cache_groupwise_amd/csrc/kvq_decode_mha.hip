@@ -412,7 +412,9 @@ __device__ __forceinline__ float unit_sum(float v) {
 }
 
 template <int D, int BK, int BV, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
+    int z = blockIdx.z;
+    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
     constexpr int UPR = D / 32;   // units per row = lanes per token
     constexpr int TPW = 64 / UPR; // tokens per sub-tile
     constexpr int KPL = D / 64;   // channels per lane in the per-block prologue
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a) {
     __shared__ float mrg_ml[NW][2];
     constexpr int NT = NW * 64;  // threads
 
-    const int seq = a.seq_list ? a.seq_list[blockIdx.z] : (int)blockIdx.z;
+    const int seq = a.seq_list ? a.seq_list[z] : z;
     const int kvh = blockIdx.y, split = blockIdx.x;
     const int len = a.len[seq];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -738,7 +740,7 @@ hipError_t launch_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t
 #define KVQ_CAT(a, b) KVQ_CAT2(a, b)
 hipError_t KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                           hipStream_t s) {
-    dim3 grid(a.max_chunks, a.kv_heads, nseqs);
+    dim3 grid(a.max_chunks, a.kv_heads, nseqs * a.n_layers);
     return launch_bk<KVQ_MHA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
 }
 

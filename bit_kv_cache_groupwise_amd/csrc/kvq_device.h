@@ -25,6 +25,23 @@ __device__ __forceinline__ uint4 ld_stream4(const uint32_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The arguments of the layer that workgroup index z of a multi-layer launch
+// serves (per_layer indices per layer); z becomes the index within the layer.
+__device__ __forceinline__ DecodeArgs layer_args(const DecodeArgs& a0, int& z, int per_layer) {
+    if (a0.n_layers <= 1) return a0;
+    const int lz = z / per_layer;
+    z -= lz * per_layer;
+    DecodeArgs a = a0;
+    const size_t rows = (size_t)lz * a.num_seqs * a.q_heads;  // query rows of the layers before
+    a.table += (size_t)lz * a.num_seqs;
+    a.len = a.len_base + ((size_t)((a.len_parity >> lz) & 1u) * a.layers_total + a.layer0 + lz) * a.num_seqs;
+    a.q = (const uint8_t*)a.q + rows * a.head_dim * (a.in_dtype == 0 ? 4 : 2);
+    a.out += rows * a.head_dim;
+    a.ws_ml += rows * a.max_chunks * 2;
+    a.ws_o += rows * a.max_chunks * a.head_dim;
+    return a;
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
 }

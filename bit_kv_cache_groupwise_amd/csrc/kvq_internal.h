@@ -77,6 +77,15 @@ struct DecodeArgs {
     int32_t split_floor;        // splits per seq: 0 -> ceil(len/chunk), 1 -> max(1, len/chunk)
     int32_t log2_group_k, log2_group_v;
     int32_t waves_per_group;    // single-query kernel: waves per workgroup (4)
+    // Several consecutive layers in one launch (n_layers > 1): the grid's
+    // sequence index (z of the decode grids, y of the merge grid) runs over
+    // n_layers equal ranges, one per layer; layer_args() maps a workgroup to
+    // its layer's table, lengths, q, out and workspace slices.
+    int32_t n_layers;           // 1 for a single-layer call
+    int32_t layers_total;       // layers of the cache
+    int32_t layer0;             // first layer of the launch
+    uint64_t len_parity;        // bit i: current length buffer of layer layer0 + i
+    const int32_t* len_base;    // both length buffers, [2][layers_total][num_seqs]
 };
 
 struct DequantArgs {

@@ -289,9 +289,11 @@ __device__ __forceinline__ void value_pass(const uint8_t* vc, const uint32_t* vm
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     extern __shared__ float smem[];
-    const int seq = blockIdx.z, kvh = blockIdx.y, chunk = blockIdx.x;
+    int z = blockIdx.z;
+    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
+    const int seq = z, kvh = blockIdx.y, chunk = blockIdx.x;
     const int len = a.len[seq];
     const int C = a.chunk, t0 = chunk * C;
     if (t0 >= len) return;
@@ -436,11 +438,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
 // Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
 // out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-    // grid = (q_heads, num_seqs, ceil(D / 16)): 16 channels per workgroup; its
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
+    // grid = (q_heads, num_seqs x layers, ceil(D / 16)): 16 channels per workgroup; its
     // 256 threads are 16 split groups x 16 channels (split i goes to group
     // i mod 16), meeting in LDS in a fixed order.
-    const int hq = blockIdx.x, seq = blockIdx.y, D = a.head_dim;
+    int y = blockIdx.y;
+    const DecodeArgs a = layer_args(a0, y, gridDim.y / a0.n_layers);
+    const int hq = blockIdx.x, seq = y, D = a.head_dim;
     const int lane = threadIdx.x & 63, sg = threadIdx.x >> 4, cl = threadIdx.x & 15;
     const int c = blockIdx.z * 16 + cl;
     const int len = a.len[seq];
@@ -565,13 +569,14 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 15) / 16), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs * a.n_layers, (a.head_dim + 15) / 16), dim3(kThreads), 0, s,
+                       a);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int R = a.q_heads / a.kv_heads;
-    dim3 grid(a.max_chunks, a.kv_heads, a.num_seqs);
+    dim3 grid(a.max_chunks, a.kv_heads, a.num_seqs * a.n_layers);
     const size_t lds = decode_lds_bytes(R, a.head_dim, a.chunk);
     switch (a.in_dtype) {
         case 0: hipLaunchKernelGGL(decode_split_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
@@ -580,7 +585,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs, (a.head_dim + 15) / 16), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs * a.n_layers, (a.head_dim + 15) / 16), dim3(kThreads), 0, s,
+                       a);
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
-            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe")
+            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -69,6 +69,8 @@ _lib.kvq_quantize_append.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_decode_workspace_size.argtypes = [_P]
 _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.kvq_decode_attention_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_float, _P, _P,
+                                             ctypes.c_size_t, _P]
 _lib.kvq_dequantize.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
 _lib.kvq_seq_lengths.argtypes = [_P, ctypes.c_int32, _I32P]
 _lib.kvq_read_probe.argtypes = [_P, ctypes.c_uint64, _P, _P]
@@ -80,7 +82,7 @@ _lib.kvq_last_error.restype = ctypes.c_char_p
 _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
-           "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe"):
+           "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -192,6 +194,15 @@ def kvq_decode_attention(handle, layer, q, softmax_scale, out, workspace, worksp
                                      _ptr(workspace), workspace_bytes, _stream(stream)), "kvq_decode_attention")
 
 
+def kvq_decode_attention_layers(handle, layer0, n_layers, q, softmax_scale, out, workspace, workspace_bytes=None,
+                                stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.kvq_decode_attention_layers(handle, layer0, n_layers, _ptr(q), ctypes.c_float(softmax_scale),
+                                            _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "kvq_decode_attention_layers")
+
+
 def kvq_read_probe(buf, nbytes, sink, stream=None):
     """Streaming read of nbytes of device memory at buf (measurement aid)."""
     _check(_lib.kvq_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_read_probe")
@@ -258,10 +269,12 @@ class Cache:
     def append(self, layer, k_new, v_new, n_new, stream=None):
         kvq_quantize_append(self.handle, layer, k_new, v_new, n_new, stream)
 
-    def workspace(self):
+    def workspace(self, n_layers=1):
+        """Decode workspace for calls covering up to n_layers layers (grown on demand)."""
         import torch
-        if self._ws is None:
-            self._ws = torch.empty(kvq_decode_workspace_size(self.handle), dtype=torch.uint8, device=self.codes.device)
+        need = n_layers * kvq_decode_workspace_size(self.handle)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.codes.device)
         return self._ws
 
     def decode(self, layer, q, softmax_scale, out=None, stream=None):
@@ -271,6 +284,17 @@ class Cache:
             out = torch.empty((g.num_seqs, g.q_heads, g.head_dim), dtype=torch.float32, device=q.device)
         ws = self.workspace()
         kvq_decode_attention(self.handle, layer, q, softmax_scale, out, ws, ws.numel(), stream)
+        return out
+
+    def decode_layers(self, layer0, n_layers, q, softmax_scale, out=None, stream=None):
+        """Decode attention of layers [layer0, layer0 + n_layers) in one call;
+        q: [n_layers][num_seqs][q_heads][head_dim]."""
+        import torch
+        g = self.geom
+        if out is None:
+            out = torch.empty((n_layers, g.num_seqs, g.q_heads, g.head_dim), dtype=torch.float32, device=q.device)
+        ws = self.workspace(n_layers)
+        kvq_decode_attention_layers(self.handle, layer0, n_layers, q, softmax_scale, out, ws, ws.numel(), stream)
         return out
 
     def dequantize(self, layer, seq, stream=None):

@@ -175,6 +175,19 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvq_decode_attention for the n_layers consecutive layers [layer0, layer0 +
+ * n_layers) in one call whose kernels each cover all of them: the decode step
+ * of a whole model whose per-layer caches are too small to fill the GPU alone.
+ * Layer layer0 + i reads q + i * num_seqs * q_heads * head_dim elements and
+ * writes out + i * num_seqs * q_heads * head_dim floats; the results equal n_layers
+ * single-layer calls up to the summation order of split partials. workspace:
+ * at least n_layers * kvq_decode_workspace_size(cache) bytes, 256-byte aligned.
+ * 1 <= n_layers <= 64 (more: KVQ_ERR_UNSUPPORTED); other errors as for
+ * kvq_decode_attention, checked before any launch. */
+kvq_status kvq_decode_attention_layers(const kvq_cache* cache, int32_t layer0, int32_t n_layers, const void* q,
+                                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* The unfused path ([N] "Kuantisasi dapat memindahkan pekerjaan ke decode
  * path": dequantize into a temporary floating-point tensor): write x_hat =
  * fma(code, s, z) in float32 for every cached token of one sequence, residual

@@ -305,3 +305,51 @@ def test_read_probe_reads_and_validates():
     with pytest.raises(kvq.KVQError) as e:
         kvq.kvq_read_probe(buf.data_ptr() + 8, 16, sink.data_ptr())
     assert e.value.status == kvq.KVQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama", "mixed", "gqa_ktoken"])
+def test_multi_layer_decode(name):
+    """kvq_decode_attention_layers over three layers (their length buffers at
+    different parities: layer 1 is filled in three appends) equals one
+    kvq_decode_attention per layer up to the summation order of split partials
+    (the split choice sees every layer's workgroups), the last layer meets the
+    oracle tolerance, and a span starting at layer 1 reads layers 1 and 2."""
+    L = 3
+    w = CASES[name].scaled(layers=L)
+    _note(f"[multi-layer] case={name} layers={L} S={w.num_seqs} Hq={w.q_heads} Hkv={w.kv_heads} D={w.head_dim}")
+    kvq = H.kvq()
+    cache = H.make_cache(w, layers=L)
+    hist = {}
+    for layer in range(L):
+        prefix, new = H.history(w, layer)
+        # layer 1: the prefix in two appends, so three in all and the other length buffer
+        H.append_chunks(cache, layer, prefix[0], prefix[1], prefix[2], [max(w.lengths) // 2 + 1] if layer == 1
+                        else None)
+        H.append_chunks(cache, layer, new[0], new[1], new[2])
+        hist[layer] = (prefix, new)
+    torch.cuda.synchronize()
+    q = torch.stack([W.draw_q(w, layer) for layer in range(L)]).cuda()
+    multi = cache.decode_layers(0, L, q, w.softmax_scale).cpu().numpy()
+    tail = cache.decode_layers(1, L - 1, q[1:].contiguous(), w.softmax_scale).cpu().numpy()
+    for layer in range(L):
+        single = cache.decode(layer, q[layer].contiguous(), w.softmax_scale).cpu().numpy()
+        assert np.max(H.row_rel_err(multi[layer], single)) < 2e-5, layer
+        if layer >= 1:
+            assert np.max(H.row_rel_err(tail[layer - 1], single)) < 2e-5, layer
+    layer = L - 1
+    prefix, new = hist[layer]
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.encode(w, k, v, s, h) for h in range(w.kv_heads)]
+        ref = H.attn_ref(w, q[layer, s].float().cpu().numpy(), encs)
+        assert np.all(H.row_rel_err(multi[layer, s], ref) <= H.ATTN_TOL), (name, s)
+    ws = cache.workspace(L)
+    out = torch.empty_like(q, dtype=torch.float32)
+    for args, status in (((0, 0), kvq.KVQ_ERR_ARG), ((2, 2), kvq.KVQ_ERR_ARG), ((-1, 2), kvq.KVQ_ERR_ARG)):
+        with pytest.raises(kvq.KVQError) as e:
+            kvq.kvq_decode_attention_layers(cache.handle, args[0], args[1], q, w.softmax_scale, out, ws, ws.numel())
+        assert e.value.status == status
+    with pytest.raises(kvq.KVQError) as e:
+        kvq.kvq_decode_attention_layers(cache.handle, 0, L, q, w.softmax_scale, out, ws, 0)
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    cache.close()
