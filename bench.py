@@ -8,8 +8,9 @@ sequences, 32 heads of 128 channels, 4096 cached tokens, fp16, 2-bit K
 per-channel / V per-token, groups of 32), one layer per step. Independent
 layer caches are rotated so that each step reads memory that is not resident
 in the 256 MB last-level cache. A multi-layer workload (the GPT-2 shape, 12
-layers) appends into each layer and then decodes all of them in one
-kvq_decode_attention_layers call (--per-layer-decode: one call per layer).
+layers) appends into all of them in one kvq_quantize_append_layers call and
+decodes them in one kvq_decode_attention_layers call (--per-layer-decode: one
+append and one decode call per layer).
 
 Prints one JSON line: metric/value (decode-step GB/s of algorithmic bytes),
 tokens/s, the decode kernel's roofline (HIP events on the launch stream) and
@@ -63,7 +64,7 @@ def main():
                     choices=["tiny", "gpt2-small", "llama2-7b", "long-gqa", "mixed"])
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
     ap.add_argument("--per-layer-decode", action="store_true",
-                    help="multi-layer workloads: one decode call per layer instead of one call for all layers")
+                    help="multi-layer workloads: one append and one decode call per layer instead of one each for all layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -136,9 +137,15 @@ def main():
     dec_per_step = 1 if multi else model_layers
     new_k, new_v, qs = [], [], []
     for st in range(total_steps):
-        k, v = W.draw_kv(w, 0, [n_new] * S, device=dev, stream=1 + st)
-        new_k.append(k)
-        new_v.append(v)
+        if multi:
+            kv = [W.draw_kv(w, m, [n_new] * S, device=dev, stream=1 + st) for m in range(model_layers)]
+            new_k.append(torch.stack([x[0] for x in kv]))
+            new_v.append(torch.stack([x[1] for x in kv]))
+            del kv
+        else:
+            k, v = W.draw_kv(w, 0, [n_new] * S, device=dev, stream=1 + st)
+            new_k.append(k)
+            new_v.append(v)
         if multi:
             qs.append(torch.stack([W.draw_q(w, m, device=dev, step=st) for m in range(model_layers)]))
         else:
@@ -158,6 +165,18 @@ def main():
 
     def step(st, dec_events=None, app_events=None):
         base = (st % rot) * model_layers
+        if multi:
+            if app_events is not None:
+                app_events[0][0].record()
+            kvq.kvq_quantize_append_layers(cache.handle, base, model_layers, kp[st], vp[st], counts_c, stream)
+            if app_events is not None:
+                app_events[0][1].record()
+            if dec_events is not None:
+                dec_events[0][0].record()
+            kvq.kvq_decode_attention_layers(cache.handle, base, model_layers, qp[st], scale, out_p, ws_p, ws_b, stream)
+            if dec_events is not None:
+                dec_events[0][1].record()
+            return
         for m in range(model_layers):
             l = base + m
             if app_events is not None:
@@ -165,18 +184,11 @@ def main():
             kvq.kvq_quantize_append(cache.handle, l, kp[st], vp[st], counts_c, stream)
             if app_events is not None:
                 app_events[m][1].record()
-            if not multi:
-                if dec_events is not None:
-                    dec_events[m][0].record()
-                kvq.kvq_decode_attention(cache.handle, l, qp[st], scale, out_p, ws_p, ws_b, stream)
-                if dec_events is not None:
-                    dec_events[m][1].record()
-        if multi:
             if dec_events is not None:
-                dec_events[0][0].record()
-            kvq.kvq_decode_attention_layers(cache.handle, base, model_layers, qp[st], scale, out_p, ws_p, ws_b, stream)
+                dec_events[m][0].record()
+            kvq.kvq_decode_attention(cache.handle, l, qp[st], scale, out_p, ws_p, ws_b, stream)
             if dec_events is not None:
-                dec_events[0][1].record()
+                dec_events[m][1].record()
 
     for st in range(args.warmup):
         step(st)
@@ -193,11 +205,11 @@ def main():
     t1 = time.perf_counter()
     wall_s = t1 - t0
     dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(dec_per_step)]
-    aevs = [[[ev(), ev()] for _ in range(model_layers)] for _ in range(append_timing_steps)]
+    aevs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(append_timing_steps)]
     for j in range(append_timing_steps):
         step(args.warmup + args.steps + j, app_events=aevs[j])
     torch.cuda.synchronize()
-    app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(model_layers)]
+    app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(dec_per_step)]
     # algorithmic bytes of every timed decode launch, from the lengths each saw
     lens = {l: list(v) for l, v in lens0.items()}
     dec_bytes = []  # per decode call (all model layers of a step when multi)

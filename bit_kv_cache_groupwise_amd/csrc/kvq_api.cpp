@@ -350,21 +350,28 @@ kvq_status kvq_get_region(const kvq_cache* c, int32_t layer, int32_t seq, kvq_re
     return KVQ_OK;
 }
 
-kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new,
-                               const int32_t* n_new, void* stream) {
-    g_last_error.clear();
-    if (!c || !n_new) return fail(KVQ_ERR_ARG, "cache or n_new is NULL");
+}  // extern "C"
+
+namespace {
+
+// Quantize-append of the same per-sequence counts into layers [layer, layer +
+// n_layers) in one launch (1 <= n_layers <= 64, checked by the callers).
+// k_new, v_new: [n_layers][sum n_new][kv_heads][head_dim].
+kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
+                         const int32_t* n_new, void* stream) {
     const kvq_geometry& g = c->g;
-    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
     const int S = g.num_seqs;
-    int32_t* lens = &c->lens[(size_t)layer * S];
     long total = 0;
     int max_n = 0;
     bool uniform = true;
     for (int s = 0; s < S; ++s) {
         if (n_new[s] < 0) return fail(KVQ_ERR_ARG, "n_new[%d] = %d is negative", s, n_new[s]);
-        if ((long)lens[s] + n_new[s] > c->cap[s])
-            return fail(KVQ_ERR_CAPACITY, "sequence %d: length %d + %d exceeds capacity %d", s, lens[s], n_new[s], c->cap[s]);
+        for (int l = layer; l < layer + n_layers; ++l) {
+            const int len = c->lens[(size_t)l * S + s];
+            if ((long)len + n_new[s] > c->cap[s])
+                return fail(KVQ_ERR_CAPACITY, "layer %d sequence %d: length %d + %d exceeds capacity %d", l, s, len,
+                            n_new[s], c->cap[s]);
+        }
         total += n_new[s];
         max_n = std::max(max_n, n_new[s]);
         uniform = uniform && n_new[s] == n_new[0];
@@ -420,20 +427,53 @@ kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, c
         a.in_dtype = g.in_dtype;
         a.axis = axes[t];
         a.rows_per_block = kvq::kThreads / (g.head_dim / 32);
+        a.n_layers = n_layers;
+        a.layers_total = g.layers;
+        a.layer0 = layer;
+        a.len_base = len_base;
+        for (int i = 0; i < n_layers; ++i) a.len_parity |= (uint64_t)(c->parity[layer + i] & 1) << i;
+        a.src_layer_bytes = (uint64_t)total * g.kv_heads * g.head_dim * in_bytes(g.in_dtype);
         if (axes[t] == KVQ_AXIS_TOKEN) {
             gx[t] = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
         } else {
             gx[t] = 1;
-            for (int s = 0; s < S; ++s)
-                gx[t] = std::max(gx[t], (lens[s] + n_new[s]) / groups[t] - lens[s] / groups[t]);
+            for (int l = layer; l < layer + n_layers; ++l)
+                for (int s = 0; s < S; ++s) {
+                    const int len = c->lens[(size_t)l * S + s];
+                    gx[t] = std::max(gx[t], (len + n_new[s]) / groups[t] - len / groups[t]);
+                }
         }
     }
     if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");
     hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], hs);
     if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
-    for (int s = 0; s < S; ++s) lens[s] += n_new[s];
-    c->parity[layer] ^= 1;
+    for (int l = layer; l < layer + n_layers; ++l) {
+        for (int s = 0; s < S; ++s) c->lens[(size_t)l * S + s] += n_new[s];
+        c->parity[l] ^= 1;
+    }
     return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize_append(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                               const int32_t* n_new, void* stream) {
+    g_last_error.clear();
+    if (!c || !n_new) return fail(KVQ_ERR_ARG, "cache or n_new is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    return append_layers(c, layer, 1, k_new, v_new, n_new, stream);
+}
+
+kvq_status kvq_quantize_append_layers(kvq_cache* c, int32_t layer0, int32_t n_layers, const void* k_new,
+                                      const void* v_new, const int32_t* n_new, void* stream) {
+    g_last_error.clear();
+    if (!c || !n_new) return fail(KVQ_ERR_ARG, "cache or n_new is NULL");
+    if (n_layers < 1 || layer0 < 0 || layer0 > c->g.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    if (n_layers > 64) return fail(KVQ_ERR_UNSUPPORTED, "%d layers in one call (at most 64)", n_layers);
+    return append_layers(c, layer0, n_layers, k_new, v_new, n_new, stream);
 }
 
 size_t kvq_decode_workspace_size(const kvq_cache* c) {

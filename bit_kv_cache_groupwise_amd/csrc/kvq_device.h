@@ -42,6 +42,20 @@ __device__ __forceinline__ DecodeArgs layer_args(const DecodeArgs& a0, int& z, i
     return a;
 }
 
+// The same for one tensor of a multi-layer append (grid z = layer * num_seqs + seq).
+__device__ __forceinline__ TensorArgs layer_args(const TensorArgs& a0, int& z, int per_layer) {
+    if (a0.n_layers <= 1) return a0;
+    const int lz = z / per_layer;
+    z -= lz * per_layer;
+    TensorArgs a = a0;
+    const size_t p = (a.len_parity >> lz) & 1u;
+    a.table += (size_t)lz * a.num_seqs;
+    a.len_in = a.len_base + (p * a.layers_total + a.layer0 + lz) * a.num_seqs;
+    if (a0.len_out) a.len_out = a.len_base + ((1 - p) * a.layers_total + a.layer0 + lz) * a.num_seqs;
+    a.src = (const uint8_t*)a.src + lz * a.src_layer_bytes;
+    return a;
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
 }

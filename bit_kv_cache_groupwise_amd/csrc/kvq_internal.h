@@ -55,6 +55,13 @@ struct TensorArgs {
     int32_t num_seqs, kv_heads, head_dim, group, in_dtype;
     int32_t rows_per_block;     // token axis: rows per workgroup
     int32_t axis;               // KVQ_AXIS_CHANNEL (0) or KVQ_AXIS_TOKEN (1)
+    // Several consecutive layers in one launch (n_layers > 1): the grid's z
+    // runs over n_layers ranges of num_seqs, one per layer (layer_args()).
+    int32_t n_layers;           // 1 for a single-layer call
+    int32_t layers_total, layer0;
+    uint64_t len_parity;        // bit i: current length buffer of layer layer0 + i
+    int32_t* len_base;          // both length buffers, [2][layers_total][num_seqs]
+    uint64_t src_layer_bytes;   // bytes of new rows per layer in src
 };
 
 struct DecodeArgs {

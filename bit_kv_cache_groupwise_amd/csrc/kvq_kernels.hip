@@ -210,11 +210,14 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
 
 // One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
 // keys, [gx_k, gx_k + gx_v) the values, each with its own axis.
-// grid = (gx_k + gx_v, kv_heads, num_seqs)
+// grid = (gx_k + gx_v, kv_heads, num_seqs x layers)
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k, TensorArgs v, int gx_k) {
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, TensorArgs v0, int gx_k) {
     extern __shared__ uint32_t quant_smem[];
-    const int seq = blockIdx.z, head = blockIdx.y;
+    int z = blockIdx.z, zv = blockIdx.z;
+    const TensorArgs k = layer_args(k0, z, gridDim.z / k0.n_layers);
+    const TensorArgs v = layer_args(v0, zv, gridDim.z / v0.n_layers);
+    const int seq = z, head = blockIdx.y;
     uint32_t* smem = quant_smem;
     if ((int)blockIdx.x < gx_k) {
         if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
@@ -556,7 +559,7 @@ size_t decode_lds_bytes(int R, int D, int C) {
 }
 
 hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, hipStream_t s) {
-    dim3 grid(gx_k + gx_v, k.kv_heads, k.num_seqs);
+    dim3 grid(gx_k + gx_v, k.kv_heads, k.num_seqs * k.n_layers);
     size_t lds = 0;
     for (const TensorArgs* t : {&k, &v})
         if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));

@@ -33,7 +33,8 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
-            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers")
+            "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
+            "kvq_quantize_append_layers")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -66,6 +67,7 @@ _lib.kvq_cache_create.argtypes = [ctypes.POINTER(kvq_geometry), _I32P, _U8P, _U8
 _lib.kvq_cache_destroy.argtypes = [_P]
 _lib.kvq_cache_destroy.restype = None
 _lib.kvq_quantize_append.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P]
+_lib.kvq_quantize_append_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_decode_workspace_size.argtypes = [_P]
 _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
@@ -82,7 +84,8 @@ _lib.kvq_last_error.restype = ctypes.c_char_p
 _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
-           "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers"):
+           "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers",
+            "kvq_quantize_append_layers"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -183,6 +186,11 @@ def kvq_quantize_append(handle, layer, k_new, v_new, n_new, stream=None):
            "kvq_quantize_append")
 
 
+def kvq_quantize_append_layers(handle, layer0, n_layers, k_new, v_new, n_new, stream=None):
+    _check(_lib.kvq_quantize_append_layers(handle, layer0, n_layers, _ptr(k_new), _ptr(v_new), _i32(n_new),
+                                           _stream(stream)), "kvq_quantize_append_layers")
+
+
 def kvq_decode_workspace_size(handle) -> int:
     return int(_lib.kvq_decode_workspace_size(handle))
 
@@ -268,6 +276,11 @@ class Cache:
 
     def append(self, layer, k_new, v_new, n_new, stream=None):
         kvq_quantize_append(self.handle, layer, k_new, v_new, n_new, stream)
+
+    def append_layers(self, layer0, k_new, v_new, n_new, stream=None):
+        """Append into layers [layer0, layer0 + len(k_new)); k_new, v_new:
+        [n_layers][sum n_new][kv_heads][head_dim]."""
+        kvq_quantize_append_layers(self.handle, layer0, int(k_new.shape[0]), k_new, v_new, n_new, stream)
 
     def workspace(self, n_layers=1):
         """Decode workspace for calls covering up to n_layers layers (grown on demand)."""

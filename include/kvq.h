@@ -175,6 +175,17 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvq_quantize_append of the same per-sequence counts n_new into each of the
+ * n_layers consecutive layers [layer0, layer0 + n_layers), in one launch: the
+ * append of a whole model's decode step. k_new, v_new: device, in_dtype,
+ * [n_layers][sum n_new][kv_heads][head_dim] (layer layer0 + i takes slice i).
+ * The stored bytes equal n_layers single-layer appends. 1 <= n_layers <= 64
+ * (more: KVQ_ERR_UNSUPPORTED); capacity is checked for every layer and
+ * sequence before anything is written (KVQ_ERR_CAPACITY); other errors as
+ * for kvq_quantize_append. */
+kvq_status kvq_quantize_append_layers(kvq_cache* cache, int32_t layer0, int32_t n_layers, const void* k_new,
+                                      const void* v_new, const int32_t* n_new, void* stream);
+
 /* kvq_decode_attention for the n_layers consecutive layers [layer0, layer0 +
  * n_layers) in one call whose kernels each cover all of them: the decode step
  * of a whole model whose per-layer caches are too small to fill the GPU alone.

@@ -353,3 +353,50 @@ def test_multi_layer_decode(name):
         kvq.kvq_decode_attention_layers(cache.handle, 0, L, q, w.softmax_scale, out, ws, 0)
     assert e.value.status == kvq.KVQ_ERR_WORKSPACE
     cache.close()
+
+
+@pytest.mark.parametrize("name", ["gpt2", "mixed", "gqa_ktoken"])
+def test_multi_layer_append(name):
+    """kvq_quantize_append_layers stores, in every layer, the bytes the oracle
+    gives for that layer's tokens (channel-axis blocks flushing in some layers
+    and not others, layers whose length buffers differ in parity), and rejects
+    an append that would overflow any one layer before writing anything."""
+    L = 3
+    w = CASES[name].scaled(layers=L)
+    _note(f"[multi-layer append] case={name} layers={L}")
+    kvq = H.kvq()
+    cache = H.make_cache(w, layers=L, extra=8)
+    hist = {l: H.history(w, l) for l in range(L)}
+    # the prefixes: layer 1 gets one token fewer at first, then one more append
+    for l in range(L):
+        (kp, vp, cp), _ = hist[l]
+        if l == 1:
+            first = [max(0, c - 1) for c in cp]
+            off = W.seq_offsets(cp)
+            pick = lambda t: torch.cat([t[off[s]:off[s] + first[s]] for s in range(len(cp))])
+            rest = lambda t: torch.cat([t[off[s] + first[s]:off[s + 1]] for s in range(len(cp))])
+            cache.append(l, pick(kp).cuda().contiguous(), pick(vp).cuda().contiguous(), first)
+            cache.append(l, rest(kp).cuda().contiguous(), rest(vp).cuda().contiguous(),
+                         [c - f for c, f in zip(cp, first)])
+        else:
+            cache.append(l, kp.cuda(), vp.cuda(), cp)
+    # the new tokens of every layer in one call
+    kn = torch.stack([hist[l][1][0] for l in range(L)]).cuda()
+    vn = torch.stack([hist[l][1][1] for l in range(L)]).cuda()
+    cache.append_layers(0, kn, vn, hist[0][1][2])
+    torch.cuda.synchronize()
+    for l in range(L):
+        assert cache.lengths(l) == [x + w.new_tokens for x in w.lengths]
+        prefix, new = hist[l]
+        for s in range(w.num_seqs):
+            k, v = H.full_seq(prefix, new, s)
+            for h in range(w.kv_heads):
+                H.assert_head_bytes(cache, w, l, s, h, k, v)
+    before = [cache.lengths(l) for l in range(L)]
+    too_many = [9] * w.num_seqs  # capacity leaves 8 spare tokens
+    big = torch.zeros((2, sum(too_many), w.kv_heads, w.head_dim), dtype=kn.dtype, device="cuda")
+    with pytest.raises(kvq.KVQError) as e:
+        cache.append_layers(1, big, big, too_many)
+    assert e.value.status == kvq.KVQ_ERR_CAPACITY
+    assert [cache.lengths(l) for l in range(L)] == before
+    cache.close()
