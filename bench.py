@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized KV cache on one MI355X.
 
-One step = kvq_quantize_append of the new token of every sequence into one
-layer, then kvq_decode_attention over that layer (every cached token, the new
-one included). The default workload is the Llama-2-7B-shaped cache (16
+One step = the new token of every sequence appended into one layer, then
+decode attention over that layer (every cached token, the new one included),
+as one kvq_decode_step call (one launch where the single-query kernel serves
+the cache and no key block completes; --unfused-step: kvq_quantize_append then
+kvq_decode_attention). The default workload is the Llama-2-7B-shaped cache (16
 sequences, 32 heads of 128 channels, 4096 cached tokens, fp16, 2-bit K
 per-channel / V per-token, groups of 32), one layer per step. Independent
 layer caches are rotated so that each step reads memory that is not resident
@@ -65,6 +67,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
     ap.add_argument("--per-layer-decode", action="store_true",
                     help="multi-layer workloads: one append and one decode call per layer instead of one each for all layers")
+    ap.add_argument("--unfused-step", action="store_true",
+                    help="single-layer workloads: kvq_quantize_append then kvq_decode_attention instead of "
+                         "kvq_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -134,6 +139,7 @@ def main():
     # ---- per-step inputs, drawn up front. A multi-layer step decodes all its
     # layers in one kvq_decode_attention_layers call (one query per layer).
     multi = model_layers > 1 and not args.per_layer_decode
+    fused_step = model_layers == 1 and not args.unfused_step
     dec_per_step = 1 if multi else model_layers
     new_k, new_v, qs = [], [], []
     for st in range(total_steps):
@@ -174,6 +180,15 @@ def main():
             if dec_events is not None:
                 dec_events[0][0].record()
             kvq.kvq_decode_attention_layers(cache.handle, base, model_layers, qp[st], scale, out_p, ws_p, ws_b, stream)
+            if dec_events is not None:
+                dec_events[0][1].record()
+            return
+        if fused_step and app_events is None:
+            # kvq_decode_step: one launch appends and attends where it can
+            if dec_events is not None:
+                dec_events[0][0].record()
+            kvq.kvq_decode_step(cache.handle, base, kp[st], vp[st], counts_c, qp[st], scale, out_p, ws_p, ws_b,
+                                stream)
             if dec_events is not None:
                 dec_events[0][1].record()
             return
@@ -223,6 +238,7 @@ def main():
                                  * H for T, (bk, bv) in zip(lens[l], w.bits)))
         dec_bytes.extend([sum(per_layer)] if multi else per_layer)
     app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
+    call_bytes = [b + app_bytes for b in dec_bytes] if fused_step else dec_bytes  # what one timed call moves
     ms_per_step = wall_s * 1e3 / args.steps
     step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
     value = step_total_bytes / (ms_per_step * 1e-3) / 1e9
@@ -233,7 +249,7 @@ def main():
     # the byte count of one decode call, timed the same way (one event pair on
     # the launch stream) and kept cold by cycling through windows of a buffer
     # at least 4x the last-level cache
-    probe_bytes = int(np.mean(dec_bytes)) // 16 * 16
+    probe_bytes = int(np.mean(call_bytes)) // 16 * 16
     win = (probe_bytes + 4095) // 4096 * 4096
     nwin = max(8, math.ceil(4 * LLC_BYTES / win))
     pbuf = torch.empty(win * nwin, dtype=torch.uint8, device=dev)
@@ -249,7 +265,7 @@ def main():
             probe_ms.append(e0.elapsed_time(e1))
     del pbuf
     ceiling_gbps = probe_bytes / (float(np.median(probe_ms)) * 1e-3) / 1e9
-    dec_gbps = float(np.mean(dec_bytes)) / (dec_avg_ms * 1e-3) / 1e9
+    dec_gbps = float(np.mean(call_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = S * n_new / (ms_per_step * 1e-3)
 
     result = {
@@ -280,8 +296,9 @@ def main():
         "prefill_tokens": prefill_tokens,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "kvq_decode_attention_layers" if multi else "kvq_decode_attention",
-                     "bytes_per_launch": int(np.mean(dec_bytes)),
+                     "kernel": ("kvq_decode_attention_layers" if multi else
+                                "kvq_decode_step (append + decode attention)" if fused_step else "kvq_decode_attention"),
+                     "bytes_per_launch": int(np.mean(call_bytes)),
                      "measured_ceiling": {"kernel": "kvq_read_probe", "bytes": probe_bytes,
                                           "GBps": round(ceiling_gbps, 2),
                                           "frac_of_peak": round(ceiling_gbps / HBM_PEAK_GBPS, 4),

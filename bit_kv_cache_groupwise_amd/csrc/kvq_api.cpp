@@ -357,9 +357,12 @@ namespace {
 // Quantize-append of the same per-sequence counts into layers [layer, layer +
 // n_layers) in one launch (1 <= n_layers <= 64, checked by the callers).
 // k_new, v_new: [n_layers][sum n_new][kv_heads][head_dim].
-kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
-                         const int32_t* n_new, void* stream) {
+// Validate an append and build its launch arguments (uploading non-uniform
+// counts); *empty when no sequence gains a token (nothing to launch).
+kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
+                          const int32_t* n_new, void* stream, kvq::TensorArgs (&ta)[2], int (&gx)[2], bool* empty) {
     const kvq_geometry& g = c->g;
+    *empty = false;
     const int S = g.num_seqs;
     long total = 0;
     int max_n = 0;
@@ -376,7 +379,10 @@ kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const vo
         max_n = std::max(max_n, n_new[s]);
         uniform = uniform && n_new[s] == n_new[0];
     }
-    if (total == 0) return KVQ_OK;
+    if (total == 0) {
+        *empty = true;
+        return KVQ_OK;
+    }
     if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new and v_new must be non-NULL when tokens are appended");
     if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(KVQ_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
     if (total > (1L << 30)) return fail(KVQ_ERR_ARG, "too many tokens in one append");
@@ -404,8 +410,6 @@ kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const vo
     const void* srcs[2] = {k_new, v_new};
     const int groups[2] = {g.group_k, g.group_v};
     const int axes[2] = {g.axis_k, g.axis_v};
-    kvq::TensorArgs ta[2];
-    int gx[2];
     for (int t = 0; t < 2; ++t) {
         kvq::TensorArgs& a = ta[t];
         a = kvq::TensorArgs{};
@@ -445,12 +449,28 @@ kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const vo
         }
     }
     if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");
-    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], hs);
-    if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
+    return KVQ_OK;
+}
+
+// The host side of an append that has been launched: lengths and buffer parity.
+void commit_append(kvq_cache* c, int32_t layer, int32_t n_layers, const int32_t* n_new) {
+    const int S = c->g.num_seqs;
     for (int l = layer; l < layer + n_layers; ++l) {
         for (int s = 0; s < S; ++s) c->lens[(size_t)l * S + s] += n_new[s];
         c->parity[l] ^= 1;
     }
+}
+
+kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
+                         const int32_t* n_new, void* stream) {
+    kvq::TensorArgs ta[2];
+    int gx[2];
+    bool empty;
+    kvq_status st = prepare_append(c, layer, n_layers, k_new, v_new, n_new, stream, ta, gx, &empty);
+    if (st != KVQ_OK || empty) return st;
+    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
+    commit_append(c, layer, n_layers, n_new);
     return KVQ_OK;
 }
 
@@ -491,8 +511,15 @@ namespace {
 // Decode attention of layers [layer, layer + n_layers) in one launch per
 // kernel (1 <= n_layers <= 64, checked by the callers; the length-buffer
 // parities travel as a 64-bit mask). q, out: [n_layers][S][Hq][D].
+// Options of a decode call inside a decode step (kvq_decode_step).
+struct StepOpts {
+    const int32_t* add = nullptr;         // host [num_seqs]: tokens the step appends (lengths seen = current + add)
+    bool dry_run = false;                 // validate only
+    const kvq::TensorArgs* fused = nullptr;  // [2]: the append, fused into the single-query kernel
+};
+
 kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, const void* q, float softmax_scale,
-                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                         float* out, void* workspace, size_t workspace_bytes, void* stream, const StepOpts& opt = {}) {
     const kvq_geometry& g = c->g;
     if (group_size(c) > kvq::kMaxQueryGroup)
         return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d", group_size(c), kvq::kMaxQueryGroup);
@@ -501,6 +528,12 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     if (!aligned(q, in_bytes(g.in_dtype)) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "q or out misaligned");
     const int S = g.num_seqs;
     const int32_t* lens = &c->lens[(size_t)layer * S];
+    std::vector<int32_t> step_lens;
+    if (opt.add) {  // one layer: the lengths after the step's append
+        step_lens.assign(lens, lens + S);
+        for (int s = 0; s < S; ++s) step_lens[s] += opt.add[s];
+        lens = step_lens.data();
+    }
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     const bool mha = group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
     bool gqa = group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
@@ -517,6 +550,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     if (!workspace || workspace_bytes < need)
         return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes, %llu needed", workspace_bytes, (unsigned long long)need);
     if (!aligned(workspace, kvq::kAlign)) return fail(KVQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (opt.dry_run) return KVQ_OK;
     kvq::DecodeArgs a{};
     a.q = q;
     a.out = out;
@@ -549,12 +583,21 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
     if (mha) {
+        if (opt.fused) {
+            a.append_fused = 1;
+            a.app_k = opt.fused[0];
+            a.app_v = opt.fused[1];
+        }
         for (const auto& pr : c->pairs) {
             a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
             hipError_t e = kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching decode attention");
         }
         if (max_chunks > 1) {
+            if (opt.fused) {  // the merge reads the lengths the decode kernel wrote
+                a.append_fused = 0;
+                a.len = opt.fused[0].len_out;
+            }
             a.split_floor = 1;
             hipError_t e = kvq::launch_merge(a, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching the split merge");
@@ -586,6 +629,51 @@ kvq_status kvq_decode_attention(const kvq_cache* c, int32_t layer, const void* q
     g_last_error.clear();
     if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
     if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    return decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new, const int32_t* n_new,
+                           const void* q, float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    g_last_error.clear();
+    if (!c || !n_new || !q || !out) return fail(KVQ_ERR_ARG, "cache, n_new, q or out is NULL");
+    const kvq_geometry& g = c->g;
+    if (layer < 0 || layer >= g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    const int S = g.num_seqs;
+    for (int s = 0; s < S; ++s)
+        if (n_new[s] < 0) return fail(KVQ_ERR_ARG, "n_new[%d] = %d is negative", s, n_new[s]);
+    StepOpts opt;
+    opt.add = n_new;
+    opt.dry_run = true;
+    kvq_status st = decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream, opt);
+    if (st != KVQ_OK) return st;
+    kvq::TensorArgs ta[2];
+    int gx[2];
+    bool empty;
+    st = prepare_append(c, layer, 1, k_new, v_new, n_new, stream, ta, gx, &empty);
+    if (st != KVQ_OK) return st;
+    // Fused when the single-query kernel serves the cache and the step only
+    // adds residual key rows (no key block completes) and at most one
+    // workgroup's worth of value rows per sequence.
+    const int32_t* lens = &c->lens[(size_t)layer * S];
+    bool fuse = !empty && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
+                kvq::mha_supported(g.head_dim);
+    for (int s = 0; fuse && s < S; ++s)
+        fuse = (lens[s] + n_new[s]) / g.group_k == lens[s] / g.group_k && n_new[s] <= 256 / (g.head_dim / 32);
+    for (const auto& pr : c->pairs) fuse = fuse && kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv);
+    opt.dry_run = false;
+    if (fuse) {
+        opt.fused = ta;
+        st = decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream, opt);
+        if (st != KVQ_OK) return st;
+        commit_append(c, layer, 1, n_new);
+        return KVQ_OK;
+    }
+    if (!empty) {
+        hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
+        commit_append(c, layer, 1, n_new);
+    }
     return decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 

@@ -33,6 +33,7 @@
 // (moved only when a score exceeds it by more than 2^8), so rescaling is
 // rare. Splits of one (seq, head) are merged by merge_kernel; a sequence that
 // fits one split is written directly.
+#include "kvq_append.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -411,7 +412,27 @@ __device__ __forceinline__ float unit_sum(float v) {
     return v;
 }
 
-template <int D, int BK, int BV, int NW, int NS>
+// Fused decode step: append the new rows of (seq, head), which only the
+// last split's residual loop reads: values quantized per row (one thread per
+// 32-channel unit, rows of whole groups), keys copied into the residual.
+__device__ __forceinline__ void fused_append(const DecodeArgs& a, int head, int seq, int len0, int n, int nthreads) {
+    const int UPR = a.head_dim >> 5;
+    const int r = (int)threadIdx.x / UPR, u = (int)threadIdx.x % UPR;
+    if (a.in_dtype == 0) {
+        if (r < n) token_axis_row<0>(a.app_v, r, u, head, seq, len0);
+        residual_rows<0>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+    } else if (a.in_dtype == 1) {
+        if (r < n) token_axis_row<1>(a.app_v, r, u, head, seq, len0);
+        residual_rows<1>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+    } else {
+        if (r < n) token_axis_row<2>(a.app_v, r, u, head, seq, len0);
+        residual_rows<2>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+    }
+}
+
+// FUSED: the instantiation of the fused decode step (the append prologue is
+// compiled only there, so the attention loop of the plain call is unchanged).
+template <int D, int BK, int BV, int NW, int NS, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     int z = blockIdx.z;
     const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
@@ -431,8 +452,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 
     const int seq = a.seq_list ? a.seq_list[z] : z;
     const int kvh = blockIdx.y, split = blockIdx.x;
-    const int len = a.len[seq];
+    const int len_old = a.len[seq];
+    const int n_app = FUSED ? (a.app_v.n_new ? a.app_v.n_new[seq] : a.app_v.n_uniform) : 0;
+    const int len = len_old + n_app;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (FUSED && kvh == 0 && split == 0 && tid == 0) a.app_k.len_out[seq] = len;
     float* out = a.out + ((size_t)seq * a.q_heads + kvh) * D;
     if (len == 0) {
         if (split == 0)
@@ -442,6 +466,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     const int CW = a.chunk;
     const int nsplit = max(1, len / CW);
     if (split >= nsplit) return;
+    // Fused step: the new rows are only read by this split's residual loop, so
+    // their stores complete while the quantized tokens stream; the barrier
+    // before that loop (workgroup scope: one compute unit) orders them.
+    const bool appended = FUSED && n_app > 0 && split == nsplit - 1;
+    if (appended) fused_append(a, kvh, seq, len_old, n_app, NT);
     const int wa = split * CW, wb = split == nsplit - 1 ? len : wa + CW;
     const int ts = lane / UPR, cg = lane % UPR;
     const SeqEntry& e = a.table[seq];
@@ -624,6 +653,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     }
 
     // ---- residual keys (input dtype), fewer than G tokens, one wave
+    if (appended) __syncthreads();  // the step's new rows are in place
     if (wave == 0) {
         for (int st = max(wa, nqk); st < wb; st += 64) {
             uint32_t vw[UPR][BV], vmw[UPR];
@@ -705,9 +735,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 
 // 4 waves per workgroup with a 3-stage register ring measured fastest on the
 // Llama-2-7B-shaped step (6 waves with 2 stages was ~20% slower).
+// Whether the fused instantiation (a few more registers) keeps the plain
+// one's resident workgroups per compute unit; asked once per bit pair.
+template <int D, int BK, int BV>
+bool fused_keeps_occupancy() {
+    static int cached = -1;  // racing first calls compute the same value
+    if (cached < 0) {
+        int plain = 0, fused = 0;
+        const bool ok =
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, false>,
+                                                         4 * 64, 0) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&fused, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, true>,
+                                                         4 * 64, 0) == hipSuccess;
+        cached = ok && fused >= plain ? 1 : 0;
+    }
+    return cached == 1;
+}
+
+template <int D, int BK>
+bool fused_ok_bv(int bv) {
+    switch (bv) {
+        case 2: return fused_keeps_occupancy<D, BK, 2>();
+        case 3: return fused_keeps_occupancy<D, BK, 3>();
+        case 4: return fused_keeps_occupancy<D, BK, 4>();
+        case 6: return fused_keeps_occupancy<D, BK, 6>();
+        default: return fused_keeps_occupancy<D, BK, 8>();
+    }
+}
+
 template <int D, int BK, int BV>
 hipError_t launch_nw(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3>), grid, dim3(4 * 64), 0, s, a);
+    if (a.append_fused) hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, true>), grid, dim3(4 * 64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, false>), grid, dim3(4 * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -738,6 +797,17 @@ hipError_t launch_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t
 // This file is compiled once per head_dim (KVQ_MHA_HEAD_DIM = 64, 128, 256).
 #define KVQ_CAT2(a, b) a##b
 #define KVQ_CAT(a, b) KVQ_CAT2(a, b)
+bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
+    constexpr int D = KVQ_MHA_HEAD_DIM;
+    switch (bits_k) {
+        case 2: return fused_ok_bv<D, 2>(bits_v);
+        case 3: return fused_ok_bv<D, 3>(bits_v);
+        case 4: return fused_ok_bv<D, 4>(bits_v);
+        case 6: return fused_ok_bv<D, 6>(bits_v);
+        default: return fused_ok_bv<D, 8>(bits_v);
+    }
+}
+
 hipError_t KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                           hipStream_t s) {
     dim3 grid(a.max_chunks, a.kv_heads, nseqs * a.n_layers);

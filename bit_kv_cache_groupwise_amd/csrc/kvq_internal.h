@@ -93,6 +93,13 @@ struct DecodeArgs {
     int32_t layer0;             // first layer of the launch
     uint64_t len_parity;        // bit i: current length buffer of layer layer0 + i
     const int32_t* len_base;    // both length buffers, [2][layers_total][num_seqs]
+    // Fused decode step (append_fused != 0; single-query kernel, one layer):
+    // the last split of each (seq, kv head) first appends that sequence's new
+    // rows (values quantized on the token axis, keys copied into the residual;
+    // no key block completes in the step), then attends with the post-append
+    // length. `len` then holds the lengths before the append.
+    int32_t append_fused;
+    TensorArgs app_k, app_v;
 };
 
 struct DequantArgs {
@@ -121,6 +128,15 @@ inline hipError_t launch_decode_gqa(const DecodeArgs& a, int bits_k, int bits_v,
                                : launch_decode_gqa_d256(a, bits_k, bits_v, nseqs, s);
 }
 inline bool mha_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+bool mha_fused_ok_d64(int bits_k, int bits_v);
+bool mha_fused_ok_d128(int bits_k, int bits_v);
+bool mha_fused_ok_d256(int bits_k, int bits_v);
+// Whether the fused decode step keeps the single-query kernel's occupancy for this bit pair.
+inline bool mha_fused_ok(int head_dim, int bits_k, int bits_v) {
+    return head_dim == 64    ? mha_fused_ok_d64(bits_k, bits_v)
+           : head_dim == 128 ? mha_fused_ok_d128(bits_k, bits_v)
+                             : mha_fused_ok_d256(bits_k, bits_v);
+}
 inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     return a.head_dim == 64    ? launch_decode_mha_d64(a, bits_k, bits_v, nseqs, s)
            : a.head_dim == 128 ? launch_decode_mha_d128(a, bits_k, bits_v, nseqs, s)

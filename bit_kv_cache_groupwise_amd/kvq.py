@@ -34,7 +34,7 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
             "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers")
+            "kvq_quantize_append_layers", "kvq_decode_step")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -68,6 +68,7 @@ _lib.kvq_cache_destroy.argtypes = [_P]
 _lib.kvq_cache_destroy.restype = None
 _lib.kvq_quantize_append.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_quantize_append_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _I32P, _P]
+_lib.kvq_decode_step.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.kvq_decode_workspace_size.argtypes = [_P]
 _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
@@ -85,7 +86,7 @@ _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
            "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers"):
+            "kvq_quantize_append_layers", "kvq_decode_step"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -189,6 +190,15 @@ def kvq_quantize_append(handle, layer, k_new, v_new, n_new, stream=None):
 def kvq_quantize_append_layers(handle, layer0, n_layers, k_new, v_new, n_new, stream=None):
     _check(_lib.kvq_quantize_append_layers(handle, layer0, n_layers, _ptr(k_new), _ptr(v_new), _i32(n_new),
                                            _stream(stream)), "kvq_quantize_append_layers")
+
+
+def kvq_decode_step(handle, layer, k_new, v_new, n_new, q, softmax_scale, out, workspace, workspace_bytes=None,
+                    stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.kvq_decode_step(handle, layer, _ptr(k_new), _ptr(v_new), _i32(n_new), _ptr(q),
+                                ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace), workspace_bytes,
+                                _stream(stream)), "kvq_decode_step")
 
 
 def kvq_decode_workspace_size(handle) -> int:
@@ -297,6 +307,16 @@ class Cache:
             out = torch.empty((g.num_seqs, g.q_heads, g.head_dim), dtype=torch.float32, device=q.device)
         ws = self.workspace()
         kvq_decode_attention(self.handle, layer, q, softmax_scale, out, ws, ws.numel(), stream)
+        return out
+
+    def step(self, layer, k_new, v_new, n_new, q, softmax_scale, out=None, stream=None):
+        """Append the new rows and attend (one decode step of one layer)."""
+        import torch
+        g = self.geom
+        if out is None:
+            out = torch.empty((g.num_seqs, g.q_heads, g.head_dim), dtype=torch.float32, device=q.device)
+        ws = self.workspace()
+        kvq_decode_step(self.handle, layer, k_new, v_new, n_new, q, softmax_scale, out, ws, ws.numel(), stream)
         return out
 
     def decode_layers(self, layer0, n_layers, q, softmax_scale, out=None, stream=None):

@@ -175,6 +175,19 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step of `layer`: kvq_quantize_append(k_new, v_new, n_new) then
+ * kvq_decode_attention(q), with the same arguments, results and errors (all
+ * checked before anything is launched or written). Where the single-query
+ * kernel serves the cache (q_heads == kv_heads, keys per channel, values per
+ * token) and the step completes no key block and adds at most
+ * 256 / (head_dim / 32) rows per sequence, both run in one launch: each
+ * (sequence, kv head) workgroup that attends the newest tokens first appends
+ * them (for bit pairs where the fused kernel keeps the plain one's
+ * occupancy). Otherwise the two run as consecutive launches. */
+kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                           const int32_t* n_new, const void* q, float softmax_scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* kvq_quantize_append of the same per-sequence counts n_new into each of the
  * n_layers consecutive layers [layer0, layer0 + n_layers), in one launch: the
  * append of a whole model's decode step. k_new, v_new: device, in_dtype,

@@ -400,3 +400,56 @@ def test_multi_layer_append(name):
     assert e.value.status == kvq.KVQ_ERR_CAPACITY
     assert [cache.lengths(l) for l in range(L)] == before
     cache.close()
+
+
+@pytest.mark.parametrize("name,counts", [
+    ("llama", None), ("gpt2", None), ("tiny", None), ("llama", (1, 3, 0)), ("mixed", None)])
+def test_decode_step_equals_append_then_decode(name, counts):
+    """kvq_decode_step over 40 steps (fused where the single-query kernel
+    serves the cache and no key block completes; two launches on the steps
+    that complete a block, and for query groups) gives the same outputs, bit
+    for bit, as kvq_quantize_append followed by kvq_decode_attention, and
+    leaves the bytes the oracle gives; a step past capacity is rejected
+    before anything changes."""
+    base = CASES[name]
+    w = base.scaled(layers=1)
+    counts = list(counts) if counts else [1] * w.num_seqs
+    if len(counts) != w.num_seqs:
+        counts = (counts * w.num_seqs)[:w.num_seqs]
+    steps = 40
+    _note(f"[decode step] case={name} counts={counts} steps={steps}")
+    kvq = H.kvq()
+    extra = steps * max(counts)
+    ca, cb = H.make_cache(w, extra=extra), H.make_cache(w, extra=extra)
+    prefix, _ = H.history(w, 0)
+    for c in (ca, cb):
+        c.append(0, prefix[0].cuda(), prefix[1].cuda(), prefix[2])
+    ks, vs = [prefix[0]], [prefix[1]]
+    all_counts = [prefix[2]]
+    for st in range(steps):
+        kn, vn = W.draw_kv(w, 0, counts, device="cpu", stream=1 + st)
+        q = W.draw_q(w, 0, step=st).cuda()
+        oa = ca.step(0, kn.cuda(), vn.cuda(), counts, q, w.softmax_scale)
+        cb.append(0, kn.cuda(), vn.cuda(), counts)
+        ob = cb.decode(0, q, w.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), (name, st)
+        assert ca.lengths(0) == cb.lengths(0)
+        ks.append(kn)
+        vs.append(vn)
+        all_counts.append(counts)
+    # stored bytes against the oracle: every sequence's rows in arrival order
+    for s in range(w.num_seqs):
+        k = torch.cat([H.seq_rows(x, c, s) for x, c in zip(ks, all_counts)]).float().numpy()
+        v = torch.cat([H.seq_rows(x, c, s) for x, c in zip(vs, all_counts)]).float().numpy()
+        for h in range(w.kv_heads):
+            H.assert_head_bytes(ca, w, 0, s, h, k, v)
+    before = ca.lengths(0)
+    big = [extra + 1] + [0] * (w.num_seqs - 1)
+    kn = torch.zeros((sum(big), w.kv_heads, w.head_dim), dtype=w.torch_dtype, device="cuda")
+    with pytest.raises(kvq.KVQError) as e:
+        ca.step(0, kn, kn, big, q, w.softmax_scale)
+    assert e.value.status == kvq.KVQ_ERR_CAPACITY
+    assert ca.lengths(0) == before
+    ca.close()
+    cb.close()
