@@ -70,6 +70,9 @@ def main():
     ap.add_argument("--unfused-step", action="store_true",
                     help="single-layer workloads: kvq_quantize_append then kvq_decode_attention instead of "
                          "kvq_decode_step")
+    ap.add_argument("--no-append-timing", action="store_true",
+                    help="skip the separately timed appends after the timed region (profiled runs: every append "
+                         "after the prefill then belongs to a timed decode step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -97,7 +100,8 @@ def main():
     step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
                      for T, (bk, bv) in zip(step_lens, w.bits)) * model_layers
     rot = args.rotate or rotation_for(step_bytes)
-    append_timing_steps = min(10, args.steps)  # after the timed region: events around the append alone
+    # after the timed region: events around the append alone
+    append_timing_steps = 0 if args.no_append_timing else min(10, args.steps)
     total_steps = args.warmup + args.steps + append_timing_steps
     appends_per_layer = math.ceil(total_steps / rot) + 1
     layers = rot * model_layers
@@ -290,7 +294,7 @@ def main():
         "decode_attention_GBps": round(dec_gbps, 2),
         "decode_attention_us": round(dec_avg_ms * 1e3, 3),
         "decode_attention_us_p10_p50_p90": [round(p10, 3), round(p50, 3), round(p90, 3)],
-        "append_us": round(float(np.mean(app_ms)) * 1e3, 3),
+        "append_us": round(float(np.mean(app_ms)) * 1e3, 3) if app_ms else None,
         "quantize_GBps": round(quantize_gbps, 2),
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
         "prefill_tokens": prefill_tokens,
