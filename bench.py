@@ -70,6 +70,9 @@ def main():
     ap.add_argument("--unfused-step", action="store_true",
                     help="single-layer workloads: kvq_quantize_append then kvq_decode_attention instead of "
                          "kvq_decode_step")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="bracket the decode calls of every N-th timed step with a HIP event pair (an event pair "
+                         "adds ~6 us of GPU-side gap to its step)")
     ap.add_argument("--no-append-timing", action="store_true",
                     help="skip the separately timed appends after the timed region (profiled runs: every append "
                          "after the prefill then belongs to a timed decode step)")
@@ -79,6 +82,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="plain device copy of this size before timing (calibrates HBM byte counters); 0 = none")
     args = ap.parse_args()
+    if args.event_every < 1:
+        ap.error("--event-every must be >= 1")
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -219,11 +224,12 @@ def main():
     lens0 = {l: cache.lengths(l) for l in range(layers)}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, dec_events=evs[i])
+        step(args.warmup + i, dec_events=evs[i] if i % args.event_every == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in range(args.steps) for m in range(dec_per_step)]
+    timed = [i for i in range(args.steps) if i % args.event_every == 0]
+    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in timed for m in range(dec_per_step)]
     aevs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(append_timing_steps)]
     for j in range(append_timing_steps):
         step(args.warmup + args.steps + j, app_events=aevs[j])
@@ -242,7 +248,8 @@ def main():
                                  * H for T, (bk, bv) in zip(lens[l], w.bits)))
         dec_bytes.extend([sum(per_layer)] if multi else per_layer)
     app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
-    call_bytes = [b + app_bytes for b in dec_bytes] if fused_step else dec_bytes  # what one timed call moves
+    call_bytes = [b + app_bytes for b in dec_bytes] if fused_step else dec_bytes  # what one call moves
+    ev_bytes = [call_bytes[i * dec_per_step + m] for i in timed for m in range(dec_per_step)]  # event-timed calls
     ms_per_step = wall_s * 1e3 / args.steps
     step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
     value = step_total_bytes / (ms_per_step * 1e-3) / 1e9
@@ -269,7 +276,7 @@ def main():
             probe_ms.append(e0.elapsed_time(e1))
     del pbuf
     ceiling_gbps = probe_bytes / (float(np.median(probe_ms)) * 1e-3) / 1e9
-    dec_gbps = float(np.mean(call_bytes)) / (dec_avg_ms * 1e-3) / 1e9
+    dec_gbps = float(np.mean(ev_bytes)) / (dec_avg_ms * 1e-3) / 1e9
     tokens_per_s = S * n_new / (ms_per_step * 1e-3)
 
     result = {
