@@ -124,3 +124,20 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.kvq_dequantize(None, 0, 0, None, None, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_workspace_size(None) == 0
     lib.kvq_cache_destroy(None)
+    f = ctypes.c_float(1.0)
+    assert lib.kvq_decode_step(None, 0, None, None, None, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_quantize_append_layers(None, 0, 1, None, None, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_decode_attention_layers(None, 0, 1, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG
+
+
+def test_read_probe_validates_before_launching():
+    """The measurement probe rejects NULL pointers, sizes that are not whole
+    16-byte vectors and misaligned pointers without touching the device (the
+    pointers below are never dereferenced)."""
+    lib = kvq.raw()
+    assert lib.kvq_read_probe(None, 16, 0x1000, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_read_probe(0x1000, 16, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_read_probe(0x1000, 24, 0x2000, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_read_probe(0x1008, 32, 0x2000, None) == kvq.KVQ_ERR_ALIGN
+    assert lib.kvq_read_probe(0x1000, 32, 0x2002, None) == kvq.KVQ_ERR_ALIGN
+    assert lib.kvq_read_probe(0x1000, 0, 0x2000, None) == kvq.KVQ_OK  # nothing to read: no launch
