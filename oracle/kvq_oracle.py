@@ -319,3 +319,69 @@ def effective_bits(bits_k: int, bits_v: int, group_elems_k: int, group_elems_v: 
                    meta_bits: int = 32) -> float:
     """Average stored bits per K/V element including one (step, zero) pair per group."""
     return ((bits_k + meta_bits / group_elems_k) + (bits_v + meta_bits / group_elems_v)) / 2.0
+
+
+# ----------------------------------------------------------------------------
+# Full-precision recent window and attention sinks ([U] "O Imposto dos
+# Sistemas e Por Que Nao E um Detalhe": the most recent tokens, up to a window
+# of about 128, stay in full precision and are quantized in groups once enough
+# have accumulated; [U] "O Que Fazer Com Isso": keep a full-precision window of
+# recently generated tokens; [U] "Onde o Trabalho Esta Indo": InnerQ keeps
+# high-precision windows for recent tokens and for attention-sink tokens; [N] "Pengecualian
+# recent-token mengubah perhitungan memory": the recent part is a
+# high-precision region next to the packed cache).
+#
+# Reading W1 (the pages give the policy, not its boundary): with a window of R
+# tokens and S sink tokens, the attention reads token t in full precision when
+# t < S (a sink) or t lies in the recent part; every key block of Gb tokens that
+# lies wholly inside [S, len - R) is read quantized. Gb is the block length of
+# the channel-axis tensor (its G; 1 when no tensor groups along tokens), and S
+# is a multiple of Gb. So between R and R + Gb - 1 recent tokens are full
+# precision once len >= S + R. Both tensors share the boundary. The window is
+# off (R4 alone) when R == S == 0.
+# ----------------------------------------------------------------------------
+
+def token_block(axis_k: int, group_k: int, axis_v: int, group_v: int) -> int:
+    """Gb: tokens per quantization block along the token axis (W1)."""
+    g = [group for axis, group in ((axis_k, group_k), (axis_v, group_v)) if axis == AXIS_CHANNEL]
+    return max(g) if g else 1
+
+
+def full_precision_mask(length: int, window: int, sinks: int, block: int) -> np.ndarray:
+    """Boolean [length]: True where the attention reads the token in full
+    precision under W1. The quantized tokens are [S, Q) with
+    Q = max(S, Gb * floor((len - R) / Gb))."""
+    if window < 0 or sinks < 0 or sinks % block:
+        raise ValueError("window >= 0, sinks >= 0 and a multiple of the block")
+    t = np.arange(length)
+    if window == 0 and sinks == 0:
+        return np.zeros(length, dtype=bool)
+    q = max(sinks, block * ((length - window) // block))  # floor division
+    return (t < sinks) | (t >= q)
+
+
+def apply_window(x, x_hat, mask) -> np.ndarray:
+    """Rows of the float64 reconstruction where the mask is set are replaced by
+    the exact input rows (W1)."""
+    out = np.array(x_hat, dtype=np.float64, copy=True)
+    m = np.asarray(mask, dtype=bool)
+    out[m] = np.asarray(x, dtype=np.float32)[m].astype(np.float64)
+    return out
+
+
+def encode_head_window(k, v, *, window: int, sinks: int, group_k: int, group_v: int, axis_k: int,
+                       axis_v: int, bits_k: int, bits_v: int, meta_dtype: str = "f16") -> dict:
+    """encode_head plus the full-precision window: the stored codes, metadata and
+    residual are unchanged (every token is still quantized as it arrives); the
+    reconstructions the attention reads, ``k_hat`` and ``v_hat``, take the
+    exact input rows where ``full_precision_mask`` is set. ``k_hat_q`` and
+    ``v_hat_q`` keep the reconstructions without the window."""
+    enc = encode_head(k, v, group_k=group_k, group_v=group_v, axis_k=axis_k, axis_v=axis_v,
+                      bits_k=bits_k, bits_v=bits_v, meta_dtype=meta_dtype)
+    block = token_block(axis_k, group_k, axis_v, group_v)
+    mask = full_precision_mask(np.asarray(k).shape[0], window, sinks, block)
+    enc["k_hat_q"], enc["v_hat_q"] = enc["k_hat"], enc["v_hat"]
+    enc["k_hat"] = apply_window(k, enc["k_hat_q"], mask)
+    enc["v_hat"] = apply_window(v, enc["v_hat_q"], mask)
+    enc["fp_mask"] = mask
+    return enc

@@ -423,10 +423,78 @@ def check_sizing_pages(o):
     assert round(8.6 * (1 - eb / 16), 1) == figs["qwen_k4v8_saved_gb"]
 
 
+# ----------------------------------------------------------------------------
+# Full-precision recent window and sinks ([U] "O Imposto dos Sistemas ...",
+# "O Que Fazer Com Isso", "Onde o Trabalho Esta Indo")
+# ----------------------------------------------------------------------------
+
+def check_window_blocks(o):
+    """The quantized tokens under a window of R and S sinks are exactly the
+    union of the whole key blocks inside [S, len - R), enumerated block by block;
+    the recent full-precision part then holds between R and R + Gb - 1 tokens."""
+    for block in (1, 32, 64):
+        for sinks in (0, block, 2 * block) if block > 1 else (0, 1, 4):
+            for window in (0, 1, 31, 32, 100, 128):
+                if window == 0 and sinks == 0:
+                    continue
+                for length in list(range(0, 300, 7)) + [sinks + window + block, 1000, 1023, 1024, 1025]:
+                    quant = np.zeros(length, dtype=bool)
+                    b = 0
+                    while (b + 1) * block <= length:
+                        lo, hi = b * block, (b + 1) * block
+                        if lo >= sinks and hi <= length - window:
+                            quant[lo:hi] = True
+                        b += 1
+                    got = o.full_precision_mask(length, window, sinks, block)
+                    assert got.shape == (length,) and got.dtype == bool
+                    assert np.array_equal(~got, quant), (block, sinks, window, length)
+                    if length >= sinks + window:
+                        recent = int(got[sinks:].sum())
+                        assert window <= recent <= window + block - 1, (block, sinks, window, length, recent)
+    # no window: nothing beyond the residual of R4
+    assert not o.full_precision_mask(100, 0, 0, 32).any()
+    assert o.token_block(o.AXIS_CHANNEL, 64, o.AXIS_TOKEN, 32) == 64
+    assert o.token_block(o.AXIS_TOKEN, 64, o.AXIS_TOKEN, 32) == 1
+
+
+def check_window_exact_attention(o, seed=11):
+    """A window at least as long as the cache (or sinks covering it) makes the
+    attention exact: torch's scaled_dot_product_attention in float64 over the
+    unquantized rows. A partial window keeps the stored bytes of the plain
+    encoding, takes exact rows where the mask is set and the plain
+    reconstruction elsewhere."""
+    import torch
+    rng = np.random.default_rng(seed)
+    T, D = 100, 64
+    k = (rng.standard_normal((T, D)) * rng.uniform(0.5, 8, D)).astype(np.float32)
+    v = rng.standard_normal((T, D)).astype(np.float32)
+    q = rng.standard_normal((2, D))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k.astype(np.float64))[None, None].expand(1, 2, T, D),
+        torch.from_numpy(v.astype(np.float64))[None, None].expand(1, 2, T, D), scale=0.125)[0, :, 0, :].numpy()
+    kw = dict(group_k=32, group_v=32, axis_k=o.AXIS_CHANNEL, axis_v=o.AXIS_TOKEN, bits_k=2, bits_v=2)
+    for window, sinks in ((T, 0), (T + 5, 32), (0, 128), (200, 96)):
+        enc = o.encode_head_window(k, v, window=window, sinks=sinks, **kw)
+        assert np.array_equal(enc["k_hat"], k.astype(np.float64)) and np.array_equal(enc["v_hat"], v.astype(np.float64))
+        assert np.allclose(o.attend(q, enc["k_hat"], enc["v_hat"], 0.125), ref, rtol=1e-12, atol=1e-13)
+    plain = o.encode_head(k, v, **kw)
+    enc = o.encode_head_window(k, v, window=20, sinks=32, **kw)
+    for name in ("k_words", "v_words", "k_meta", "v_meta", "k_resid"):
+        assert np.array_equal(enc[name], plain[name]), name
+    m = enc["fp_mask"]
+    # sinks [0, 32); block [32, 64) ends before 100 - 20 = 80; block [64, 96) does not
+    assert np.array_equal(np.nonzero(~m)[0], np.arange(32, 64))
+    for x, hat, ph in ((k, enc["k_hat"], plain["k_hat"]), (v, enc["v_hat"], plain["v_hat"])):
+        assert np.array_equal(hat[m], x[m].astype(np.float64))
+        assert np.array_equal(hat[~m], ph[~m])
+    # the quantized part must be used: 2-bit keys move the output away from exact
+    assert not np.allclose(o.attend(q, enc["k_hat"], enc["v_hat"], 0.125), ref, atol=1e-3)
+
+
 ALL_CHECKS = [
     check_worked_example, check_brute_force_nearest, check_half_step_bound, check_min_max_codes,
     check_monotone, check_exact_reconstruction, check_b8_bound, check_constant_group,
     check_meta_rounding, check_axis_semantics, check_dequant_exact, check_pack_golden,
     check_pack_bigint, check_meta_words, check_attention_closed_forms, check_attention_vs_torch,
-    check_sizes, check_sizing_pages,
+    check_sizes, check_sizing_pages, check_window_blocks, check_window_exact_attention,
 ]

@@ -131,9 +131,49 @@ def m_meta_bytes_halved(o):
     o.effective_bits = lambda bk, bv, gk, gv, meta_bits=32: orig_eb(bk, bv, gk, gv, 16)
 
 
+def m_window_rounds_up(o):
+    def fpm(length, window, sinks, block):
+        t = np.arange(length)
+        if window == 0 and sinks == 0:
+            return np.zeros(length, dtype=bool)
+        q = max(sinks, block * (-(-(length - window) // block)))  # ceiling: a block too many
+        return (t < sinks) | (t >= q)
+    o.full_precision_mask = fpm
+
+
+def m_window_no_sinks(o):
+    orig = o.full_precision_mask
+
+    def fpm(length, window, sinks, block):
+        m = orig(length, window, sinks, block)
+        m[:sinks] = False if window else m[:sinks]
+        return m
+    o.full_precision_mask = fpm
+
+
+def m_window_keys_only(o):
+    orig = o.apply_window
+    calls = {"n": 0}
+
+    def aw(x, x_hat, mask):
+        calls["n"] += 1
+        return orig(x, x_hat, mask) if calls["n"] % 2 == 1 else np.array(x_hat, dtype=np.float64)
+    o.apply_window = aw
+
+
+def m_window_exact_tokens(o):
+    def fpm(length, window, sinks, block):
+        t = np.arange(length)
+        if window == 0 and sinks == 0:
+            return np.zeros(length, dtype=bool)
+        return (t < sinks) | (t >= length - window)  # ignores the block boundary
+    o.full_precision_mask = fpm
+
+
 MUTANTS = [m_levels_pow2, m_round_half_up, m_clamp_off_by_one, m_zero_is_max, m_unrounded_grid,
            m_meta_truncate, m_axis_swapped, m_pack_msb_first, m_dequant_midrise, m_softmax_no_scale,
-           m_gqa_modulo, m_weights_unnormalised, m_residual_dropped, m_meta_bytes_halved]
+           m_gqa_modulo, m_weights_unnormalised, m_residual_dropped, m_meta_bytes_halved,
+           m_window_rounds_up, m_window_no_sinks, m_window_keys_only, m_window_exact_tokens]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
