@@ -67,6 +67,29 @@ bool valid_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 6 || b == 8; 
 
 bool aligned(const void* p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Full-precision window and sinks: on when either is non-zero.
+bool win_mode(const kvq_geometry& g) { return g.window != 0 || g.sinks != 0; }
+
+// Token length of a key block: the larger channel-axis group, 1 when no tensor
+// groups along tokens.
+int token_block(const kvq_geometry& g) {
+    int b = 1;
+    if (g.axis_k == KVQ_AXIS_CHANNEL) b = std::max(b, g.group_k);
+    if (g.axis_v == KVQ_AXIS_CHANNEL) b = std::max(b, g.group_v);
+    return b;
+}
+
+// Rows of the window area per (tensor, head): the sinks, then a ring of
+// window + block rows for the recent tokens.
+int win_rows(const kvq_geometry& g) { return g.window + token_block(g); }
+
+// Byte offset of the window area inside tensor t's head region of the residual
+// pool (after the G residual rows of a channel-axis tensor).
+uint32_t win_off(const kvq_geometry& g, int t) {
+    const int axis = t == 0 ? g.axis_k : g.axis_v, G = t == 0 ? g.group_k : g.group_v;
+    return axis == KVQ_AXIS_CHANNEL ? (uint32_t)((uint64_t)G * g.head_dim * in_bytes(g.in_dtype)) : 0u;
+}
+
 kvq_status check_geometry(const kvq_geometry* g) {
     if (!g) return fail(KVQ_ERR_ARG, "geometry is NULL");
     if (g->layers < 1 || g->num_seqs < 1 || g->kv_heads < 1 || g->q_heads < 1)
@@ -91,6 +114,13 @@ kvq_status check_geometry(const kvq_geometry* g) {
     if (g->meta_dtype == KVQ_F32 || g->meta_dtype == KVQ_BF16)
         return fail(KVQ_ERR_UNSUPPORTED, "only fp16 step/zero metadata is stored by this build");
     if (g->meta_dtype != KVQ_F16) return fail(KVQ_ERR_ARG, "meta_dtype (%d) is not a kvq dtype", g->meta_dtype);
+    if (g->window < 0 || g->sinks < 0) return fail(KVQ_ERR_ARG, "window (%d) and sinks (%d) must be >= 0", g->window, g->sinks);
+    if (win_mode(*g)) {
+        const int b = token_block(*g);
+        if (g->sinks % b) return fail(KVQ_ERR_ARG, "sinks (%d) must be a multiple of the key block (%d tokens)", g->sinks, b);
+        if ((long)g->sinks + g->window + b > 4096)
+            return fail(KVQ_ERR_ARG, "sinks + window + block = %ld exceeds 4096", (long)g->sinks + g->window + b);
+    }
     return KVQ_OK;
 }
 
@@ -122,7 +152,8 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
                 const uint64_t rows = ch ? (c / G) * G : c;
                 const uint64_t code_b = rows * D * B / 8;
                 const uint64_t meta_b = (ch ? (c / G) * D : c * (D / G)) * 4;
-                const uint64_t res_b = ch ? G * D * ib : 0;
+                const uint64_t res_b = (ch ? G * D * ib : 0) +
+                                       (win_mode(*g) ? (uint64_t)(g->sinks + win_rows(*g)) * D * ib : 0);
                 e.codes[t] = oc;
                 e.codes_hs[t] = align_up(code_b, kvq::kAlign);
                 oc += e.codes_hs[t] * H;
@@ -227,6 +258,13 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
 
 int min_chunk(const kvq_cache* c) {
     return c->g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, c->g.group_k) : 64;
+}
+
+// Workgroups of the full-precision window kernel per (seq, kv head): enough for
+// the most full-precision tokens a sequence can have (sinks + window + block - 1).
+int win_splits(const kvq_cache* c) {
+    if (!win_mode(c->g)) return 0;
+    return (c->g.sinks + win_rows(c->g) - 1 + kvq::kWinTokens - 1) / kvq::kWinTokens;
 }
 
 }  // namespace
@@ -360,7 +398,8 @@ namespace {
 // Validate an append and build its launch arguments (uploading non-uniform
 // counts); *empty when no sequence gains a token (nothing to launch).
 kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
-                          const int32_t* n_new, void* stream, kvq::TensorArgs (&ta)[2], int (&gx)[2], bool* empty) {
+                          const int32_t* n_new, void* stream, kvq::TensorArgs (&ta)[2], int (&gx)[2], bool* empty,
+                          int* max_new) {
     const kvq_geometry& g = c->g;
     *empty = false;
     const int S = g.num_seqs;
@@ -437,6 +476,10 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
         a.len_base = len_base;
         for (int i = 0; i < n_layers; ++i) a.len_parity |= (uint64_t)(c->parity[layer + i] & 1) << i;
         a.src_layer_bytes = (uint64_t)total * g.kv_heads * g.head_dim * in_bytes(g.in_dtype);
+        a.win_mode = win_mode(g);
+        a.sinks = g.sinks;
+        a.win_rows = win_rows(g);
+        a.win_off = win_off(g, t);
         if (axes[t] == KVQ_AXIS_TOKEN) {
             gx[t] = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
         } else {
@@ -449,7 +492,16 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
         }
     }
     if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");
+    *max_new = max_n;
     return KVQ_OK;
+}
+
+// The launches of a prepared append: quantize (and the full-precision window copy).
+hipError_t launch_append(const kvq_cache* c, const kvq::TensorArgs (&ta)[2], const int (&gx)[2], int max_new,
+                         hipStream_t s) {
+    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], s);
+    if (e == hipSuccess && win_mode(c->g)) e = kvq::launch_window_store(ta[0], ta[1], max_new, s);
+    return e;
 }
 
 // The host side of an append that has been launched: lengths and buffer parity.
@@ -464,11 +516,11 @@ void commit_append(kvq_cache* c, int32_t layer, int32_t n_layers, const int32_t*
 kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const void* k_new, const void* v_new,
                          const int32_t* n_new, void* stream) {
     kvq::TensorArgs ta[2];
-    int gx[2];
+    int gx[2], max_new = 0;
     bool empty;
-    kvq_status st = prepare_append(c, layer, n_layers, k_new, v_new, n_new, stream, ta, gx, &empty);
+    kvq_status st = prepare_append(c, layer, n_layers, k_new, v_new, n_new, stream, ta, gx, &empty, &max_new);
     if (st != KVQ_OK || empty) return st;
-    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], (hipStream_t)stream);
+    hipError_t e = launch_append(c, ta, gx, max_new, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
     commit_append(c, layer, n_layers, n_new);
     return KVQ_OK;
@@ -499,7 +551,7 @@ kvq_status kvq_quantize_append_layers(kvq_cache* c, int32_t layer0, int32_t n_la
 size_t kvq_decode_workspace_size(const kvq_cache* c) {
     if (!c) return 0;
     const kvq_geometry& g = c->g;
-    const uint64_t chunks = std::max<uint64_t>(1, (c->max_cap + min_chunk(c) - 1) / min_chunk(c));
+    const uint64_t chunks = std::max<uint64_t>(1, (c->max_cap + min_chunk(c) - 1) / min_chunk(c)) + win_splits(c);
     const uint64_t slots = (uint64_t)g.num_seqs * g.q_heads * chunks;
     return align_up(slots * 2 * 4, kvq::kAlign) + align_up(slots * g.head_dim * 4, kvq::kAlign);
 }
@@ -543,7 +595,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const int C = mha   ? choose_split_mha(c, max_len, n_layers)
                   : gqa ? choose_split_gqa(c, lens, n_layers)
                         : choose_chunk(c, max_len, n_layers);
-    const int max_chunks = mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C);
+    const int max_chunks = (mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C)) + win_splits(c);
     const uint64_t slots = (uint64_t)n_layers * S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
     const uint64_t need = ml_bytes + align_up(slots * g.head_dim * 4, kvq::kAlign);
@@ -582,6 +634,23 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     for (int i = 0; i < n_layers; ++i) a.len_parity |= (uint64_t)(c->parity[layer + i] & 1) << i;
     a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
+    a.split_floor = mha ? 1 : 0;
+    if (win_mode(g)) {
+        a.win_mode = 1;
+        a.window = g.window;
+        a.sinks = g.sinks;
+        a.tblock = token_block(g);
+        a.win_rows = win_rows(g);
+        a.win_off[0] = win_off(g, 0);
+        a.win_off[1] = win_off(g, 1);
+        a.ws_scale = mha ? 16777216.0f : 1.0f;  // the single-query kernel's partials carry 2^24
+        a.win_splits = win_splits(c);
+    }
+    if (a.win_mode) {  // the full-precision rows' partials, merged after the quantized kernels
+        if (opt.fused) return fail(KVQ_ERR_UNSUPPORTED, "fused decode step with a window");
+        hipError_t e = kvq::launch_decode_window(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "launching the window attention");
+    }
     if (mha) {
         if (opt.fused) {
             a.append_fused = 1;
@@ -593,7 +662,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
             hipError_t e = kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching decode attention");
         }
-        if (max_chunks > 1) {
+        if (max_chunks > 1 || a.win_mode) {
             if (opt.fused) {  // the merge reads the lengths the decode kernel wrote
                 a.append_fused = 0;
                 a.len = opt.fused[0].len_out;
@@ -648,16 +717,16 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
     kvq_status st = decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream, opt);
     if (st != KVQ_OK) return st;
     kvq::TensorArgs ta[2];
-    int gx[2];
+    int gx[2], max_new = 0;
     bool empty;
-    st = prepare_append(c, layer, 1, k_new, v_new, n_new, stream, ta, gx, &empty);
+    st = prepare_append(c, layer, 1, k_new, v_new, n_new, stream, ta, gx, &empty, &max_new);
     if (st != KVQ_OK) return st;
     // Fused when the single-query kernel serves the cache and the step only
     // adds residual key rows (no key block completes) and at most one
     // workgroup's worth of value rows per sequence.
     const int32_t* lens = &c->lens[(size_t)layer * S];
     bool fuse = !empty && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
-                kvq::mha_supported(g.head_dim);
+                kvq::mha_supported(g.head_dim) && !win_mode(g);
     for (int s = 0; fuse && s < S; ++s)
         fuse = (lens[s] + n_new[s]) / g.group_k == lens[s] / g.group_k && n_new[s] <= 256 / (g.head_dim / 32);
     for (const auto& pr : c->pairs) fuse = fuse && kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv);
@@ -670,7 +739,7 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
         return KVQ_OK;
     }
     if (!empty) {
-        hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], (hipStream_t)stream);
+        hipError_t e = launch_append(c, ta, gx, max_new, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
         commit_append(c, layer, 1, n_new);
     }
@@ -714,6 +783,14 @@ kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float*
         a.group = groups[t];
         a.axis = axes[t];
         a.in_dtype = g.in_dtype;
+        if (win_mode(g)) {
+            a.win_mode = 1;
+            a.window = g.window;
+            a.sinks = g.sinks;
+            a.tblock = token_block(g);
+            a.win_rows = win_rows(g);
+            a.win_off = win_off(g, t);
+        }
         hipError_t e = kvq::launch_dequant(a, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "launching dequantize");
     }

@@ -370,10 +370,14 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     const int seq = a.seq_list ? a.seq_list[z] : z;
     const int kvh = blockIdx.y, split = blockIdx.x;
     const int len = a.len[seq];
+    // Quantized tokens [tb, te): all of them, or with a full-precision window
+    // the whole key blocks inside [sinks, len - window).
+    int tb, te;
+    quant_range(a, len, tb, te);
     const int CW = a.chunk;
-    const int wa = split * CW;
-    if (wa >= len) return;  // merge_kernel sees ceil(len / CW) splits
-    const int wb = min(wa + CW, len);
+    const int wa = tb + split * CW;
+    if (wa >= te) return;  // merge_kernel sees ceil((te - tb) / CW) splits
+    const int wb = min(wa + CW, te);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
     const int cw0 = wave * DW;  // first channel of this wave
@@ -381,7 +385,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     const SeqEntry& e = a.table[seq];
     const int lgk = a.log2_group_k, lgv = a.log2_group_v;
     const int Gk = 1 << lgk;
-    const int nqk = (len >> lgk) << lgk;  // tokens with quantized keys
+    const int nqk = a.win_mode ? te : (len >> lgk) << lgk;  // tokens read with quantized keys
     const int qend = min(wb, nqk);
     const int vgpr = D >> lgv;            // value groups per token
     const int g0 = cw0 >> lgv;            // first value group of this wave

@@ -459,24 +459,29 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     if (FUSED && kvh == 0 && split == 0 && tid == 0) a.app_k.len_out[seq] = len;
     float* out = a.out + ((size_t)seq * a.q_heads + kvh) * D;
     if (len == 0) {
-        if (split == 0)
+        if (split == 0 && !a.win_mode)
             for (int c = tid; c < D; c += NT) out[c] = 0.f;
         return;
     }
+    // Quantized tokens [tb, te): all of them, or with a full-precision window
+    // the whole key blocks inside [sinks, len - window) (the window kernel
+    // covers the rest and the merge combines the partials).
+    int tb, te;
+    quant_range(a, len, tb, te);
     const int CW = a.chunk;
-    const int nsplit = max(1, len / CW);
+    const int nsplit = a.win_mode ? quant_splits(a, tb, te) : max(1, len / CW);
     if (split >= nsplit) return;
     // Fused step: the new rows are only read by this split's residual loop, so
     // their stores complete while the quantized tokens stream; the barrier
     // before that loop (workgroup scope: one compute unit) orders them.
     const bool appended = FUSED && n_app > 0 && split == nsplit - 1;
     if (appended) fused_append(a, kvh, seq, len_old, n_app, NT);
-    const int wa = split * CW, wb = split == nsplit - 1 ? len : wa + CW;
+    const int wa = tb + split * CW, wb = split == nsplit - 1 ? te : wa + CW;
     const int ts = lane / UPR, cg = lane % UPR;
     const SeqEntry& e = a.table[seq];
     const int lgk = a.log2_group_k;
     const bool two_blocks = lgk == 5;  // a 64-token super-tile spans two 32-token key blocks
-    const int nqk = (len >> lgk) << lgk;
+    const int nqk = a.win_mode ? te : (len >> lgk) << lgk;
     const int qend = min(wb, nqk);
 
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
@@ -724,10 +729,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
         float o = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) o = fmaf(mrg_o[w][c], wgt[w], o);
-        if (nsplit == 1) out[c] = o * inv;
+        if (nsplit == 1 && !a.win_mode) out[c] = o * inv;
         else a.ws_o[slot * D + c] = o;
     }
-    if (nsplit > 1 && tid == 0) {
+    if ((nsplit > 1 || a.win_mode) && tid == 0) {
         a.ws_ml[slot * 2 + 0] = M;
         a.ws_ml[slot * 2 + 1] = L;
     }

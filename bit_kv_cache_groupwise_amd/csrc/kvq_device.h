@@ -56,6 +56,46 @@ __device__ __forceinline__ TensorArgs layer_args(const TensorArgs& a0, int& z, i
     return a;
 }
 
+// Full-precision window and sinks: the tokens [tb, te) a decode kernel reads
+// quantized, the whole key blocks inside [sinks, len - window); everything else
+// below len is read in full precision. Without a window, [0, len).
+__device__ __forceinline__ void quant_range(const DecodeArgs& a, int len, int& tb, int& te) {
+    if (!a.win_mode) {
+        tb = 0;
+        te = len;
+        return;
+    }
+    const int r = len - a.window;
+    const int q = r > 0 ? r / a.tblock * a.tblock : 0;
+    tb = a.sinks;
+    te = q > a.sinks ? q : a.sinks;
+}
+
+// Quantized splits of [tb, te) (window mode): split_floor 1 -> the single-query
+// kernel's max(1, n / chunk), else ceil(n / chunk); 0 when the range is empty.
+__device__ __forceinline__ int quant_splits(const DecodeArgs& a, int tb, int te) {
+    const int n = te - tb;
+    if (n <= 0) return 0;
+    return a.split_floor ? (n / a.chunk > 1 ? n / a.chunk : 1) : (n + a.chunk - 1) / a.chunk;
+}
+
+// Full-precision tokens of a sequence of length len (window mode): the sinks
+// [0, min(sinks, len)) then the recent tokens [max(te, sinks), len); fp_token(i)
+// is the i-th of them and window_row(t) its row in the head's window area.
+__device__ __forceinline__ int fp_count(const DecodeArgs& a, int len, int te) {
+    const int ns = len < a.sinks ? len : a.sinks;
+    const int rs = te > ns ? te : ns;
+    return ns + (len > rs ? len - rs : 0);
+}
+__device__ __forceinline__ int fp_token(const DecodeArgs& a, int len, int te, int i) {
+    const int ns = len < a.sinks ? len : a.sinks;
+    const int rs = te > ns ? te : ns;
+    return i < ns ? i : rs + (i - ns);
+}
+__device__ __forceinline__ int window_row(int t, int sinks, int win_rows) {
+    return t < sinks ? t : sinks + t % win_rows;
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
 }

@@ -62,6 +62,10 @@ struct TensorArgs {
     uint64_t len_parity;        // bit i: current length buffer of layer layer0 + i
     int32_t* len_base;          // both length buffers, [2][layers_total][num_seqs]
     uint64_t src_layer_bytes;   // bytes of new rows per layer in src
+    // Full-precision window and sinks (win_mode != 0): new rows are also copied
+    // into the window area of the head's residual region (window_store_kernel).
+    int32_t win_mode, sinks, win_rows;  // win_rows = window + block (the recent ring)
+    uint32_t win_off;           // byte offset of the window area inside a head's residual region
 };
 
 struct DecodeArgs {
@@ -100,6 +104,14 @@ struct DecodeArgs {
     // length. `len` then holds the lengths before the append.
     int32_t append_fused;
     TensorArgs app_k, app_v;
+    // Full-precision window and sinks (win_mode != 0): the quantized kernels
+    // read tokens [sinks, Q) only (quant_range) and always write split
+    // partials; decode_window_kernel writes the full-precision rows' partials
+    // after them (slots nq .. nq + nfs - 1) and merge_kernel merges both.
+    int32_t win_mode, window, sinks, tblock, win_rows;  // tblock: key block in tokens
+    uint32_t win_off[2];        // byte offset of the window area inside a head's residual region [K, V]
+    float ws_scale;             // factor the quantized kernel's partial l and o carry (2^24: single query)
+    int32_t win_splits;         // grid x of decode_window_kernel (full-precision splits at most)
 };
 
 struct DequantArgs {
@@ -109,7 +121,11 @@ struct DequantArgs {
     const uint8_t* resid;
     SeqEntry entry;
     int32_t tensor, len, kv_heads, head_dim, group, axis, in_dtype;
+    int32_t win_mode, window, sinks, tblock, win_rows;  // as in DecodeArgs
+    uint32_t win_off;
 };
+
+constexpr int kWinTokens = 64;  // full-precision tokens per decode_window_kernel workgroup
 
 // Keys and values of one append in one launch: gx_k workgroups per (head, seq)
 // for the keys, then gx_v for the values.
@@ -143,6 +159,8 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
                                : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
 }
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_window_store(const TensorArgs& k, const TensorArgs& v, int max_new, hipStream_t s);
+hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace kvq

@@ -243,15 +243,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
     const int seq = z, kvh = blockIdx.y, chunk = blockIdx.x;
     const int len = a.len[seq];
-    const int C = a.chunk, t0 = chunk * C;
-    if (t0 >= len) return;
-    const int t1 = min(t0 + C, len), nt = t1 - t0;
+    int tb, te;  // quantized tokens: all, or the whole key blocks inside [sinks, len - window)
+    quant_range(a, len, tb, te);
+    const int C = a.chunk, t0 = tb + chunk * C;
+    if (t0 >= te) return;
+    const int t1 = min(t0 + C, te), nt = t1 - t0;
     const int D = a.head_dim, UPR = D >> 5, R = a.q_heads / a.kv_heads;
     const int Gk = a.group_k, Gv = a.group_v;
     const bool kch = a.axis_k == 0;
     const SeqEntry& e = a.table[seq];
     const int BK = e.bits[0], BV = e.bits[1];
-    const int nqk = kch ? (len / Gk) * Gk : len;
+    const int nqk = a.win_mode ? te : kch ? (len / Gk) * Gk : len;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     constexpr int IB = In<DT>::bytes;
 
@@ -397,11 +399,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
     const int c = blockIdx.z * 16 + cl;
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
-    if (a.split_floor) {
+    int nch;
+    if (a.win_mode) {
+        // quantized splits, then the full-precision rows' splits
+        int tb, te;
+        quant_range(a, len, tb, te);
+        nch = len == 0 ? 0 : quant_splits(a, tb, te) + (fp_count(a, len, te) + kWinTokens - 1) / kWinTokens;
+    } else {
         // single-query kernel: max(1, len / chunk) splits; one split was written directly
-        if (len / a.chunk <= 1) return;
+        if (a.split_floor && len / a.chunk <= 1) return;
+        nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     }
-    const int nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     if (nch == 0) {
         if (sg == 0 && c < D) out[c] = 0.f;
         return;
@@ -433,6 +441,155 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
 #pragma unroll
         for (int g = 0; g < 16; ++g) t += part[g][cl];
         out[c] = t / L;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Full-precision window and sinks ([U] "O Imposto dos Sistemas ...": recent
+// tokens in full precision; [U] "Onde o Trabalho Esta Indo": sink tokens too).
+// Workgroup = (split of kWinTokens full-precision tokens, kv head, seq): the
+// attention partial (m, l, o) of every query head of the kv head over its
+// tokens, read from the window area in the input dtype, written as split
+// nq + blockIdx.x (after the quantized kernel's nq splits). Scores: thread =
+// (token, quarter of the channels), the 16 query heads' sums in registers;
+// values: thread = (token part, channel), the 16 outputs in registers.
+// LDS: q [R][D] | weights [R][kWinTokens] | per-head m, l | [kThreads] reduction.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) {
+    extern __shared__ float win_smem[];
+    int z = blockIdx.z;
+    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
+    const int seq = z, kvh = blockIdx.y, D = a.head_dim, R = a.q_heads / a.kv_heads;
+    const int len = a.len[seq];
+    int tb, te;
+    quant_range(a, len, tb, te);
+    const int nfp = fp_count(a, len, te);
+    const int i0 = blockIdx.x * kWinTokens;
+    if (len == 0 || i0 >= nfp) return;
+    const int n = min(kWinTokens, nfp - i0);
+    const int nq = quant_splits(a, tb, te);
+    const int tid = threadIdx.x;
+    constexpr int IB = In<DT>::bytes;
+    const SeqEntry& e = a.table[seq];
+    const uint8_t* kw = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0] + a.win_off[0];
+    const uint8_t* vw = a.resid + e.resid[1] + (size_t)kvh * e.resid_hs[1] + a.win_off[1];
+    float* q_s = win_smem;                 // [R][D], scaled to the log2 domain
+    float* p_s = q_s + R * D;              // [R][kWinTokens]: scores, then weights
+    float* ml_s = p_s + R * kWinTokens;    // [R][2]
+    float* red = ml_s + 2 * R;             // [TP][D] = kThreads floats
+    for (int i = tid; i < R * D; i += kThreads)
+        q_s[i] = load_in<DT>(a.q, ((size_t)seq * a.q_heads + (size_t)kvh * R) * D + i) * a.qscale;
+    __syncthreads();
+
+    // ---- scores: thread = (token i, channel quarter p)
+    {
+        const int i = tid >> 2, p = tid & 3, DQ = D >> 2;
+        float acc[kMaxQueryGroup];
+#pragma unroll
+        for (int r = 0; r < kMaxQueryGroup; ++r) acc[r] = 0.f;
+        if (i < n) {
+            const int t = fp_token(a, len, te, i0 + i);
+            const uint8_t* row = kw + (size_t)window_row(t, a.sinks, a.win_rows) * D * IB;
+            for (int c0 = p * DQ; c0 < (p + 1) * DQ; c0 += 8) {
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = load_in<DT>(row, c0 + j);
+#pragma unroll
+                for (int r = 0; r < kMaxQueryGroup; ++r) {
+                    if (r < R) {
+                        const float* qr = q_s + r * D + c0;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[r] = fmaf(qr[j], x[j], acc[r]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxQueryGroup; ++r) {
+            if (r < R) {
+                float v = acc[r];
+                v += __shfl_xor(v, 1);
+                v += __shfl_xor(v, 2);
+                if (p == 0 && i < kWinTokens) p_s[r * kWinTokens + i] = i < n ? v : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- softmax of this split per query head: wave w takes heads w, w + 4, ...
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int r = wave; r < R; r += kThreads / 64) {
+            const float sc = p_s[r * kWinTokens + lane];
+            const float m = wave_max(sc);
+            const float w = lane < n ? exp2f(sc - m) : 0.f;
+            p_s[r * kWinTokens + lane] = w;
+            const float l = wave_sum(w);
+            if (lane == 0) {
+                ml_s[2 * r] = m;
+                ml_s[2 * r + 1] = l;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- values: thread = (token part tp, channel c); outputs of all heads in registers
+    const int TP = kThreads / D, tp = tid / D, c = tid % D;
+    float o[kMaxQueryGroup];
+#pragma unroll
+    for (int r = 0; r < kMaxQueryGroup; ++r) o[r] = 0.f;
+    for (int i = tp; i < n; i += TP) {
+        const int t = fp_token(a, len, te, i0 + i);
+        const float v = load_in<DT>(vw + (size_t)window_row(t, a.sinks, a.win_rows) * D * IB, c);
+#pragma unroll
+        for (int r = 0; r < kMaxQueryGroup; ++r)
+            if (r < R) o[r] = fmaf(p_s[r * kWinTokens + i], v, o[r]);
+    }
+    const int slot0 = nq + blockIdx.x;
+    for (int r = 0; r < R; ++r) {
+        red[tp * D + c] = o[r];
+        __syncthreads();
+        if (tid < D) {
+            float sum = 0.f;
+            for (int k = 0; k < TP; ++k) sum += red[k * D + tid];
+            const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + slot0;
+            a.ws_o[slot * D + tid] = sum * a.ws_scale;
+            if (tid == 0) {
+                a.ws_ml[slot * 2 + 0] = ml_s[2 * r];
+                a.ws_ml[slot * 2 + 1] = ml_s[2 * r + 1] * a.ws_scale;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Copy the new rows of an append that the window keeps into the window area of
+// (seq, head): sink tokens t < sinks, and the later tokens t >= len1 - win_rows
+// (no two of them share a row). One element per thread, keys and values.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void window_store_kernel(TensorArgs k0, TensorArgs v0) {
+    int z = blockIdx.z, zv = blockIdx.z;
+    const TensorArgs k = layer_args(k0, z, gridDim.z / k0.n_layers);
+    const TensorArgs v = layer_args(v0, zv, gridDim.z / v0.n_layers);
+    const int seq = z, head = blockIdx.y, D = k.head_dim;
+    const int len0 = k.len_in[seq];
+    const int n = k.n_new ? k.n_new[seq] : k.n_uniform;
+    const int row_start = k.row_start ? k.row_start[seq] : seq * k.n_uniform;
+    const int len1 = len0 + n;
+    const int keep_from = max(len1 - k.win_rows, 0);
+    constexpr int IB = In<DT>::bytes;
+    const SeqEntry& e = k.table[seq];
+    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n * D; idx += gridDim.x * kThreads) {
+        const int i = idx / D, ch = idx % D, t = len0 + i;
+        if (t >= k.sinks && t < keep_from) continue;
+        const size_t so = ((size_t)(row_start + i) * k.kv_heads + head) * D + ch;
+        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows) * D + ch;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const TensorArgs& x = T == 0 ? k : v;
+            uint8_t* w = x.resid + e.resid[T] + (size_t)head * e.resid_hs[T] + x.win_off;
+            if constexpr (IB == 4) ((uint32_t*)w)[dof] = ((const uint32_t*)x.src)[so];
+            else ((uint16_t*)w)[dof] = ((const uint16_t*)x.src)[so];
+        }
     }
 }
 
@@ -471,6 +628,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
     const bool ch = a.axis == 0;
     const int nq = ch ? (a.len / G) * G : a.len;
     float* out = a.out + ((size_t)head * a.len + t) * D + 32 * u;
+    if (a.win_mode) {
+        // the full-precision tokens of the window and the sinks, as the attention reads them
+        const int r = a.len - a.window;
+        const int q = max(r > 0 ? r / a.tblock * a.tblock : 0, a.sinks);
+        if (t < a.sinks || t >= q) {
+            const uint8_t* wrow = a.resid + a.entry.resid[T] + (size_t)head * a.entry.resid_hs[T] + a.win_off +
+                                  (size_t)window_row(t, a.sinks, a.win_rows) * D * In<DT>::bytes;
+            for (int j = 0; j < 32; ++j) out[j] = load_in<DT>(wrow, 32 * u + j);
+            return;
+        }
+    }
     if (t < nq) {
         const uint32_t* unit = (const uint32_t*)(a.codes + a.entry.codes[T] + (size_t)head * a.entry.codes_hs[T] +
                                                  (size_t)t * (D * B / 8)) + u * B;
@@ -535,6 +703,30 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs * a.n_layers, (a.head_dim + 15) / 16), dim3(kThreads), 0, s,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s) {
+    const int R = a.q_heads / a.kv_heads;
+    dim3 grid(a.win_splits, a.kv_heads, a.num_seqs * a.n_layers);
+    const size_t lds = sizeof(float) * ((size_t)R * a.head_dim + (size_t)R * kWinTokens + 2 * R + kThreads);
+    switch (a.in_dtype) {
+        case 0: hipLaunchKernelGGL(decode_window_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
+        case 1: hipLaunchKernelGGL(decode_window_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
+        default: hipLaunchKernelGGL(decode_window_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_window_store(const TensorArgs& k, const TensorArgs& v, int max_new, hipStream_t s) {
+    const long elems = (long)max_new * k.head_dim;
+    const int gx = (int)std::min<long>(std::max<long>(1, (elems + kThreads - 1) / kThreads), 1024);
+    dim3 grid(gx, k.kv_heads, k.num_seqs * k.n_layers);
+    switch (k.in_dtype) {
+        case 0: hipLaunchKernelGGL(window_store_kernel<0>, grid, dim3(kThreads), 0, s, k, v); break;
+        case 1: hipLaunchKernelGGL(window_store_kernel<1>, grid, dim3(kThreads), 0, s, k, v); break;
+        default: hipLaunchKernelGGL(window_store_kernel<2>, grid, dim3(kThreads), 0, s, k, v); break;
+    }
     return hipGetLastError();
 }
 

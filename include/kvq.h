@@ -43,6 +43,11 @@
  *              channel axis: [block][channel]; token axis: [token][group].
  *   residual   channel-axis tensors only: G rows of D input-dtype values per
  *              (layer, seq, head); token t lives in row t mod G.
+ *   window     with a window or sinks (kvq_geometry), each tensor's head region
+ *              of the residual pool continues (after the G residual rows of a
+ *              channel-axis tensor) with sinks + window + block rows of D
+ *              input-dtype values: sink token t in row t, later token t in row
+ *              sinks + (t mod (window + block)).
  *   pools      four caller-owned device buffers (codes, metadata, residual,
  *              table) sized by kvq_plan; regions are ordered layer -> seq ->
  *              tensor (K, V) -> head, each head region 256-byte aligned.
@@ -101,6 +106,25 @@ typedef struct kvq_geometry {
     int32_t axis_v;     /* KVQ_AXIS_TOKEN   (default for values)                 */
     int32_t in_dtype;   /* KVQ_F32, KVQ_F16 or KVQ_BF16: K/V/q inputs, residual  */
     int32_t meta_dtype; /* KVQ_F16 (the only metadata type this build stores)    */
+    /* Full-precision recent window and attention sinks ([U] "O Imposto dos
+     * Sistemas ...": the most recent tokens, up to a window of about 128,
+     * stay in full precision; [U] "O Que Fazer Com Isso" and "Onde o
+     * Trabalho Esta Indo": high-precision windows for recent and sink tokens;
+     * [N] "Pengecualian recent-token ...": a high-precision region next to the
+     * packed cache). Both 0 (the default): off, only the channel-axis
+     * residual above is unquantized. Otherwise the decode attention (and
+     * kvq_dequantize) reads a token in the input dtype when t < sinks or when
+     * it is not inside a whole key block lying in [sinks, len - window); the
+     * blocks inside are read quantized. A block is the token length of a
+     * channel-axis group (the larger one when both tensors are on the channel
+     * axis; 1 token when neither is). So between window and
+     * window + block - 1 recent tokens are full precision. Both tensors share
+     * the boundary. Every token is still quantized on arrival (the stored
+     * codes do not depend on the window); the full-precision rows are kept
+     * besides, in the residual pool. Limits: 0 <= window, 0 <= sinks,
+     * sinks a multiple of the key block, sinks + window + block <= 4096. */
+    int32_t window;     /* R: recent tokens kept in full precision (0: none)    */
+    int32_t sinks;      /* S: first tokens kept in full precision (0: none)     */
 } kvq_geometry;
 
 /* Byte counts. The pool sizes include 256-byte alignment of every head
@@ -114,7 +138,9 @@ typedef struct kvq_sizes {
     uint64_t table_bytes;            /* table buffer (offsets, lengths, call args)   */
     uint64_t formula_codes_bytes;    /* sum rows * kv_heads * D * B / 8              */
     uint64_t formula_meta_bytes;     /* 4 bytes per group                            */
-    uint64_t formula_residual_bytes; /* G * D * in_bytes per channel-axis tensor head */
+    uint64_t formula_residual_bytes; /* G * D * in_bytes per channel-axis tensor head,
+                                        plus (sinks + window + block) * D * in_bytes per
+                                        tensor head with a window or sinks            */
 } kvq_sizes;
 
 /* Byte offsets of one (layer, seq) in the pools, head 0, plus per-head
@@ -183,7 +209,8 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const voi
  * 256 / (head_dim / 32) rows per sequence, both run in one launch: each
  * (sequence, kv head) workgroup that attends the newest tokens first appends
  * them (for bit pairs where the fused kernel keeps the plain one's
- * occupancy). Otherwise the two run as consecutive launches. */
+ * occupancy, and without a window or sinks). Otherwise the two run as
+ * consecutive launches. */
 kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                            const int32_t* n_new, const void* q, float softmax_scale, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);

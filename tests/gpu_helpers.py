@@ -18,17 +18,17 @@ def kvq():
     return k
 
 
-def geom_of(w: W.Workload, layers=None):
+def geom_of(w: W.Workload, layers=None, window=0, sinks=0):
     k = kvq()
     return k.geometry(layers=layers or w.layers, num_seqs=w.num_seqs, kv_heads=w.kv_heads, q_heads=w.q_heads,
                       head_dim=w.head_dim, group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v,
-                      in_dtype=w.in_dtype)
+                      in_dtype=w.in_dtype, window=window, sinks=sinks)
 
 
-def make_cache(w: W.Workload, extra=0, layers=None, capacity=None):
+def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0):
     k = kvq()
     cap = capacity or [L + w.new_tokens + extra for L in w.lengths]
-    return k.Cache(geom_of(w, layers), cap, [b[0] for b in w.bits], [b[1] for b in w.bits])
+    return k.Cache(geom_of(w, layers, window, sinks), cap, [b[0] for b in w.bits], [b[1] for b in w.bits])
 
 
 def history(w: W.Workload, layer: int, device="cpu"):
@@ -77,6 +77,12 @@ def encode(w: W.Workload, k, v, seq: int, head: int) -> dict:
     bk, bv = w.bits[seq]
     return o.encode_head(k[:, head, :], v[:, head, :], group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k,
                          axis_v=w.axis_v, bits_k=bk, bits_v=bv)
+
+
+def encode_window(w: W.Workload, k, v, seq: int, head: int, window: int, sinks: int) -> dict:
+    bk, bv = w.bits[seq]
+    return o.encode_head_window(k[:, head, :], v[:, head, :], window=window, sinks=sinks, group_k=w.group_k,
+                                group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, bits_k=bk, bits_v=bv)
 
 
 def _u32(pool, off, nbytes):

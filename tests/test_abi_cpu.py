@@ -76,6 +76,26 @@ def test_plan_matches_closed_form(dt, ib):
     assert sz.codes_bytes - sz.formula_codes_bytes < 256 * 2 * 3 * 4 * 2
 
 
+@pytest.mark.parametrize("window,sinks,axis_k,block", [(128, 32, 0, 32), (0, 64, 0, 32), (50, 3, 1, 1)])
+def test_plan_window_area(window, sinks, axis_k, block):
+    """With a window or sinks every tensor head also holds sinks + window + block
+    full-precision rows; codes and metadata are those of the plain cache."""
+    caps = [0, 1000, 4097]
+    plain = kvq.kvq_plan(_geom(axis_k=axis_k), caps, [2, 6, 4], [2, 4, 8])
+    sz = kvq.kvq_plan(_geom(axis_k=axis_k, window=window, sinks=sinks), caps, [2, 6, 4], [2, 4, 8])
+    assert sz.formula_codes_bytes == plain.formula_codes_bytes
+    assert sz.formula_meta_bytes == plain.formula_meta_bytes
+    rows = sinks + window + block
+    assert sz.formula_residual_bytes == plain.formula_residual_bytes + 2 * 3 * 2 * 4 * rows * 128 * 2
+    assert sz.residual_bytes >= sz.formula_residual_bytes
+
+
+@pytest.mark.parametrize("window,sinks", [(0, 16), (-1, 0), (0, -32), (4096, 0), (3000, 1088)])
+def test_plan_rejects_bad_window(window, sinks):
+    assert kvq.kvq_plan_status(_geom(window=window, sinks=sinks), [10] * 3, [2] * 3, [2] * 3) == kvq.KVQ_ERR_ARG
+    assert kvq.kvq_last_error()
+
+
 def test_plan_gpt2_effective_bits():
     """GPT-2-shaped cache (K6/V4, per-head 64-channel groups): 5.5 stored bits per
     element at a length that is a multiple of G, as the hatterialabs.com page
