@@ -37,9 +37,20 @@ LLC_BYTES = 256 << 20  # MI355X Infinity Cache
 METRIC = "quantized decode-attention HBM GB/s (% of peak) and tokens/s; quantize GB/s"
 
 
-def algorithmic_head_bytes(T, D, axis_k, axis_v, Gk, Gv, bk, bv, ib):
+def algorithmic_head_bytes(T, D, axis_k, axis_v, Gk, Gv, bk, bv, ib, window=0, sinks=0):
     """Bytes decode attention must read for one (seq, kv head) at length T:
-    packed codes + 4-byte (step, zero) pairs + residual rows in the input dtype."""
+    packed codes + 4-byte (step, zero) pairs + residual rows in the input dtype.
+    With a full-precision window or sinks: the codes and pairs of the whole key
+    blocks inside [sinks, T - window), and every other token's key and value
+    rows in the input dtype."""
+    if window or sinks:
+        blk = max([G for axis, G in ((axis_k, Gk), (axis_v, Gv)) if axis == 0] or [1])
+        q = max(sinks, blk * ((T - window) // blk))
+        nq = max(0, q - sinks)
+        tot = 2 * (T - nq) * D * ib
+        for axis, G, B in ((axis_k, Gk, bk), (axis_v, Gv, bv)):
+            tot += nq * D * B // 8 + (nq // G * D if axis == 0 else nq * (D // G)) * 4
+        return tot
     tot = 0
     for axis, G, B in ((axis_k, Gk, bk), (axis_v, Gv, bv)):
         if axis == 0:
@@ -76,6 +87,9 @@ def main():
     ap.add_argument("--no-append-timing", action="store_true",
                     help="skip the separately timed appends after the timed region (profiled runs: every append "
                          "after the prefill then belongs to a timed decode step)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="recent tokens kept in full precision (the decode reads them unquantized)")
+    ap.add_argument("--sinks", type=int, default=0, help="first tokens kept in full precision")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -102,7 +116,8 @@ def main():
     n_new = w.new_tokens
     model_layers = w.layers  # layers attended per step (12 for the GPT-2 shape, else 1)
     step_lens = [L + n_new for L in w.lengths]
-    step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib) * H
+    WS = dict(window=args.window, sinks=args.sinks)
+    step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib, **WS) * H
                      for T, (bk, bv) in zip(step_lens, w.bits)) * model_layers
     rot = args.rotate or rotation_for(step_bytes)
     # after the timed region: events around the append alone
@@ -112,7 +127,8 @@ def main():
     layers = rot * model_layers
     cap = [L + n_new * appends_per_layer for L in w.lengths]
     geom = kvq.geometry(layers=layers, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D, group_k=w.group_k,
-                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype)
+                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype,
+                        window=args.window, sinks=args.sinks)
     cache = kvq.Cache(geom, cap, [b[0] for b in w.bits], [b[1] for b in w.bits], device=dev)
 
     # ---- bulk prefill = quantize-append into an empty cache (timed: quantize GB/s)
@@ -244,10 +260,12 @@ def main():
         for m in range(model_layers):
             l = base + m
             lens[l] = [x + n_new for x in lens[l]]
-            per_layer.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib)
-                                 * H for T, (bk, bv) in zip(lens[l], w.bits)))
+            per_layer.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib,
+                                                        **WS) * H for T, (bk, bv) in zip(lens[l], w.bits)))
         dec_bytes.extend([sum(per_layer)] if multi else per_layer)
     app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
+    if args.window or args.sinks:  # the new rows are also copied into the full-precision window
+        app_bytes += S * n_new * H * 4 * D * ib
     call_bytes = [b + app_bytes for b in dec_bytes] if fused_step else dec_bytes  # what one call moves
     ev_bytes = [call_bytes[i * dec_per_step + m] for i in timed for m in range(dec_per_step)]  # event-timed calls
     ms_per_step = wall_s * 1e3 / args.steps
@@ -295,7 +313,9 @@ def main():
         "config": {"workload": w.name, "num_seqs": S, "kv_heads": H, "q_heads": w.q_heads, "head_dim": D,
                    "cached_tokens": list(sorted(set(w.lengths)))[:4] if len(set(w.lengths)) > 1 else w.lengths[0],
                    "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
-                   "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu"},
+                   "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu",
+                   **({"full_precision_window": args.window, "sinks": args.sinks} if args.window or args.sinks
+                      else {})},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_attention_GBps": round(dec_gbps, 2),
@@ -316,7 +336,7 @@ def main():
                                           "decode_frac_of_ceiling": round(dec_gbps / ceiling_gbps, 4)}},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds, args.window, args.sinks)
     print(json.dumps(result), flush=True)
 
 
@@ -350,7 +370,7 @@ def measured_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, window=0, sinks=0):
     """The CPU oracle, untuned, on a bounded sample of the same decode step:
     for a few sequences it encodes each kv head's cache (quantize + pack),
     dequantizes in float64 and runs the attention of the head's queries. The
@@ -380,12 +400,16 @@ def cpu_baseline(w, budget_s):
             v = v.float().numpy()
             for h in range(w.kv_heads):
                 t0 = time.perf_counter()
-                e = o.encode_head(k[:, h], v[:, h], group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k,
-                                  axis_v=w.axis_v, bits_k=bk, bits_v=bv)
+                kw = dict(group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, bits_k=bk,
+                          bits_v=bv)
+                if window or sinks:
+                    e = o.encode_head_window(k[:, h], v[:, h], window=window, sinks=sinks, **kw)
+                else:
+                    e = o.encode_head(k[:, h], v[:, h], **kw)
                 o.attend(q[h * R:(h + 1) * R], e["k_hat"], e["v_hat"], w.softmax_scale)
                 t_cpu += time.perf_counter() - t0
                 done_bytes += algorithmic_head_bytes(T, w.head_dim, w.axis_k, w.axis_v, w.group_k, w.group_v,
-                                                     bk, bv, ib)
+                                                     bk, bv, ib, window, sinks)
                 heads += 1
                 if t_cpu >= budget_s:
                     break

@@ -349,6 +349,7 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
         delete c;
         return hip_fail(e, "writing the cache table");
     }
+
     *out = c;
     return KVQ_OK;
 }
@@ -496,12 +497,9 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
     return KVQ_OK;
 }
 
-// The launches of a prepared append: quantize (and the full-precision window copy).
-hipError_t launch_append(const kvq_cache* c, const kvq::TensorArgs (&ta)[2], const int (&gx)[2], int max_new,
-                         hipStream_t s) {
-    hipError_t e = kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], s);
-    if (e == hipSuccess && win_mode(c->g)) e = kvq::launch_window_store(ta[0], ta[1], max_new, s);
-    return e;
+// The launch of a prepared append: quantize (and the full-precision window copy).
+hipError_t launch_append(const kvq::TensorArgs (&ta)[2], const int (&gx)[2], int max_new, hipStream_t s) {
+    return kvq::launch_quant_append(ta[0], ta[1], gx[0], gx[1], max_new, s);
 }
 
 // The host side of an append that has been launched: lengths and buffer parity.
@@ -520,7 +518,7 @@ kvq_status append_layers(kvq_cache* c, int32_t layer, int32_t n_layers, const vo
     bool empty;
     kvq_status st = prepare_append(c, layer, n_layers, k_new, v_new, n_new, stream, ta, gx, &empty, &max_new);
     if (st != KVQ_OK || empty) return st;
-    hipError_t e = launch_append(c, ta, gx, max_new, (hipStream_t)stream);
+    hipError_t e = launch_append(ta, gx, max_new, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
     commit_append(c, layer, n_layers, n_new);
     return KVQ_OK;
@@ -595,7 +593,10 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const int C = mha   ? choose_split_mha(c, max_len, n_layers)
                   : gqa ? choose_split_gqa(c, lens, n_layers)
                         : choose_chunk(c, max_len, n_layers);
-    const int max_chunks = (mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C)) + win_splits(c);
+    // the full-precision window's slots after the quantized splits (the
+    // single-query kernel's last split reads those rows itself: none there)
+    const int wsl = mha ? 0 : win_splits(c);
+    const int max_chunks = (mha ? std::max(1, max_len / C) : std::max(1, (max_len + C - 1) / C)) + wsl;
     const uint64_t slots = (uint64_t)n_layers * S * g.q_heads * max_chunks;
     const uint64_t ml_bytes = align_up(slots * 2 * 4, kvq::kAlign);
     const uint64_t need = ml_bytes + align_up(slots * g.head_dim * 4, kvq::kAlign);
@@ -643,13 +644,15 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         a.win_rows = win_rows(g);
         a.win_off[0] = win_off(g, 0);
         a.win_off[1] = win_off(g, 1);
-        a.ws_scale = mha ? 16777216.0f : 1.0f;  // the single-query kernel's partials carry 2^24
-        a.win_splits = win_splits(c);
+        a.ws_scale = 1.0f;  // the query-group and generic kernels' partials carry no factor
+        a.win_splits = wsl;
     }
-    if (a.win_mode) {  // the full-precision rows' partials, merged after the quantized kernels
+    if (a.win_mode) {
         if (opt.fused) return fail(KVQ_ERR_UNSUPPORTED, "fused decode step with a window");
-        hipError_t e = kvq::launch_decode_window(a, (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail(e, "launching the window attention");
+        if (!mha) {  // the full-precision rows' partials (the single-query kernel reads those rows itself)
+            hipError_t e = kvq::launch_decode_window(a, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "launching the window attention");
+        }
     }
     if (mha) {
         if (opt.fused) {
@@ -662,7 +665,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
             hipError_t e = kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching decode attention");
         }
-        if (max_chunks > 1 || a.win_mode) {
+        if (max_chunks > 1) {
             if (opt.fused) {  // the merge reads the lengths the decode kernel wrote
                 a.append_fused = 0;
                 a.len = opt.fused[0].len_out;
@@ -685,6 +688,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         return KVQ_OK;
     }
     hipError_t e = kvq::launch_decode(a, (hipStream_t)stream);
+    if (e == hipSuccess) e = kvq::launch_merge(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "launching decode attention");
     return KVQ_OK;
 }
@@ -739,7 +743,7 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
         return KVQ_OK;
     }
     if (!empty) {
-        hipError_t e = launch_append(c, ta, gx, max_new, (hipStream_t)stream);
+        hipError_t e = launch_append(ta, gx, max_new, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "launching the quantize kernel");
         commit_append(c, layer, 1, n_new);
     }

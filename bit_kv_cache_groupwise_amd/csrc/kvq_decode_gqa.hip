@@ -793,7 +793,9 @@ hipError_t gqa_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s)
 #define KVQ_GCAT(a, b) KVQ_GCAT2(a, b)
 hipError_t KVQ_GCAT(launch_decode_gqa_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                            hipStream_t s) {
-    dim3 grid(a.max_chunks, a.kv_heads, nseqs * a.n_layers);
+    // x: the quantized splits only (the workspace's full-precision slots have no
+    // workgroups here: empty ones would leave the busy ones on a few XCDs)
+    dim3 grid(a.max_chunks - a.win_splits, a.kv_heads, nseqs * a.n_layers);
     return gqa_bk<KVQ_GQA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
 }
 

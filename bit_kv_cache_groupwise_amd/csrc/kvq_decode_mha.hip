@@ -459,17 +459,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     if (FUSED && kvh == 0 && split == 0 && tid == 0) a.app_k.len_out[seq] = len;
     float* out = a.out + ((size_t)seq * a.q_heads + kvh) * D;
     if (len == 0) {
-        if (split == 0 && !a.win_mode)
+        if (split == 0)
             for (int c = tid; c < D; c += NT) out[c] = 0.f;
         return;
     }
     // Quantized tokens [tb, te): all of them, or with a full-precision window
-    // the whole key blocks inside [sinks, len - window) (the window kernel
-    // covers the rest and the merge combines the partials).
+    // the whole key blocks inside [sinks, len - window), whose last split also
+    // attends the full-precision rows (possibly with no quantized token).
     int tb, te;
     quant_range(a, len, tb, te);
     const int CW = a.chunk;
-    const int nsplit = a.win_mode ? quant_splits(a, tb, te) : max(1, len / CW);
+    const int nsplit = max(1, (te - tb) / CW);
     if (split >= nsplit) return;
     // Fused step: the new rows are only read by this split's residual loop, so
     // their stores complete while the quantized tokens stream; the barrier
@@ -694,6 +694,64 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
         }
     }
 
+    // ---- full-precision window and sinks (last split): keys and values in the
+    // input dtype from the window area, 64-token super-tiles across the waves.
+    // A value row enters acc[j] as p * v_j * 2^(code_shift(j) - 24), which the
+    // code-shift undo below turns into p * v_j.
+    if (a.win_mode && split == nsplit - 1) {
+        const int nfp = fp_count(a, len, te);
+        const uint8_t* kwn = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0] + a.win_off[0];
+        const uint8_t* vwn = a.resid + e.resid[1] + (size_t)kvh * e.resid_hs[1] + a.win_off[1];
+        auto row32 = [&](const uint8_t* base, size_t off, float (&x)[32]) {
+            if (a.in_dtype == 0) load32<0>(base, off, x);
+            else if (a.in_dtype == 1) load32<1>(base, off, x);
+            else load32<2>(base, off, x);
+        };
+        for (int st = 64 * wave; st < nfp; st += 64 * NW) {
+            float sc[UPR];
+            bool valid[UPR];
+            int rows[UPR];
+#pragma unroll
+            for (int s = 0; s < UPR; ++s) {
+                const int i = st + s * TPW + ts;
+                valid[s] = i < nfp;
+                rows[s] = valid[s] ? window_row(fp_token(a, len, te, i), a.sinks, a.win_rows) : 0;
+                float x[32];
+                row32(kwn, (size_t)rows[s] * D + 32 * cg, x);
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                part = group_sum<UPR>(part);
+                sc[s] = valid[s] ? part : -INFINITY;
+            }
+            float tmax = sc[0];
+#pragma unroll
+            for (int s = 1; s < UPR; ++s) tmax = fmaxf(tmax, sc[s]);
+            const float mn = wave_max_f(tmax);
+            if (mn > m) {  // exact maximum here: this loop runs once per split
+                const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) acc[j] *= alpha;
+                zacc *= alpha;
+                lsum *= alpha;
+                m = mn;
+            }
+            const float m24 = m - 24.0f;
+#pragma unroll
+            for (int s = 0; s < UPR; ++s) {
+                if (valid[s]) {
+                    const float p = __builtin_amdgcn_exp2f(sc[s] - m24);
+                    lsum += p;
+                    float v[32];
+                    row32(vwn, (size_t)rows[s] * D + 32 * cg, v);
+#pragma unroll
+                    for (int j = 0; j < 32; ++j)
+                        acc[j] = fmaf(p * ((float)(1 << code_shift<BV>(j)) * (1.0f / 16777216.0f)), v[j], acc[j]);
+                }
+            }
+        }
+    }
+
     // ---- wave result: undo the code shifts, add the zero-point sums, reduce over tokens
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = acc[j] * (float)(1 << (24 - code_shift<BV>(j))) + zacc;
@@ -729,10 +787,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
         float o = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) o = fmaf(mrg_o[w][c], wgt[w], o);
-        if (nsplit == 1 && !a.win_mode) out[c] = o * inv;
+        if (nsplit == 1) out[c] = o * inv;
         else a.ws_o[slot * D + c] = o;
     }
-    if ((nsplit > 1 || a.win_mode) && tid == 0) {
+    if (nsplit > 1 && tid == 0) {
         a.ws_ml[slot * 2 + 0] = M;
         a.ws_ml[slot * 2 + 1] = L;
     }
@@ -815,7 +873,9 @@ bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
 
 hipError_t KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                           hipStream_t s) {
-    dim3 grid(a.max_chunks, a.kv_heads, nseqs * a.n_layers);
+    // x: the quantized splits only (the workspace's full-precision slots have no
+    // workgroups here: empty ones would leave the busy ones on a few XCDs)
+    dim3 grid(a.max_chunks - a.win_splits, a.kv_heads, nseqs * a.n_layers);
     return launch_bk<KVQ_MHA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
 }
 

@@ -126,10 +126,13 @@ struct DequantArgs {
 };
 
 constexpr int kWinTokens = 64;  // full-precision tokens per decode_window_kernel workgroup
+constexpr int kWinHeads = 4;    // query heads per decode_window_kernel workgroup
 
 // Keys and values of one append in one launch: gx_k workgroups per (head, seq)
-// for the keys, then gx_v for the values.
-hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, hipStream_t s);
+// for the keys, then gx_v for the values, then (window mode) the copy of the
+// rows the full-precision window keeps (max_new: most tokens a sequence appends).
+hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, int max_new,
+                               hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mha_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
@@ -159,7 +162,6 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
                                : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
 }
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
-hipError_t launch_window_store(const TensorArgs& k, const TensorArgs& v, int max_new, hipStream_t s);
 hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 

@@ -153,18 +153,54 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     }
 }
 
-// One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
-// keys, [gx_k, gx_k + gx_v) the values, each with its own axis.
-// grid = (gx_k + gx_v, kv_heads, num_seqs x layers)
+// Copy the new rows of an append that the window keeps into the window area of
+// (seq, head): sink tokens t < sinks, and the later tokens t >= len1 - win_rows
+// (no two of them share a row). One element per thread, keys and values;
+// workgroup `item` of `nitems` takes every nitems-th block of elements.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, TensorArgs v0, int gx_k) {
+__device__ __forceinline__ void window_store_part(const TensorArgs& k, const TensorArgs& v, int seq, int head,
+                                                  int item, int nitems) {
+    const int D = k.head_dim;
+    const int len0 = k.len_in[seq];
+    const int n = k.n_new ? k.n_new[seq] : k.n_uniform;
+    const int row_start = k.row_start ? k.row_start[seq] : seq * k.n_uniform;
+    const int len1 = len0 + n;
+    // kept rows: sinks [len0, min(len1, sinks)), then [max(len0, sinks, len1 - win_rows), len1)
+    const int n1 = max(0, min(len1, k.sinks) - len0);
+    const int s2 = max(max(len0, k.sinks), len1 - k.win_rows);
+    const int n2 = max(0, len1 - s2);
+    constexpr int IB = In<DT>::bytes;
+    const SeqEntry& e = k.table[seq];
+    for (int idx = item * kThreads + threadIdx.x; idx < (n1 + n2) * D; idx += nitems * kThreads) {
+        const int j = idx / D, ch = idx % D;
+        const int t = j < n1 ? len0 + j : s2 + (j - n1), i = t - len0;
+        const size_t so = ((size_t)(row_start + i) * k.kv_heads + head) * D + ch;
+        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows) * D + ch;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const TensorArgs& x = T == 0 ? k : v;
+            uint8_t* w = x.resid + e.resid[T] + (size_t)head * e.resid_hs[T] + x.win_off;
+            if constexpr (IB == 4) ((uint32_t*)w)[dof] = ((const uint32_t*)x.src)[so];
+            else ((uint16_t*)w)[dof] = ((const uint16_t*)x.src)[so];
+        }
+    }
+}
+
+// One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
+// keys, [gx_k, gx_kv) the values, each with its own axis, and with a
+// full-precision window [gx_kv, gridDim.x) copy the rows the window keeps.
+// grid = (gx_kv + window workgroups, kv_heads, num_seqs x layers)
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, TensorArgs v0, int gx_k, int gx_kv) {
     extern __shared__ uint32_t quant_smem[];
     int z = blockIdx.z, zv = blockIdx.z;
     const TensorArgs k = layer_args(k0, z, gridDim.z / k0.n_layers);
     const TensorArgs v = layer_args(v0, zv, gridDim.z / v0.n_layers);
     const int seq = z, head = blockIdx.y;
     uint32_t* smem = quant_smem;
-    if ((int)blockIdx.x < gx_k) {
+    if ((int)blockIdx.x >= gx_kv) {
+        window_store_part<DT>(k, v, seq, head, (int)blockIdx.x - gx_kv, (int)gridDim.x - gx_kv);
+    } else if ((int)blockIdx.x < gx_k) {
         if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
         else channel_axis_part<DT>(k, blockIdx.x, head, seq, smem);
     } else {
@@ -400,7 +436,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
     int nch;
-    if (a.win_mode) {
+    if (a.win_mode && a.split_floor) {
+        // single-query kernel: max(1, (te - tb) / chunk) splits, the last of
+        // which also read the full-precision rows; one split was written directly
+        int tb, te;
+        quant_range(a, len, tb, te);
+        nch = max(1, (te - tb) / a.chunk);
+        if (len == 0 || nch <= 1) return;
+    } else if (a.win_mode) {
         // quantized splits, then the full-precision rows' splits
         int tb, te;
         quant_range(a, len, tb, te);
@@ -447,20 +490,50 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
 // ---------------------------------------------------------------------------
 // Full-precision window and sinks ([U] "O Imposto dos Sistemas ...": recent
 // tokens in full precision; [U] "Onde o Trabalho Esta Indo": sink tokens too).
-// Workgroup = (split of kWinTokens full-precision tokens, kv head, seq): the
-// attention partial (m, l, o) of every query head of the kv head over its
+// Workgroup = (split of kWinTokens full-precision tokens, (kv head, group of up
+// to kWinHeads of its query heads), seq): the attention partial (m, l, o) of
+// each of those query heads over its
 // tokens, read from the window area in the input dtype, written as split
 // nq + blockIdx.x (after the quantized kernel's nq splits). Scores: thread =
-// (token, quarter of the channels), the 16 query heads' sums in registers;
-// values: thread = (token part, channel), the 16 outputs in registers.
+// (token, quarter of the channels) with its inputs in registers; values:
+// thread = (token part, channel) with its tokens' inputs in registers; one
+// query head at a time against them.
 // LDS: q [R][D] | weights [R][kWinTokens] | per-head m, l | [kThreads] reduction.
 // ---------------------------------------------------------------------------
+// 8 consecutive input elements at element offset `off` (16-byte aligned for
+// 2-byte inputs, 32-byte for float32) as floats.
 template <int DT>
+__device__ __forceinline__ void load8(const uint8_t* base, size_t off, float (&x)[8]) {
+    if constexpr (DT == 0) {
+        const uint4* p = (const uint4*)((const float*)base + off);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(w[j]);
+    } else {
+        const uint4 a = *(const uint4*)((const uint16_t*)base + off);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = half_to_f32<DT>(w[j]);
+            x[2 * j + 1] = half_to_f32<DT>(w[j] >> 16);
+        }
+    }
+}
+
+template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) {
     extern __shared__ float win_smem[];
+    constexpr int DQ = D / 4;          // channels per thread in the score phase
+    constexpr int TP = kThreads / D;   // token parts in the value phase
+    constexpr int TPT = kWinTokens / TP;  // tokens per thread in the value phase
+    constexpr int QPT = (kWinHeads * D + kThreads - 1) / kThreads;  // query elements per thread, at most
     int z = blockIdx.z;
     const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
-    const int seq = z, kvh = blockIdx.y, D = a.head_dim, R = a.q_heads / a.kv_heads;
+    // y = (kv head, group of up to kWinHeads of its query heads)
+    const int RA = a.q_heads / a.kv_heads, HG = (RA + kWinHeads - 1) / kWinHeads;
+    const int seq = z, kvh = blockIdx.y / HG, h0 = (blockIdx.y % HG) * kWinHeads;
+    const int R = min(kWinHeads, RA - h0);  // query heads of this workgroup: h0 .. h0 + R - 1
     const int len = a.len[seq];
     int tb, te;
     quant_range(a, len, tb, te);
@@ -470,49 +543,57 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
     const int n = min(kWinTokens, nfp - i0);
     const int nq = quant_splits(a, tb, te);
     const int tid = threadIdx.x;
-    constexpr int IB = In<DT>::bytes;
     const SeqEntry& e = a.table[seq];
     const uint8_t* kw = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0] + a.win_off[0];
     const uint8_t* vw = a.resid + e.resid[1] + (size_t)kvh * e.resid_hs[1] + a.win_off[1];
     float* q_s = win_smem;                 // [R][D], scaled to the log2 domain
     float* p_s = q_s + R * D;              // [R][kWinTokens]: scores, then weights
     float* ml_s = p_s + R * kWinTokens;    // [R][2]
-    float* red = ml_s + 2 * R;             // [TP][D] = kThreads floats
-    for (int i = tid; i < R * D; i += kThreads)
-        q_s[i] = load_in<DT>(a.q, ((size_t)seq * a.q_heads + (size_t)kvh * R) * D + i) * a.qscale;
+    float* red = ml_s + 2 * R;             // [TP][R][D] partial outputs (TP > 1)
+    int* row_s = (int*)(red + (TP > 1 ? TP * R * D : 0));  // [kWinTokens]: window row of each token
+    {
+        // the R query rows: every load issued before the first use. Loads are
+        // unconditional, from clamped (valid) addresses: a load under a branch
+        // is followed by its own wait, which would serialize them.
+        const size_t qo = ((size_t)seq * a.q_heads + (size_t)kvh * RA + h0) * D;
+        float qv[QPT];
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) qv[k] = load_in<DT>(a.q, qo + min(tid + k * kThreads, R * D - 1));
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < R * D) q_s[i] = qv[k] * a.qscale;
+        }
+    }
+    if (tid < kWinTokens)
+        row_s[tid] = tid < n ? window_row(fp_token(a, len, te, i0 + tid), a.sinks, a.win_rows) : 0;
     __syncthreads();
 
-    // ---- scores: thread = (token i, channel quarter p)
+    // ---- scores: thread = (token i, channel quarter p); the quarter's inputs come
+    // in 16-byte loads issued up front, the 16 query heads' sums stay in registers
     {
-        const int i = tid >> 2, p = tid & 3, DQ = D >> 2;
-        float acc[kMaxQueryGroup];
+        const int i = tid >> 2, p = tid & 3;
+        float x[DQ];
+        const size_t base = (size_t)row_s[i] * D + p * DQ;
+        // (row_s is 0 past n: a valid row, whose contents are discarded)
 #pragma unroll
-        for (int r = 0; r < kMaxQueryGroup; ++r) acc[r] = 0.f;
-        if (i < n) {
-            const int t = fp_token(a, len, te, i0 + i);
-            const uint8_t* row = kw + (size_t)window_row(t, a.sinks, a.win_rows) * D * IB;
-            for (int c0 = p * DQ; c0 < (p + 1) * DQ; c0 += 8) {
-                float x[8];
+        for (int j = 0; j < DQ; j += 8) {
+            float y[8];
+            load8<DT>(kw, base + j, y);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = load_in<DT>(row, c0 + j);
-#pragma unroll
-                for (int r = 0; r < kMaxQueryGroup; ++r) {
-                    if (r < R) {
-                        const float* qr = q_s + r * D + c0;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[r] = fmaf(qr[j], x[j], acc[r]);
-                    }
-                }
-            }
+            for (int u = 0; u < 8; ++u) x[j + u] = i < n ? y[u] : 0.f;
         }
+        // one query head per iteration, not unrolled: the code stays small
+        // (it runs once per workgroup, so its instruction fetches are cold)
+#pragma unroll 1
+        for (int r = 0; r < R; ++r) {
+            const float* qr = q_s + r * D + p * DQ;
+            float v = 0.f;
 #pragma unroll
-        for (int r = 0; r < kMaxQueryGroup; ++r) {
-            if (r < R) {
-                float v = acc[r];
-                v += __shfl_xor(v, 1);
-                v += __shfl_xor(v, 2);
-                if (p == 0 && i < kWinTokens) p_s[r * kWinTokens + i] = i < n ? v : -INFINITY;
-            }
+            for (int j = 0; j < DQ; ++j) v = fmaf(qr[j], x[j], v);
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            if (p == 0) p_s[r * kWinTokens + i] = i < n ? v : -INFINITY;
         }
     }
     __syncthreads();
@@ -532,64 +613,50 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
         }
     }
     __syncthreads();
-    // ---- values: thread = (token part tp, channel c); outputs of all heads in registers
-    const int TP = kThreads / D, tp = tid / D, c = tid % D;
-    float o[kMaxQueryGroup];
+    // ---- values: thread = (token part tp, channel c); its tokens' inputs are
+    // loaded up front and one query head at a time is applied. Threads past TP * D
+    // (when D does not divide kThreads) only join the barriers; rows past n may
+    // never have been written, so they are not read.
+    const int tp = tid / D, c = tid % D;
+    const bool active = tp < TP;
+    const int tpc = active ? tp : 0;  // clamped: every load is unconditional and in bounds
+    float v[TPT];
 #pragma unroll
-    for (int r = 0; r < kMaxQueryGroup; ++r) o[r] = 0.f;
-    for (int i = tp; i < n; i += TP) {
-        const int t = fp_token(a, len, te, i0 + i);
-        const float v = load_in<DT>(vw + (size_t)window_row(t, a.sinks, a.win_rows) * D * IB, c);
+    for (int k = 0; k < TPT; ++k) v[k] = load_in<DT>(vw, (size_t)row_s[tpc + k * TP] * D + c);
 #pragma unroll
-        for (int r = 0; r < kMaxQueryGroup; ++r)
-            if (r < R) o[r] = fmaf(p_s[r * kWinTokens + i], v, o[r]);
-    }
+    for (int k = 0; k < TPT; ++k) v[k] = active && tp + k * TP < n ? v[k] : 0.f;
     const int slot0 = nq + blockIdx.x;
-    for (int r = 0; r < R; ++r) {
-        red[tp * D + c] = o[r];
-        __syncthreads();
-        if (tid < D) {
-            float sum = 0.f;
-            for (int k = 0; k < TP; ++k) sum += red[k * D + tid];
-            const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + slot0;
-            a.ws_o[slot * D + tid] = sum * a.ws_scale;
-            if (tid == 0) {
-                a.ws_ml[slot * 2 + 0] = ml_s[2 * r];
-                a.ws_ml[slot * 2 + 1] = ml_s[2 * r + 1] * a.ws_scale;
+    const size_t slot_base = ((size_t)seq * a.q_heads + (size_t)kvh * RA + h0) * a.max_chunks + slot0;
+    if constexpr (TP > 1) {
+        if (active) {
+#pragma unroll 1
+            for (int r = 0; r < R; ++r) {
+                float o = 0.f;
+#pragma unroll
+                for (int k = 0; k < TPT; ++k) o = fmaf(p_s[r * kWinTokens + tp + k * TP], v[k], o);
+                red[(tp * R + r) * D + c] = o;
             }
         }
         __syncthreads();
-    }
-}
-
-// Copy the new rows of an append that the window keeps into the window area of
-// (seq, head): sink tokens t < sinks, and the later tokens t >= len1 - win_rows
-// (no two of them share a row). One element per thread, keys and values.
-template <int DT>
-__global__ __launch_bounds__(kThreads) void window_store_kernel(TensorArgs k0, TensorArgs v0) {
-    int z = blockIdx.z, zv = blockIdx.z;
-    const TensorArgs k = layer_args(k0, z, gridDim.z / k0.n_layers);
-    const TensorArgs v = layer_args(v0, zv, gridDim.z / v0.n_layers);
-    const int seq = z, head = blockIdx.y, D = k.head_dim;
-    const int len0 = k.len_in[seq];
-    const int n = k.n_new ? k.n_new[seq] : k.n_uniform;
-    const int row_start = k.row_start ? k.row_start[seq] : seq * k.n_uniform;
-    const int len1 = len0 + n;
-    const int keep_from = max(len1 - k.win_rows, 0);
-    constexpr int IB = In<DT>::bytes;
-    const SeqEntry& e = k.table[seq];
-    for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < n * D; idx += gridDim.x * kThreads) {
-        const int i = idx / D, ch = idx % D, t = len0 + i;
-        if (t >= k.sinks && t < keep_from) continue;
-        const size_t so = ((size_t)(row_start + i) * k.kv_heads + head) * D + ch;
-        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows) * D + ch;
+        for (int i = tid; i < R * D; i += kThreads) {
+            const int r = i / D, ch = i % D;
+            float sum = 0.f;
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            const TensorArgs& x = T == 0 ? k : v;
-            uint8_t* w = x.resid + e.resid[T] + (size_t)head * e.resid_hs[T] + x.win_off;
-            if constexpr (IB == 4) ((uint32_t*)w)[dof] = ((const uint32_t*)x.src)[so];
-            else ((uint16_t*)w)[dof] = ((const uint16_t*)x.src)[so];
+            for (int k = 0; k < TP; ++k) sum += red[(k * R + r) * D + ch];
+            a.ws_o[(slot_base + (size_t)r * a.max_chunks) * D + ch] = sum * a.ws_scale;
         }
+    } else if (active) {
+#pragma unroll 1
+        for (int r = 0; r < R; ++r) {
+            float o = 0.f;
+#pragma unroll
+            for (int k = 0; k < TPT; ++k) o = fmaf(p_s[r * kWinTokens + tp + k * TP], v[k], o);
+            a.ws_o[(slot_base + (size_t)r * a.max_chunks) * D + c] = o * a.ws_scale;
+        }
+    }
+    if (tid < R) {
+        a.ws_ml[(slot_base + (size_t)tid * a.max_chunks) * 2 + 0] = ml_s[2 * tid];
+        a.ws_ml[(slot_base + (size_t)tid * a.max_chunks) * 2 + 1] = ml_s[2 * tid + 1] * a.ws_scale;
     }
 }
 
@@ -671,15 +738,21 @@ size_t decode_lds_bytes(int R, int D, int C) {
     return sizeof(float) * ((size_t)R * D + C + 8 * 256 + 64 + 256 * 32);
 }
 
-hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, hipStream_t s) {
-    dim3 grid(gx_k + gx_v, k.kv_heads, k.num_seqs * k.n_layers);
+hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, int max_new, hipStream_t s) {
+    int gx_w = 0;  // window copy: enough workgroups for the rows kept, at most 64
+    if (k.win_mode) {
+        const long elems = (long)std::min(max_new, k.sinks + k.win_rows) * k.head_dim;
+        gx_w = (int)std::min<long>(std::max<long>(1, (elems + kThreads - 1) / kThreads), 64);
+    }
+    const int gx_kv = gx_k + gx_v;
+    dim3 grid(gx_kv + gx_w, k.kv_heads, k.num_seqs * k.n_layers);
     size_t lds = 0;
     for (const TensorArgs* t : {&k, &v})
         if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));
     switch (k.in_dtype) {
-        case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
-        case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
-        default: hipLaunchKernelGGL(quant_append_kernel<2>, grid, dim3(kThreads), lds, s, k, v, gx_k); break;
+        case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
+        case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
+        default: hipLaunchKernelGGL(quant_append_kernel<2>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
     }
     return hipGetLastError();
 }
@@ -692,40 +765,41 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int R = a.q_heads / a.kv_heads;
-    dim3 grid(a.max_chunks, a.kv_heads, a.num_seqs * a.n_layers);
+    dim3 grid(a.max_chunks - a.win_splits, a.kv_heads, a.num_seqs * a.n_layers);  // quantized splits only
     const size_t lds = decode_lds_bytes(R, a.head_dim, a.chunk);
     switch (a.in_dtype) {
         case 0: hipLaunchKernelGGL(decode_split_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
         case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
         default: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs * a.n_layers, (a.head_dim + 15) / 16), dim3(kThreads), 0, s,
-                       a);
-    return hipGetLastError();
+    return hipGetLastError();  // the caller launches the split merge
+}
+
+template <int DT>
+void window_d(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+    switch (a.head_dim) {
+        case 32: hipLaunchKernelGGL((decode_window_kernel<DT, 32>), grid, dim3(kThreads), lds, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_window_kernel<DT, 64>), grid, dim3(kThreads), lds, s, a); break;
+        case 96: hipLaunchKernelGGL((decode_window_kernel<DT, 96>), grid, dim3(kThreads), lds, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_window_kernel<DT, 128>), grid, dim3(kThreads), lds, s, a); break;
+        case 160: hipLaunchKernelGGL((decode_window_kernel<DT, 160>), grid, dim3(kThreads), lds, s, a); break;
+        case 192: hipLaunchKernelGGL((decode_window_kernel<DT, 192>), grid, dim3(kThreads), lds, s, a); break;
+        case 224: hipLaunchKernelGGL((decode_window_kernel<DT, 224>), grid, dim3(kThreads), lds, s, a); break;
+        default: hipLaunchKernelGGL((decode_window_kernel<DT, 256>), grid, dim3(kThreads), lds, s, a); break;
+    }
 }
 
 hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s) {
-    const int R = a.q_heads / a.kv_heads;
-    dim3 grid(a.win_splits, a.kv_heads, a.num_seqs * a.n_layers);
-    const size_t lds = sizeof(float) * ((size_t)R * a.head_dim + (size_t)R * kWinTokens + 2 * R + kThreads);
+    const int RA = a.q_heads / a.kv_heads, R = std::min(RA, kWinHeads);
+    dim3 grid(a.win_splits, a.kv_heads * ((RA + kWinHeads - 1) / kWinHeads), a.num_seqs * a.n_layers);
+    const int TP = kThreads / a.head_dim;
+    const size_t lds = sizeof(float) * ((size_t)R * a.head_dim + (size_t)R * kWinTokens + 2 * R +
+                                        (TP > 1 ? (size_t)TP * R * a.head_dim : 0)) +
+                       sizeof(int) * kWinTokens;
     switch (a.in_dtype) {
-        case 0: hipLaunchKernelGGL(decode_window_kernel<0>, grid, dim3(kThreads), lds, s, a); break;
-        case 1: hipLaunchKernelGGL(decode_window_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
-        default: hipLaunchKernelGGL(decode_window_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_window_store(const TensorArgs& k, const TensorArgs& v, int max_new, hipStream_t s) {
-    const long elems = (long)max_new * k.head_dim;
-    const int gx = (int)std::min<long>(std::max<long>(1, (elems + kThreads - 1) / kThreads), 1024);
-    dim3 grid(gx, k.kv_heads, k.num_seqs * k.n_layers);
-    switch (k.in_dtype) {
-        case 0: hipLaunchKernelGGL(window_store_kernel<0>, grid, dim3(kThreads), 0, s, k, v); break;
-        case 1: hipLaunchKernelGGL(window_store_kernel<1>, grid, dim3(kThreads), 0, s, k, v); break;
-        default: hipLaunchKernelGGL(window_store_kernel<2>, grid, dim3(kThreads), 0, s, k, v); break;
+        case 0: window_d<0>(a, grid, lds, s); break;
+        case 1: window_d<1>(a, grid, lds, s); break;
+        default: window_d<2>(a, grid, lds, s); break;
     }
     return hipGetLastError();
 }

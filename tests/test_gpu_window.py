@@ -43,6 +43,9 @@ CASES = {
                                      bits=((6, 4),) * 2, axis_k=o.AXIS_TOKEN), 50, 3),
     # generic split kernel: head_dim 32, fp32 input, 3-bit
     "d32": (W.tiny().scaled(head_dim=32, lengths=(395,), bits=((3, 3),)), 40, 32),
+    # head_dims that do not divide 256 (generic split kernel), fp32 input, query groups of 2
+    "d96": (W.tiny().scaled(head_dim=96, lengths=(300,), bits=((4, 4),)), 64, 32),
+    "d160": (W.tiny().scaled(head_dim=160, kv_heads=2, q_heads=4, lengths=(200,), bits=((3, 4),)), 40, 0),
     # key blocks of 256 tokens, window only
     "bigG": (W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=4, lengths=(1700, 256), group_k=256,
                                   group_v=128, bits=((4, 6), (8, 3))), 128, 0),
