@@ -16,7 +16,10 @@ far worse than a per-token one even when its reconstruction error is smaller
 [U] "Chaves: Os Valores Extremos Vivem em Canais Fixos"; the per-element bound
 of half a step: [U] "O Que o Erro de Quantizacao E Realmente Feito"). Group
 granularity (whole vector, per head, 64, 32 channels) is the other lever
-([H] "Asymetrie kvantizace KV cache", the granularity comparison).
+([H] "Asymetrie kvantizace KV cache", the granularity comparison), and so is a
+full-precision window of recent tokens plus attention-sink tokens ([U] "O
+Imposto dos Sistemas e Por Que Nao E um Detalhe", "O Que Fazer Com Isso"),
+which the library reads unquantized.
 
 Inputs: the Llama-2-7B-shaped recipe of bench.py (key channel magnitudes
 lognormal(0, 1), 1% of channels 20x; queries N(0,1)), 4 sequences of 2048
@@ -69,8 +72,10 @@ def top_mass(weights, frac=0.05):
     return float(np.mean(w[:, :n].sum(axis=1)))
 
 
-def run_config(w, device="cuda"):
-    """Quantize w's cache on the GPU, read it back and decode; return the error metrics."""
+def run_config(w, device="cuda", window=0, sinks=0):
+    """Quantize w's cache on the GPU, read it back and decode; return the error
+    metrics. With a window or sinks, the reconstruction read back is the one the
+    attention reads (those tokens unquantized)."""
     import torch
 
     from bit_kv_cache_groupwise_amd import kvq
@@ -78,7 +83,8 @@ def run_config(w, device="cuda"):
 
     S, H, D, T = w.num_seqs, w.kv_heads, w.head_dim, w.lengths[0]
     geom = kvq.geometry(layers=1, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D, group_k=w.group_k,
-                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype)
+                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype,
+                        window=window, sinks=sinks)
     cache = kvq.Cache(geom, list(w.lengths), [b[0] for b in w.bits], [b[1] for b in w.bits], device=device)
     k, v = W.draw_kv(w, 0, w.lengths, device=device, stream=0)
     cache.append(0, k, v, list(w.lengths))
@@ -116,7 +122,7 @@ def run_config(w, device="cuda"):
     cache.close()
     return {
         "axis_k": AXIS_NAME[w.axis_k], "axis_v": AXIS_NAME[w.axis_v], "group_k": w.group_k, "group_v": w.group_v,
-        "bits": list(w.bits[0]), "v_dist": w.v_dist,
+        "bits": list(w.bits[0]), "v_dist": w.v_dist, "window": window, "sinks": sinks,
         "k_recon_rel": math.sqrt(kd2 / kn2), "v_recon_rel": math.sqrt(vd2 / vn2),
         "logit_rms_over_std": float(np.mean(acc["logit_rms"])), "logit_max_abs": float(np.max(acc["logit_max"])),
         "out_rel_dequant": float(np.mean(acc["out_deq"])), "out_rel_dequant_max": float(np.max(acc["out_deq_max"])),
@@ -142,15 +148,23 @@ def configs(T=2048):
         for G in (64, 128):
             out.append(base.scaled(group_k=G, group_v=G, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
         out.append(base.scaled(group_k=256, group_v=128, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
-    return out
+    return [(x, 0, 0) for x in out] + window_configs(base)
+
+
+def window_configs(base):
+    """Full-precision recent window and sinks at 2 bits (keys per channel,
+    values per token, groups of 32): (workload, window, sinks)."""
+    w2 = base.scaled(group_k=32, group_v=32, bits=((2, 2),) * 4, v_dist="token_lognormal")
+    return [(w2, win, snk) for win, snk in ((32, 0), (128, 0), (512, 0), (128, 32), (0, 64))]
 
 
 def table(rows):
-    lines = ["| K axis | V axis | G (K, V) | bits | V recipe | K recon | V recon | logit rms/std | out (dequant) "
-             "| out (fused) | top-5% mass |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    lines = ["| K axis | V axis | G (K, V) | bits | window, sinks | V recipe | K recon | V recon | logit rms/std "
+             "| out (dequant) | out (fused) | top-5% mass |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         fused = f"{r['out_rel_fused']:.2e}" if r["out_rel_fused"] is not None else "—"
         lines.append(f"| {r['axis_k']} | {r['axis_v']} | {r['group_k']}, {r['group_v']} | {r['bits'][0]} | "
+                     f"{r['window']}, {r['sinks']} | "
                      f"{r['v_dist']} | {r['k_recon_rel']:.3e} | {r['v_recon_rel']:.3e} | "
                      f"{r['logit_rms_over_std']:.3e} | {r['out_rel_dequant']:.3e} | {fused} | "
                      f"{r['top5pct_attention_mass']:.2f} |")
@@ -162,8 +176,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=2048)
     args = ap.parse_args()
     rows = []
-    for w in configs(args.tokens):
-        r = run_config(w)
+    for w, window, sinks in configs(args.tokens):
+        r = run_config(w, window=window, sinks=sinks)
         rows.append(r)
         print(json.dumps(r), flush=True)
     print(table(rows), flush=True)

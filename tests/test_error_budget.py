@@ -35,8 +35,9 @@ def test_attention_closed_forms():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("axes", [(eb.CH, eb.TOK), (eb.TOK, eb.CH)])
-def test_gpu_metrics_match_the_oracle(axes):
+@pytest.mark.parametrize("axes,window,sinks", [((eb.CH, eb.TOK), 0, 0), ((eb.TOK, eb.CH), 0, 0),
+                                               ((eb.CH, eb.TOK), 64, 32)])
+def test_gpu_metrics_match_the_oracle(axes, window, sinks):
     import torch
 
     from bit_kv_cache_groupwise_amd import workloads as W
@@ -45,7 +46,7 @@ def test_gpu_metrics_match_the_oracle(axes):
     ak, av = axes
     w = W.llama2_7b().scaled(name="error-budget", num_seqs=2, kv_heads=2, q_heads=2, lengths=(256, 256),
                              bits=((2, 2),) * 2, axis_k=ak, axis_v=av, v_dist="token_lognormal")
-    r = eb.run_config(w)
+    r = eb.run_config(w, window=window, sinks=sinks)
     k, v = W.draw_kv(w, 0, w.lengths, device="cuda", stream=0)
     q = W.draw_q(w, 0, device="cuda").double().cpu().numpy()
     k = k.float().cpu().numpy()
@@ -55,7 +56,8 @@ def test_gpu_metrics_match_the_oracle(axes):
     outs = []
     for s in range(w.num_seqs):
         ks, vs = k[s * T:(s + 1) * T], v[s * T:(s + 1) * T]
-        encs = [H.encode(w, ks, vs, s, h) for h in range(w.kv_heads)]
+        encs = [H.encode_window(w, ks, vs, s, h, window, sinks) if window or sinks else H.encode(w, ks, vs, s, h)
+                for h in range(w.kv_heads)]
         kh = np.stack([e["k_hat"] for e in encs])
         vh = np.stack([e["v_hat"] for e in encs])
         kx = ks.astype(np.float64).transpose(1, 0, 2)

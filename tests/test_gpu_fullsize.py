@@ -46,13 +46,16 @@ def _samples(w):
     return [(l, s, h) for l in layers for s in seqs for h in heads]
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2-small", "llama2-7b", "long-gqa", "mixed"])
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,window,sinks", [
+    ("tiny", 0, 0), ("gpt2-small", 0, 0), ("llama2-7b", 0, 0), ("long-gqa", 0, 0), ("mixed", 0, 0),
+    # with a full-precision window of 128 recent tokens and 32 sinks (bench.py --window 128 --sinks 32)
+    ("llama2-7b", 128, 32), ("long-gqa", 128, 32)])
+def test_full_size_workload(name, window, sinks):
     w = W.get(name)
     R = w.q_heads // w.kv_heads
     _note(f"[fullsize] {name}: S={w.num_seqs} L={w.layers} Hq={w.q_heads} Hkv={w.kv_heads} D={w.head_dim} "
-          f"tokens={sum(w.lengths)} +{w.new_tokens}/seq")
-    cache = H.make_cache(w)
+          f"tokens={sum(w.lengths)} +{w.new_tokens}/seq window={window} sinks={sinks}")
+    cache = H.make_cache(w, window=window, sinks=sinks)
     outs = {}
     for layer in range(w.layers):
         prefix, new = H.history(w, layer, device="cuda")
@@ -77,6 +80,8 @@ def test_full_size_workload(name):
         for s, h in units:
             k, v = H.full_seq(prefix, new, s)
             enc = H.assert_head_bytes(cache, w, layer, s, h, k, v)
+            if window or sinks:
+                enc = H.encode_window(w, k, v, s, h, window, sinks)
             qs = q[s, h * R:(h + 1) * R].float().numpy().astype(np.float64)
             ref = o.attend_heads(qs, [enc["k_hat"]], [enc["v_hat"]], w.softmax_scale)
             err = H.row_rel_err(out[s, h * R:(h + 1) * R], ref)
