@@ -326,7 +326,9 @@ def main():
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
         "prefill_tokens": prefill_tokens,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name + (f"_window{args.window}_sinks{args.sinks}"
+                                                           if args.window or args.sinks else "")),
                      "kernel": ("kvq_decode_attention_layers" if multi else
                                 "kvq_decode_step (append + decode attention)" if fused_step else "kvq_decode_attention"),
                      "bytes_per_launch": int(np.mean(call_bytes)),
@@ -356,7 +358,8 @@ def kernel_source_hash(sources=None):
 
 def measured_traffic(workload):
     """HBM bytes per decode launch from the committed counter summary
-    (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE of the decode
+    (profiles/traffic_<workload>.json, <workload>_window<R>_sinks<S> with a
+    full-precision window: FETCH_SIZE and WRITE_SIZE of the decode
     kernel, each divided by the bytes-per-byte factor the same counter reads on
     a plain copy of known size), or None when absent or when any source file of
     the kernels it counted (listed in the summary) has changed since."""
