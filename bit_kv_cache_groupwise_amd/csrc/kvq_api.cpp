@@ -648,7 +648,6 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         a.win_splits = wsl;
     }
     if (a.win_mode) {
-        if (opt.fused) return fail(KVQ_ERR_UNSUPPORTED, "fused decode step with a window");
         if (!mha) {  // the full-precision rows' partials (the single-query kernel reads those rows itself)
             hipError_t e = kvq::launch_decode_window(a, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching the window attention");
@@ -730,7 +729,7 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
     // workgroup's worth of value rows per sequence.
     const int32_t* lens = &c->lens[(size_t)layer * S];
     bool fuse = !empty && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
-                kvq::mha_supported(g.head_dim) && !win_mode(g);
+                kvq::mha_supported(g.head_dim);
     for (int s = 0; fuse && s < S; ++s)
         fuse = (lens[s] + n_new[s]) / g.group_k == lens[s] / g.group_k && n_new[s] <= 256 / (g.head_dim / 32);
     for (const auto& pr : c->pairs) fuse = fuse && kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv);

@@ -413,20 +413,24 @@ __device__ __forceinline__ float unit_sum(float v) {
 }
 
 // Fused decode step: append the new rows of (seq, head), which only the
-// last split's residual loop reads: values quantized per row (one thread per
-// 32-channel unit, rows of whole groups), keys copied into the residual.
+// last split's residual loop (or full-precision loop) reads: values quantized
+// per row (one thread per 32-channel unit, rows of whole groups), keys copied
+// into the residual, and with a window both copied into the window area.
 __device__ __forceinline__ void fused_append(const DecodeArgs& a, int head, int seq, int len0, int n, int nthreads) {
     const int UPR = a.head_dim >> 5;
     const int r = (int)threadIdx.x / UPR, u = (int)threadIdx.x % UPR;
     if (a.in_dtype == 0) {
         if (r < n) token_axis_row<0>(a.app_v, r, u, head, seq, len0);
         residual_rows<0>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+        if (a.win_mode) window_rows<0>(a.app_k, a.app_v, seq, head, 0, 1, nthreads);
     } else if (a.in_dtype == 1) {
         if (r < n) token_axis_row<1>(a.app_v, r, u, head, seq, len0);
         residual_rows<1>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+        if (a.win_mode) window_rows<1>(a.app_k, a.app_v, seq, head, 0, 1, nthreads);
     } else {
         if (r < n) token_axis_row<2>(a.app_v, r, u, head, seq, len0);
         residual_rows<2>(a.app_k, head, seq, len0, len0, len0 + n, nthreads);
+        if (a.win_mode) window_rows<2>(a.app_k, a.app_v, seq, head, 0, 1, nthreads);
     }
 }
 
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     }
 
     // ---- residual keys (input dtype), fewer than G tokens, one wave
-    if (appended) __syncthreads();  // the step's new rows are in place
+    if (appended) __syncthreads();  // the step's new rows are in place (residual and window rows)
     if (wave == 0) {
         for (int st = max(wa, nqk); st < wb; st += 64) {
             uint32_t vw[UPR][BV], vmw[UPR];

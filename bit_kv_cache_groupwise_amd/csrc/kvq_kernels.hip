@@ -153,39 +153,6 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     }
 }
 
-// Copy the new rows of an append that the window keeps into the window area of
-// (seq, head): sink tokens t < sinks, and the later tokens t >= len1 - win_rows
-// (no two of them share a row). One element per thread, keys and values;
-// workgroup `item` of `nitems` takes every nitems-th block of elements.
-template <int DT>
-__device__ __forceinline__ void window_store_part(const TensorArgs& k, const TensorArgs& v, int seq, int head,
-                                                  int item, int nitems) {
-    const int D = k.head_dim;
-    const int len0 = k.len_in[seq];
-    const int n = k.n_new ? k.n_new[seq] : k.n_uniform;
-    const int row_start = k.row_start ? k.row_start[seq] : seq * k.n_uniform;
-    const int len1 = len0 + n;
-    // kept rows: sinks [len0, min(len1, sinks)), then [max(len0, sinks, len1 - win_rows), len1)
-    const int n1 = max(0, min(len1, k.sinks) - len0);
-    const int s2 = max(max(len0, k.sinks), len1 - k.win_rows);
-    const int n2 = max(0, len1 - s2);
-    constexpr int IB = In<DT>::bytes;
-    const SeqEntry& e = k.table[seq];
-    for (int idx = item * kThreads + threadIdx.x; idx < (n1 + n2) * D; idx += nitems * kThreads) {
-        const int j = idx / D, ch = idx % D;
-        const int t = j < n1 ? len0 + j : s2 + (j - n1), i = t - len0;
-        const size_t so = ((size_t)(row_start + i) * k.kv_heads + head) * D + ch;
-        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows) * D + ch;
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            const TensorArgs& x = T == 0 ? k : v;
-            uint8_t* w = x.resid + e.resid[T] + (size_t)head * e.resid_hs[T] + x.win_off;
-            if constexpr (IB == 4) ((uint32_t*)w)[dof] = ((const uint32_t*)x.src)[so];
-            else ((uint16_t*)w)[dof] = ((const uint16_t*)x.src)[so];
-        }
-    }
-}
-
 // One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
 // keys, [gx_k, gx_kv) the values, each with its own axis, and with a
 // full-precision window [gx_kv, gridDim.x) copy the rows the window keeps.
@@ -199,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, T
     const int seq = z, head = blockIdx.y;
     uint32_t* smem = quant_smem;
     if ((int)blockIdx.x >= gx_kv) {
-        window_store_part<DT>(k, v, seq, head, (int)blockIdx.x - gx_kv, (int)gridDim.x - gx_kv);
+        window_rows<DT>(k, v, seq, head, (int)blockIdx.x - gx_kv, (int)gridDim.x - gx_kv, kThreads);
     } else if ((int)blockIdx.x < gx_k) {
         if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
         else channel_axis_part<DT>(k, blockIdx.x, head, seq, smem);

@@ -208,9 +208,9 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const voi
  * token) and the step completes no key block and adds at most
  * 256 / (head_dim / 32) rows per sequence, both run in one launch: each
  * (sequence, kv head) workgroup that attends the newest tokens first appends
- * them (for bit pairs where the fused kernel keeps the plain one's
- * occupancy, and without a window or sinks). Otherwise the two run as
- * consecutive launches. */
+ * them, and with a window or sinks also copies them into the window area
+ * (for bit pairs where the fused kernel keeps the plain one's occupancy).
+ * Otherwise the two run as consecutive launches. */
 kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                            const int32_t* n_new, const void* q, float softmax_scale, float* out, void* workspace,
                            size_t workspace_bytes, void* stream);

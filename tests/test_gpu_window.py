@@ -123,10 +123,12 @@ def test_window_covering_the_cache_is_exact_attention():
 
 @pytest.mark.parametrize("name", ["llama", "gqa", "ktoken"])
 def test_window_decode_step_and_layers(name):
-    """kvq_decode_step with a window (append then decode: the window disables the
-    fused launch) equals the two calls; 40 steps cross key-block edges and the
-    recent ring's wrap; kvq_decode_attention_layers over two layers equals
-    the per-layer calls; the last step meets the oracle."""
+    """kvq_decode_step with a window (one fused launch for one query per kv head
+    on the steps that complete no key block, where the workgroup that attends
+    the window first copies the new rows into it) equals the two calls bit for
+    bit; 40 steps cross key-block edges and the recent ring's wrap;
+    kvq_decode_attention_layers over two layers equals the per-layer calls; the
+    last step meets the oracle."""
     w, window, sinks = CASES[name]
     w = w.scaled(layers=2, lengths=tuple(min(L, 500) for L in w.lengths), new_tokens=1)
     _note(f"[window step] case={name} R={window} S={sinks}")
