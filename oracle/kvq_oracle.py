@@ -385,3 +385,43 @@ def encode_head_window(k, v, *, window: int, sinks: int, group_k: int, group_v: 
     enc["v_hat"] = apply_window(v, enc["v_hat_q"], mask)
     enc["fp_mask"] = mask
     return enc
+
+
+# ----------------------------------------------------------------------------
+# Pre-rotation keys ([U] "Embebedos Rotatorios Complicam as Chaves": rotary
+# position embeddings turn pairs of channels by an angle that grows with the
+# token's position, which spreads a fixed outlier channel into its partner;
+# KVQuant's answer is to quantize the keys before the rotation and to rotate
+# after dequantization).
+#
+# Reading P1 (the pages name the rotation, not its formula): the standard
+# rotary embedding with frequencies theta_i = base^(-2i/D), i < D/2, rotating
+# the channel pair (i, i + D/2) of a key at position t by the angle t*theta_i;
+# positions are the token indices 0, 1, 2, ... of the cache. The query is given
+# already rotated at its own position, so a score is q . rope(k_hat_t, t).
+# ----------------------------------------------------------------------------
+
+def rope_frequencies(head_dim: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/D) for i < D/2, float64 (reading P1)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / head_dim)
+
+
+def rope(x, positions, base: float) -> np.ndarray:
+    """Rotate rows x[t] (float64 [T][D]) by positions[t]: channel pair
+    (i, i + D/2) becomes (a cos - b sin, a sin + b cos) at angle
+    positions[t] * theta_i (reading P1)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[1]
+    h = D // 2
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_frequencies(D, base)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[:, :h], x[:, h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=1)
+
+
+def attend_rope(q, khat, vhat, scale: float, base: float) -> np.ndarray:
+    """Attention over pre-rotation keys: the reconstructed key of token t is
+    rotated to position t after dequantization, then scored against q."""
+    khat = np.asarray(khat, dtype=np.float64)
+    return attend(q, rope(khat, np.arange(khat.shape[0]), base), vhat, scale)

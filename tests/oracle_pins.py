@@ -491,10 +491,59 @@ def check_window_exact_attention(o, seed=11):
     assert not np.allclose(o.attend(q, enc["k_hat"], enc["v_hat"], 0.125), ref, atol=1e-3)
 
 
+# ----------------------------------------------------------------------------
+# Rotary positions after dequantization ([U] "Embebedos Rotatorios Complicam
+# as Chaves")
+# ----------------------------------------------------------------------------
+
+def check_rope_complex_form(o, seed=12):
+    """The rotation equals complex multiplication: channel pair (i, i + D/2) as
+    a + jb times e^(j t theta_i); frequencies from the golden values (base
+    10000, D = 8: 1, 0.1, 0.01, 0.001); position 0 is the identity; norms and
+    relative positions are preserved."""
+    g = _read_kv(os.path.join(GOLDEN, "rope_frequencies.txt"))
+    th = o.rope_frequencies(int(g["head_dim"][0]), float(g["base"][0]))
+    np.testing.assert_allclose(th, [float(v) for v in g["theta"]], rtol=1e-15)
+    rng = np.random.default_rng(seed)
+    D, T = 64, 50
+    x = rng.standard_normal((T, D))
+    pos = rng.integers(0, 300000, T)
+    got = o.rope(x, pos, 10000.0)
+    z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * np.exp(1j * np.outer(pos, o.rope_frequencies(D, 10000.0)))
+    np.testing.assert_allclose(got, np.concatenate([z.real, z.imag], axis=1), rtol=1e-9, atol=1e-9)
+    np.testing.assert_array_equal(o.rope(x, np.zeros(T, int), 10000.0), x)
+    np.testing.assert_allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    q, k = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    d0 = float((o.rope(q, [17], 500.0) @ o.rope(k, [5], 500.0).T)[0, 0])
+    d1 = float((o.rope(q, [1017], 500.0) @ o.rope(k, [1005], 500.0).T)[0, 0])
+    assert abs(d0 - d1) < 1e-9 * max(1.0, abs(d0))
+
+
+def check_rope_attention(o, seed=13):
+    """attend_rope scores q against the key rotated to its own position: a single
+    key rotated by hand (2 x 2 rotations), and position-0 rotation being the plain
+    attention."""
+    rng = np.random.default_rng(seed)
+    D = 4
+    k = np.array([[1.0, 2.0, 3.0, 4.0], [0.5, -1.0, 0.0, 2.0]])
+    v = rng.standard_normal((2, D))
+    q = rng.standard_normal((1, D))
+    th = [1.0, 0.01]  # base 10000, D = 4
+    k1 = k[1]
+    k1r = np.array([k1[0] * math.cos(th[0]) - k1[2] * math.sin(th[0]), k1[1] * math.cos(th[1]) - k1[3] * math.sin(th[1]),
+                    k1[0] * math.sin(th[0]) + k1[2] * math.cos(th[0]), k1[1] * math.sin(th[1]) + k1[3] * math.cos(th[1])])
+    lg = np.array([q[0] @ k[0], q[0] @ k1r]) * 0.5
+    w = np.exp(lg - lg.max())
+    w /= w.sum()
+    np.testing.assert_allclose(o.attend_rope(q, k, v, 0.5, 10000.0)[0], w @ v, rtol=1e-12)
+    np.testing.assert_allclose(o.attend_rope(q, k[:1], v[:1], 0.5, 10000.0), o.attend(q, k[:1], v[:1], 0.5))
+
+
 ALL_CHECKS = [
     check_worked_example, check_brute_force_nearest, check_half_step_bound, check_min_max_codes,
     check_monotone, check_exact_reconstruction, check_b8_bound, check_constant_group,
     check_meta_rounding, check_axis_semantics, check_dequant_exact, check_pack_golden,
     check_pack_bigint, check_meta_words, check_attention_closed_forms, check_attention_vs_torch,
     check_sizes, check_sizing_pages, check_window_blocks, check_window_exact_attention,
+    check_rope_complex_form, check_rope_attention,
 ]

@@ -170,10 +170,34 @@ def m_window_exact_tokens(o):
     o.full_precision_mask = fpm
 
 
+def m_rope_sign(o):
+    orig = o.rope
+    o.rope = lambda x, positions, base: orig(x, -np.asarray(positions), base)
+
+
+def m_rope_interleaved(o):
+    def rope(x, positions, base):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[1]
+        ang = np.asarray(positions, dtype=np.float64)[:, None] * o.rope_frequencies(D, base)[None, :]
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[:, 0::2], x[:, 1::2]  # pairs (2i, 2i+1) instead of (i, i + D/2)
+        out = np.empty_like(x)
+        out[:, 0::2] = a * c - b * s
+        out[:, 1::2] = a * s + b * c
+        return out
+    o.rope = rope
+
+
+def m_rope_freq_exponent(o):
+    o.rope_frequencies = lambda head_dim, base: np.power(float(base), -np.arange(head_dim // 2) / head_dim)
+
+
 MUTANTS = [m_levels_pow2, m_round_half_up, m_clamp_off_by_one, m_zero_is_max, m_unrounded_grid,
            m_meta_truncate, m_axis_swapped, m_pack_msb_first, m_dequant_midrise, m_softmax_no_scale,
            m_gqa_modulo, m_weights_unnormalised, m_residual_dropped, m_meta_bytes_halved,
-           m_window_rounds_up, m_window_no_sinks, m_window_keys_only, m_window_exact_tokens]
+           m_window_rounds_up, m_window_no_sinks, m_window_keys_only, m_window_exact_tokens,
+           m_rope_sign, m_rope_interleaved, m_rope_freq_exponent]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
