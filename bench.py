@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="recent tokens kept in full precision (the decode reads them unquantized)")
     ap.add_argument("--sinks", type=int, default=0, help="first tokens kept in full precision")
+    ap.add_argument("--rope-base", type=float, default=0.0,
+                    help="keys cached before the rotary embedding with this base, rotated inside the decode (0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
@@ -128,7 +130,7 @@ def main():
     cap = [L + n_new * appends_per_layer for L in w.lengths]
     geom = kvq.geometry(layers=layers, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D, group_k=w.group_k,
                         group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype,
-                        window=args.window, sinks=args.sinks)
+                        window=args.window, sinks=args.sinks, rope_base=args.rope_base)
     cache = kvq.Cache(geom, cap, [b[0] for b in w.bits], [b[1] for b in w.bits], device=dev)
 
     # ---- bulk prefill = quantize-append into an empty cache (timed: quantize GB/s)
@@ -315,7 +317,7 @@ def main():
                    "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
                    "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu",
                    **({"full_precision_window": args.window, "sinks": args.sinks} if args.window or args.sinks
-                      else {})},
+                      else {}), **({"rope_base": args.rope_base} if args.rope_base else {})},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_attention_GBps": round(dec_gbps, 2),
@@ -328,7 +330,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name + (f"_window{args.window}_sinks{args.sinks}"
-                                                           if args.window or args.sinks else "")),
+                                                           if args.window or args.sinks else "")
+                                                 + (f"_rope{args.rope_base:g}" if args.rope_base else "")),
                      "kernel": ("kvq_decode_attention_layers" if multi else
                                 "kvq_decode_step (append + decode attention)" if fused_step else "kvq_decode_attention"),
                      "bytes_per_launch": int(np.mean(call_bytes)),

@@ -115,6 +115,8 @@ kvq_status check_geometry(const kvq_geometry* g) {
         return fail(KVQ_ERR_UNSUPPORTED, "only fp16 step/zero metadata is stored by this build");
     if (g->meta_dtype != KVQ_F16) return fail(KVQ_ERR_ARG, "meta_dtype (%d) is not a kvq dtype", g->meta_dtype);
     if (g->window < 0 || g->sinks < 0) return fail(KVQ_ERR_ARG, "window (%d) and sinks (%d) must be >= 0", g->window, g->sinks);
+    if (!(g->rope_base >= 0.0) || g->rope_base > 1e30) return fail(KVQ_ERR_ARG, "rope_base must be finite and >= 0");
+    if (g->rope_base > 0.0 && g->rope_base <= 1.0) return fail(KVQ_ERR_ARG, "rope_base must be > 1 (or 0: off)");
     if (win_mode(*g)) {
         const int b = token_block(*g);
         if (g->sinks % b) return fail(KVQ_ERR_ARG, "sinks (%d) must be a multiple of the key block (%d tokens)", g->sinks, b);
@@ -574,6 +576,9 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     if (group_size(c) > kvq::kMaxQueryGroup)
         return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d", group_size(c), kvq::kMaxQueryGroup);
     if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
+    const bool rope = g.rope_base > 0.0;
+    if (rope && (g.axis_k != KVQ_AXIS_CHANNEL || win_mode(g)))
+        return fail(KVQ_ERR_UNSUPPORTED, "rotary keys need channel-axis keys and no window or sinks in this build");
     if (!(softmax_scale == softmax_scale)) return fail(KVQ_ERR_ARG, "softmax_scale is NaN");
     if (!aligned(q, in_bytes(g.in_dtype)) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "q or out misaligned");
     const int S = g.num_seqs;
@@ -585,8 +590,9 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         lens = step_lens.data();
     }
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
-    const bool mha = group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
-    bool gqa = group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
+    // rotary keys: the generic split kernel
+    const bool mha = !rope && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
+    bool gqa = !rope && group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
                kvq::mha_supported(g.head_dim);
     for (const auto& pr : c->pairs)  // a lane's key channels must start on a word boundary
         gqa = gqa && (g.head_dim * pr.bk) % 128 == 0;
@@ -636,6 +642,7 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     a.log2_group_k = __builtin_ctz((unsigned)g.group_k);
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
     a.split_floor = mha ? 1 : 0;
+    a.rope_base = g.rope_base;
     if (win_mode(g)) {
         a.win_mode = 1;
         a.window = g.window;
@@ -729,7 +736,7 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
     // workgroup's worth of value rows per sequence.
     const int32_t* lens = &c->lens[(size_t)layer * S];
     bool fuse = !empty && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
-                kvq::mha_supported(g.head_dim);
+                kvq::mha_supported(g.head_dim) && !(g.rope_base > 0.0);
     for (int s = 0; fuse && s < S; ++s)
         fuse = (lens[s] + n_new[s]) / g.group_k == lens[s] / g.group_k && n_new[s] <= 256 / (g.head_dim / 32);
     for (const auto& pr : c->pairs) fuse = fuse && kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv);

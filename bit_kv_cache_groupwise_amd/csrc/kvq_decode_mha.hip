@@ -668,29 +668,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
             uint32_t vw[UPR][BV], vmw[UPR];
             float sc[UPR];
             bool valid[UPR];
+            // loads are unconditional, from the clamped token (a load under a
+            // branch waits on its own), so they can be issued ahead of the sums
 #pragma unroll
             for (int s = 0; s < UPR; ++s) {
                 const int t = st + s * TPW + ts;
                 valid[s] = t < wb;
+                const int tc = valid[s] ? t : wb - 1;
+                load_words<BV>((const uint32_t*)(vc + (size_t)tc * (D * BV / 8)) + cg * BV, vw[s]);
+                vmw[s] = vm[(size_t)tc * vgpr + vg];
+                const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 32 * cg;
+                float x[32];
+                if (a.in_dtype == 0) load32<0>(kr, base, x);
+                else if (a.in_dtype == 1) load32<1>(kr, base, x);
+                else load32<2>(kr, base, x);
                 float part = 0.f;
-                if (valid[s]) {
-                    load_words<BV>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + cg * BV, vw[s]);
-                    vmw[s] = vm[(size_t)t * vgpr + vg];
-                    const size_t base = (size_t)(t & ((1 << lgk) - 1)) * D + 32 * cg;
-                    float x[32];
-                    if (a.in_dtype == 0) {
 #pragma unroll
-                        for (int j = 0; j < 32; ++j) x[j] = load_in<0>(kr, base + j);
-                    } else if (a.in_dtype == 1) {
-#pragma unroll
-                        for (int j = 0; j < 32; ++j) x[j] = load_in<1>(kr, base + j);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 32; ++j) x[j] = load_in<2>(kr, base + j);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
-                }
+                for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
                 part = group_sum<UPR>(part);
                 sc[s] = valid[s] ? part : -INFINITY;
             }
@@ -743,11 +737,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
             const float m24 = m - 24.0f;
 #pragma unroll
             for (int s = 0; s < UPR; ++s) {
+                float v[32];
+                row32(vwn, (size_t)rows[s] * D + 32 * cg, v);  // unconditional: invalid rows are not used
                 if (valid[s]) {
                     const float p = __builtin_amdgcn_exp2f(sc[s] - m24);
                     lsum += p;
-                    float v[32];
-                    row32(vwn, (size_t)rows[s] * D + 32 * cg, v);
 #pragma unroll
                     for (int j = 0; j < 32; ++j)
                         acc[j] = fmaf(p * ((float)(1 << code_shift<BV>(j)) * (1.0f / 16777216.0f)), v[j], acc[j]);

@@ -112,6 +112,9 @@ struct DecodeArgs {
     uint32_t win_off[2];        // byte offset of the window area inside a head's residual region [K, V]
     float ws_scale;             // factor the quantized kernel's partial l and o carry (2^24: single query)
     int32_t win_splits;         // grid x of decode_window_kernel (full-precision splits at most)
+    // Keys cached before the rotary embedding (rope_base > 0; generic split
+    // kernel): the reconstructed key of token t is rotated to position t.
+    double rope_base;
 };
 
 struct DequantArgs {

@@ -239,6 +239,51 @@ __device__ __forceinline__ void value_pass(const uint8_t* vc, const uint32_t* vm
     }
 }
 
+// Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
+// Complicam as Chaves"): cos and sin of the angle t * theta, reduced modulo
+// 2 pi in float64 (t * theta reaches 1e5-1e8 radians at long context, where a
+// float32 product would be off by 1e-2 rad), then evaluated in float32.
+__device__ __forceinline__ void rope_cs(int t, double theta, float& c, float& s) {
+    const double ang = (double)t * theta;
+    const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    sincosf((float)r, &s, &c);
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t code_of(const uint32_t* row, int ch) {
+    const uint32_t* unit = row + (ch >> 5) * B;
+    const int pos = (ch & 31) * B, wi = pos >> 5, sh = pos & 31;
+    uint32_t v = unit[wi] >> sh;
+    if (sh + B > 32) v |= unit[wi + 1] << (32 - sh);
+    return v & ((1u << B) - 1u);
+}
+
+// Score of token t: the key reconstructed per channel (fma(code, s, z), block
+// metadata bm[D]) or read from the residual row `rrow` (input dtype), rotated to
+// position t pair by pair (i, i + D/2), dotted with the query q.
+template <int DT, int BK>
+__device__ float rope_score(const uint32_t* row, const uint32_t* bm, const uint8_t* rrow, const float* q,
+                            const double* th, int D, int t) {
+    const int h = D >> 1;
+    float acc = 0.f;
+    for (int i = 0; i < h; ++i) {
+        float xa, xb;
+        if (row) {
+            const uint32_t ma = bm[i], mb = bm[i + h];
+            xa = fmaf((float)code_of<BK>(row, i), f16_to_f32(ma), f16_to_f32(ma >> 16));
+            xb = fmaf((float)code_of<BK>(row, i + h), f16_to_f32(mb), f16_to_f32(mb >> 16));
+        } else {
+            xa = load_in<DT>(rrow, i);
+            xb = load_in<DT>(rrow, i + h);
+        }
+        float c, s;
+        rope_cs(t, th[i], c, s);
+        acc = fmaf(q[i], xa * c - xb * s, acc);
+        acc = fmaf(q[i + h], xa * s + xb * c, acc);
+    }
+    return acc;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     extern __shared__ float smem[];
@@ -266,6 +311,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     float* qk = sc + C;
     float* small = qk + 8 * 256;  // [0,8) bias, [8,16) qsum, [16,20) reduction scratch
     float* red = small + 64;
+    double* th = (double*)(red + 256 * 32);  // rotary frequencies [D/2] (rope_base > 0)
+    const bool rope = a.rope_base > 0.0;
 
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
     const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
@@ -277,13 +324,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
         const int r = i / D, ch = i % D;
         q_s[i] = load_in<DT>(a.q, ((size_t)seq * a.q_heads + kvh * R + r) * D + ch) * a.qscale;
     }
+    if (rope)
+        for (int i = tid; i < D / 2; i += kThreads) th[i] = pow(a.rope_base, -2.0 * i / D);
     __syncthreads();
 
     for (int r = 0; r < R; ++r) {
         const float* qr = q_s + r * D;
         const int hq = kvh * R + r;
         // ---- keys -------------------------------------------------------
-        if (kch) {
+        if (kch && rope) {
+            // one thread per token: reconstruct, rotate to the token's position, score
+            for (int t = t0 + tid; t < t1; t += kThreads) {
+                const bool quant = t < nqk;
+                const uint32_t* row = quant ? (const uint32_t*)(kc + (size_t)t * (D * BK / 8)) : nullptr;
+                const uint32_t* bm = km + (size_t)(t / Gk) * D;
+                const uint8_t* rrow = kr + (size_t)(t % Gk) * D * IB;
+                float acc;
+                switch (BK) {
+                    case 2: acc = rope_score<DT, 2>(row, bm, rrow, qr, th, D, t); break;
+                    case 3: acc = rope_score<DT, 3>(row, bm, rrow, qr, th, D, t); break;
+                    case 4: acc = rope_score<DT, 4>(row, bm, rrow, qr, th, D, t); break;
+                    case 6: acc = rope_score<DT, 6>(row, bm, rrow, qr, th, D, t); break;
+                    default: acc = rope_score<DT, 8>(row, bm, rrow, qr, th, D, t); break;
+                }
+                sc[t - t0] = acc;
+            }
+        } else if (kch) {
             const int kend = min(t1, nqk);
             for (int tile0 = t0; tile0 < kend; tile0 += kThreads) {
                 const int tile_end = min(tile0 + kThreads, kend);
@@ -702,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
 // ---------------------------------------------------------------------------
 
 size_t decode_lds_bytes(int R, int D, int C) {
-    return sizeof(float) * ((size_t)R * D + C + 8 * 256 + 64 + 256 * 32);
+    return sizeof(float) * ((size_t)R * D + C + 8 * 256 + 64 + 256 * 32) + sizeof(double) * kMaxHeadDim / 2;
 }
 
 hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_k, int gx_v, int max_new, hipStream_t s) {

@@ -40,7 +40,7 @@ EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_a
 class kvq_geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "layers", "num_seqs", "kv_heads", "q_heads", "head_dim", "group_k", "group_v",
-        "axis_k", "axis_v", "in_dtype", "meta_dtype", "window", "sinks")]
+        "axis_k", "axis_v", "in_dtype", "meta_dtype", "window", "sinks")] + [("rope_base", ctypes.c_double)]
 
 
 class kvq_sizes(ctypes.Structure):
@@ -125,9 +125,9 @@ def _stream(stream):
 
 def geometry(*, layers, num_seqs, kv_heads, q_heads, head_dim, group_k, group_v,
              axis_k=KVQ_AXIS_CHANNEL, axis_v=KVQ_AXIS_TOKEN, in_dtype="f16", meta_dtype=KVQ_F16,
-             window=0, sinks=0):
+             window=0, sinks=0, rope_base=0.0):
     return kvq_geometry(layers, num_seqs, kv_heads, q_heads, head_dim, group_k, group_v, axis_k, axis_v,
-                        DTYPE_CODE.get(in_dtype, in_dtype), meta_dtype, window, sinks)
+                        DTYPE_CODE.get(in_dtype, in_dtype), meta_dtype, window, sinks, float(rope_base))
 
 
 # ---------------------------------------------------------------------------

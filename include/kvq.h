@@ -125,6 +125,17 @@ typedef struct kvq_geometry {
      * sinks a multiple of the key block, sinks + window + block <= 4096. */
     int32_t window;     /* R: recent tokens kept in full precision (0: none)    */
     int32_t sinks;      /* S: first tokens kept in full precision (0: none)     */
+    /* Keys cached before the rotary position embedding ([U] "Embebedos
+     * Rotatorios Complicam as Chaves": rotation spreads a fixed outlier
+     * channel into its partner, so the keys are quantized before it and
+     * rotated after dequantization). 0: off. Otherwise the appended keys are
+     * taken as un-rotated, and the decode attention rotates the reconstructed
+     * key of token t to position t: channel pair (i, i + head_dim/2) turns by
+     * t * rope_base^(-2i/head_dim); q must be given rotated to its own
+     * position. kvq_dequantize returns the un-rotated keys. This build:
+     * channel-axis keys, no window or sinks (else KVQ_ERR_UNSUPPORTED at
+     * decode), computed by the generic split kernel. */
+    double rope_base;
 } kvq_geometry;
 
 /* Byte counts. The pool sizes include 256-byte alignment of every head

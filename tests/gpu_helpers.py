@@ -18,17 +18,18 @@ def kvq():
     return k
 
 
-def geom_of(w: W.Workload, layers=None, window=0, sinks=0):
+def geom_of(w: W.Workload, layers=None, window=0, sinks=0, rope_base=0.0):
     k = kvq()
     return k.geometry(layers=layers or w.layers, num_seqs=w.num_seqs, kv_heads=w.kv_heads, q_heads=w.q_heads,
                       head_dim=w.head_dim, group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v,
-                      in_dtype=w.in_dtype, window=window, sinks=sinks)
+                      in_dtype=w.in_dtype, window=window, sinks=sinks, rope_base=rope_base)
 
 
-def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0):
+def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0, rope_base=0.0):
     k = kvq()
     cap = capacity or [L + w.new_tokens + extra for L in w.lengths]
-    return k.Cache(geom_of(w, layers, window, sinks), cap, [b[0] for b in w.bits], [b[1] for b in w.bits])
+    return k.Cache(geom_of(w, layers, window, sinks, rope_base), cap, [b[0] for b in w.bits],
+                   [b[1] for b in w.bits])
 
 
 def history(w: W.Workload, layer: int, device="cpu"):

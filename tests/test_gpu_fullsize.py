@@ -46,16 +46,19 @@ def _samples(w):
     return [(l, s, h) for l in layers for s in seqs for h in heads]
 
 
-@pytest.mark.parametrize("name,window,sinks", [
-    ("tiny", 0, 0), ("gpt2-small", 0, 0), ("llama2-7b", 0, 0), ("long-gqa", 0, 0), ("mixed", 0, 0),
+@pytest.mark.parametrize("name,window,sinks,rope", [
+    ("tiny", 0, 0, 0.0), ("gpt2-small", 0, 0, 0.0), ("llama2-7b", 0, 0, 0.0), ("long-gqa", 0, 0, 0.0),
+    ("mixed", 0, 0, 0.0),
     # with a full-precision window of 128 recent tokens and 32 sinks (bench.py --window 128 --sinks 32)
-    ("llama2-7b", 128, 32), ("long-gqa", 128, 32)])
-def test_full_size_workload(name, window, sinks):
+    ("llama2-7b", 128, 32, 0.0), ("long-gqa", 128, 32, 0.0),
+    # keys before the rotary embedding, rotated in the kernel (bench.py --rope-base 10000): positions to 262k
+    ("long-gqa", 0, 0, 10000.0)])
+def test_full_size_workload(name, window, sinks, rope):
     w = W.get(name)
     R = w.q_heads // w.kv_heads
     _note(f"[fullsize] {name}: S={w.num_seqs} L={w.layers} Hq={w.q_heads} Hkv={w.kv_heads} D={w.head_dim} "
-          f"tokens={sum(w.lengths)} +{w.new_tokens}/seq window={window} sinks={sinks}")
-    cache = H.make_cache(w, window=window, sinks=sinks)
+          f"tokens={sum(w.lengths)} +{w.new_tokens}/seq window={window} sinks={sinks} rope={rope}")
+    cache = H.make_cache(w, window=window, sinks=sinks, rope_base=rope)
     outs = {}
     for layer in range(w.layers):
         prefix, new = H.history(w, layer, device="cuda")
@@ -83,7 +86,10 @@ def test_full_size_workload(name, window, sinks):
             if window or sinks:
                 enc = H.encode_window(w, k, v, s, h, window, sinks)
             qs = q[s, h * R:(h + 1) * R].float().numpy().astype(np.float64)
-            ref = o.attend_heads(qs, [enc["k_hat"]], [enc["v_hat"]], w.softmax_scale)
+            if rope:
+                ref = o.attend_rope(qs, enc["k_hat"], enc["v_hat"], w.softmax_scale, rope)
+            else:
+                ref = o.attend_heads(qs, [enc["k_hat"]], [enc["v_hat"]], w.softmax_scale)
             err = H.row_rel_err(out[s, h * R:(h + 1) * R], ref)
             worst = max(worst, float(err.max()))
             assert np.all(err <= H.ATTN_TOL), (name, layer, s, h, float(err.max()))
