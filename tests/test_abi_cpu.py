@@ -96,6 +96,29 @@ def test_plan_rejects_bad_window(window, sinks):
     assert kvq.kvq_last_error()
 
 
+@pytest.mark.parametrize("base,status", [(0.0, 0), (10000.0, 0), (500000.0, 0), (1.0, -1), (0.5, -1), (-2.0, -1),
+                                         (float("nan"), -1), (float("inf"), -1)])
+def test_plan_rope_base(base, status):
+    """The rotary base (a double after the int32 fields) reaches the library: a base
+    in (0, 1], a negative one or a non-finite one is rejected; sizes do not depend
+    on it."""
+    assert kvq.kvq_plan_status(_geom(rope_base=base), [10] * 3, [2] * 3, [2] * 3) == status
+    if status == 0:
+        assert kvq.kvq_plan(_geom(rope_base=base), [100] * 3, [2] * 3, [2] * 3).codes_bytes == \
+            kvq.kvq_plan(_geom(), [100] * 3, [2] * 3, [2] * 3).codes_bytes
+
+
+def test_geometry_struct_layout():
+    """The binding's geometry has the header's fields in the header's order."""
+    import ctypes
+    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    body = hdr[hdr.index("typedef struct kvq_geometry {"):hdr.index("} kvq_geometry;")]
+    import re
+    names = re.findall(r"^\s*(?:int32_t|double)\s+(\w+);", body, flags=re.M)
+    assert [f[0] for f in kvq.kvq_geometry._fields_] == names
+    assert kvq.kvq_geometry.rope_base.offset == 56 and ctypes.sizeof(kvq.kvq_geometry) == 64
+
+
 def test_plan_gpt2_effective_bits():
     """GPT-2-shaped cache (K6/V4, per-head 64-channel groups): 5.5 stored bits per
     element at a length that is a multiple of G, as the hatterialabs.com page
