@@ -176,3 +176,31 @@ def test_window_geometry_errors():
         with pytest.raises(kvq.KVQError) as e:
             kvq.kvq_plan(H.geom_of(w, window=window, sinks=sinks), [100], [2], [2])
         assert e.value.status == kvq.KVQ_ERR_ARG, (window, sinks)
+
+
+def test_window_multi_layer_append():
+    """kvq_quantize_append_layers with a window: every layer keeps its own window
+    rows (prefix by per-layer appends, then 70 tokens into three layers in one
+    call, more than the recent ring of 64 + 32 rows), and each layer's decode
+    meets the oracle."""
+    w = W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=2, lengths=(300, 100), bits=((2, 2),) * 2,
+                             new_tokens=70)
+    L, window, sinks = 3, 64, 32
+    cache = H.make_cache(w.scaled(layers=L), layers=L, window=window, sinks=sinks)
+    hist = {l: H.history(w, l) for l in range(L)}
+    for l in range(L):
+        (kp, vp, cp), _ = hist[l]
+        cache.append(l, kp.cuda(), vp.cuda(), cp)
+    kn = torch.stack([hist[l][1][0] for l in range(L)]).cuda()
+    vn = torch.stack([hist[l][1][1] for l in range(L)]).cuda()
+    cache.append_layers(0, kn, vn, hist[0][1][2])
+    for l in range(L):
+        q = W.draw_q(w, l)
+        out = cache.decode(l, q.cuda(), w.softmax_scale).cpu().numpy()
+        prefix, new = hist[l]
+        for s in range(w.num_seqs):
+            k, v = H.full_seq(prefix, new, s)
+            encs = [H.encode_window(w, k, v, s, h, window, sinks) for h in range(w.kv_heads)]
+            ref = H.attn_ref(w, q[s].float().numpy(), encs)
+            assert np.all(H.row_rel_err(out[s], ref) <= H.ATTN_TOL), (l, s)
+    cache.close()
