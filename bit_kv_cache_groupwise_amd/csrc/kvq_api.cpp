@@ -807,6 +807,53 @@ kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float*
     return KVQ_OK;
 }
 
+kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* src, int32_t src_seq, int32_t layer0,
+                             int32_t n_layers, void* stream) {
+    g_last_error.clear();
+    if (!dst || !src) return fail(KVQ_ERR_ARG, "cache is NULL");
+    const kvq_geometry &gd = dst->g, &gs = src->g;
+    const bool same = gd.layers == gs.layers && gd.num_seqs == gs.num_seqs && gd.kv_heads == gs.kv_heads &&
+                      gd.q_heads == gs.q_heads && gd.head_dim == gs.head_dim && gd.group_k == gs.group_k &&
+                      gd.group_v == gs.group_v && gd.axis_k == gs.axis_k && gd.axis_v == gs.axis_v &&
+                      gd.in_dtype == gs.in_dtype && gd.meta_dtype == gs.meta_dtype && gd.window == gs.window &&
+                      gd.sinks == gs.sinks && gd.rope_base == gs.rope_base;
+    if (!same) return fail(KVQ_ERR_ARG, "the caches' geometries differ");
+    if (dst_seq < 0 || dst_seq >= gd.num_seqs || src_seq < 0 || src_seq >= gs.num_seqs)
+        return fail(KVQ_ERR_ARG, "sequence index out of range");
+    if (dst == src && dst_seq == src_seq) return fail(KVQ_ERR_ARG, "a sequence copied onto itself");
+    if (n_layers < 1 || layer0 < 0 || layer0 > gd.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    if (dst->bits_k[dst_seq] != src->bits_k[src_seq] || dst->bits_v[dst_seq] != src->bits_v[src_seq] ||
+        dst->cap[dst_seq] != src->cap[src_seq])
+        return fail(KVQ_ERR_ARG, "the sequences' bits or capacities differ");
+    hipStream_t hs = (hipStream_t)stream;
+    const int S = gd.num_seqs;
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const SeqEntry& ed = dst->entries[(size_t)l * S + dst_seq];
+        const SeqEntry& es = src->entries[(size_t)l * S + src_seq];
+        for (int t = 0; t < 2; ++t) {
+            // a tensor's heads are contiguous, with equal strides for equal bits and capacity
+            const struct { uint8_t *d; const uint8_t* s; uint64_t n; } parts[3] = {
+                {dst->codes + ed.codes[t], src->codes + es.codes[t], es.codes_hs[t] * gd.kv_heads},
+                {dst->meta + ed.meta[t], src->meta + es.meta[t], es.meta_hs[t] * gd.kv_heads},
+                {dst->resid + ed.resid[t], src->resid + es.resid[t], es.resid_hs[t] * gd.kv_heads}};
+            for (const auto& p : parts) {
+                if (p.n == 0) continue;
+                hipError_t e = hipMemcpyAsync(p.d, p.s, p.n, hipMemcpyDeviceToDevice, hs);
+                if (e != hipSuccess) return hip_fail(e, "copying a sequence");
+            }
+        }
+        // the length, in the destination layer's current length buffer
+        int32_t* len_dev = (int32_t*)(dst->table + dst->tl.len_off) + ((size_t)dst->parity[l] * gd.layers + l) * S;
+        const int32_t* len_src = (const int32_t*)(src->table + src->tl.len_off) +
+                                 ((size_t)src->parity[l] * gs.layers + l) * S;
+        hipError_t e = hipMemcpyAsync(len_dev + dst_seq, len_src + src_seq, sizeof(int32_t), hipMemcpyDeviceToDevice, hs);
+        if (e != hipSuccess) return hip_fail(e, "copying a sequence length");
+        dst->lens[(size_t)l * S + dst_seq] = src->lens[(size_t)l * S + src_seq];
+    }
+    return KVQ_OK;
+}
+
 kvq_status kvq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
     g_last_error.clear();
     if (!buf || !sink) return fail(KVQ_ERR_ARG, "buffer or sink is NULL");

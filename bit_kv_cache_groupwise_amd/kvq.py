@@ -67,6 +67,7 @@ _lib.kvq_cache_create.argtypes = [ctypes.POINTER(kvq_geometry), _I32P, _U8P, _U8
 _lib.kvq_cache_destroy.argtypes = [_P]
 _lib.kvq_cache_destroy.restype = None
 _lib.kvq_quantize_append.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P]
+_lib.kvq_copy_sequence.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
 _lib.kvq_quantize_append_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_decode_step.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.kvq_decode_workspace_size.argtypes = [_P]
@@ -222,6 +223,11 @@ def kvq_decode_attention_layers(handle, layer0, n_layers, q, softmax_scale, out,
            "kvq_decode_attention_layers")
 
 
+def kvq_copy_sequence(dst_handle, dst_seq, src_handle, src_seq, layer0, n_layers, stream=None):
+    _check(_lib.kvq_copy_sequence(dst_handle, dst_seq, src_handle, src_seq, layer0, n_layers, _stream(stream)),
+           "kvq_copy_sequence")
+
+
 def kvq_read_probe(buf, nbytes, sink, stream=None):
     """Streaming read of nbytes of device memory at buf (measurement aid)."""
     _check(_lib.kvq_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_read_probe")
@@ -339,6 +345,10 @@ class Cache:
         v = torch.empty_like(k)
         kvq_dequantize(self.handle, layer, seq, k, v, stream)
         return k, v
+
+    def copy_sequence(self, dst_seq, src_cache, src_seq, layer0=0, n_layers=None, stream=None):
+        n = self.geom.layers - layer0 if n_layers is None else n_layers
+        kvq_copy_sequence(self.handle, dst_seq, src_cache.handle, src_seq, layer0, n, stream)
 
     def lengths(self, layer):
         return kvq_seq_lengths(self.handle, layer, self.geom.num_seqs)

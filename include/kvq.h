@@ -266,6 +266,20 @@ kvq_status kvq_dequantize(const kvq_cache* cache, int32_t layer, int32_t seq, fl
  * pointer, size not a multiple of 16), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 kvq_status kvq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
 
+/* Copy sequence src_seq of `src` over sequence dst_seq of `dst`, for layers
+ * [layer0, layer0 + n_layers): its packed codes, metadata, residual rows,
+ * window rows and length, so that dst_seq then decodes exactly as src_seq
+ * (beam forks, prefix reuse: [N] "State quantized cache harus tetap selaras
+ * dengan posisi": the scales and packing metadata must move with the codes
+ * they describe). `dst` and `src` may be the same cache (then dst_seq !=
+ * src_seq). Requires equal geometry (every kvq_geometry field) and, for the
+ * two sequences, equal bits_k, bits_v and capacity. Device-to-device copies
+ * enqueued on `stream`; only the bytes of the first `length` tokens are
+ * defined afterwards. Errors: KVQ_ERR_ARG (NULL cache, index out of range,
+ * mismatch, same sequence), KVQ_ERR_HIP. */
+kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* src, int32_t src_seq, int32_t layer0,
+                             int32_t n_layers, void* stream);
+
 /* Current cached lengths of `layer`: host array of num_seqs entries. */
 kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t* out);
 

@@ -171,6 +171,7 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.kvq_decode_step(None, 0, None, None, None, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_quantize_append_layers(None, 0, 1, None, None, None, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_attention_layers(None, 0, 1, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_copy_sequence(None, 0, None, 1, 0, 1, None) == kvq.KVQ_ERR_ARG
 
 
 def test_read_probe_validates_before_launching():

@@ -204,3 +204,58 @@ def test_window_multi_layer_append():
             ref = H.attn_ref(w, q[s].float().numpy(), encs)
             assert np.all(H.row_rel_err(out[s], ref) <= H.ATTN_TOL), (l, s)
     cache.close()
+
+
+@pytest.mark.parametrize("window,sinks", [(0, 0), (64, 32)])
+def test_copy_sequence(window, sinks):
+    """kvq_copy_sequence forks a sequence (beam search, prefix reuse): the copy,
+    within the cache and into a second cache, then takes further appends and
+    decodes exactly as the source's history says; mismatches are rejected."""
+    kvq = H.kvq()
+    w = W.llama2_7b().scaled(num_seqs=3, kv_heads=2, q_heads=2, lengths=(300, 100, 300), bits=((2, 2),) * 3,
+                             new_tokens=5)
+    L = 2
+    wl = w.scaled(layers=L)
+    a = H.make_cache(wl, layers=L, extra=10, window=window, sinks=sinks)
+    b = H.make_cache(wl, layers=L, extra=10, window=window, sinks=sinks)
+    hist = {l: H.history(w, l) for l in range(L)}
+    for l in range(L):
+        (kp, vp, cp), _ = hist[l]
+        a.append(l, kp.cuda(), vp.cuda(), cp)
+    a.copy_sequence(2, a, 0)          # seq 2 of a becomes seq 0's history (it had its own)
+    b.copy_sequence(2, a, 0, 1, 1)    # layer 1 of b's seq 2 as well
+    assert a.lengths(0)[2] == 300 and a.lengths(1)[2] == 300 and b.lengths(1)[2] == 300 and b.lengths(0)[2] == 0
+    for h in range(w.kv_heads):
+        k, v = H.full_seq(hist[1][0], (hist[1][1][0][:0], hist[1][1][1][:0], [0] * 3), 0)
+        H.assert_head_bytes(b, w, 1, 2, h, k, v)  # the copy into the second cache
+    # then the same new tokens go to seq 0 and its fork
+    for l in range(L):
+        (kn, vn, _) = hist[l][1]
+        kk = torch.cat([H.seq_rows(kn, [5] * 3, 0)] * 3).cuda()
+        vv = torch.cat([H.seq_rows(vn, [5] * 3, 0)] * 3).cuda()
+        a.append(l, kk, vv, [5, 0, 5])
+    for l in range(L):
+        prefix, new = hist[l]
+        k, v = H.full_seq(prefix, new, 0)
+        q = W.draw_q(w, l)
+        q[2] = q[0]
+        out = a.decode(l, q.cuda(), w.softmax_scale).cpu().numpy()
+        np.testing.assert_array_equal(out[2], out[0])
+        for h in range(w.kv_heads):
+            H.assert_head_bytes(a, w, l, 2, h, k, v)  # the fork's stored bytes: seq 0's history
+        if window or sinks:
+            encs = [H.encode_window(w, k, v, 0, h, window, sinks) for h in range(w.kv_heads)]
+        else:
+            encs = [H.encode(w, k, v, 0, h) for h in range(w.kv_heads)]
+        ref = H.attn_ref(w, q[0].float().numpy(), encs)
+        assert np.all(H.row_rel_err(out[2], ref) <= H.ATTN_TOL), l
+    for args, st in (((2, a, 2), kvq.KVQ_ERR_ARG), ((3, a, 0), kvq.KVQ_ERR_ARG), ((0, a, 0, 1, 2), kvq.KVQ_ERR_ARG)):
+        with pytest.raises(kvq.KVQError) as e:
+            a.copy_sequence(*args)
+        assert e.value.status == st
+    other = H.make_cache(wl, layers=L, extra=11, window=window, sinks=sinks)  # capacities differ
+    with pytest.raises(kvq.KVQError) as e:
+        other.copy_sequence(0, a, 0)
+    assert e.value.status == kvq.KVQ_ERR_ARG
+    for c in (a, b, other):
+        c.close()
