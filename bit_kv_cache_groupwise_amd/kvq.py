@@ -34,7 +34,7 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
             "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step")
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -87,7 +87,7 @@ _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
            "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step"):
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
