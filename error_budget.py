@@ -72,10 +72,23 @@ def top_mass(weights, frac=0.05):
     return float(np.mean(w[:, :n].sum(axis=1)))
 
 
-def run_config(w, device="cuda", window=0, sinks=0):
+def recent_queries(k, S, T, H, D, gen):
+    """Queries that attend to the most recent tokens: per (sequence, head), the
+    sum of the last 8 keys scaled to norm 4*sqrt(D), plus N(0,1) noise. A stand-in
+    for decode steps whose attention concentrates on recent tokens, the case the
+    full-precision window targets ([U] "O Imposto dos Sistemas ..."); synthetic,
+    not a trained model's queries."""
+    import torch
+    kk = k.float().reshape(S, T, H, D)[:, T - 8:].sum(dim=1)  # [S][H][D]
+    kk = kk / kk.norm(dim=-1, keepdim=True) * (4.0 * D ** 0.5)
+    return kk + torch.randn(kk.shape, generator=gen, device=k.device)
+
+
+def run_config(w, device="cuda", window=0, sinks=0, q_recent=False):
     """Quantize w's cache on the GPU, read it back and decode; return the error
     metrics. With a window or sinks, the reconstruction read back is the one the
-    attention reads (those tokens unquantized)."""
+    attention reads (those tokens unquantized). q_recent: queries from
+    recent_queries instead of N(0,1)."""
     import torch
 
     from bit_kv_cache_groupwise_amd import kvq
@@ -89,6 +102,10 @@ def run_config(w, device="cuda", window=0, sinks=0):
     k, v = W.draw_kv(w, 0, w.lengths, device=device, stream=0)
     cache.append(0, k, v, list(w.lengths))
     q = W.draw_q(w, 0, device=device)
+    if q_recent:
+        gen = torch.Generator(device=device)
+        gen.manual_seed(4242)
+        q = recent_queries(k, S, T, H, D, gen).to(q.dtype)
     fused = None
     if w.axis_v == TOK:  # the fused decode reads token-axis values
         fused = cache.decode(0, q, w.softmax_scale).double().cpu().numpy()
@@ -123,6 +140,7 @@ def run_config(w, device="cuda", window=0, sinks=0):
     return {
         "axis_k": AXIS_NAME[w.axis_k], "axis_v": AXIS_NAME[w.axis_v], "group_k": w.group_k, "group_v": w.group_v,
         "bits": list(w.bits[0]), "v_dist": w.v_dist, "window": window, "sinks": sinks,
+        "queries": "recent" if q_recent else "normal",
         "k_recon_rel": math.sqrt(kd2 / kn2), "v_recon_rel": math.sqrt(vd2 / vn2),
         "logit_rms_over_std": float(np.mean(acc["logit_rms"])), "logit_max_abs": float(np.max(acc["logit_max"])),
         "out_rel_dequant": float(np.mean(acc["out_deq"])), "out_rel_dequant_max": float(np.max(acc["out_deq_max"])),
@@ -148,24 +166,28 @@ def configs(T=2048):
         for G in (64, 128):
             out.append(base.scaled(group_k=G, group_v=G, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
         out.append(base.scaled(group_k=256, group_v=128, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
-    return [(x, 0, 0) for x in out] + window_configs(base)
+    return [(x, 0, 0, False) for x in out] + window_configs(base)
 
 
 def window_configs(base):
     """Full-precision recent window and sinks at 2 bits (keys per channel,
     values per token, groups of 32): (workload, window, sinks)."""
     w2 = base.scaled(group_k=32, group_v=32, bits=((2, 2),) * 4, v_dist="token_lognormal")
-    return [(w2, win, snk) for win, snk in ((32, 0), (128, 0), (512, 0), (128, 32), (0, 64))]
+    rows = [(w2, win, snk, False) for win, snk in ((32, 0), (128, 0), (512, 0), (128, 32), (0, 64))]
+    # queries that attend to the most recent tokens
+    return rows + [(w2, win, snk, True) for win, snk in ((0, 0), (32, 0), (128, 0), (128, 32))]
 
 
 def table(rows):
-    lines = ["| K axis | V axis | G (K, V) | bits | window, sinks | V recipe | K recon | V recon | logit rms/std "
-             "| out (dequant) | out (fused) | top-5% mass |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    lines = ["| K axis | V axis | G (K, V) | bits | window, sinks | V recipe | queries | K recon | V recon "
+             "| logit rms/std | out (dequant) | out (fused) | top-5% mass |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         fused = f"{r['out_rel_fused']:.2e}" if r["out_rel_fused"] is not None else "—"
         lines.append(f"| {r['axis_k']} | {r['axis_v']} | {r['group_k']}, {r['group_v']} | {r['bits'][0]} | "
                      f"{r['window']}, {r['sinks']} | "
-                     f"{r['v_dist']} | {r['k_recon_rel']:.3e} | {r['v_recon_rel']:.3e} | "
+                     f"{r['v_dist']} | {r['queries']} | "
+                     f"{r['k_recon_rel']:.3e} | {r['v_recon_rel']:.3e} | "
                      f"{r['logit_rms_over_std']:.3e} | {r['out_rel_dequant']:.3e} | {fused} | "
                      f"{r['top5pct_attention_mass']:.2f} |")
     return "\n".join(lines)
@@ -176,8 +198,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=2048)
     args = ap.parse_args()
     rows = []
-    for w, window, sinks in configs(args.tokens):
-        r = run_config(w, window=window, sinks=sinks)
+    for w, window, sinks, q_recent in configs(args.tokens):
+        r = run_config(w, window=window, sinks=sinks, q_recent=q_recent)
         rows.append(r)
         print(json.dumps(r), flush=True)
     print(table(rows), flush=True)
