@@ -41,28 +41,42 @@ def _run(cmd):
     return r
 
 
+def units():
+    """(source, object, extra flags, is_device_code) of every translation unit."""
+    return [("kvq_kernels.hip", "kvq_kernels.o", [], True),
+            *[("kvq_decode_mha.hip", f"kvq_decode_mha_d{d}.o", [f"-DKVQ_MHA_HEAD_DIM={d}"], True)
+              for d in MHA_HEAD_DIMS],
+            *[("kvq_decode_gqa.hip", f"kvq_decode_gqa_d{d}.o", [f"-DKVQ_GQA_HEAD_DIM={d}"], True)
+              for d in MHA_HEAD_DIMS],
+            ("kvq_api.cpp", "kvq_api.o", [], False)]
+
+
+def _compile_cmd(cc, src, obj, extra, device):
+    out = os.path.join(BUILD, obj)
+    if device:
+        return [cc, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, src), "-o", out]
+    return [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), *extra, "-c",
+            os.path.join(CSRC, src), "-o", out]
+
+
+def link() -> str:
+    cc = hipcc()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+          *[os.path.join(BUILD, u[1]) for u in units()]])
+    os.replace(tmp, LIB)
+    return LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    jobs = [
-        [cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kvq_kernels.hip"), "-o", os.path.join(BUILD, "kvq_kernels.o")],
-        *[[cc, *COMMON, *DEVICE, f"-DKVQ_MHA_HEAD_DIM={d}", "-c", os.path.join(CSRC, "kvq_decode_mha.hip"), "-o",
-            os.path.join(BUILD, f"kvq_decode_mha_d{d}.o")] for d in MHA_HEAD_DIMS],
-        *[[cc, *COMMON, *DEVICE, f"-DKVQ_GQA_HEAD_DIM={d}", "-c", os.path.join(CSRC, "kvq_decode_gqa.hip"), "-o",
-            os.path.join(BUILD, f"kvq_decode_gqa_d{d}.o")] for d in MHA_HEAD_DIMS],
-        [cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", os.path.join(BUILD, "kvq_api.o")],
-    ]
+    jobs = [_compile_cmd(cc, *u) for u in units()]
     with ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 4)) as ex:
         for r in ex.map(_run, jobs):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout, r.stderr, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-          os.path.join(BUILD, "kvq_kernels.o"), *[os.path.join(BUILD, f"kvq_decode_mha_d{d}.o") for d in MHA_HEAD_DIMS],
-          *[os.path.join(BUILD, f"kvq_decode_gqa_d{d}.o") for d in MHA_HEAD_DIMS],
-          os.path.join(BUILD, "kvq_api.o")])
-    os.replace(tmp, LIB)
-    return LIB
+    return link()
 
 
 if __name__ == "__main__":

@@ -20,7 +20,9 @@
 //         2^(8-sh) that undoes the code shift,
 //     bias[r] = sum_c q_rc z_c on the VALU;
 //   the waves' partial scores are summed through LDS (one barrier per tile);
-//   O[r][c]  += 2^(24-KB-sh) * sum_t (2^KB p_rt s_t,g(c))[hi + lo] V[t][c],
+//   O[r][c]  += 2^(24-kb-sh) * sum_t (2^kb p_rt s_t,g(c))[hi + lo] V[t][c],
+//     kb = the wave's running value-product exponent (at most BV + 2, lowered
+//     when a tile's largest value step would push 2^kb p s past 2^15),
 //     V = value codes as fp16 values (code << sh) * 2^-24, from an LDS byte tile;
 //   Z[r][g]  += 2^-KZ * sum_t (2^KZ p_rt)[hi + lo] * (z_t,g | 1),
 //     one MFMA against a [token][group] fragment of zero points whose column
@@ -350,8 +352,10 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     constexpr int KALIGN = pow2_align(D * BK / 8) < pow2_align(KWL * 4) ? pow2_align(D * BK / 8) : pow2_align(KWL * 4);
     constexpr int VALIGN = pow2_align(D * BV / 8) < pow2_align(BV * 4) ? pow2_align(D * BV / 8) : pow2_align(BV * 4);
     constexpr int KSH = code_shift(BK), VSH = code_shift(BV);
-    // Softmax weight scales (p <= 1): 2^KB p * s <= 2^(BV+2) * range / (2^BV - 1)
-    // stays far inside fp16 while small weights stay normal; 2^KZ p <= 16384.
+    // Softmax weight scales (p <= 1): 2^kb p * s with kb <= KB = BV + 2 keeps
+    // small weights normal in fp16; kb drops below KB where a tile's value
+    // steps are large (running_value_exponent), so that 2^kb p s < 2^15;
+    // 2^KZ p <= 16384.
     constexpr int KB = BV + 2, KZ = 14;
     constexpr int XS = 2 * NWV * 64 * 8 > NWV * 16 * DW ? 2 * NWV * 64 * 8 : NWV * 16 * DW;
     using KF = KeyFrag<BK>;
@@ -426,6 +430,8 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4lg+i][col ln]: zero-point sums (ln < ngw), denominator (ln == ngw)
     float m = kFarBelow;              // reference maximum of query ln (the same in every wave)
+    int kb = KB;                      // value-product exponent (wave-uniform, never rises)
+    int kb_tile = KB;                 // the exponent the staged tile's value steps allow
 
     // ---- prefetch registers: two sets, so the tiles two ahead are in flight
     struct Pref {
@@ -481,6 +487,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
 #pragma unroll
             for (int k = 0; k < 4; ++k) ((uint2*)dst)[k] = make_uint2(by[2 * k], by[2 * k + 1]);
         }
+        uint32_t smx = 0;  // largest fp16 value step of the wave's tile (steps are >= 0: bit order = value order)
 #pragma unroll
         for (int u = 0; u < NVML; ++u) {
             const int f = lane + 64 * u;
@@ -488,8 +495,17 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
                 const int tt = f >> lng, g = f & (ngw - 1);
                 st_lds[wave][g][tt] = (uint16_t)(P.vmw[u] & 0xffffu);
                 zt_lds[wave][g][tt] = (uint16_t)(P.vmw[u] >> 16);
+                smx = max(smx, P.vmw[u] & 0x7fffu);
             }
         }
+        // the wave's largest biased exponent e (a scalar: binary search over ballots);
+        // s < 2^(e - 14), so 2^kb p s < 2^15 with kb = 29 - e
+        const int el = (int)(smx >> 10);
+        int emax = 0;
+#pragma unroll
+        for (int b = 16; b; b >>= 1)
+            if (__builtin_amdgcn_ballot_w64(el >= emax + b)) emax += b;
+        kb_tile = min(KB, 29 - emax);
         if (with_keys && lane < DW / 2) {
             sp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x05040100u);
             zp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x07060302u);
@@ -613,18 +629,25 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
             }
             m = mnew;
         }
+        if (kb_tile < kb) {  // a tile with larger value steps: lower the exponent (exact rescale)
+            const float f = __builtin_amdgcn_ldexpf(1.0f, kb_tile - kb);
+#pragma unroll
+            for (int n = 0; n < NSUB; ++n) acc[n] *= f;
+            kb = kb_tile;
+        }
         // p <= 1 (exact running maximum), kept in fp16 range with power-of-two
-        // scales: 2^KB for the value product, 2^KZ for zero points / denominator
+        // scales: 2^kb for the value product, 2^KZ for zero points / denominator
         float p[8];
-        const float mb = m - (float)KB;
+        const float mb = m - (float)kb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
         Frag ph, pl, pb;  // 2^KZ p as hi + lo; 2^KB p truncated to fp16 pairs
         {
             Frag zf;
             float pz[8];
+            const float zscale = __builtin_amdgcn_ldexpf(1.0f, KZ - kb);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pz[j] = p[j] * (float)(1 << (KZ - KB));
+            for (int j = 0; j < 8; ++j) pz[j] = p[j] * zscale;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 split2(pz[2 * jj], pz[2 * jj + 1], ph.u[jj], pl.u[jj]);
@@ -732,7 +755,7 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
         for (int b = 0; b < NSUB / 2; ++b) {
             // zero-point sum of (r, group), carrying 2^KZ
             const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv)) * (1.0f / (float)(1 << KZ));
-            constexpr float oscale = kTwo24 / (float)(1 << (KB + VSH));
+            const float oscale = __builtin_amdgcn_ldexpf(1.0f, 24 - kb - VSH);
             o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], oscale, zs);
             o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], oscale, zs);
         }

@@ -25,11 +25,62 @@ def geom_of(w: W.Workload, layers=None, window=0, sinks=0, rope_base=0.0):
                       in_dtype=w.in_dtype, window=window, sinks=sinks, rope_base=rope_base)
 
 
-def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0, rope_base=0.0):
+def poison_(t):
+    """Fill a device buffer with 0xFF bytes: NaN as fp32, fp16 and bf16, all-ones
+    codes. A kernel that reads a byte nobody wrote, or leaves an output byte
+    unwritten, then shows it as a NaN or a wrong code."""
+    t.view(torch.uint8).fill_(0xFF)
+
+
+def poison_cache(c):
+    """Poison the codes, metadata and residual pools of a new cache (the table
+    holds the library's offsets and lengths and is left alone), and make its
+    decode, step and dequantize calls start from poisoned workspace and NaN
+    outputs on every call."""
+    for t in (c.codes, c.meta, c.resid):
+        poison_(t)
+    plain_ws = c.workspace
+
+    def workspace(n_layers=1):
+        ws = plain_ws(n_layers)
+        poison_(ws)
+        return ws
+
+    def nan_out(q, lead=()):
+        g = c.geom
+        return torch.full(tuple(lead) + (g.num_seqs, g.q_heads, g.head_dim), float("nan"), dtype=torch.float32,
+                          device=q.device)
+
+    plain_decode, plain_step, plain_layers = c.decode, c.step, c.decode_layers
+
+    def decode(layer, q, softmax_scale, out=None, stream=None):
+        return plain_decode(layer, q, softmax_scale, nan_out(q) if out is None else out, stream)
+
+    def step(layer, k_new, v_new, n_new, q, softmax_scale, out=None, stream=None):
+        return plain_step(layer, k_new, v_new, n_new, q, softmax_scale, nan_out(q) if out is None else out, stream)
+
+    def decode_layers(layer0, n_layers, q, softmax_scale, out=None, stream=None):
+        return plain_layers(layer0, n_layers, q, softmax_scale, nan_out(q, (n_layers,)) if out is None else out,
+                            stream)
+
+    def dequantize(layer, seq, stream=None):
+        g = c.geom
+        n = c.lengths(layer)[seq]
+        k = torch.full((g.kv_heads, n, g.head_dim), float("nan"), dtype=torch.float32, device=c.codes.device)
+        v = torch.full_like(k, float("nan"))
+        kvq().kvq_dequantize(c.handle, layer, seq, k, v, stream)
+        return k, v
+
+    c.workspace, c.decode, c.step, c.decode_layers, c.dequantize = workspace, decode, step, decode_layers, dequantize
+    return c
+
+
+def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0, rope_base=0.0, poison=True):
     k = kvq()
     cap = capacity or [L + w.new_tokens + extra for L in w.lengths]
-    return k.Cache(geom_of(w, layers, window, sinks, rope_base), cap, [b[0] for b in w.bits],
-                   [b[1] for b in w.bits])
+    c = k.Cache(geom_of(w, layers, window, sinks, rope_base), cap, [b[0] for b in w.bits],
+                [b[1] for b in w.bits])
+    return poison_cache(c) if poison else c
 
 
 def history(w: W.Workload, layer: int, device="cpu"):

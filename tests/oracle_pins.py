@@ -539,11 +539,89 @@ def check_rope_attention(o, seed=13):
     np.testing.assert_allclose(o.attend_rope(q, k[:1], v[:1], 0.5, 10000.0), o.attend(q, k[:1], v[:1], 0.5))
 
 
+
+# ----------------------------------------------------------------------------
+# Adversarial groups, in exact rational arithmetic
+# ----------------------------------------------------------------------------
+
+def round_to_format(fr: Fraction, frac_bits: int, emin: int) -> Fraction:
+    """Nearest value (ties to even) of a binary floating-point format with
+    ``frac_bits`` fraction bits and smallest normal exponent ``emin``
+    (subnormals included; no overflow in the inputs used here)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - frac_bits)
+    return sign * round_half_even(a / ulp) * ulp
+
+
+def r32(fr):
+    return round_to_format(fr, 23, -126)
+
+
+def r16(fr):
+    return round_to_format(fr, 10, -14)
+
+
+def check_edge_groups_exact(o):
+    """Constant groups, fp16-subnormal and underflowing steps, exact ties,
+    clamping after the fp16 rounding of the step or the zero, magnitudes below
+    fp16's range and near 65504: step, zero, codes and reconstruction of the
+    oracle equal the definition evaluated in exact rationals with every float32
+    and fp16 rounding written out (zero = min, step = fp32(fp32(max - min) /
+    (2^B - 1)), both stored in fp16; t = fp32(fp32(x - z) / s); code =
+    clamp(round-half-even(t), 0, 2^B - 1); 0 where s = 0; x_hat = z + code*s)
+    ([U] "O Que o Erro de Quantizacao ..."; [N] "Scale menentukan ...")."""
+    from tests import edge_inputs as E
+    seen = set()
+    for dtype in ("f32", "f16", "bf16"):
+        for bits in (2, 3, 4, 6, 8):
+            L = (1 << bits) - 1
+            for name, g in E.groups(bits, dtype, seed=5):
+                xs = [Fraction(float(v)) for v in g]
+                mn, mx = min(xs), max(xs)
+                s = r16(r32(r32(mx - mn) / L))
+                z = r16(mn)
+                want = []
+                for x in xs:
+                    if s == 0:
+                        want.append(0)
+                    else:
+                        t = r32(r32(x - z) / s)
+                        want.append(min(max(round_half_even(t), 0), L))
+                gs, gz = o.group_params(g.min(), g.max(), bits)
+                assert Fraction(float(gs)) == s and Fraction(float(gz)) == z, (dtype, bits, name, gs, gz, s, z)
+                codes = o.encode_values(g, gs, gz, bits)
+                assert [int(c) for c in codes] == want, (dtype, bits, name)
+                xq = o.dequantize_tensor(codes[:, None], np.array([[gs]]), np.array([[gz]]), np.zeros((0, 1)),
+                                         o.AXIS_CHANNEL, len(g))
+                for c, v in zip(want, xq[:, 0]):
+                    assert Fraction(float(v)) == z + c * s, (dtype, bits, name)
+                seen.add(name.split("_")[0])
+                if name.startswith("substep") and L + 1 <= int(name.split("_")[1]) <= 2 * L - 1:
+                    seen.add("clamp_top" if max(want) == L and any(
+                        round_half_even(r32(r32(x - z) / s)) > L for x in xs) else "noclamp")
+                if name.startswith("zero_rounds_up"):
+                    seen.add("zero_above_min" if z > mn else "zero_below")
+                if s == 0 and mx > mn:
+                    seen.add("step_underflow")
+    # the cases exercise what they are named for
+    for need in ("const", "ties", "substep", "underflow", "tiny", "big", "clamp_top", "zero_above_min",
+                 "step_underflow"):
+        assert need in seen, need
+
+
 ALL_CHECKS = [
     check_worked_example, check_brute_force_nearest, check_half_step_bound, check_min_max_codes,
     check_monotone, check_exact_reconstruction, check_b8_bound, check_constant_group,
     check_meta_rounding, check_axis_semantics, check_dequant_exact, check_pack_golden,
     check_pack_bigint, check_meta_words, check_attention_closed_forms, check_attention_vs_torch,
     check_sizes, check_sizing_pages, check_window_blocks, check_window_exact_attention,
-    check_rope_complex_form, check_rope_attention,
+    check_rope_complex_form, check_rope_attention, check_edge_groups_exact,
 ]

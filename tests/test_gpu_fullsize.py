@@ -1,12 +1,15 @@
-"""The five benchmark workloads at full size, through the C ABI, in the launch
-configuration bench.py times: the whole cached prefix appended in one call,
-then the decode step's new tokens, then one decode-attention call per layer
+"""The five benchmark workloads at full size, through the C ABI, in the calls
+and launch configuration bench.py times: the whole cached prefix appended in
+one call, then the decode step itself -- kvq_decode_step (the new tokens
+appended and attended in one call; one launch where the single-query kernel
+serves the cache) for the one-layer workloads, and kvq_quantize_append_layers
+plus kvq_decode_attention_layers over all 12 layers for the GPT-2 shape --
 with the library's default split sizes. Sampled (layer, seq, kv head) units
 are checked against the CPU oracle computed for that unit alone: packed codes,
 metadata and residual rows bit-exact, and the attention rows of the unit's
 query heads within 2e-3 of the fp64 oracle over the quantized cache. Every
 other unit is checked for what holds at any size: lengths advanced by the
-append and finite outputs."""
+append and finite outputs. Pools, workspace and outputs start poisoned."""
 
 import sys
 
@@ -60,18 +63,35 @@ def test_full_size_workload(name, window, sinks, rope):
           f"tokens={sum(w.lengths)} +{w.new_tokens}/seq window={window} sinks={sinks} rope={rope}")
     cache = H.make_cache(w, window=window, sinks=sinks, rope_base=rope)
     outs = {}
-    for layer in range(w.layers):
-        prefix, new = H.history(w, layer, device="cuda")
-        cache.append(layer, prefix[0], prefix[1], prefix[2])
-        cache.append(layer, new[0], new[1], new[2])
-        del prefix, new
-        q = W.draw_q(w, layer)
-        out = cache.decode(layer, q.cuda(), w.softmax_scale)
+    counts = [w.new_tokens] * w.num_seqs
+    if w.layers == 1:  # the bench step: kvq_decode_step
+        prefix, new = H.history(w, 0, device="cuda")
+        cache.append(0, prefix[0], prefix[1], prefix[2])
+        q = W.draw_q(w, 0)
+        out = cache.step(0, new[0], new[1], counts, q.cuda(), w.softmax_scale)
         torch.cuda.synchronize()
-        assert cache.lengths(layer) == [L + w.new_tokens for L in w.lengths]
+        outs[0] = (q, out.cpu().numpy())
+        del prefix, new
+    else:  # the bench step of a multi-layer model: one append and one decode call over all layers
+        news = []
+        for layer in range(w.layers):
+            prefix, new = H.history(w, layer, device="cuda")
+            cache.append(layer, prefix[0], prefix[1], prefix[2])
+            news.append(new)
+            del prefix
+        kn = torch.stack([n[0] for n in news])
+        vn = torch.stack([n[1] for n in news])
+        cache.append_layers(0, kn, vn, counts)
+        del news, kn, vn
+        qs = [W.draw_q(w, layer) for layer in range(w.layers)]
+        out = cache.decode_layers(0, w.layers, torch.stack(qs).cuda(), w.softmax_scale)
+        torch.cuda.synchronize()
         out = out.cpu().numpy()
-        assert np.isfinite(out).all(), (name, layer)
-        outs[layer] = (q, out)
+        for layer in range(w.layers):
+            outs[layer] = (qs[layer], out[layer])
+    for layer in range(w.layers):
+        assert cache.lengths(layer) == [L + w.new_tokens for L in w.lengths]
+        assert np.isfinite(outs[layer][1]).all(), (name, layer)
     _note(f"[fullsize] {name}: cache filled and decoded; checking {len(_samples(w))} sampled units")
     worst = 0.0
     by_layer = {}

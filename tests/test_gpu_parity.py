@@ -248,6 +248,45 @@ def test_single_query_matrix(head_dim, chunk, monkeypatch):
     cache.close()
 
 
+ALL_PAIRS = tuple((a, b) for a in (2, 3, 4, 6, 8) for b in (2, 3, 4, 6, 8))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("q_heads", [2, 16], ids=["single_query", "query_groups_of_8"])
+def test_every_bit_pair_step_and_decode(head_dim, q_heads):
+    """Every (K, V) bit pair, one cache per pair, so each pair's compiled
+    kernels run: kvq_decode_step (the fused one-launch instantiation where the
+    single-query kernel serves the cache: no key block completes in the step)
+    equals kvq_quantize_append + kvq_decode_attention bit for bit, and both meet
+    the oracle; stored bytes bit-exact. Lengths span several splits."""
+    kv = 2
+    _note(f"[pairs] D={head_dim} Hq={q_heads} Hkv={kv}")
+    worst = 0.0
+    for pair in ALL_PAIRS:
+        w = W.llama2_7b().scaled(num_seqs=2, kv_heads=kv, q_heads=q_heads, head_dim=head_dim, lengths=(300, 45),
+                                 bits=(pair, pair), in_dtype="bf16" if head_dim == 256 else "f16")
+        ca, cb = H.make_cache(w), H.make_cache(w)
+        prefix, new = H.history(w, 0)
+        for c in (ca, cb):
+            c.append(0, prefix[0].cuda(), prefix[1].cuda(), prefix[2])
+        q = W.draw_q(w, 0)
+        oa = ca.step(0, new[0].cuda(), new[1].cuda(), new[2], q.cuda(), w.softmax_scale)
+        cb.append(0, new[0].cuda(), new[1].cuda(), new[2])
+        ob = cb.decode(0, q.cuda(), w.softmax_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), (head_dim, q_heads, pair)
+        out = oa.cpu().numpy()
+        for s in range(w.num_seqs):
+            k, v = H.full_seq(prefix, new, s)
+            encs = [H.assert_head_bytes(ca, w, 0, s, h, k, v) for h in range(kv)]
+            err = H.row_rel_err(out[s], H.attn_ref(w, q[s].float().numpy(), encs))
+            worst = max(worst, float(err.max()))
+            assert np.all(err <= H.ATTN_TOL), (head_dim, q_heads, pair, s, float(err.max()))
+        ca.close()
+        cb.close()
+    _note(f"[pairs] D={head_dim} Hq={q_heads} worst row rel err {worst:.3e}")
+
+
 @pytest.mark.parametrize("group_k", [64, 128])
 def test_single_query_large_key_blocks(group_k):
     w = W.llama2_7b().scaled(num_seqs=3, kv_heads=3, q_heads=3, lengths=(1000, 129, 4000), group_k=group_k,
