@@ -1,22 +1,25 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the quantized KV cache on one MI355X.
 
-One step = the new token of every sequence appended into one layer, then
-decode attention over that layer (every cached token, the new one included),
-as one kvq_decode_step call (one launch where the single-query kernel serves
-the cache and no key block completes; --unfused-step: kvq_quantize_append then
-kvq_decode_attention). The default workload is the Llama-2-7B-shaped cache (16
-sequences, 32 heads of 128 channels, 4096 cached tokens, fp16, 2-bit K
-per-channel / V per-token, groups of 32), one layer per step. Independent
-layer caches are rotated so that each step reads memory that is not resident
-in the 256 MB last-level cache. A multi-layer workload (the GPT-2 shape, 12
-layers) appends into all of them in one kvq_quantize_append_layers call and
-decodes them in one kvq_decode_attention_layers call (--per-layer-decode: one
-append and one decode call per layer).
+One step = the new tokens of every sequence appended into one layer, then
+decode attention over that layer (every cached token, the new ones included),
+as one kvq_decode_step call (--unfused-step: kvq_quantize_append then
+kvq_decode_attention). The default workload is the largest single-GPU
+configuration, the mixed batch: 64 sequences with lengths uniform in
+[512, 32768], 64 query heads over 8 kv heads of 128 channels, fp16,
+per-sequence (K, V) bits from {(2,2),(3,3),(4,4),(6,4),(4,8)}, groups of 32,
+16 new tokens per sequence per step (so about half the sequences complete a
+key block on every step). Independent layer caches are rotated where one
+layer is smaller than 4x the 256 MB last-level cache, and the timed steps
+cover whole key-block cycles of every rotated cache. A multi-layer workload
+(the GPT-2 shape, 12 layers) appends into all of them in one
+kvq_quantize_append_layers call and decodes them in one
+kvq_decode_attention_layers call (--per-layer-decode: one of each per layer).
 
 Prints one JSON line: metric/value (decode-step GB/s of algorithmic bytes),
-tokens/s, the decode kernel's roofline (HIP events on the launch stream) and
-the CPU oracle timed on a bounded sample.
+tokens/s, the step's roofline (HIP events on the launch stream, a separate
+loop of at least 20 event-bracketed steps after the wall-clock region) and
+the CPU oracle timed on the host (one core, and all allowed cores).
 """
 
 from __future__ import annotations
@@ -71,9 +74,10 @@ def rotation_for(step_bytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0: 50, or more so that every rotated cache completes a key-block cycle)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama2-7b",
+    ap.add_argument("--workload", default="mixed",
                     choices=["tiny", "gpt2-small", "llama2-7b", "long-gqa", "mixed"])
     ap.add_argument("--rotate", type=int, default=0, help="independent layer caches to cycle through (0 = auto)")
     ap.add_argument("--per-layer-decode", action="store_true",
@@ -81,9 +85,9 @@ def main():
     ap.add_argument("--unfused-step", action="store_true",
                     help="single-layer workloads: kvq_quantize_append then kvq_decode_attention instead of "
                          "kvq_decode_step")
-    ap.add_argument("--event-every", type=int, default=5,
-                    help="bracket the decode calls of every N-th timed step with a HIP event pair (an event pair "
-                         "adds ~6 us of GPU-side gap to its step)")
+    ap.add_argument("--event-steps", type=int, default=0,
+                    help="steps of the event-timed loop after the wall-clock region (0: max(20, steps)); each "
+                         "step's decode call is bracketed by a HIP event pair on the launch stream")
     ap.add_argument("--no-append-timing", action="store_true",
                     help="skip the separately timed appends after the timed region (profiled runs: every append "
                          "after the prefill then belongs to a timed decode step)")
@@ -93,13 +97,14 @@ def main():
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="keys cached before the rotary embedding with this base, rotated inside the decode (0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-sample-seconds", type=float, default=10.0,
+                    help="CPU seconds per oracle leg (one core; all cores)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the all-core oracle leg (0: min(cpu count, 16))")
     ap.add_argument("--probe-reps", type=int, default=30, help="timed repetitions of the streaming-read probe")
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="plain device copy of this size before timing (calibrates HBM byte counters); 0 = none")
     args = ap.parse_args()
-    if args.event_every < 1:
-        ap.error("--event-every must be >= 1")
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -107,12 +112,18 @@ def main():
     import numpy as np
     import torch
 
-    from bit_kv_cache_groupwise_amd import kvq
     from bit_kv_cache_groupwise_amd import workloads as W
+
+    w = W.get(args.workload)
+    # The CPU oracle first: its worker processes are forked before this process
+    # touches the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_seconds, args.window, args.sinks,
+                                                         args.cpu_workers)
+
+    from bit_kv_cache_groupwise_amd import kvq
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = W.get(args.workload)
     ib = 4 if w.in_dtype == "f32" else 2
     S, H, D = w.num_seqs, w.kv_heads, w.head_dim
     n_new = w.new_tokens
@@ -122,9 +133,13 @@ def main():
     step_bytes = sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib, **WS) * H
                      for T, (bk, bv) in zip(step_lens, w.bits)) * model_layers
     rot = args.rotate or rotation_for(step_bytes)
-    # after the timed region: events around the append alone
-    append_timing_steps = 0 if args.no_append_timing else min(10, args.steps)
-    total_steps = args.warmup + args.steps + append_timing_steps
+    # a key block of the cache in tokens; a rotated cache completes one every `cycle` of its appends
+    blk = max([G for axis, G in ((w.axis_k, w.group_k), (w.axis_v, w.group_v)) if axis == 0] or [1])
+    cycle = max(1, math.ceil(blk / n_new))
+    steps = args.steps or max(50, rot * cycle)
+    event_steps = args.event_steps or max(20, steps)
+    append_timing_steps = 0 if args.no_append_timing else min(10, steps)
+    total_steps = args.warmup + steps + event_steps + append_timing_steps
     appends_per_layer = math.ceil(total_steps / rot) + 1
     layers = rot * model_layers
     cap = [L + n_new * appends_per_layer for L in w.lengths]
@@ -147,10 +162,7 @@ def main():
         qz_ms.append(e0.elapsed_time(e1))
         del k, v
     prefill_tokens = sum(w.lengths)
-    qz_bytes = 0
-    for T, (bk, bv) in zip(w.lengths, w.bits):
-        qz_bytes += H * (2 * T * D * ib + algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v,
-                                                                 bk, bv, ib))
+    qz_bytes = sum(H * append_head_bytes(0, T, D, w, bk, bv, ib) for T, (bk, bv) in zip(w.lengths, w.bits))
     quantize_gbps = qz_bytes / (np.median(qz_ms) * 1e-3) / 1e9
 
     # ---- calibration copy: a plain device-to-device copy of known size whose
@@ -211,7 +223,7 @@ def main():
                 dec_events[0][1].record()
             return
         if fused_step and app_events is None:
-            # kvq_decode_step: one launch appends and attends where it can
+            # kvq_decode_step: the append and the attention in one call
             if dec_events is not None:
                 dec_events[0][0].record()
             kvq.kvq_decode_step(cache.handle, base, kp[st], vp[st], counts_c, qp[st], scale, out_p, ws_p, ws_b,
@@ -232,47 +244,65 @@ def main():
             if dec_events is not None:
                 dec_events[m][1].record()
 
-    for st in range(args.warmup):
-        step(st)
-    torch.cuda.synchronize()
-    # the timed region carries one event pair per decode launch (its duration on
-    # the launch stream); the append alone is timed afterwards
-    evs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(args.steps)]
-    # bytes attended in the timed steps (lengths grow by one token per append)
-    lens0 = {l: cache.lengths(l) for l in range(layers)}
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, dec_events=evs[i] if i % args.event_every == 0 else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_s = t1 - t0
-    timed = [i for i in range(args.steps) if i % args.event_every == 0]
-    dec_ms = [evs[i][m][0].elapsed_time(evs[i][m][1]) for i in timed for m in range(dec_per_step)]
-    aevs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(append_timing_steps)]
-    for j in range(append_timing_steps):
-        step(args.warmup + args.steps + j, app_events=aevs[j])
-    torch.cuda.synchronize()
-    app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(dec_per_step)]
-    # algorithmic bytes of every timed decode launch, from the lengths each saw
-    lens = {l: list(v) for l, v in lens0.items()}
-    dec_bytes = []  # per decode call (all model layers of a step when multi)
-    for i in range(args.steps):
-        base = ((args.warmup + i) % rot) * model_layers
-        per_layer = []
+    # host mirror of the lengths, for the algorithmic bytes of every call
+    lens = {l: list(w.lengths) for l in range(layers)}
+
+    def account(st):
+        """(decode bytes, append bytes) of step st's calls, per decode call; advances the mirror."""
+        base = (st % rot) * model_layers
+        dec, app = [], []
         for m in range(model_layers):
             l = base + m
+            app.append(sum(H * append_head_bytes(L, n_new, D, w, bk, bv, ib) for L, (bk, bv) in
+                           zip(lens[l], w.bits)))
             lens[l] = [x + n_new for x in lens[l]]
-            per_layer.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib,
-                                                        **WS) * H for T, (bk, bv) in zip(lens[l], w.bits)))
-        dec_bytes.extend([sum(per_layer)] if multi else per_layer)
-    app_bytes = S * n_new * H * (3 * D * ib + sum(D * bv // 8 + 4 * D // w.group_v for _, bv in w.bits) / S)
-    if args.window or args.sinks:  # the new rows are also copied into the full-precision window
-        app_bytes += S * n_new * H * 4 * D * ib
-    call_bytes = [b + app_bytes for b in dec_bytes] if fused_step else dec_bytes  # what one call moves
-    ev_bytes = [call_bytes[i * dec_per_step + m] for i in timed for m in range(dec_per_step)]  # event-timed calls
-    ms_per_step = wall_s * 1e3 / args.steps
-    step_total_bytes = sum(dec_bytes) / args.steps + app_bytes * model_layers
+            dec.append(sum(algorithmic_head_bytes(T, D, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib,
+                                                  **WS) * H for T, (bk, bv) in zip(lens[l], w.bits)))
+        if args.window or args.sinks:  # the new rows are also copied into the full-precision window
+            app = [a + S * n_new * H * 4 * D * ib for a in app]
+        if multi:
+            return [sum(dec)], [sum(app)]
+        return dec, app
+
+    for st in range(args.warmup):
+        step(st)
+        account(st)
+    torch.cuda.synchronize()
+    # ---- the timed region: `steps` steps, wall clock, no events
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    dec_bytes, app_bytes = [], []
+    for i in range(steps):
+        d, a = account(args.warmup + i)
+        dec_bytes.extend(d)
+        app_bytes.extend(a)
+    # ---- the event-timed loop: every step's decode call bracketed on the launch stream
+    base_st = args.warmup + steps
+    evs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(event_steps)]
+    for j in range(event_steps):
+        step(base_st + j, dec_events=evs[j])
+    torch.cuda.synchronize()
+    dec_ms = [evs[j][m][0].elapsed_time(evs[j][m][1]) for j in range(event_steps) for m in range(dec_per_step)]
+    ev_bytes = []
+    for j in range(event_steps):
+        d, a = account(base_st + j)
+        ev_bytes.extend([x + y for x, y in zip(d, a)] if fused_step else d)
+    # ---- the append alone, for its latency
+    base_st += event_steps
+    aevs = [[[ev(), ev()] for _ in range(dec_per_step)] for _ in range(append_timing_steps)]
+    for j in range(append_timing_steps):
+        step(base_st + j, app_events=aevs[j])
+        account(base_st + j)
+    torch.cuda.synchronize()
+    app_ms = [aevs[j][m][0].elapsed_time(aevs[j][m][1]) for j in range(append_timing_steps) for m in range(dec_per_step)]
+
+    ms_per_step = wall_s * 1e3 / steps
+    step_total_bytes = (sum(dec_bytes) + sum(app_bytes)) / steps
     value = step_total_bytes / (ms_per_step * 1e-3) / 1e9
+    call_bytes = [x + y for x, y in zip(dec_bytes, app_bytes)] if fused_step else dec_bytes
     dec_avg_ms = float(np.mean(dec_ms))
     p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(dec_ms, [10, 50, 90]))
 
@@ -304,25 +334,31 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.in_dtype,
+        "accumulate": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": S, "kv_heads": H, "q_heads": w.q_heads, "head_dim": D,
-                   "cached_tokens": list(sorted(set(w.lengths)))[:4] if len(set(w.lengths)) > 1 else w.lengths[0],
-                   "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step, "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
+                   "cached_tokens": (list(sorted(set(w.lengths)))[:4] + ["..."] if len(set(w.lengths)) > 4 else
+                                     sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
+                   "cached_tokens_total": sum(w.lengths), "new_tokens_per_seq": n_new,
+                   "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step,
+                   "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
                    "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu",
                    **({"full_precision_window": args.window, "sinks": args.sinks} if args.window or args.sinks
                       else {}), **({"rope_base": args.rope_base} if args.rope_base else {})},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
+        "decode_step_bytes": int(step_total_bytes),
         "decode_attention_GBps": round(dec_gbps, 2),
-        "decode_attention_us": round(dec_avg_ms * 1e3, 3),
-        "decode_attention_us_p10_p50_p90": [round(p10, 3), round(p50, 3), round(p90, 3)],
+        "decode_call_us": round(dec_avg_ms * 1e3, 3),
+        "decode_call_us_p10_p50_p90": [round(p10, 3), round(p50, 3), round(p90, 3)],
+        "event_samples": len(dec_ms),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 3) if app_ms else None,
         "quantize_GBps": round(quantize_gbps, 2),
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
@@ -334,15 +370,35 @@ def main():
                                                  + (f"_rope{args.rope_base:g}" if args.rope_base else "")),
                      "kernel": ("kvq_decode_attention_layers" if multi else
                                 "kvq_decode_step (append + decode attention)" if fused_step else "kvq_decode_attention"),
-                     "bytes_per_launch": int(np.mean(call_bytes)),
+                     "bytes_per_launch": int(np.mean(ev_bytes)),
                      "measured_ceiling": {"kernel": "kvq_read_probe", "bytes": probe_bytes,
                                           "GBps": round(ceiling_gbps, 2),
                                           "frac_of_peak": round(ceiling_gbps / HBM_PEAK_GBPS, 4),
                                           "decode_frac_of_ceiling": round(dec_gbps / ceiling_gbps, 4)}},
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds, args.window, args.sinks)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
+
+
+def append_head_bytes(L, n, D, w, bk, bv, ib):
+    """Bytes an append of n tokens to one (seq, kv head) at length L must move:
+    the new rows read; channel-axis tensors: the residual rows a completed block
+    reads back, the codes and (step, zero) pairs of completed blocks and the new
+    rows that stay in the residual written; token-axis tensors: codes and pairs
+    of every new row written."""
+    tot = 0
+    for axis, G, B in ((w.axis_k, w.group_k, bk), (w.axis_v, w.group_v, bv)):
+        tot += n * D * ib
+        if axis == 0:
+            nb = (L + n) // G - L // G
+            if nb:
+                tot += (L % G) * D * ib + nb * (G * D * B // 8 + 4 * D) + ((L + n) % G) * D * ib
+            else:
+                tot += n * D * ib
+        else:
+            tot += n * (D * B // 8 + 4 * (D // G))
+    return tot
 
 
 def kernel_source_hash(sources=None):
@@ -376,26 +432,38 @@ def measured_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s, window=0, sinks=0):
-    """The CPU oracle, untuned, on a bounded sample of the same decode step:
-    for a few sequences it encodes each kv head's cache (quantize + pack),
-    dequantizes in float64 and runs the attention of the head's queries. The
-    rate is the same algorithmic decode bytes per second as the GPU figure."""
-    import numpy as np
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_units(w, seqs, budget_s, window, sinks):
+    """The CPU oracle, untuned, on whole (sequence, kv head) units of one decode
+    step: encode the head's history (quantize + pack + fp64 dequantize), then
+    attend its query heads in fp64. Stops after budget_s seconds of oracle time.
+    Returns (units, algorithmic decode bytes, quantize seconds, attention seconds).
+    Inputs are drawn per sequence (not timed); one BLAS / torch thread."""
     import torch
     from threadpoolctl import threadpool_limits
 
     from bit_kv_cache_groupwise_amd import workloads as W
     from oracle import kvq_oracle as o
 
+    torch.set_num_threads(1)
     ib = 4 if w.in_dtype == "f32" else 2
     R = w.q_heads // w.kv_heads
-    done_bytes = 0
-    heads = 0
-    t_cpu = 0.0
+    units = done = 0
+    tq = ta = 0.0
     with threadpool_limits(limits=1):
-        s = 0
-        while t_cpu < budget_s and s < w.num_seqs:
+        for s in seqs:
+            if tq + ta >= budget_s:
+                break
             T = w.lengths[s] + w.new_tokens
             bk, bv = w.bits[s]
             counts = [0] * w.num_seqs
@@ -404,25 +472,71 @@ def cpu_baseline(w, budget_s, window=0, sinks=0):
             q = W.draw_q(w, 0)[s].double().numpy()
             k = k.float().numpy()
             v = v.float().numpy()
+            kw = dict(group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, bits_k=bk, bits_v=bv)
             for h in range(w.kv_heads):
                 t0 = time.perf_counter()
-                kw = dict(group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, bits_k=bk,
-                          bits_v=bv)
                 if window or sinks:
                     e = o.encode_head_window(k[:, h], v[:, h], window=window, sinks=sinks, **kw)
                 else:
                     e = o.encode_head(k[:, h], v[:, h], **kw)
+                t1 = time.perf_counter()
                 o.attend(q[h * R:(h + 1) * R], e["k_hat"], e["v_hat"], w.softmax_scale)
-                t_cpu += time.perf_counter() - t0
-                done_bytes += algorithmic_head_bytes(T, w.head_dim, w.axis_k, w.axis_v, w.group_k, w.group_v,
-                                                     bk, bv, ib, window, sinks)
-                heads += 1
-                if t_cpu >= budget_s:
+                t2 = time.perf_counter()
+                tq += t1 - t0
+                ta += t2 - t1
+                done += algorithmic_head_bytes(T, w.head_dim, w.axis_k, w.axis_v, w.group_k, w.group_v, bk, bv, ib,
+                                               window, sinks)
+                units += 1
+                if tq + ta >= budget_s:
                     break
-            s += 1
-    return {"value": round(done_bytes / t_cpu / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} (seq, kv head) caches of {w.name}: quantize+pack, fp64 dequantize, fp64 attention",
-            "seconds": round(t_cpu, 2)}
+    return units, done, tq, ta
+
+
+def _oracle_worker(a):
+    return _oracle_units(*a)
+
+
+def cpu_baseline(w, budget_s, window=0, sinks=0, workers=0):
+    """The CPU oracle as it stands, timed on the host: on one core for about
+    budget_s seconds, and on all allowed cores (forked worker processes, one
+    thread each, sequences dealt round-robin) for about budget_s seconds each.
+    The rate is the same algorithmic decode bytes per second as the GPU figure;
+    quantize (encode) and attention seconds are reported apart."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+
+    order = [int(x) for x in np.random.Generator(np.random.PCG64(7)).permutation(w.num_seqs)]
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    nw = workers or max(1, min(allowed, 16))
+    # all cores first: the pool forks before this process has run any threaded work
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=nw, mp_context=mp.get_context("fork")) as ex:
+        parts = list(ex.map(_oracle_worker, [(w, order[i::nw], budget_s, window, sinks) for i in range(nw)]))
+    wall = time.perf_counter() - t0
+    mu = sum(p[0] for p in parts)
+    mb = sum(p[1] for p in parts)
+    mq = sum(p[2] for p in parts)
+    ma = sum(p[3] for p in parts)
+    u1, b1, q1, a1 = _oracle_units(w, order, budget_s, window, sinks)
+    total_units = w.num_seqs * w.kv_heads
+    return {"value": round(mb / wall / 1e9, 6), "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "sample": f"{mu} of the {total_units} (seq, kv head) units of one {w.name} decode step"
+                      f"{' (the whole step)' if mu == total_units else ''} on {nw} worker processes (1 thread each), "
+                      f"{u1} units on one core: quantize + pack + fp64 dequantize, fp64 attention",
+            "seconds": round(wall, 2),
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "allowed_cpus": allowed,
+            "all_cores": {"GBps": round(mb / wall / 1e9, 6), "units": mu, "wall_s": round(wall, 2),
+                          "quantize_s_per_unit": round(mq / max(mu, 1), 4),
+                          "attention_s_per_unit": round(ma / max(mu, 1), 4)},
+            "single_core": {"GBps": round(b1 / max(q1 + a1, 1e-9) / 1e9, 6), "units": u1,
+                            "quantize_s": round(q1, 2), "attention_s": round(a1, 2),
+                            "quantize_s_per_unit": round(q1 / max(u1, 1), 4),
+                            "attention_s_per_unit": round(a1 / max(u1, 1), 4)}}
 
 
 if __name__ == "__main__":
