@@ -229,10 +229,13 @@ int choose_split_mha(const kvq_cache* c, int max_len, int n_layers) {
 }
 
 // Tokens per workgroup of the query-group kernel (a multiple of 128, at least
-// 512). One launch per (bits_k, bits_v) pair; each launch runs its workgroups
-// in rounds of the resident count (three 64-channel waves per SIMD, head_dim/64
-// waves per workgroup). The choice minimises sum over launches of
-// rounds * (tokens per workgroup + a fixed per-workgroup cost of 128 tokens).
+// 512). One launch over every bit pair (one per pair for batches beyond the
+// work list's size); a launch runs its workgroups
+// in rounds of the resident count (4-wave workgroups, one wave per SIMD each;
+// three per compute unit, two for head_dim 256). The choice minimises sum over launches of rounds *
+// (tokens per workgroup + a fixed per-workgroup cost of 512 tokens: loading
+// the queries, merging the waves and writing a split partial that the merge
+// reads back).
 // lens: [n_layers][num_seqs], the layers of one launch.
 int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
     const kvq_geometry& g = c->g;
@@ -240,19 +243,22 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
         const int v = std::atoi(env);
         if (v >= 128 && v % 128 == 0 && v <= (1 << 24)) return v;
     }
-    const long slots = 3L * 1024 / std::max(1, g.head_dim / 64);
+    const long slots = 256L * (g.head_dim >= 256 ? 2 : 3);
+    const bool one_launch = (long)n_layers * g.num_seqs <= kvq::kGqaListMax;
     long best_cost = -1;
     int best = 512;
-    for (int cw : {512, 640, 768, 896, 1024, 1280, 1536, 2048, 3072, 4096}) {
-        long cost = 0;
+    for (int cw : {512, 640, 768, 896, 1024, 1280, 1536, 2048, 2560, 3072, 4096, 6144, 8192}) {
+        long cost = 0, all = 0;
         for (const auto& pr : c->pairs) {
             long wgs = 0;
             for (int l = 0; l < n_layers; ++l)
                 for (int i = 0; i < pr.count; ++i)
                     wgs += (lens[(size_t)l * g.num_seqs + c->pair_list[pr.offset + i]] + cw - 1) / cw;
-            wgs *= g.kv_heads;
-            cost += (wgs + slots - 1) / slots * (cw + 128);
+            wgs *= (long)g.kv_heads * ((group_size(c) + 15) / 16);
+            cost += (wgs + slots - 1) / slots * (cw + 512);
+            all += wgs;
         }
+        if (one_launch) cost = (all + slots - 1) / slots * (cw + 512);
         if (best_cost < 0 || cost < best_cost) best_cost = cost, best = cw;
     }
     return best;
@@ -573,8 +579,6 @@ struct StepOpts {
 kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, const void* q, float softmax_scale,
                          float* out, void* workspace, size_t workspace_bytes, void* stream, const StepOpts& opt = {}) {
     const kvq_geometry& g = c->g;
-    if (group_size(c) > kvq::kMaxQueryGroup)
-        return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d", group_size(c), kvq::kMaxQueryGroup);
     if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
     const bool rope = g.rope_base > 0.0;
     if (rope && (g.axis_k != KVQ_AXIS_CHANNEL || win_mode(g)))
@@ -592,10 +596,12 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     // rotary keys: the generic split kernel
     const bool mha = !rope && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
-    bool gqa = !rope && group_size(c) > 1 && group_size(c) <= 16 && g.axis_k == KVQ_AXIS_CHANNEL &&
-               kvq::mha_supported(g.head_dim);
-    for (const auto& pr : c->pairs)  // a lane's key channels must start on a word boundary
-        gqa = gqa && (g.head_dim * pr.bk) % 128 == 0;
+    bool gqa = !rope && group_size(c) > 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
+    for (const auto& pr : c->pairs)  // head_dim 64: a lane group's half unit of key codes must be whole words
+        gqa = gqa && (g.head_dim >= 128 || pr.bk % 2 == 0);
+    if (!mha && !gqa && group_size(c) > kvq::kMaxQueryGroup)
+        return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d on the generic decode kernel",
+                    group_size(c), kvq::kMaxQueryGroup);
     const int C = mha   ? choose_split_mha(c, max_len, n_layers)
                   : gqa ? choose_split_gqa(c, lens, n_layers)
                         : choose_chunk(c, max_len, n_layers);
@@ -683,10 +689,43 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         return KVQ_OK;
     }
     if (gqa) {
-        for (const auto& pr : c->pairs) {
-            a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
-            hipError_t e = kvq::launch_decode_gqa(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
-            if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+        if ((long)n_layers * S <= kvq::kGqaListMax) {
+            // one launch over every bit pair: the active (layer, seq) entries in
+            // bit-pair order, each with its splits x kv heads x query groups
+            kvq::GqaList list;
+            list.count = 0;
+            int items = 0;
+            const int nh = g.kv_heads * ((group_size(c) + 15) / 16);
+            for (const auto& pr : c->pairs)
+                for (int l = 0; l < n_layers; ++l)
+                    for (int i = 0; i < pr.count; ++i) {
+                        const int s2 = c->pair_list[pr.offset + i];
+                        int tb = 0, te = lens[(size_t)l * S + s2];
+                        if (win_mode(g)) {
+                            const int r = te - g.window, blk = token_block(g);
+                            const int q = r > 0 ? r / blk * blk : 0;
+                            tb = g.sinks;
+                            te = std::max(q, g.sinks);
+                        }
+                        const int nsplit = te > tb ? (te - tb + C - 1) / C : 0;
+                        if (!nsplit) continue;
+                        list.start[list.count] = items;
+                        list.seq[list.count] = (uint16_t)s2;
+                        list.layer[list.count] = (uint8_t)l;
+                        ++list.count;
+                        items += nsplit * nh;
+                    }
+            list.start[list.count] = items;
+            if (items > 0) {
+                hipError_t e = kvq::launch_decode_gqa_list(a, list, items, (hipStream_t)stream);
+                if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+            }
+        } else {
+            for (const auto& pr : c->pairs) {
+                a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
+                hipError_t e = kvq::launch_decode_gqa(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
+                if (e != hipSuccess) return hip_fail(e, "launching decode attention");
+            }
         }
         a.split_floor = 0;
         hipError_t e = kvq::launch_merge(a, (hipStream_t)stream);

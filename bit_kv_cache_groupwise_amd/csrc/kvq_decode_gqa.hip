@@ -1,44 +1,53 @@
-// Decode attention for query groups (q_heads / kv_heads = R in 2..16): the R
+// Decode attention for query groups (q_heads / kv_heads = R >= 2): the R
 // queries that share a kv head turn the decode step into a small dense
-// contraction, so both products run on MFMA (v_mfma_f32_16x16x32_f16) with the
-// packed codes as exact fp16 operands. Keys on the channel axis, values on the
-// token axis.
+// contraction, so both products run on MFMA (v_mfma_f32_16x16x32_f16) with
+// the packed codes as exact fp16 operands. Keys on the channel axis, values on
+// the token axis.
 //
 // Sources, by page title and section:
 //   [N] nalar.dev, "Kuantisasi KV cache untuk mengurangi memory inferensi
 //       long-context", "Kuantisasi dapat memindahkan pekerjaan ke decode path"
+//       (unpack and apply the scales inside the attention kernel)
 //   [N] same page, "Ukuran cache bertambah mengikuti token, layer, dan KV head"
 //       (grouped-query attention shares kv heads among query heads)
+//   [U] unite.ai (pt), "Por Que o Cache KV E Onde Isso Morde" (decode reads the
+//       whole cache once per generated token)
 //
-// Work decomposition: workgroup = (split of the token axis, kv head, seq); its
-// waves share every 32-token tile, wave w owning 64 of the head's channels
-// (128 for 3-bit keys). Per tile a wave computes
-//   partial scores^T[t][r] = 2^16 * sum_c A[t][c] B[c][r] + bias[r] over its channels,
-//     A = key codes of token t as fp16 values (code << sh) * 2^-24, unpacked
-//         from the lane's own row words (exact),
-//     B = q'_rc * s_c in fp16 hi + lo parts (two MFMAs), where q' carries the
-//         2^(8-sh) that undoes the code shift,
-//     bias[r] = sum_c q_rc z_c on the VALU;
-//   the waves' partial scores are summed through LDS (one barrier per tile);
-//   O[r][c]  += 2^(24-kb-sh) * sum_t (2^kb p_rt s_t,g(c))[hi + lo] V[t][c],
-//     kb = the wave's running value-product exponent (at most BV + 2, lowered
-//     when a tile's largest value step would push 2^kb p s past 2^15),
-//     V = value codes as fp16 values (code << sh) * 2^-24, from an LDS byte tile;
-//   Z[r][g]  += 2^-KZ * sum_t (2^KZ p_rt)[hi + lo] * (z_t,g | 1),
-//     one MFMA against a [token][group] fragment of zero points whose column
-//     after the last group is 1, so it also yields the softmax denominator.
-// The score layout (lane: 1 query x 8 consecutive tokens) is the operand layout
-// the value products need for P, so softmax weights never leave registers.
+// Work decomposition: workgroup = (split of the token axis, (kv head, group of
+// up to 16 of its query heads), seq), 4 waves. The waves take interleaved
+// 32-token tiles and never exchange data inside the loop: each keeps its own
+// running maximum, denominator and output rows for the 16 query rows (zero
+// padded), and the four are merged once at the end, in LDS, in a fixed order.
 //
-// Pipeline: the next tile's codes and metadata are loaded into registers as
-// soon as the current ones are consumed (value words after they are staged in
-// LDS, key words after the score MFMAs), so every wave keeps one tile in
-// flight while it computes the current one.
+// Per tile and wave (lane l: n = l % 16, g = l / 16):
+//   scores^T[t][r] = 2^16 sum_c A[t][c] B[c][r] + bias[r]
+//     A = key codes of token t as fp16 values (code << sh) 2^-24, unpacked from
+//         the lane's own row words (exact); lane group g holds a quarter of
+//         the channels, of token rows t0 + 8(m >> 2) + 4h + (m & 3) (h = 0, 1);
+//     B = q'_rc s_c in fp16 hi + lo parts (two MFMAs), q' = q * softmax scale *
+//         log2(e) * 2^(8 - sh), built per tile from q' in LDS and the block's
+//         steps staged in LDS; bias[r] = sum_c q'_rc z_c on the VALU;
+//   the score layout (lane: query n, 8 consecutive tokens 8g..8g+7) is the
+//   A-operand layout of the value product, so softmax weights stay in place;
+//   O[r][c] += 2^(24-kb-vsh) sum_t (2^kb p_rt s_t,g(c))[hi + lo] V[t][c],
+//     V = value codes of the tile staged in LDS as one byte per code
+//         [token][channel]; ds_read_b64_tr_b8 hands lane n the tokens
+//         8g..8g+7 of one channel (the B-operand layout), and v_perm turns two
+//         bytes into two fp16 (code << vsh) 2^-24;
+//   Z[r][k] += 2^-KZ sum_t (2^KZ p_rt)[hi + lo] (z_t,k | 1): zero-point sums per
+//     value group and, in the column after the last group, the denominator.
 //
-// Softmax: online in the log2 domain with the exact running maximum, so
-// weights are <= 1; they enter the fp16 operands pre-scaled by powers of two
-// (2^(BV+2) for p * s, 2^14 for the zero-point / denominator product) so that
-// small weights keep full fp16 precision. Splits are merged by merge_kernel.
+// Softmax: online in the log2 domain with the exact running maximum, so weights
+// are <= 1. They enter the fp16 operands pre-scaled by powers of two: 2^kb for
+// p * s (kb <= BV + 2, lowered per tile when large value steps would push
+// 2^kb p s past 2^15; the accumulators are rescaled exactly), 2^KZ for the zero
+// points. q' is kept below 2^14 by a power of two per workgroup, and the key
+// weights q' s of a block whose steps would push them past 2^15 are scaled by
+// 2^-f. Splits are merged by merge_kernel.
+//
+// Pipeline: one tile of codes and metadata in registers per wave: the value and
+// metadata words of tile i + 4 are requested as soon as tile i's are staged in
+// LDS, its key words as soon as tile i's key products are issued.
 #include <utility>
 
 #include "kvq_device.h"
@@ -51,6 +60,7 @@ using namespace dev;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 union Frag {
     half8_t h;
@@ -123,16 +133,18 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
     lo = pk_rtz(rem_lo(hi, x0), rem_hi(hi, x1));
 }
 
-// Integer codes enter the MFMAs as fp16 values code * 2^(sh-24): subnormals,
-// or normals of exponent 1, where the value is still (code << sh) * 2^-24.
-// The MFMA's sum of products loses low bits of products whose subnormal
-// operand uses only the bottom of the mantissa, so every code is shifted until
-// its top bit reaches bit 9 or 10 (code << sh < 2048): sh = code_shift(B).
-__host__ __device__ constexpr int code_shift(int B) { return B == 2 ? 9 : B == 3 ? 8 : B == 4 ? 7 : B == 6 ? 5 : 3; }
+// Integer codes enter the MFMAs as fp16 values (code << sh) 2^-24: subnormals,
+// or normals of exponent 1, where the value is still linear in the bit pattern
+// (below 2048). The MFMA's sum of products loses low bits of products whose
+// subnormal operand uses only the bottom of the mantissa, so every code is
+// shifted until its top bit reaches mantissa bit 9 or 10.
+__host__ __device__ constexpr int key_shift(int B) { return B == 2 ? 9 : B == 3 ? 8 : B == 4 ? 7 : B == 6 ? 5 : 3; }
+// Value codes come out of LDS one byte each; 2- and 3-bit codes go to the high
+// byte of a half (one v_perm per pair, no shift).
+__host__ __device__ constexpr int val_shift(int B) { return B <= 3 ? 8 : B == 4 ? 7 : B == 6 ? 5 : 3; }
 
-// Key-code fragments: chunk k of a lane's channel range (8 channels) as 8 fp16
-// halves. Half j of the fragment holds channel 8k + PERM[j] of the range as the
-// integer code << code_shift(B).
+// Key-code fragments: 8-code chunk K of a lane's code range as 8 fp16 halves.
+// Half j of the fragment holds code 8K + PERM[j] of the range as code << key_shift(B).
 template <int B>
 struct KeyFrag;
 
@@ -189,7 +201,7 @@ __device__ __forceinline__ uint32_t unit_code(const uint32_t* w) {
 template <int B>
 struct KeyFragStraddle {
     static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
-    static constexpr int SH = code_shift(B);
+    static constexpr int SH = key_shift(B);
     template <int K>
     static __device__ __forceinline__ void get(const uint32_t* w, Frag& f) {
         // chunk K covers codes 8K..8K+7 of the lane's range; a 32-code unit is B words
@@ -242,10 +254,7 @@ __device__ __forceinline__ int val_chan(int p) {
     else return p;
 }
 
-// N consecutive words from p, whose byte address is a multiple of ALIGN. Plain
-// loads, not the non-temporal streaming ones: the waves of a workgroup read
-// different channel slices of the same cache lines, and the hint made those
-// lines miss for the later waves (~20% slower on a 262k-token query group).
+// N consecutive words from p, whose byte address is a multiple of ALIGN.
 template <int N, int ALIGN>
 __device__ __forceinline__ void load_n(const uint32_t* p, uint32_t* w) {
     if constexpr (ALIGN >= 16 && N % 4 == 0) {
@@ -265,25 +274,12 @@ __device__ __forceinline__ void load_n(const uint32_t* p, uint32_t* w) {
         for (int k = 0; k < N; ++k) w[k] = p[k];
     }
 }
-template <int N>
-__device__ __forceinline__ void store_lds_n(uint32_t* p, const uint32_t* w) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int k = 0; k < N / 4; ++k) ((uint4*)p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int k = 0; k < N / 2; ++k) ((uint2*)p)[k] = make_uint2(w[2 * k], w[2 * k + 1]);
-    } else {
-        p[0] = w[0];
-    }
-}
 
 constexpr int pow2_align(int bytes) { return (bytes & 15) == 0 ? 16 : (bytes & 7) == 0 ? 8 : (bytes & 3) == 0 ? 4 : 1; }
+constexpr int min_align(int a, int b) { return a < b ? a : b; }
 
 // Sums and maxima over the 4 lanes that share l % 16 (lanes l, l^16, l^32, l^48),
-// with the row-swap permutes (no LDS round trip): after permlane16_swap(v, v)
-// the two results hold rows (0,0,2,2) and (1,1,3,3); after permlane32_swap(v, v)
-// they hold halves (lo, lo) and (hi, hi).
+// with the row-swap permutes.
 __device__ __forceinline__ float col4_sum(float v) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -297,12 +293,32 @@ __device__ __forceinline__ float col4_max(float v) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// LDS writes of this wave visible to this wave (each wave owns its tile areas).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+__device__ __forceinline__ void wg_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
+// Largest value over the wave of a BITS-bit unsigned field (scalar result:
+// binary search over ballots).
+template <int BITS>
+__device__ __forceinline__ int wave_max_field(int e) {
+    int emax = 0;
+#pragma unroll
+    for (int b = 1 << (BITS - 1); b; b >>= 1)
+        if (__builtin_amdgcn_ballot_w64(e >= emax + b)) emax += b;
+    return emax;
+}
+
+__device__ __forceinline__ float load_in_rt(const void* p, size_t i, int dt) {
+    return dt == 0 ? load_in<0>(p, i) : dt == 1 ? load_in<1>(p, i) : load_in<2>(p, i);
+}
 template <int DT>
 __device__ __forceinline__ void load8_in(const void* p, size_t i, float* v) {
 #pragma unroll
@@ -314,65 +330,79 @@ __device__ __forceinline__ void load8_rt(const void* p, size_t i, int dt, float*
     else load8_in<2>(p, i, v);
 }
 
-constexpr float kTwo16 = 65536.0f;
-constexpr float kTwo24 = 16777216.0f;
-constexpr float kFarBelow = -1.0e30f;  // initial reference maximum: exp2(score - kFarBelow) never taken
-
-// Channels per wave: the workgroup's waves share each tile, wave w taking
-// channels [w*DW, (w+1)*DW) of the head. A lane group of a wave must own whole
-// key words, so 3-bit keys take 128 channels per wave.
-template <int BK>
-constexpr int wave_channels() { return BK == 3 ? 128 : 64; }
-
-__device__ __forceinline__ void wg_lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// fp16 bit pattern of 2^-k (k >= 0; normal, subnormal, or 0 below 2^-24).
+__device__ __forceinline__ uint32_t f16_pow2_neg(int k) {
+    return k <= 14 ? (uint32_t)(15 - k) << 10 : k <= 24 ? 1u << (24 - k) : 0u;
 }
 
-// Three waves per SIMD for 64-channel waves (registers capped at 168, no
-// spills); 128-channel waves need more and run two.
+constexpr float kFarBelow = -1.0e30f;  // initial maximum: exp2(score - kFarBelow) is never taken
+
+// Byte layout of the workgroup's LDS. Loop-time areas: q' (fp32, natural
+// channel order), q' as fp16 pairs in key-fragment order, and per wave the key
+// steps / zero points of its tile's block (fp16 pairs, fragment order), the
+// value code bytes [token][position], value steps [group][token] and the
+// zero-point fragment rows [row][token]. After the loop the same bytes hold the
+// four waves' output rows and their (m, l) for the merge.
+template <int D>
+struct Lds {
+    static constexpr int U = D / 32;
+    static constexpr int VROW = D + 16;  // bytes per token row of the value tile (padded)
+    static constexpr int ZROW = 40;      // halves per row of the zero-point fragment (padded)
+    // q' rows padded by 4 words: the 8 lanes of a 16-byte LDS read (rows n..n+7)
+    // then fall on different banks
+    static constexpr int QFS = D + 4;      // floats per q' row
+    static constexpr int QHS = D / 2 + 4;  // fp16 pairs per q' row
+    static constexpr int QF = 0;
+    static constexpr int QH = QF + 16 * QFS * 4;
+    static constexpr int RED = QH + 16 * QHS * 4;  // 4 ints: per-wave exponent maxima
+    static constexpr int WAVE0 = RED + 16;
+    static constexpr int SP = 0, ZP = SP + D * 2, VT = ZP + D * 2, ST = VT + 32 * VROW, ZT = ST + U * 32 * 2;
+    static constexpr int WAVE = ZT + 16 * ZROW * 2;
+    static constexpr int LOOP = WAVE0 + 4 * WAVE;
+    static constexpr int MO = 0, ML = 4 * 16 * D * 4;
+    static constexpr int MERGE = ML + 4 * 16 * 2 * 4;
+    static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
+    static_assert(WAVE % 16 == 0 && WAVE0 % 16 == 0 && VT % 16 == 0 && ST % 16 == 0 && ZT % 16 == 0, "LDS alignment");
+};
+
+// One workgroup's work: split `split` of the quantized tokens of (seq, kv head
+// hy / nqg, query rows 16 (hy % nqg) ..), with the layer's arguments `a`.
 template <int D, int BK, int BV>
-__global__ __launch_bounds__(D / wave_channels<BK>() * 64)
-__attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void decode_gqa_kernel(DecodeArgs a0) {
-    int z = blockIdx.z;
-    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
-    constexpr int DW = wave_channels<BK>();  // channels of this wave
-    constexpr int NWV = D / DW;               // waves per workgroup (they share every tile)
-    constexpr int NT = 64 * NWV;
-    constexpr int DQ = DW / 4;                // key channels of one lane group (lg)
-    constexpr int NCH = DQ / 8;               // 8-channel MFMA chunks per lane group
-    constexpr int NSUB = DW / 16;             // 16-column output tiles of the wave
-    constexpr int KWL = DQ * BK / 32;         // key words of a lane per token
-    constexpr int VROW = DW + 8;              // bytes per token row of the wave's value tile
-    constexpr int UPW = DW / 32;              // value units of the wave per token
-    constexpr int UPL = UPW / 2;              // value units per lane per tile (32 tokens)
-    constexpr int NVML = DW / 64;             // value metadata words per lane per tile
-    constexpr int ZROW = 40;                  // halves per row of the zero-point tile (padded)
-    constexpr int KALIGN = pow2_align(D * BK / 8) < pow2_align(KWL * 4) ? pow2_align(D * BK / 8) : pow2_align(KWL * 4);
-    constexpr int VALIGN = pow2_align(D * BV / 8) < pow2_align(BV * 4) ? pow2_align(D * BV / 8) : pow2_align(BV * 4);
-    constexpr int KSH = code_shift(BK), VSH = code_shift(BV);
-    // Softmax weight scales (p <= 1): 2^kb p * s with kb <= KB = BV + 2 keeps
-    // small weights normal in fp16; kb drops below KB where a tile's value
-    // steps are large (running_value_exponent), so that 2^kb p s < 2^15;
-    // 2^KZ p <= 16384.
+__device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int seq, int hy, int split) {
+    constexpr int U = D / 32;                      // 32-channel units per row
+    constexpr int KU = U >= 4 ? U / 4 : 1;         // key units per lane group (head_dim 64: half a unit)
+    constexpr int KWL = U >= 4 ? KU * BK : BK / 2; // key words per lane and token
+    constexpr int NCH = U;                         // 8-code key chunks per lane and token
+    constexpr int NOT = 2 * U;                     // 16-channel output tiles
+    constexpr int VRB = D * BV / 8;                // bytes of a value row
+    constexpr int VUL = U / 2;                     // value units per lane (half a row)
+    constexpr int VWL = VUL * BV;                  // value words per lane
+    constexpr int NKP = D / 2 > 64 ? D / 128 : 1;  // key step pairs per lane per block
+    constexpr int NVML = U / 2 > 1 ? U / 2 : 1;    // value metadata words per lane per tile
+    constexpr int KSH = key_shift(BK), VSH = val_shift(BV);
     constexpr int KB = BV + 2, KZ = 14;
-    constexpr int XS = 2 * NWV * 64 * 8 > NWV * 16 * DW ? 2 * NWV * 64 * 8 : NWV * 16 * DW;
+    constexpr int KLOFF = U >= 4 ? KU * BK * 4 : 2 * BK;  // byte offset between lane groups' key words
+    constexpr int KALIGN = min_align(pow2_align(D * BK / 8), pow2_align(KLOFF));
+    constexpr int VALIGN = pow2_align(VRB / 2);
     using KF = KeyFrag<BK>;
-    static_assert(KWL * 32 == DQ * BK, "lane key range must be whole words");
-    static_assert(UPL >= 1 && NVML >= 1, "wave tile shape");
+    using L = Lds<D>;
+    static_assert(U >= 4 || BK % 2 == 0, "head_dim 64 needs even key bits (half a unit per lane group)");
 
-    // Key pairs follow the fragment order: dword 4w + jj of a wave row holds
-    // channels 8w + PERM[2jj] (low half) and 8w + PERM[2jj+1] (high half).
-    __shared__ __align__(16) float xbuf[XS];                   // partial scores [2][NWV][64][8]; output staging
-    __shared__ __align__(16) uint32_t sp_lds[NWV][DW / 2];     // key scales of the tile's block, fp16 pairs
-    __shared__ __align__(16) uint32_t zp_lds[NWV][DW / 2];     // key zero points, fp16 pairs
-    __shared__ __align__(16) uint8_t vt_lds[NWV][32 * VROW];  // value codes of the tile, one byte each
-    __shared__ __align__(16) uint16_t st_lds[NWV][4][32];     // value scales [group][token]
-    __shared__ __align__(16) uint16_t zt_lds[NWV][16][ZROW];  // value zero points [group][token]; row G = 1.0
+    float* qf_lds = (float*)(smem + L::QF);
+    uint32_t* qh_lds = (uint32_t*)(smem + L::QH);
 
-    const int seq = a.seq_list ? a.seq_list[z] : z;
-    const int kvh = blockIdx.y, split = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    uint8_t* wbase = smem + L::WAVE0 + wave * L::WAVE;
+    uint32_t* sp_lds = (uint32_t*)(wbase + L::SP);
+    uint32_t* zp_lds = (uint32_t*)(wbase + L::ZP);
+    uint8_t* vt_lds = wbase + L::VT;
+    uint16_t* st_lds = (uint16_t*)(wbase + L::ST);
+    uint16_t* zt_lds = (uint16_t*)(wbase + L::ZT);
+
+    const int R = a.q_heads / a.kv_heads;
+    const int nqg = (R + 15) >> 4;
+    const int kvh = hy / nqg, q0 = (hy - kvh * nqg) * 16;
+    const int RQ = min(16, R - q0);  // query rows of this workgroup
     const int len = a.len[seq];
     // Quantized tokens [tb, te): all of them, or with a full-precision window
     // the whole key blocks inside [sinks, len - window).
@@ -382,20 +412,13 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     const int wa = tb + split * CW;
     if (wa >= te) return;  // merge_kernel sees ceil((te - tb) / CW) splits
     const int wb = min(wa + CW, te);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int ln = lane & 15, lg = lane >> 4;
-    const int cw0 = wave * DW;  // first channel of this wave
-    const int R = a.q_heads / a.kv_heads;
     const SeqEntry& e = a.table[seq];
     const int lgk = a.log2_group_k, lgv = a.log2_group_v;
     const int Gk = 1 << lgk;
     const int nqk = a.win_mode ? te : (len >> lgk) << lgk;  // tokens read with quantized keys
-    const int qend = min(wb, nqk);
-    const int vgpr = D >> lgv;            // value groups per token
-    const int g0 = cw0 >> lgv;            // first value group of this wave
-    const int ngw = lgv <= 5 + __builtin_ctz(UPW) ? DW >> lgv : 1;  // value groups of this wave
-    const int lng = __builtin_ctz(ngw);
-    const int bpg = lgv - 5;              // log2 of 32-channel blocks per value group
+    const int ngrp = D >> lgv;                              // value groups per token
+    const int lng = __builtin_ctz(ngrp);
+    const int tpg = lgv >= 4 ? 1 << (lgv - 4) : 1;          // 16-channel output tiles per value group
 
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
     const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
@@ -403,215 +426,246 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
     const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
 
-    // ---- query ln of this kv head, channels cw0 + lg*DQ + [0, DQ), in registers:
-    // q' = q * scale * 2^(8 - KSH) and its fp16 pairs in fragment order
-    float qf[DQ];
-    uint32_t qh[DQ / 2];
+    // ---- one tile of codes and metadata in registers
+    uint32_t kw[2][KWL];    // key words: token rows 8(n>>2) + 4h + (n&3), lane group g's channels
+    uint32_t kmw[2 * NKP];  // key (step, zero) words of the lane's fragment pairs
+    uint32_t vw[VWL];       // value words: token row lane >> 1, half lane & 1
+    uint32_t vmw[NVML];     // value (step, zero) words
+
+    // channel block (8 channels) of lane group g, chunk c
+    auto cbase = [&](int c) -> int {
+        if constexpr (U >= 4) return 32 * (g * KU + c / 4) + 8 * (c % 4);
+        else return 32 * (g >> 1) + 16 * (g & 1) + 8 * c;
+    };
+    auto load_keys = [&](int t0) {
+        const int wo = U >= 4 ? g * KU * BK : (g >> 1) * BK + (g & 1) * (BK / 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), nqk - 1);
+            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + wo, kw[h]);
+        }
+    };
+    auto load_kmeta = [&](int t0) {
+        const uint32_t* src = km + (size_t)(t0 >> lgk) * D;
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+            const int p = min(lane + 64 * k, D / 2 - 1), cb = (p >> 2) * 8, jj = p & 3;
+            int c0 = 0, c1 = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (jj == q) c0 = KF::PERM[2 * q], c1 = KF::PERM[2 * q + 1];
+            kmw[2 * k] = src[cb + c0];
+            kmw[2 * k + 1] = src[cb + c1];
+        }
+    };
+    auto load_values = [&](int t0) {
+        const int t = min(t0 + (lane >> 1), wb - 1);
+        load_n<VWL, VALIGN>((const uint32_t*)(vc + (size_t)t * VRB + (lane & 1) * (VRB / 2)), vw);
+#pragma unroll
+        for (int k = 0; k < NVML; ++k) {
+            const int f = min(lane + 64 * k, 32 * ngrp - 1);
+            const int tt = min(t0 + (f >> lng), wb - 1);
+            vmw[k] = vm[(size_t)tt * ngrp + (f & (ngrp - 1))];
+        }
+    };
+
+    // the first tile's loads go out before the query setup, whose latency they share
+    const int ntiles = (wb - wa + 31) >> 5;
+    int i = wave;
+    if (i < ntiles) {
+        const int t0 = wa + 32 * i;
+        load_values(t0);
+        if (t0 < nqk) {
+            load_kmeta(t0);
+            load_keys(t0);
+        }
+    }
+    // ---- q' rows of this workgroup (rows >= RQ are 0), kept below 2^14 by
+    // 2^-eqs: fp32 in natural channel order, and fp16 pairs in key-fragment order
+    // (8-channel block cb: pair jj = channels cb + PERM[2jj], cb + PERM[2jj + 1])
+    int eqs, eq;
     {
-        const size_t qrow = ((size_t)seq * a.q_heads + kvh * R + min(ln, R - 1)) * D + cw0 + lg * DQ;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) load8_rt(a.q, qrow + 8 * k, a.in_dtype, qf + 8 * k);
-#pragma unroll
-        for (int j = 0; j < DQ; ++j) qf[j] = ln < R ? qf[j] * a.qscale * ((float)(1 << 8) / (float)(1 << KSH)) : 0.f;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                qh[4 * k + jj] = pk_rtz(qf[8 * k + KF::PERM[2 * jj]], qf[8 * k + KF::PERM[2 * jj + 1]]);
+        const float qs = a.qscale * ((float)(1 << 8) / (float)(1 << KSH));
+        const size_t qrow0 = ((size_t)seq * a.q_heads + kvh * R + q0) * D;
+        float qm = 0.f;
+        for (int i = tid; i < 16 * D; i += 256) {
+            const int r = i / D;
+            const float v = r < RQ ? load_in_rt(a.q, qrow0 + i, a.in_dtype) * qs : 0.f;
+            qf_lds[r * L::QFS + (i - r * D)] = v;
+            qm = fmaxf(qm, fabsf(v));
+        }
+        int* red = (int*)(smem + L::RED);
+        const int e8w = wave_max_field<8>((int)(__float_as_uint(qm) >> 23));
+        if (lane == 0) red[wave] = e8w;
+        __syncthreads();
+        const int e8 = max(max(red[0], red[1]), max(red[2], red[3]));  // |q'| < 2^(e8 - 126)
+        eqs = max(0, e8 - 140);
+        eq = e8 - eqs;
+        if (eqs) {
+            const float f = __builtin_amdgcn_ldexpf(1.0f, -eqs);
+            for (int i = tid; i < 16 * D; i += 256) qf_lds[(i / D) * L::QFS + i % D] *= f;
+            __syncthreads();
+        }
+        for (int i = tid; i < 16 * D / 2; i += 256) {
+            const int r = i / (D / 2), p = i % (D / 2), cb = (p >> 2) * 8, jj = p & 3;
+            const float* qr = qf_lds + r * L::QFS + cb;
+            qh_lds[r * L::QHS + p] = pk_rtz(qr[KF::PERM[2 * jj]], qr[KF::PERM[2 * jj + 1]]);
+        }
     }
-    // constant rows of the zero-point fragment: 1.0 in row ngw, 0 above it
-    for (int i = lane; i < 16 * 32; i += 64) {
-        const int g = i >> 5;
-        if (g >= ngw) zt_lds[wave][g][i & 31] = g == ngw ? (uint16_t)0x3c00u : (uint16_t)0u;
+    // constant rows of the zero-point fragment: 1.0 in row ngrp, 0 below it
+    for (int i = lane; i < 16 * L::ZROW; i += 64) {
+        const int r = i / L::ZROW;
+        if (r >= ngrp) zt_lds[i] = r == ngrp ? (uint16_t)0x3c00u : (uint16_t)0u;
     }
+    __syncthreads();
 
-    f32x4 acc[NSUB];
+    f32x4 acc[NOT];
 #pragma unroll
-    for (int n = 0; n < NSUB; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4lg+i][col ln]: zero-point sums (ln < ngw), denominator (ln == ngw)
-    float m = kFarBelow;              // reference maximum of query ln (the same in every wave)
+    for (int o = 0; o < NOT; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4g+k][column n]: zero-point sums (n < ngrp), denominator (n == ngrp)
+    float m = kFarBelow;              // running maximum of query n
     int kb = KB;                      // value-product exponent (wave-uniform, never rises)
-    int kb_tile = KB;                 // the exponent the staged tile's value steps allow
 
-    // ---- prefetch registers: two sets, so the tiles two ahead are in flight
-    struct Pref {
-        uint32_t kw[2][KWL];   // key words of token rows 8(ln>>2) + 4s + (ln&3), lane group lg
-        uint32_t kmw[2];       // the two key metadata words of this lane's fragment pair
-        uint32_t vw[UPL][BV];  // value units of the wave
-        uint32_t vmw[NVML];    // value metadata words
-    };
-    Pref pf[2];
+    for (; i < ntiles; i += 4) {
+        const int t0 = wa + 32 * i;
+        const int tn = wa + 32 * (i + 4 < ntiles ? i + 4 : i);  // the last tile re-requests itself (cache hits)
+        const bool quant = t0 < nqk;
 
-    auto load_keys = [&](Pref& P, int t0) {
+        // ---- stage the value codes (bytes), value metadata and key metadata in LDS
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int t = min(t0 + 8 * (ln >> 2) + 4 * s + (ln & 3), nqk - 1);
-            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8) + (cw0 + lg * DQ) * BK / 8), P.kw[s]);
-        }
-    };
-    // Lane -> fragment pair (window kw8, pair kjj) of the wave's key channels.
-    const int kpair = lane % (DW / 2), kw8 = kpair >> 2, kjj = kpair & 3;
-    auto load_kmeta = [&](Pref& P, int t0) {
-        const uint32_t* src = km + (size_t)(t0 >> lgk) * D + cw0 + 8 * kw8;
-        int c0 = 0, c1 = 0;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            if (kjj == jj) c0 = KF::PERM[2 * jj], c1 = KF::PERM[2 * jj + 1];
-        P.kmw[0] = src[c0];
-        P.kmw[1] = src[c1];
-    };
-    auto load_values = [&](Pref& P, int t0) {
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            const int f = lane + 64 * u;
-            const int t = min(t0 + f / UPW, wb - 1);
-            load_n<BV, VALIGN>((const uint32_t*)(vc + (size_t)t * (D * BV / 8) + (cw0 / 32 + f % UPW) * BV * 4), P.vw[u]);
-        }
-        // a fixed count of loads (clamped indices), so the compiler's wait counts
-        // never have to assume a load was skipped
-#pragma unroll
-        for (int u = 0; u < NVML; ++u) {
-            const int f = min(lane + 64 * u, 32 * ngw - 1);
-            const int t = min(t0 + (f >> lng), wb - 1);
-            P.vmw[u] = vm[(size_t)t * vgpr + g0 + (f & (ngw - 1))];
-        }
-    };
-    // Stage value bytes, value scales / zero points and key metadata of the tile in LDS.
-    auto stage = [&](Pref& P, bool with_keys) {
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            const int f = lane + 64 * u;
+        for (int u = 0; u < VUL; ++u) {
             uint32_t by[8];
-            unit_to_bytes<BV>(P.vw[u], by);
-            uint32_t* dst = (uint32_t*)&vt_lds[wave][(f / UPW) * VROW + (f % UPW) * 32];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) ((uint2*)dst)[k] = make_uint2(by[2 * k], by[2 * k + 1]);
+            unit_to_bytes<BV>(vw + u * BV, by);
+            uint32_t* dst = (uint32_t*)(vt_lds + (lane >> 1) * L::VROW + ((lane & 1) * VUL + u) * 32);
+            ((uint4*)dst)[0] = make_uint4(by[0], by[1], by[2], by[3]);
+            ((uint4*)dst)[1] = make_uint4(by[4], by[5], by[6], by[7]);
         }
-        uint32_t smx = 0;  // largest fp16 value step of the wave's tile (steps are >= 0: bit order = value order)
+        uint32_t smx = 0;  // largest fp16 value step of the tile (steps are >= 0: bit order = value order)
 #pragma unroll
-        for (int u = 0; u < NVML; ++u) {
-            const int f = lane + 64 * u;
-            if (f < 32 * ngw) {
-                const int tt = f >> lng, g = f & (ngw - 1);
-                st_lds[wave][g][tt] = (uint16_t)(P.vmw[u] & 0xffffu);
-                zt_lds[wave][g][tt] = (uint16_t)(P.vmw[u] >> 16);
-                smx = max(smx, P.vmw[u] & 0x7fffu);
+        for (int k = 0; k < NVML; ++k) {
+            const int f = lane + 64 * k;
+            if (f < 32 * ngrp) {
+                const int tt = f >> lng, gg = f & (ngrp - 1);
+                st_lds[gg * 32 + tt] = (uint16_t)(vmw[k] & 0xffffu);
+                zt_lds[gg * L::ZROW + tt] = (uint16_t)(vmw[k] >> 16);
+                smx = max(smx, vmw[k] & 0x7fffu);
             }
         }
-        // the wave's largest biased exponent e (a scalar: binary search over ballots);
-        // s < 2^(e - 14), so 2^kb p s < 2^15 with kb = 29 - e
-        const int el = (int)(smx >> 10);
-        int emax = 0;
+        // s < 2^(e - 14) for biased fp16 exponent e: 2^kb p s < 2^15 with kb = 29 - e
+        // (one ballot in the common case that no step needs kb below KB)
+        const int kb_tile = __builtin_amdgcn_ballot_w64((int)(smx >> 10) > 29 - KB)
+                                ? min(KB, 29 - wave_max_field<5>((int)(smx >> 10)))
+                                : KB;
+        int fk = 0;  // key weights q' s scaled by 2^-fk (fp16 range)
+        if (quant) {
+            uint32_t kmx = 0;
 #pragma unroll
-        for (int b = 16; b; b >>= 1)
-            if (__builtin_amdgcn_ballot_w64(el >= emax + b)) emax += b;
-        kb_tile = min(KB, 29 - emax);
-        if (with_keys && lane < DW / 2) {
-            sp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x05040100u);
-            zp_lds[wave][kpair] = __builtin_amdgcn_perm(P.kmw[1], P.kmw[0], 0x07060302u);
+            for (int k = 0; k < NKP; ++k) {
+                const int p = lane + 64 * k;
+                if (p < D / 2) {
+                    sp_lds[p] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x05040100u);
+                    zp_lds[p] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x07060302u);
+                    kmx = max(kmx, max(kmw[2 * k] & 0x7fffu, kmw[2 * k + 1] & 0x7fffu));
+                }
+            }
+            // |q'| < 2^(eq - 126), s < 2^(es - 14): q' s < 2^(eq + es - 140); keep it below 2^15
+            if (__builtin_amdgcn_ballot_w64((int)(kmx >> 10) > 155 - eq))
+                fk = max(0, eq + wave_max_field<5>((int)(kmx >> 10)) - 155);
         }
-    };
+        __builtin_amdgcn_sched_barrier(0);
+        load_values(tn);
+        if (tn < nqk) load_kmeta(tn);
+        __builtin_amdgcn_sched_barrier(0);  // the requests go out before the arithmetic
+        wave_lds_sync();
 
-    // Partial key scores over this wave's channels of a quantized tile:
-    // sc[j] for query ln, token t0 + 8lg + j.
-    auto key_scores_quant = [&](const Pref& P, float* sc) {
-        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-        float bz = 0.f;
-        uint4 spc = *(const uint4*)&sp_lds[wave][4 * (lg * NCH)];
-        uint4 zpc = *(const uint4*)&zp_lds[wave][4 * (lg * NCH)];
-        static_for<NCH>([&](auto K) {
-            constexpr int k = K;
-            uint4 spn, zpn;
-            if constexpr (k + 1 < NCH) {  // one chunk of LDS reads in flight
-                spn = *(const uint4*)&sp_lds[wave][4 * (lg * NCH + k + 1)];
-                zpn = *(const uint4*)&zp_lds[wave][4 * (lg * NCH + k + 1)];
-            }
-            const uint32_t sp[4] = {spc.x, spc.y, spc.z, spc.w};
-            const uint32_t zp[4] = {zpc.x, zpc.y, zpc.z, zpc.w};
-            Frag bh, bl;
+        // ---- key scores: sc[j] for query n, token t0 + 8g + j
+        float sc[8];
+        if (quant) {
+            f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+            float bz = 0.f;
+            const uint32_t fpair = f16_pow2_neg(fk) * 0x10001u;
+            static_for<NCH>([&](auto C) {
+                constexpr int c = C;
+                const int cb = cbase(c);
+                const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
+                const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
+                const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+                const uint4 qh4 = *(const uint4*)&qh_lds[n * L::QHS + cb / 2];
+                uint4 sp4 = *(const uint4*)&sp_lds[cb / 2];
+                const uint4 zp4 = *(const uint4*)&zp_lds[cb / 2];
+                if (fk) {
+                    sp4.x = pk_mul(sp4.x, fpair), sp4.y = pk_mul(sp4.y, fpair);
+                    sp4.z = pk_mul(sp4.z, fpair), sp4.w = pk_mul(sp4.w, fpair);
+                }
+                const uint32_t qh[4] = {qh4.x, qh4.y, qh4.z, qh4.w};
+                const uint32_t sp[4] = {sp4.x, sp4.y, sp4.z, sp4.w};
+                const uint32_t zp[4] = {zp4.x, zp4.y, zp4.z, zp4.w};
+                Frag bh, bl;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j0 = 8 * k + KF::PERM[2 * jj], j1 = 8 * k + KF::PERM[2 * jj + 1];
-                mul_split(qh[4 * k + jj], qf[j0], qf[j1], sp[jj], bh.u[jj], bl.u[jj]);
-                bz = mix_lo(zp[jj], qf[j0], bz);
-                bz = mix_hi(zp[jj], qf[j1], bz);
-            }
-            Frag a0, a1;
-            KF::template get<k>(P.kw[0], a0);
-            KF::template get<k>(P.kw[1], a1);
-            c0 = mfma(a0, bh, c0);
-            c0 = mfma(a0, bl, c0);
-            c1 = mfma(a1, bh, c1);
-            c1 = mfma(a1, bl, c1);
-            if constexpr (k + 1 < NCH) spc = spn, zpc = zpn;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float qx = qv[KF::PERM[2 * jj]], qy = qv[KF::PERM[2 * jj + 1]];
+                    mul_split(qh[jj], qx, qy, sp[jj], bh.u[jj], bl.u[jj]);
+                    bz = mix_lo(zp[jj], qx, bz);
+                    bz = mix_hi(zp[jj], qy, bz);
+                }
+                Frag a0f, a1f;
+                KF::template get<c>(kw[0], a0f);
+                KF::template get<c>(kw[1], a1f);
+                c0 = mfma(a0f, bh, c0);
+                c0 = mfma(a0f, bl, c0);
+                c1 = mfma(a1f, bh, c1);
+                c1 = mfma(a1f, bl, c1);
+            });
             __builtin_amdgcn_sched_barrier(0);
-        });
-        const float bias = col4_sum(bz * ((float)(1 << KSH) / (float)(1 << 8)));
+            if (tn < nqk) load_keys(tn);
+            __builtin_amdgcn_sched_barrier(0);
+            const float bias = col4_sum(bz) * __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
+            const float cs = __builtin_amdgcn_ldexpf(1.0f, 16 + fk + eqs);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = fmaf(c0[i], kTwo16, bias);
-            sc[4 + i] = fmaf(c1[i], kTwo16, bias);
-        }
-    };
-
-    // Partial scores of a residual tile (keys kept in the input dtype): keys and
-    // queries both split into fp16 hi + lo parts (three MFMAs).
-    auto key_scores_resid = [&](int t0, float* sc) {
-        f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        static_for<NCH>([&](auto K) {
-            constexpr int k = K;
-            const int cb = cw0 + lg * DQ + 8 * k;
-            Frag bh, bl;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float x0 = qf[8 * k + 2 * jj] * ((float)(1 << KSH) / (float)(1 << 8));
-                const float x1 = qf[8 * k + 2 * jj + 1] * ((float)(1 << KSH) / (float)(1 << 8));
-                split2(x0, x1, bh.u[jj], bl.u[jj]);
+            for (int k = 0; k < 4; ++k) {
+                sc[k] = fmaf(c0[k], cs, bias);
+                sc[4 + k] = fmaf(c1[k], cs, bias);
             }
+        } else {
+            // keys kept in the input dtype: keys and queries both as fp16 hi + lo (three MFMAs)
+            f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            static_for<NCH>([&](auto C) {
+                constexpr int cc = C;
+                const int cb = cbase(cc);
+                const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
+                const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
+                Frag bh, bl;
+                split2(qa.x, qa.y, bh.u[0], bl.u[0]);
+                split2(qa.z, qa.w, bh.u[1], bl.u[1]);
+                split2(qb.x, qb.y, bh.u[2], bl.u[2]);
+                split2(qb.z, qb.w, bh.u[3], bl.u[3]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int t = min(t0 + 8 * (ln >> 2) + 4 * s + (ln & 3), wb - 1);
-                float kv[8];
-                load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
-                Frag ah, al;
+                for (int h = 0; h < 2; ++h) {
+                    const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
+                    float kv[8];
+                    load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
+                    Frag ah, al;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
-                c[s] = mfma(ah, bh, c[s]);
-                c[s] = mfma(ah, bl, c[s]);
-                c[s] = mfma(al, bh, c[s]);
-            }
-        });
+                    for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
+                    c[h] = mfma(ah, bh, c[h]);
+                    c[h] = mfma(ah, bl, c[h]);
+                    c[h] = mfma(al, bh, c[h]);
+                }
+            });
+            const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = c[0][i];
-            sc[4 + i] = c[1][i];
-        }
-    };
-
-    // Sum the waves' partial scores (fixed order: identical in every wave), mask.
-    auto full_scores = [&](float* sc, int buf, int t0, int lim) {
-        if constexpr (NWV > 1) {
-            float* xs = xbuf + (size_t)buf * NWV * 512;
-            *(float4*)&xs[(wave * 64 + lane) * 8] = make_float4(sc[0], sc[1], sc[2], sc[3]);
-            *(float4*)&xs[(wave * 64 + lane) * 8 + 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-            wg_lds_barrier();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sc[j] = 0.f;
-#pragma unroll
-            for (int w = 0; w < NWV; ++w) {
-                const float4 u0 = *(const float4*)&xs[(w * 64 + lane) * 8];
-                const float4 u1 = *(const float4*)&xs[(w * 64 + lane) * 8 + 4];
-                sc[0] += u0.x, sc[1] += u0.y, sc[2] += u0.z, sc[3] += u0.w;
-                sc[4] += u1.x, sc[5] += u1.y, sc[6] += u1.z, sc[7] += u1.w;
+            for (int k = 0; k < 4; ++k) {
+                sc[k] = c[0][k] * cs;
+                sc[4 + k] = c[1][k] * cs;
             }
         }
+        if (t0 + 32 > wb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (t0 + 8 * lg + j >= lim) sc[j] = -INFINITY;
-    };
+            for (int j = 0; j < 8; ++j)
+                if (t0 + 8 * g + j >= wb) sc[j] = -INFINITY;
+        }
 
-    // Softmax weights of the tile and the value products of this wave's channels.
-    auto values = [&](const float* sc) {
+        // ---- online softmax (exact running maximum of query n)
         float tmax = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
@@ -619,173 +673,174 @@ __attribute__((amdgpu_waves_per_eu(BK == 3 ? 2 : 3, BK == 3 ? 2 : 3))) void deco
         if (__builtin_amdgcn_ballot_w64(tmax > m)) {
             const float mnew = fmaxf(m, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            // row 4lg + i of the accumulators belongs to query 4lg + i
+            // row 4g + k of the accumulators belongs to query 4g + k
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * lg + i);
+            for (int k = 0; k < 4; ++k) {
+                const float ak = __shfl(alpha, 4 * g + k);
 #pragma unroll
-                for (int n = 0; n < NSUB; ++n) acc[n][i] *= ai;
-                cz[i] *= ai;
+                for (int o = 0; o < NOT; ++o) acc[o][k] *= ak;
+                cz[k] *= ak;
             }
             m = mnew;
         }
         if (kb_tile < kb) {  // a tile with larger value steps: lower the exponent (exact rescale)
             const float f = __builtin_amdgcn_ldexpf(1.0f, kb_tile - kb);
 #pragma unroll
-            for (int n = 0; n < NSUB; ++n) acc[n] *= f;
+            for (int o = 0; o < NOT; ++o) acc[o] *= f;
             kb = kb_tile;
         }
-        // p <= 1 (exact running maximum), kept in fp16 range with power-of-two
-        // scales: 2^kb for the value product, 2^KZ for zero points / denominator
         float p[8];
         const float mb = m - (float)kb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
-        Frag ph, pl, pb;  // 2^KZ p as hi + lo; 2^KB p truncated to fp16 pairs
+        uint32_t pb[4];  // 2^kb p truncated to fp16 pairs
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pb[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
+
+        // ---- zero points and denominator
         {
-            Frag zf;
-            float pz[8];
+            Frag ph, pl, zf;
             const float zscale = __builtin_amdgcn_ldexpf(1.0f, KZ - kb);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pz[j] = p[j] * zscale;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                split2(pz[2 * jj], pz[2 * jj + 1], ph.u[jj], pl.u[jj]);
-                pb.u[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
-            }
-            const uint4 z4 = *(const uint4*)&zt_lds[wave][ln][8 * lg];
+            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj] * zscale, p[2 * jj + 1] * zscale, ph.u[jj], pl.u[jj]);
+            const uint4 z4 = *(const uint4*)&zt_lds[n * L::ZROW + 8 * g];
             zf.u[0] = z4.x, zf.u[1] = z4.y, zf.u[2] = z4.z, zf.u[3] = z4.w;
             cz = mfma(ph, zf, cz);
             cz = mfma(pl, zf, cz);
         }
-        // Output tiles 2b, 2b+1 take columns 32b + 2ln and 32b + 2ln + 1 of the
-        // wave's value tile: one 16-bit LDS read per token row feeds both.
-        const uint8_t* vt = &vt_lds[wave][8 * lg * VROW + 2 * ln];
-        uint32_t vb[2][8];
-        uint4 sv[2];
-        auto read_v = [&](int b, uint32_t* w, uint4& s4) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = *(const uint16_t*)&vt[j * VROW + 32 * b];
-            s4 = *(const uint4*)&st_lds[wave][(32 * b) >> lgv][8 * lg];
-        };
-        read_v(0, vb[0], sv[0]);
+
+        // ---- value products: output tile o = byte positions 16o..16o+15 of the value tile
         Frag sh, sl;
-        static_for<NSUB / 2>([&](auto B) {
-            constexpr int b = B;
-            if constexpr (b + 1 < NSUB / 2) read_v(b + 1, vb[(b + 1) & 1], sv[(b + 1) & 1]);
-            if ((b & ((1 << bpg) - 1)) == 0) {  // first block of a value group: P' = p * s
-                const uint32_t sw[4] = {sv[b & 1].x, sv[b & 1].y, sv[b & 1].z, sv[b & 1].w};
+        const uint8_t* vrow = vt_lds + (8 * g + (n >> 1)) * L::VROW + 8 * (n & 1);
+        static_for<NOT>([&](auto O) {
+            constexpr int o = O;
+            if ((o & (tpg - 1)) == 0) {  // first tile of a value group: P' = 2^kb p s
+                const int gg = (32 * (o >> 1)) >> lgv;
+                const uint4 s4 = *(const uint4*)&st_lds[gg * 32 + 8 * g];
+                const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) mul_split(pb.u[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
+                for (int jj = 0; jj < 4; ++jj) mul_split(pb[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
             }
-            // code << VSH in each half: the high byte for 2- and 3-bit codes,
-            // else the low byte shifted
-            const uint32_t* w = vb[b & 1];
-            Frag f0, f1;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                if constexpr (VSH == 8) {
-                    f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x040c000cu);
-                    f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x050c010cu);
-                } else {
-                    f0.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c040c00u) << VSH;
-                    f1.u[jj] = __builtin_amdgcn_perm(w[2 * jj + 1], w[2 * jj], 0x0c050c01u) << VSH;
-                }
+            const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2_t*)(vrow + 16 * o));
+            const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1];  // tokens 8g..8g+3, 8g+4..8g+7
+            Frag vf;
+            if constexpr (VSH == 8) {
+                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x010c000cu);
+                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x030c020cu);
+                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x050c040cu);
+                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x070c060cu);
+            } else {
+                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x0c010c00u) << VSH;
+                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x0c030c02u) << VSH;
+                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x0c050c04u) << VSH;
+                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x0c070c06u) << VSH;
             }
-            acc[2 * b] = mfma(sh, f0, acc[2 * b]);
-            acc[2 * b] = mfma(sl, f0, acc[2 * b]);
-            acc[2 * b + 1] = mfma(sh, f1, acc[2 * b + 1]);
-            acc[2 * b + 1] = mfma(sl, f1, acc[2 * b + 1]);
-            __builtin_amdgcn_sched_barrier(0);
+            acc[o] = mfma(sh, vf, acc[o]);
+            acc[o] = mfma(sl, vf, acc[o]);
         });
-    };
-
-    // ---- tiles of the split, shared by all waves
-    const int ntile = (wb - wa + 31) >> 5;
-    const int nqt = qend > wa ? (qend - wa + 31) >> 5 : 0;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (b < nqt) {
-            load_kmeta(pf[b], wa + 32 * b);
-            load_values(pf[b], wa + 32 * b);
-            load_keys(pf[b], wa + 32 * b);
-        }
-    }
-    wave_lds_sync();  // constant zero-point rows written
-    // Tile i uses set i & 1 and refills it with tile i + 2 (the last tile is
-    // repeated past the end: cache hits).
-    auto quant_tile = [&](Pref& P, int i) {
-        const int t0 = wa + 32 * i;
-        const int tn = wa + 32 * min(i + 2, nqt - 1);
-        stage(P, true);
-        load_kmeta(P, tn);
-        load_values(P, tn);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before any use of the key words
-        wave_lds_sync();
-        float sc[8];
-        key_scores_quant(P, sc);
-        load_keys(P, tn);
-        full_scores(sc, i & 1, t0, qend);
-        values(sc);
-        wave_lds_sync();  // the next stage rewrites this wave's LDS tiles
-    };
-    for (int i = 0; i < nqt; i += 2) {
-        quant_tile(pf[0], i);
-        if (i + 1 < nqt) quant_tile(pf[1], i + 1);
-    }
-    for (int i = nqt; i < ntile; ++i) {
-        const int t0 = wa + 32 * i;
-        load_values(pf[0], t0);
-        stage(pf[0], false);
-        wave_lds_sync();
-        float sc[8];
-        key_scores_resid(t0, sc);
-        full_scores(sc, i & 1, t0, wb);
-        values(sc);
-        wave_lds_sync();
+        wave_lds_sync();  // the next stage rewrites this wave's LDS areas
     }
 
-    // ---- this split's partial (m, l, o) for the R real queries: o = 2^24 acc + zero-point sums
-    float* o_lds = xbuf + wave * 16 * DW;  // [16][DW] by value-tile position
-    if constexpr (NWV > 1) wg_lds_barrier();  // every wave is done reading the partial scores
+    // ---- merge the four waves (fixed order) and write this split's partial (m, l, o)
+    float* mo = (float*)(smem + L::MO);  // [wave][row][channel]
+    float* ml = (float*)(smem + L::ML);  // [wave][row][m, l]
+    wg_lds_barrier();                    // every wave is done with the loop areas
+    {
+        const float oscale = __builtin_amdgcn_ldexpf(1.0f, 24 - kb - VSH);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * lg + i;
+        for (int k = 0; k < 4; ++k) {
+            const int r = 4 * g + k;
 #pragma unroll
-        for (int b = 0; b < NSUB / 2; ++b) {
-            // zero-point sum of (r, group), carrying 2^KZ
-            const float zs = __shfl(cz[i], 16 * lg + ((32 * b) >> lgv)) * (1.0f / (float)(1 << KZ));
-            const float oscale = __builtin_amdgcn_ldexpf(1.0f, 24 - kb - VSH);
-            o_lds[r * DW + 32 * b + 2 * ln] = fmaf(acc[2 * b][i], oscale, zs);
-            o_lds[r * DW + 32 * b + 2 * ln + 1] = fmaf(acc[2 * b + 1][i], oscale, zs);
-        }
-    }
-    wave_lds_sync();
-    for (int i = lane; i < R * DW; i += 64) {
-        const int r = i / DW, pos = i % DW;
-        const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
-        a.ws_o[slot * D + cw0 + val_chan<BV>(pos)] = o_lds[r * DW + pos];
-    }
-    if (wave == 0) {
-        // denominator of query 4lg + i sits in column ngw of cz
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * lg + i;
-            if (ln == ngw && r < R) {
-                const size_t slot = ((size_t)seq * a.q_heads + kvh * R + r) * a.max_chunks + split;
-                a.ws_ml[slot * 2 + 1] = cz[i] * (1.0f / (float)(1 << KZ));
+            for (int o = 0; o < NOT; ++o) {
+                const int gg = (32 * (o >> 1)) >> lgv;
+                const float zs = __shfl(cz[k], 16 * g + gg) * (1.0f / (float)(1 << KZ));
+                const int ch = 32 * (o >> 1) + val_chan<BV>(16 * (o & 1) + n);
+                mo[(wave * 16 + r) * D + ch] = fmaf(acc[o][k], oscale, zs);
             }
+            if (n == ngrp) ml[(wave * 16 + r) * 2 + 1] = cz[k] * (1.0f / (float)(1 << KZ));
         }
-        if (lg == 0 && ln < R) {
-            const size_t slot = ((size_t)seq * a.q_heads + kvh * R + ln) * a.max_chunks + split;
-            a.ws_ml[slot * 2 + 0] = m;
+        if (g == 0) ml[(wave * 16 + n) * 2] = m;
+    }
+    wg_lds_barrier();
+    for (int idx = tid; idx < RQ * D; idx += 256) {
+        const int r = idx / D, ch = idx - r * D;
+        float M = ml[r * 2];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = fmaxf(M, ml[(w * 16 + r) * 2]);
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float sw = __builtin_amdgcn_exp2f(ml[(w * 16 + r) * 2] - M);
+            o = fmaf(mo[(w * 16 + r) * D + ch], sw, o);
+            l = fmaf(ml[(w * 16 + r) * 2 + 1], sw, l);
         }
+        const size_t slot = ((size_t)seq * a.q_heads + kvh * R + q0 + r) * a.max_chunks + split;
+        a.ws_o[slot * D + ch] = o;
+        if (ch == 0) {
+            a.ws_ml[slot * 2 + 0] = M;
+            a.ws_ml[slot * 2 + 1] = l;
+        }
+    }
+}
+
+// One launch per (bits_k, bits_v) pair: grid = (split, kv head x query group,
+// the pair's sequences x layers).
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_gqa_kernel(DecodeArgs a0) {
+    __shared__ __align__(16) uint8_t smem[Lds<D>::BYTES];
+    int z = blockIdx.z;
+    const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
+    gqa_body<D, BK, BV>(a, smem, a.seq_list ? a.seq_list[z] : z, blockIdx.y, blockIdx.x);
+}
+
+template <int D, int BK>
+__device__ __forceinline__ void gqa_list_bv(int bv, const DecodeArgs& a, uint8_t* smem, int seq, int hy, int split) {
+    switch (bv) {
+        case 2: gqa_body<D, BK, 2>(a, smem, seq, hy, split); break;
+        case 3: gqa_body<D, BK, 3>(a, smem, seq, hy, split); break;
+        case 4: gqa_body<D, BK, 4>(a, smem, seq, hy, split); break;
+        case 6: gqa_body<D, BK, 6>(a, smem, seq, hy, split); break;
+        default: gqa_body<D, BK, 8>(a, smem, seq, hy, split); break;
+    }
+}
+
+// Every bit pair of the call in one launch: workgroup f takes the f-th active
+// (layer, seq, split, kv head x query group) item of a list ordered by bit
+// pair, found by binary search over the list's per-(layer, seq) starts.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_gqa_list_kernel(DecodeArgs a0,
+                                                                                                        GqaList list) {
+    __shared__ __align__(16) uint8_t smem[Lds<D>::BYTES];
+    const int f = blockIdx.x;
+    int lo = 0, hi = list.count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (list.start[mid] <= f) lo = mid;
+        else hi = mid - 1;
+    }
+    const int seq = list.seq[lo];
+    int z = list.layer[lo] * a0.num_seqs + seq;
+    const DecodeArgs a = layer_args(a0, z, a0.num_seqs);
+    const int R = a.q_heads / a.kv_heads;
+    const int nh = a.kv_heads * ((R + 15) >> 4);
+    const int r = f - list.start[lo];
+    const SeqEntry& e = a.table[seq];
+    const int bk = e.bits[0], bv = e.bits[1];
+    switch (bk) {
+        case 2: gqa_list_bv<D, 2>(bv, a, smem, seq, r % nh, r / nh); break;
+        case 3:
+            if constexpr (D >= 128) gqa_list_bv<D, 3>(bv, a, smem, seq, r % nh, r / nh);
+            break;
+        case 4: gqa_list_bv<D, 4>(bv, a, smem, seq, r % nh, r / nh); break;
+        case 6: gqa_list_bv<D, 6>(bv, a, smem, seq, r % nh, r / nh); break;
+        default: gqa_list_bv<D, 8>(bv, a, smem, seq, r % nh, r / nh); break;
     }
 }
 
 template <int D, int BK>
 hipError_t gqa_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
-    const dim3 block(D / wave_channels<BK>() * 64);
+    const dim3 block(256);
     switch (bv) {
         case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 2>), grid, block, 0, s, a); break;
         case 3: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 3>), grid, block, 0, s, a); break;
@@ -814,11 +869,19 @@ hipError_t gqa_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s)
 // Compiled once per head_dim (KVQ_GQA_HEAD_DIM = 64, 128, 256).
 #define KVQ_GCAT2(a, b) a##b
 #define KVQ_GCAT(a, b) KVQ_GCAT2(a, b)
+hipError_t KVQ_GCAT(launch_decode_gqa_list_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, const GqaList& list, int items,
+                                                                hipStream_t s) {
+    hipLaunchKernelGGL((decode_gqa_list_kernel<KVQ_GQA_HEAD_DIM>), dim3(items), dim3(256), 0, s, a, list);
+    return hipGetLastError();
+}
+
 hipError_t KVQ_GCAT(launch_decode_gqa_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
                                                            hipStream_t s) {
     // x: the quantized splits only (the workspace's full-precision slots have no
-    // workgroups here: empty ones would leave the busy ones on a few XCDs)
-    dim3 grid(a.max_chunks - a.win_splits, a.kv_heads, nseqs * a.n_layers);
+    // workgroups here: empty ones would leave the busy ones on a few XCDs);
+    // y: kv heads x groups of 16 query heads
+    const int R = a.q_heads / a.kv_heads;
+    dim3 grid(a.max_chunks - a.win_splits, a.kv_heads * ((R + 15) / 16), nseqs * a.n_layers);
     return gqa_bk<KVQ_GQA_HEAD_DIM>(a, bits_k, bits_v, grid, s);
 }
 

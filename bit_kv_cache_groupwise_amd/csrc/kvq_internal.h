@@ -128,6 +128,18 @@ struct DequantArgs {
     uint32_t win_off;
 };
 
+// Work list of the query-group kernel when one launch covers every bit pair of
+// a call: entry k = one (layer, seq) with start[k] its first workgroup; the
+// entries are ordered by bit pair and start[count] is the total. Passed by
+// value in the kernel arguments.
+constexpr int kGqaListMax = 256;
+struct GqaList {
+    int32_t count;
+    int32_t start[kGqaListMax + 1];
+    uint16_t seq[kGqaListMax];
+    uint8_t layer[kGqaListMax];  // offset from the call's first layer
+};
+
 constexpr int kWinTokens = 64;  // full-precision tokens per decode_window_kernel workgroup
 constexpr int kWinHeads = 4;    // query heads per decode_window_kernel workgroup
 
@@ -144,6 +156,14 @@ hipError_t launch_decode_mha_d256(const DecodeArgs& a, int bits_k, int bits_v, i
 hipError_t launch_decode_gqa_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_gqa_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_gqa_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_gqa_list_d64(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s);
+hipError_t launch_decode_gqa_list_d128(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s);
+hipError_t launch_decode_gqa_list_d256(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s);
+inline hipError_t launch_decode_gqa_list(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s) {
+    return a.head_dim == 64    ? launch_decode_gqa_list_d64(a, list, items, s)
+           : a.head_dim == 128 ? launch_decode_gqa_list_d128(a, list, items, s)
+                               : launch_decode_gqa_list_d256(a, list, items, s);
+}
 inline hipError_t launch_decode_gqa(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     return a.head_dim == 64    ? launch_decode_gqa_d64(a, bits_k, bits_v, nseqs, s)
            : a.head_dim == 128 ? launch_decode_gqa_d128(a, bits_k, bits_v, nseqs, s)

@@ -458,14 +458,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
 // Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
 // out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
-    // grid = (q_heads, num_seqs x layers, ceil(D / 16)): 16 channels per workgroup; its
-    // 256 threads are 16 split groups x 16 channels (split i goes to group
-    // i mod 16), meeting in LDS in a fixed order.
+    // grid = (ceil(q_heads / 4), num_seqs x layers): one wave per (seq, query
+    // head). Every lane computes the same maximum and denominator over the
+    // splits (lane-strided, then wave reductions); lane l owns channels
+    // l, l + 64, ... and sums the splits in order.
     int y = blockIdx.y;
     const DecodeArgs a = layer_args(a0, y, gridDim.y / a0.n_layers);
-    const int hq = blockIdx.x, seq = y, D = a.head_dim;
-    const int lane = threadIdx.x & 63, sg = threadIdx.x >> 4, cl = threadIdx.x & 15;
-    const int c = blockIdx.z * 16 + cl;
+    const int lane = threadIdx.x & 63;
+    const int hq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), seq = y, D = a.head_dim;
+    if (hq >= a.q_heads) return;
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
     int nch;
@@ -487,36 +488,34 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
         nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     }
     if (nch == 0) {
-        if (sg == 0 && c < D) out[c] = 0.f;
+        for (int c = lane; c < D; c += 64) out[c] = 0.f;
         return;
     }
     const size_t base = ((size_t)seq * a.q_heads + hq) * a.max_chunks;
     const float* ml = a.ws_ml + base * 2;
-    float M = -INFINITY;  // every wave computes the same maximum and denominator
+    float M = -INFINITY;
     for (int i = lane; i < nch; i += 64) M = fmaxf(M, ml[2 * i]);
     M = wave_max(M);
     float L = 0.f;
     for (int i = lane; i < nch; i += 64) L += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
     L = wave_sum(L);
-    float o = 0.f;
-    if (c < D) {
-        const float* src = a.ws_o + base * D + c;
-        int i = sg;
-        for (; i + 16 < nch; i += 32) {
-            const float v0 = src[(size_t)i * D], v1 = src[(size_t)(i + 16) * D];
-            o = fmaf(v0, exp2f(ml[2 * i] - M), o);
-            o = fmaf(v1, exp2f(ml[2 * (i + 16)] - M), o);
-        }
-        if (i < nch) o = fmaf(src[(size_t)i * D], exp2f(ml[2 * i] - M), o);
-    }
-    __shared__ float part[16][16];
-    part[sg][cl] = o;
-    __syncthreads();
-    if (sg == 0 && c < D) {
-        float t = 0.f;
+    const float inv = 1.0f / L;
+    const float* src = a.ws_o + base * D;
+    for (int c = lane; c < D; c += 64) {
+        // 8 splits' loads in flight at a time (clamped indices, zero weights past the end)
+        float o = 0.f;
+        for (int i0 = 0; i0 < nch; i0 += 8) {
+            float v[8], wgt[8];
 #pragma unroll
-        for (int g = 0; g < 16; ++g) t += part[g][cl];
-        out[c] = t / L;
+            for (int k = 0; k < 8; ++k) {
+                const int i = min(i0 + k, nch - 1);
+                v[k] = src[(size_t)i * D + c];
+                wgt[k] = i0 + k < nch ? exp2f(ml[2 * i] - M) : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o = fmaf(v[k], wgt[k], o);
+        }
+        out[c] = o * inv;
     }
 }
 
@@ -791,8 +790,8 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads, a.num_seqs * a.n_layers, (a.head_dim + 15) / 16), dim3(kThreads), 0, s,
-                       a);
+    hipLaunchKernelGGL(merge_kernel, dim3((a.q_heads + kThreads / 64 - 1) / (kThreads / 64), a.num_seqs * a.n_layers),
+                       dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

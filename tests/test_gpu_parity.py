@@ -214,12 +214,31 @@ def test_error_paths_leave_the_cache_untouched():
         k.kvq_decode_attention(cache.handle, 0, q, w.softmax_scale, out, ws, 16)
     assert ei.value.status == k.KVQ_ERR_WORKSPACE
     cache.close()
-    wide = W.mixed_batch().scaled(num_seqs=1, q_heads=64, kv_heads=2, lengths=(10,), bits=((2, 2),))
-    c2 = H.make_cache(wide)
+    vch = W.mixed_batch().scaled(num_seqs=1, lengths=(10,), bits=((2, 2),), axis_v=o.AXIS_CHANNEL)
+    c2 = H.make_cache(vch)
     with pytest.raises(k.KVQError) as ei:
-        c2.decode(0, torch.zeros((1, 64, 128), dtype=torch.float16, device="cuda"), 0.1)
+        c2.decode(0, torch.zeros((1, vch.q_heads, 128), dtype=torch.float16, device="cuda"), 0.1)
     assert ei.value.status == k.KVQ_ERR_UNSUPPORTED
     c2.close()
+
+
+@pytest.mark.parametrize("q_heads,head_dim", [(64, 128), (48, 256), (40, 64)])
+def test_query_groups_wider_than_16(q_heads, head_dim):
+    """32, 24 and 20 query heads per kv head (2 kv heads): the query-group
+    kernel covers them in groups of 16 query rows, each group re-reading the
+    cache; every row meets the oracle, and the split choice does not matter."""
+    w = W.mixed_batch().scaled(num_seqs=3, kv_heads=2, q_heads=q_heads, head_dim=head_dim, lengths=(700, 33, 2000),
+                               bits=((2, 2), (4, 8), (6, 4)), in_dtype="bf16" if head_dim == 256 else "f16")
+    _note(f"[wide groups] Hq={q_heads} Hkv=2 D={head_dim}")
+    cache, prefix, new = _run_case(w)
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = [H.assert_head_bytes(cache, w, 0, s, h, k, v) for h in range(w.kv_heads)]
+        err = H.row_rel_err(out[s], H.attn_ref(w, q[s].float().numpy(), encs))
+        assert np.all(err <= H.ATTN_TOL), (q_heads, head_dim, s, float(err.max()))
+    cache.close()
 
 
 MHA_BITS = ((2, 2), (3, 3), (4, 4), (6, 4), (4, 8), (8, 2), (2, 6), (3, 8), (6, 6), (8, 8))
