@@ -44,6 +44,7 @@ def _run(cmd):
 def units():
     """(source, object, extra flags, is_device_code) of every translation unit."""
     return [("kvq_kernels.hip", "kvq_kernels.o", [], True),
+            ("kvq_scratch.hip", "kvq_scratch.o", [], True),
             *[("kvq_decode_mha.hip", f"kvq_decode_mha_d{d}.o", [f"-DKVQ_MHA_HEAD_DIM={d}"], True)
               for d in MHA_HEAD_DIMS],
             *[("kvq_decode_gqa.hip", f"kvq_decode_gqa_d{d}.o", [f"-DKVQ_GQA_HEAD_DIM={d}"], True)

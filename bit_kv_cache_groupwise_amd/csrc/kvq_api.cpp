@@ -795,6 +795,26 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
     return decode_layers(c, layer, 1, q, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* c, int32_t layer, const void* q, float softmax_scale,
+                                       float* out, void* stream) {
+    g_last_error.clear();
+    if (!c || !q || !out) return fail(KVQ_ERR_ARG, "cache, q or out is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    void* ws = nullptr;
+    hipError_t e = kvq::scratch_address(&ws);
+    if (e != hipSuccess) return hip_fail(e, "taking the address of the library's scratch");
+    StepOpts opt;
+    opt.dry_run = true;
+    kvq_status st = decode_layers(c, layer, 1, q, softmax_scale, out, ws, kvq::kScratchBytes, stream, opt);
+    if (st == KVQ_ERR_WORKSPACE)
+        return fail(KVQ_ERR_WORKSPACE,
+                    "this call's split workspace exceeds the library's fixed scratch of %zu bytes (use "
+                    "kvq_decode_attention with a workspace of kvq_decode_workspace_size bytes)",
+                    (size_t)kvq::kScratchBytes);
+    if (st != KVQ_OK) return st;
+    return decode_layers(c, layer, 1, q, softmax_scale, out, ws, kvq::kScratchBytes, stream);
+}
+
 kvq_status kvq_decode_attention_layers(const kvq_cache* c, int32_t layer0, int32_t n_layers, const void* q,
                                        float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
                                        void* stream) {

@@ -185,6 +185,10 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
                                : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
 }
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+// The library's fixed device scratch (kvq_scratch.hip): its address on the
+// current device, taken on the first call there.
+constexpr size_t kScratchBytes = 64ull << 20;
+hipError_t scratch_address(void** out);
 hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 

@@ -34,7 +34,7 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
             "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence")
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -73,6 +73,7 @@ _lib.kvq_decode_step.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P, ctypes.c
 _lib.kvq_decode_workspace_size.argtypes = [_P]
 _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.kvq_decode_attention_noalloc.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P]
 _lib.kvq_decode_attention_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_float, _P, _P,
                                              ctypes.c_size_t, _P]
 _lib.kvq_dequantize.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
@@ -87,7 +88,7 @@ _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
            "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence"):
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -212,6 +213,11 @@ def kvq_decode_attention(handle, layer, q, softmax_scale, out, workspace, worksp
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.kvq_decode_attention(handle, layer, _ptr(q), ctypes.c_float(softmax_scale), _ptr(out),
                                      _ptr(workspace), workspace_bytes, _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(handle, layer, q, softmax_scale, out, stream=None):
+    _check(_lib.kvq_decode_attention_noalloc(handle, layer, _ptr(q), ctypes.c_float(softmax_scale), _ptr(out),
+                                             _stream(stream)), "kvq_decode_attention_noalloc")
 
 
 def kvq_decode_attention_layers(handle, layer0, n_layers, q, softmax_scale, out, workspace, workspace_bytes=None,

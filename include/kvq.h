@@ -212,6 +212,20 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kvq_decode_attention with the same arguments minus the workspace, and the
+ * same results bit for bit. The split workspace comes from a fixed device
+ * array of the library, 64 MiB per GPU, held until the process ends; the call
+ * allocates nothing. A call whose workspace would exceed it (about 64 MiB /
+ * (4 * (head_dim + 2) * num_seqs * q_heads) splits per sequence) fails with
+ * KVQ_ERR_WORKSPACE before anything is launched. Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. Other errors as for
+ * kvq_decode_attention; KVQ_ERR_HIP if the array's address cannot be taken. */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
+                                        float* out, void* stream);
+
 /* One decode step of `layer`: kvq_quantize_append(k_new, v_new, n_new) then
  * kvq_decode_attention(q), with the same arguments, results and errors (all
  * checked before anything is launched or written). Where the single-query
