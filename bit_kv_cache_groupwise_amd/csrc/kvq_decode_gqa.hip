@@ -356,13 +356,17 @@ struct Lds {
     static constexpr int QH = QF + 16 * QFS * 4;
     static constexpr int RED = QH + 16 * QHS * 4;  // 4 ints: per-wave exponent maxima
     static constexpr int WAVE0 = RED + 16;
-    static constexpr int SP = 0, ZP = SP + D * 2, VT = ZP + D * 2, ST = VT + 32 * VROW, ZT = ST + U * 32 * 2;
+    static constexpr int SROW = 40;      // halves per row of the value steps (padded; cols 32.. take spare writes)
+    // key step / zero-point pairs: D / 2 words plus 4 spare words for lanes without a pair
+    static constexpr int SP = 0, ZP = SP + D * 2 + 16, VT = ZP + D * 2 + 16, ST = VT + 32 * VROW,
+                         ZT = ST + U * SROW * 2;
     static constexpr int WAVE = ZT + 16 * ZROW * 2;
     static constexpr int LOOP = WAVE0 + 4 * WAVE;
     static constexpr int MO = 0, ML = 4 * 16 * D * 4;
     static constexpr int MERGE = ML + 4 * 16 * 2 * 4;
     static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
-    static_assert(WAVE % 16 == 0 && WAVE0 % 16 == 0 && VT % 16 == 0 && ST % 16 == 0 && ZT % 16 == 0, "LDS alignment");
+    static_assert(WAVE % 16 == 0 && WAVE0 % 16 == 0 && VT % 16 == 0 && ST % 16 == 0 && ZT % 16 == 0 && ZP % 16 == 0,
+                  "LDS alignment");
 };
 
 // One workgroup's work: split `split` of the quantized tokens of (seq, kv head
@@ -396,7 +400,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     uint32_t* sp_lds = (uint32_t*)(wbase + L::SP);
     uint32_t* zp_lds = (uint32_t*)(wbase + L::ZP);
     uint8_t* vt_lds = wbase + L::VT;
-    uint16_t* st_lds = (uint16_t*)(wbase + L::ST);
+    uint16_t* st_lds = (uint16_t*)(wbase + L::ST);  // [group][SROW]
     uint16_t* zt_lds = (uint16_t*)(wbase + L::ZT);
 
     const int R = a.q_heads / a.kv_heads;
@@ -471,14 +475,16 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 
     // the first tile's loads go out before the query setup, whose latency they share
     const int ntiles = (wb - wa + 31) >> 5;
-    int i = wave;
-    if (i < ntiles) {
-        const int t0 = wa + 32 * i;
+    // tiles i < nqt have quantized keys (nqk and the tile starts are multiples of
+    // 32); the residual-key tiles after them are handled by a loop of their own,
+    // so that every load of the main loop is unconditional and the compiler's
+    // wait counts stay exact
+    const int nqt = nqk > wa ? min(ntiles, (nqk - wa) >> 5) : 0;
+    if (wave < nqt) {
+        const int t0 = wa + 32 * wave;
         load_values(t0);
-        if (t0 < nqk) {
-            load_kmeta(t0);
-            load_keys(t0);
-        }
+        load_kmeta(t0);
+        load_keys(t0);
     }
     // ---- q' rows of this workgroup (rows >= RQ are 0), kept below 2^14 by
     // 2^-eqs: fp32 in natural channel order, and fp16 pairs in key-fragment order
@@ -526,12 +532,10 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     float m = kFarBelow;              // running maximum of query n
     int kb = KB;                      // value-product exponent (wave-uniform, never rises)
 
-    for (; i < ntiles; i += 4) {
-        const int t0 = wa + 32 * i;
-        const int tn = wa + 32 * (i + 4 < ntiles ? i + 4 : i);  // the last tile re-requests itself (cache hits)
-        const bool quant = t0 < nqk;
-
-        // ---- stage the value codes (bytes), value metadata and key metadata in LDS
+    // ---- staging of a tile's value codes (bytes), value metadata and key
+    // metadata in LDS, branch-free (lanes without an item write spare slots);
+    // returns the exponent the tile's value steps allow (kb_tile)
+    auto stage_values = [&]() -> int {
 #pragma unroll
         for (int u = 0; u < VUL; ++u) {
             uint32_t by[8];
@@ -544,43 +548,134 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 #pragma unroll
         for (int k = 0; k < NVML; ++k) {
             const int f = lane + 64 * k;
-            if (f < 32 * ngrp) {
-                const int tt = f >> lng, gg = f & (ngrp - 1);
-                st_lds[gg * 32 + tt] = (uint16_t)(vmw[k] & 0xffffu);
-                zt_lds[gg * L::ZROW + tt] = (uint16_t)(vmw[k] >> 16);
-                smx = max(smx, vmw[k] & 0x7fffu);
-            }
+            const bool ok = f < 32 * ngrp;
+            const int tt = f >> lng, gg = f & (ngrp - 1);
+            st_lds[ok ? gg * L::SROW + tt : 32] = (uint16_t)(vmw[k] & 0xffffu);
+            zt_lds[ok ? gg * L::ZROW + tt : 15 * L::ZROW + 32] = (uint16_t)(vmw[k] >> 16);
+            smx = max(smx, ok ? vmw[k] & 0x7fffu : 0u);
         }
         // s < 2^(e - 14) for biased fp16 exponent e: 2^kb p s < 2^15 with kb = 29 - e
         // (one ballot in the common case that no step needs kb below KB)
-        const int kb_tile = __builtin_amdgcn_ballot_w64((int)(smx >> 10) > 29 - KB)
-                                ? min(KB, 29 - wave_max_field<5>((int)(smx >> 10)))
-                                : KB;
-        int fk = 0;  // key weights q' s scaled by 2^-fk (fp16 range)
-        if (quant) {
-            uint32_t kmx = 0;
+        return __builtin_amdgcn_ballot_w64((int)(smx >> 10) > 29 - KB)
+                   ? min(KB, 29 - wave_max_field<5>((int)(smx >> 10)))
+                   : KB;
+    };
+    // returns fk: the key weights q' s are scaled by 2^-fk to stay in fp16 range
+    auto stage_kmeta = [&]() -> int {
+        uint32_t kmx = 0;
 #pragma unroll
-            for (int k = 0; k < NKP; ++k) {
-                const int p = lane + 64 * k;
-                if (p < D / 2) {
-                    sp_lds[p] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x05040100u);
-                    zp_lds[p] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x07060302u);
-                    kmx = max(kmx, max(kmw[2 * k] & 0x7fffu, kmw[2 * k + 1] & 0x7fffu));
-                }
-            }
-            // |q'| < 2^(eq - 126), s < 2^(es - 14): q' s < 2^(eq + es - 140); keep it below 2^15
-            if (__builtin_amdgcn_ballot_w64((int)(kmx >> 10) > 155 - eq))
-                fk = max(0, eq + wave_max_field<5>((int)(kmx >> 10)) - 155);
+        for (int k = 0; k < NKP; ++k) {
+            const int p = lane + 64 * k;
+            const bool ok = p < D / 2;
+            sp_lds[ok ? p : D / 2] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x05040100u);
+            zp_lds[ok ? p : D / 2] = __builtin_amdgcn_perm(kmw[2 * k + 1], kmw[2 * k], 0x07060302u);
+            kmx = max(kmx, ok ? max(kmw[2 * k] & 0x7fffu, kmw[2 * k + 1] & 0x7fffu) : 0u);
         }
+        // |q'| < 2^(eq - 126), s < 2^(es - 14): q' s < 2^(eq + es - 140); keep it below 2^15
+        return __builtin_amdgcn_ballot_w64((int)(kmx >> 10) > 155 - eq)
+                   ? max(0, eq + wave_max_field<5>((int)(kmx >> 10)) - 155)
+                   : 0;
+    };
+
+    // ---- masked scores of tile t0 -> online softmax -> zero points and the value products
+    auto attend = [&](float* sc, int t0, int kb_tile) {
+        if (t0 + 32 > wb) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + 8 * g + j >= wb) sc[j] = -INFINITY;
+        }
+        // online softmax (exact running maximum of query n)
+        float tmax = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
+        tmax = col4_max(tmax);
+        if (__builtin_amdgcn_ballot_w64(tmax > m)) {
+            const float mnew = fmaxf(m, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            // row 4g + k of the accumulators belongs to query 4g + k
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float ak = __shfl(alpha, 4 * g + k);
+#pragma unroll
+                for (int o = 0; o < NOT; ++o) acc[o][k] *= ak;
+                cz[k] *= ak;
+            }
+            m = mnew;
+        }
+        if (kb_tile < kb) {  // a tile with larger value steps: lower the exponent (exact rescale)
+            const float f = __builtin_amdgcn_ldexpf(1.0f, kb_tile - kb);
+#pragma unroll
+            for (int o = 0; o < NOT; ++o) acc[o] *= f;
+            kb = kb_tile;
+        }
+        float p[8];
+        const float mb = m - (float)kb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
+        uint32_t pb[4];  // 2^kb p truncated to fp16 pairs
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pb[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
+
+        // zero points and denominator
+        {
+            Frag ph, pl, zf;
+            const float zscale = __builtin_amdgcn_ldexpf(1.0f, KZ - kb);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj] * zscale, p[2 * jj + 1] * zscale, ph.u[jj], pl.u[jj]);
+            const uint4 z4 = *(const uint4*)&zt_lds[n * L::ZROW + 8 * g];
+            zf.u[0] = z4.x, zf.u[1] = z4.y, zf.u[2] = z4.z, zf.u[3] = z4.w;
+            cz = mfma(ph, zf, cz);
+            cz = mfma(pl, zf, cz);
+        }
+
+        // value products: output tile o = byte positions 16o..16o+15 of the value tile
+        Frag sh, sl;
+        const uint8_t* vrow = vt_lds + (8 * g + (n >> 1)) * L::VROW + 8 * (n & 1);
+        static_for<NOT>([&](auto O) {
+            constexpr int o = O;
+            if ((o & (tpg - 1)) == 0) {  // first tile of a value group: P' = 2^kb p s
+                const int gg = (32 * (o >> 1)) >> lgv;
+                const uint4 s4 = *(const uint4*)&st_lds[gg * L::SROW + 8 * g];
+                const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) mul_split(pb[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
+            }
+            const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2_t*)(vrow + 16 * o));
+            const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1];  // tokens 8g..8g+3, 8g+4..8g+7
+            Frag vf;
+            if constexpr (VSH == 8) {
+                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x010c000cu);
+                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x030c020cu);
+                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x050c040cu);
+                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x070c060cu);
+            } else {
+                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x0c010c00u) << VSH;
+                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x0c030c02u) << VSH;
+                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x0c050c04u) << VSH;
+                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x0c070c06u) << VSH;
+            }
+            acc[o] = mfma(sh, vf, acc[o]);
+            acc[o] = mfma(sl, vf, acc[o]);
+        });
+    };
+
+    // ---- tiles with quantized keys: the next tile's words are requested as
+    // soon as this tile's are consumed (the last tile re-requests itself)
+    for (int i = wave; i < nqt; i += 4) {
+        const int t0 = wa + 32 * i;
+        const int tn = wa + 32 * (i + 4 < nqt ? i + 4 : i);
+        const int kb_tile = stage_values();
+        const int fk = stage_kmeta();
         __builtin_amdgcn_sched_barrier(0);
         load_values(tn);
-        if (tn < nqk) load_kmeta(tn);
+        load_kmeta(tn);
         __builtin_amdgcn_sched_barrier(0);  // the requests go out before the arithmetic
         wave_lds_sync();
 
-        // ---- key scores: sc[j] for query n, token t0 + 8g + j
+        // key scores: sc[j] for query n, token t0 + 8g + j
         float sc[8];
-        if (quant) {
+        {
             f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
             float bz = 0.f;
             const uint32_t fpair = f16_pow2_neg(fk) * 0x10001u;
@@ -617,7 +712,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 c1 = mfma(a1f, bl, c1);
             });
             __builtin_amdgcn_sched_barrier(0);
-            if (tn < nqk) load_keys(tn);
+            load_keys(tn);
             __builtin_amdgcn_sched_barrier(0);
             const float bias = col4_sum(bz) * __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
             const float cs = __builtin_amdgcn_ldexpf(1.0f, 16 + fk + eqs);
@@ -626,120 +721,53 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 sc[k] = fmaf(c0[k], cs, bias);
                 sc[4 + k] = fmaf(c1[k], cs, bias);
             }
-        } else {
-            // keys kept in the input dtype: keys and queries both as fp16 hi + lo (three MFMAs)
-            f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            static_for<NCH>([&](auto C) {
-                constexpr int cc = C;
-                const int cb = cbase(cc);
-                const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
-                const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
-                Frag bh, bl;
-                split2(qa.x, qa.y, bh.u[0], bl.u[0]);
-                split2(qa.z, qa.w, bh.u[1], bl.u[1]);
-                split2(qb.x, qb.y, bh.u[2], bl.u[2]);
-                split2(qb.z, qb.w, bh.u[3], bl.u[3]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
-                    float kv[8];
-                    load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
-                    Frag ah, al;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
-                    c[h] = mfma(ah, bh, c[h]);
-                    c[h] = mfma(ah, bl, c[h]);
-                    c[h] = mfma(al, bh, c[h]);
-                }
-            });
-            const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                sc[k] = c[0][k] * cs;
-                sc[4 + k] = c[1][k] * cs;
-            }
         }
-        if (t0 + 32 > wb) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (t0 + 8 * g + j >= wb) sc[j] = -INFINITY;
-        }
-
-        // ---- online softmax (exact running maximum of query n)
-        float tmax = sc[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, sc[j]);
-        tmax = col4_max(tmax);
-        if (__builtin_amdgcn_ballot_w64(tmax > m)) {
-            const float mnew = fmaxf(m, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            // row 4g + k of the accumulators belongs to query 4g + k
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float ak = __shfl(alpha, 4 * g + k);
-#pragma unroll
-                for (int o = 0; o < NOT; ++o) acc[o][k] *= ak;
-                cz[k] *= ak;
-            }
-            m = mnew;
-        }
-        if (kb_tile < kb) {  // a tile with larger value steps: lower the exponent (exact rescale)
-            const float f = __builtin_amdgcn_ldexpf(1.0f, kb_tile - kb);
-#pragma unroll
-            for (int o = 0; o < NOT; ++o) acc[o] *= f;
-            kb = kb_tile;
-        }
-        float p[8];
-        const float mb = m - (float)kb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
-        uint32_t pb[4];  // 2^kb p truncated to fp16 pairs
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pb[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
-
-        // ---- zero points and denominator
-        {
-            Frag ph, pl, zf;
-            const float zscale = __builtin_amdgcn_ldexpf(1.0f, KZ - kb);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj] * zscale, p[2 * jj + 1] * zscale, ph.u[jj], pl.u[jj]);
-            const uint4 z4 = *(const uint4*)&zt_lds[n * L::ZROW + 8 * g];
-            zf.u[0] = z4.x, zf.u[1] = z4.y, zf.u[2] = z4.z, zf.u[3] = z4.w;
-            cz = mfma(ph, zf, cz);
-            cz = mfma(pl, zf, cz);
-        }
-
-        // ---- value products: output tile o = byte positions 16o..16o+15 of the value tile
-        Frag sh, sl;
-        const uint8_t* vrow = vt_lds + (8 * g + (n >> 1)) * L::VROW + 8 * (n & 1);
-        static_for<NOT>([&](auto O) {
-            constexpr int o = O;
-            if ((o & (tpg - 1)) == 0) {  // first tile of a value group: P' = 2^kb p s
-                const int gg = (32 * (o >> 1)) >> lgv;
-                const uint4 s4 = *(const uint4*)&st_lds[gg * 32 + 8 * g];
-                const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) mul_split(pb[jj], p[2 * jj], p[2 * jj + 1], sw[jj], sh.u[jj], sl.u[jj]);
-            }
-            const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2_t*)(vrow + 16 * o));
-            const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1];  // tokens 8g..8g+3, 8g+4..8g+7
-            Frag vf;
-            if constexpr (VSH == 8) {
-                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x010c000cu);
-                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x030c020cu);
-                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x050c040cu);
-                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x070c060cu);
-            } else {
-                vf.u[0] = __builtin_amdgcn_perm(x1, x0, 0x0c010c00u) << VSH;
-                vf.u[1] = __builtin_amdgcn_perm(x1, x0, 0x0c030c02u) << VSH;
-                vf.u[2] = __builtin_amdgcn_perm(x1, x0, 0x0c050c04u) << VSH;
-                vf.u[3] = __builtin_amdgcn_perm(x1, x0, 0x0c070c06u) << VSH;
-            }
-            acc[o] = mfma(sh, vf, acc[o]);
-            acc[o] = mfma(sl, vf, acc[o]);
-        });
+        attend(sc, t0, kb_tile);
         wave_lds_sync();  // the next stage rewrites this wave's LDS areas
+    }
+
+    // ---- tiles whose keys are still in the residual (the last, incomplete key
+    // block: at most one block per sequence), loaded as they come
+    for (int i = wave; i < ntiles; i += 4) {
+        if (i < nqt) continue;
+        const int t0 = wa + 32 * i;
+        load_values(t0);
+        const int kb_tile = stage_values();
+        wave_lds_sync();
+        // keys and queries both as fp16 hi + lo (three MFMAs)
+        f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        static_for<NCH>([&](auto C) {
+            constexpr int cc = C;
+            const int cb = cbase(cc);
+            const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
+            const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
+            Frag bh, bl;
+            split2(qa.x, qa.y, bh.u[0], bl.u[0]);
+            split2(qa.z, qa.w, bh.u[1], bl.u[1]);
+            split2(qb.x, qb.y, bh.u[2], bl.u[2]);
+            split2(qb.z, qb.w, bh.u[3], bl.u[3]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
+                float kv[8];
+                load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
+                Frag ah, al;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
+                c[h] = mfma(ah, bh, c[h]);
+                c[h] = mfma(ah, bl, c[h]);
+                c[h] = mfma(al, bh, c[h]);
+            }
+        });
+        float sc[8];
+        const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sc[k] = c[0][k] * cs;
+            sc[4 + k] = c[1][k] * cs;
+        }
+        attend(sc, t0, kb_tile);
+        wave_lds_sync();
     }
 
     // ---- merge the four waves (fixed order) and write this split's partial (m, l, o)
