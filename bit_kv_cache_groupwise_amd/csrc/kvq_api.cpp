@@ -30,7 +30,21 @@ struct kvq_cache {
     uint8_t* resid = nullptr;
     uint8_t* table = nullptr;
     kvq::TableLayout tl{};
-    std::vector<SeqEntry> entries;  // [layers][num_seqs]
+    std::vector<SeqEntry> entries;  // [layers][num_seqs], as on the device
+    // Regions of each slot ([layers][num_seqs]): the residual (and, with
+    // contiguous storage, code and metadata) regions laid out for sequence i
+    // at creation. A sequence uses the regions of slot[l][s], which
+    // kvq_gather_sequences remaps so that a reorder copies only extra copies.
+    std::vector<SeqEntry> slot_layout;
+    std::vector<int32_t> slot;
+    // Paged storage: the pool's free pages (a stack), the references to each
+    // page, and the host copy of the device page lists.
+    bool paged = false;
+    uint64_t page_bytes = 0;
+    uint32_t num_pages = 0;
+    std::vector<uint32_t> free_pages;
+    std::vector<uint32_t> refs;
+    std::vector<uint32_t> pt;
     std::vector<int32_t> lens;      // host mirror of the current lengths [layers][num_seqs]
     std::vector<uint8_t> parity;    // which length buffer is current, per layer
     std::vector<int32_t> args;      // staging for the call-argument area
@@ -123,6 +137,16 @@ kvq_status check_geometry(const kvq_geometry* g) {
         if ((long)g->sinks + g->window + b > 4096)
             return fail(KVQ_ERR_ARG, "sinks + window + block = %ld exceeds 4096", (long)g->sinks + g->window + b);
     }
+    if (g->page_tokens < 0 || g->num_pages < 0)
+        return fail(KVQ_ERR_ARG, "page_tokens (%d) and num_pages (%d) must be >= 0", g->page_tokens, g->num_pages);
+    if (g->page_tokens) {
+        const int P = g->page_tokens;
+        if (P < 64 || P > 65536 || (P & (P - 1)))
+            return fail(KVQ_ERR_ARG, "page_tokens (%d) must be a power of two in [64, 65536]", P);
+        if (P < token_block(*g))
+            return fail(KVQ_ERR_ARG, "page_tokens (%d) must be at least the key block (%d tokens)", P, token_block(*g));
+        if (g->sinks % P) return fail(KVQ_ERR_ARG, "sinks (%d) must be a multiple of page_tokens (%d)", g->sinks, P);
+    }
     return KVQ_OK;
 }
 
@@ -136,18 +160,31 @@ kvq_status check_seqs(const kvq_geometry* g, const int32_t* cap, const uint8_t* 
     return KVQ_OK;
 }
 
-// Pool layout: layer -> seq -> tensor (K, V) -> head, each head region 256-byte aligned.
-void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
-            std::vector<SeqEntry>* entries, kvq_sizes* sz, kvq::TableLayout* tl) {
+// Logical pages of a sequence of capacity cap (paged storage).
+uint32_t pages_of(const kvq_geometry* g, int cap) {
+    return (uint32_t)(((int64_t)cap + g->page_tokens - 1) / g->page_tokens);
+}
+
+// Pool layout. Contiguous storage: layer -> seq -> tensor (K, V) -> head, each
+// head region 256-byte aligned. Paged storage: codes and metadata inside a page
+// (K codes, V codes, K metadata, V metadata, each [head] with 256-byte aligned
+// head regions; the page stride is the largest over the sequences), residual
+// regions as with contiguous storage. Fails when the pool would not be
+// addressable (page lists or page indices beyond 32 bits).
+kvq_status layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
+                  std::vector<SeqEntry>* entries, kvq_sizes* sz, kvq::TableLayout* tl) {
     const uint64_t D = g->head_dim, H = g->kv_heads, ib = in_bytes(g->in_dtype);
     const int groups[2] = {g->group_k, g->group_v};
     const int axes[2] = {g->axis_k, g->axis_v};
-    uint64_t oc = 0, om = 0, orr = 0, fc = 0, fm = 0, fr = 0;
+    const bool paged = g->page_tokens > 0;
+    const uint64_t P = paged ? (uint64_t)g->page_tokens : 0;
+    uint64_t oc = 0, om = 0, orr = 0, fc = 0, fm = 0, fr = 0, page_bytes = 0, plist = 0;
     if (entries) entries->assign((size_t)g->layers * g->num_seqs, SeqEntry{});
     for (int l = 0; l < g->layers; ++l) {
         for (int s = 0; s < g->num_seqs; ++s) {
             SeqEntry e{};
             const int bits[2] = {bk[s], bv[s]};
+            uint64_t in_page = 0;  // paged: bytes of this sequence's page
             for (int t = 0; t < 2; ++t) {
                 const uint64_t G = groups[t], B = bits[t], c = cap[s];
                 const bool ch = axes[t] == KVQ_AXIS_CHANNEL;
@@ -156,12 +193,17 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
                 const uint64_t meta_b = (ch ? (c / G) * D : c * (D / G)) * 4;
                 const uint64_t res_b = (ch ? G * D * ib : 0) +
                                        (win_mode(*g) ? (uint64_t)(g->sinks + win_rows(*g)) * D * ib : 0);
-                e.codes[t] = oc;
-                e.codes_hs[t] = align_up(code_b, kvq::kAlign);
-                oc += e.codes_hs[t] * H;
-                e.meta[t] = om;
-                e.meta_hs[t] = align_up(meta_b, kvq::kAlign);
-                om += e.meta_hs[t] * H;
+                if (paged) {
+                    e.codes_hs[t] = align_up(P * D * B / 8, kvq::kAlign);
+                    e.meta_hs[t] = align_up((ch ? (P / G) * D : P * (D / G)) * 4, kvq::kAlign);
+                } else {
+                    e.codes[t] = oc;
+                    e.codes_hs[t] = align_up(code_b, kvq::kAlign);
+                    oc += e.codes_hs[t] * H;
+                    e.meta[t] = om;
+                    e.meta_hs[t] = align_up(meta_b, kvq::kAlign);
+                    om += e.meta_hs[t] * H;
+                }
                 e.resid[t] = orr;
                 e.resid_hs[t] = align_up(res_b, kvq::kAlign);
                 orr += e.resid_hs[t] * H;
@@ -170,9 +212,34 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
                 fr += res_b * H;
                 e.bits[t] = bits[t];
             }
+            if (paged) {
+                e.codes[0] = 0;
+                e.codes[1] = e.codes_hs[0] * H;
+                e.meta[0] = e.codes[1] + e.codes_hs[1] * H;
+                e.meta[1] = e.meta[0] + e.meta_hs[0] * H;
+                in_page = e.meta[1] + e.meta_hs[1] * H;
+                page_bytes = std::max(page_bytes, in_page);
+                e.page_shift = __builtin_ctz((unsigned)g->page_tokens);
+                e.page_list = (uint32_t)plist;
+                plist += pages_of(g, cap[s]);
+                if (plist > 0xffffffffull) return fail(KVQ_ERR_ARG, "page lists exceed 2^32 entries");
+            } else {
+                e.page_shift = kvq::kContiguousShift;
+                e.page_list = 0;
+            }
             e.cap = cap[s];
             if (entries) (*entries)[(size_t)l * g->num_seqs + s] = e;
         }
+    }
+    uint64_t num_pages = 0;
+    if (paged) {
+        num_pages = g->num_pages ? (uint64_t)g->num_pages : plist;
+        if (num_pages >= kvq::kNoPage) return fail(KVQ_ERR_ARG, "%llu pages exceed the page index range",
+                                                   (unsigned long long)num_pages);
+        if (entries)
+            for (auto& e : *entries) e.page_bytes = page_bytes;
+        oc = num_pages * page_bytes;
+        om = 0;
     }
     const uint64_t LS = (uint64_t)g->layers * g->num_seqs;
     tl->entries_bytes = align_up(LS * sizeof(SeqEntry), kvq::kAlign);
@@ -180,7 +247,8 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
     tl->args_off = tl->len_off + align_up(2 * LS * 4, kvq::kAlign);
     tl->ctr_off = tl->args_off + align_up(2 * (uint64_t)g->num_seqs * 4, kvq::kAlign);
     tl->pairs_off = tl->ctr_off + align_up((uint64_t)g->num_seqs * g->kv_heads * 4, kvq::kAlign);
-    tl->total = tl->pairs_off + align_up((uint64_t)g->num_seqs * 4, kvq::kAlign);
+    tl->pt_off = tl->pairs_off + align_up((uint64_t)g->num_seqs * 4, kvq::kAlign);
+    tl->total = tl->pt_off + align_up(std::max<uint64_t>(plist, 1) * 4, kvq::kAlign);
     sz->codes_bytes = std::max<uint64_t>(oc, kvq::kAlign);
     sz->meta_bytes = std::max<uint64_t>(om, kvq::kAlign);
     sz->residual_bytes = std::max<uint64_t>(orr, kvq::kAlign);
@@ -188,9 +256,17 @@ void layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const 
     sz->formula_codes_bytes = fc;
     sz->formula_meta_bytes = fm;
     sz->formula_residual_bytes = fr;
+    sz->page_bytes = page_bytes;
+    sz->num_pages = num_pages;
+    return KVQ_OK;
 }
 
 int group_size(const kvq_cache* c) { return c->g.q_heads / c->g.kv_heads; }
+
+// The buffer the kernels read metadata from: the page pool with paged storage.
+uint8_t* meta_pool(const kvq_cache* c) { return c->paged ? c->codes : c->meta; }
+
+const uint32_t* page_lists(const kvq_cache* c) { return (const uint32_t*)(c->table + c->tl.pt_off); }
 
 // Tokens per decode split: a multiple of the key block, grown while the grid
 // stays above ~8 workgroups per compute unit, shrunk to fit 64 KB of LDS.
@@ -216,16 +292,20 @@ int choose_chunk(const kvq_cache* c, int max_len, int n_layers) {
 int choose_split_mha(const kvq_cache* c, int max_len, int n_layers) {
     const kvq_geometry& g = c->g;
     const int unit = std::max(64, g.group_k);
+    // paged storage: a split spans at most 64 of a wave's super-tiles (the page
+    // entries the kernel keeps in one register); the last split takes up to
+    // twice the chunk
+    const long cap = c->paged ? 4096 : (1L << 24);
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
-        if (v >= unit && v % unit == 0 && v <= (1 << 24)) return v;
+        if (v >= unit && v % unit == 0 && v <= cap) return v;
     }
     // Aim at ~512 workgroups (two 4-wave workgroups per compute unit, resident
     // at once): long waves keep per-wave setup and the split merge small.
     const long pairs = (long)g.num_seqs * g.kv_heads * n_layers;
     const long nsplit = std::max(1L, 512L / pairs);
     const long cw = (max_len / nsplit) / unit * unit;
-    return (int)std::max<long>(unit, cw);
+    return (int)std::min(cap, std::max<long>(unit, cw));
 }
 
 // Tokens per workgroup of the query-group kernel (a multiple of 128, at least
@@ -241,7 +321,8 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
     const kvq_geometry& g = c->g;
     if (const char* env = std::getenv("KVQ_DECODE_CHUNK")) {  // tuning override, ignored when invalid
         const int v = std::atoi(env);
-        if (v >= 128 && v % 128 == 0 && v <= (1 << 24)) return v;
+        // (paged storage: at most 8192, 64 of a wave's tiles, whose page entries the kernel keeps in one register)
+        if (v >= 128 && v % 128 == 0 && v <= (c->paged ? 8192 : (1 << 24))) return v;
     }
     const long slots = 256L * (g.head_dim >= 256 ? 2 : 3);
     const bool one_launch = (long)n_layers * g.num_seqs <= kvq::kGqaListMax;
@@ -303,8 +384,7 @@ kvq_status kvq_plan(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk
     if ((st = check_seqs(g, cap, bk, bv))) return st;
     if (!out) return fail(KVQ_ERR_ARG, "out is NULL");
     kvq::TableLayout tl;
-    layout(g, cap, bk, bv, nullptr, out, &tl);
-    return KVQ_OK;
+    return layout(g, cap, bk, bv, nullptr, out, &tl);
 }
 
 kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
@@ -331,13 +411,32 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
     c->resid = (uint8_t*)d_residual;
     c->table = (uint8_t*)d_table;
     kvq_sizes sz;
-    layout(g, cap, bk, bv, &c->entries, &sz, &c->tl);
+    if ((st = layout(g, cap, bk, bv, &c->entries, &sz, &c->tl))) {
+        delete c;
+        return st;
+    }
+    c->slot_layout = c->entries;
+    c->slot.resize((size_t)g->layers * g->num_seqs);
+    for (size_t i = 0; i < c->slot.size(); ++i) c->slot[i] = (int32_t)(i % g->num_seqs);
+    c->paged = g->page_tokens > 0;
+    if (c->paged) {
+        c->page_bytes = sz.page_bytes;
+        c->num_pages = (uint32_t)sz.num_pages;
+        c->refs.assign(c->num_pages, 0);
+        c->free_pages.resize(c->num_pages);
+        for (uint32_t i = 0; i < c->num_pages; ++i) c->free_pages[i] = c->num_pages - 1 - i;  // page 0 on top
+        const SeqEntry& last = c->entries.back();
+        c->pt.assign((size_t)last.page_list + pages_of(g, last.cap), kvq::kNoPage);
+    } else {
+        c->pt.assign(1, 0u);
+    }
     c->lens.assign((size_t)g->layers * g->num_seqs, 0);
     c->parity.assign(g->layers, 0);
     c->args.assign(2 * (size_t)g->num_seqs, 0);
     c->max_cap = *std::max_element(cap, cap + g->num_seqs);
     std::vector<uint8_t> img(c->tl.total, 0);
     std::memcpy(img.data(), c->entries.data(), c->entries.size() * sizeof(SeqEntry));
+    std::memcpy(img.data() + c->tl.pt_off, c->pt.data(), c->pt.size() * sizeof(uint32_t));
     {
         int32_t* list = (int32_t*)(img.data() + c->tl.pairs_off);
         int n = 0;
@@ -401,6 +500,98 @@ kvq_status kvq_get_region(const kvq_cache* c, int32_t layer, int32_t seq, kvq_re
 
 namespace {
 
+// ---- paged storage: page management on the host, mirrored to the device
+
+int32_t* len_dev(const kvq_cache* c, int layer) {
+    return (int32_t*)(c->table + c->tl.len_off) + ((size_t)c->parity[layer] * c->g.layers + layer) * c->g.num_seqs;
+}
+
+// Upload the host state of one layer: its table entries and current lengths.
+kvq_status upload_layer(kvq_cache* c, int layer, hipStream_t s) {
+    const int S = c->g.num_seqs;
+    hipError_t e = hipMemcpyAsync(c->table + (size_t)layer * S * sizeof(SeqEntry), &c->entries[(size_t)layer * S],
+                                  (size_t)S * sizeof(SeqEntry), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(len_dev(c, layer), &c->lens[(size_t)layer * S], (size_t)S * sizeof(int32_t),
+                           hipMemcpyHostToDevice, s);
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "uploading the cache table");
+}
+
+// Upload changed page-list entries (indices into the host copy): a scatter
+// kernel carrying the pairs in its arguments when they are few, else copies of
+// the runs that cover them.
+kvq_status upload_pages(kvq_cache* c, std::vector<uint32_t>& idx, hipStream_t s) {
+    if (idx.empty()) return KVQ_OK;
+    std::sort(idx.begin(), idx.end());
+    idx.erase(std::unique(idx.begin(), idx.end()), idx.end());
+    uint32_t* dev = (uint32_t*)(c->table + c->tl.pt_off);
+    hipError_t e = hipSuccess;
+    if (idx.size() <= (size_t)kvq::kPageUpdateMax) {
+        kvq::PageUpdates u;
+        u.count = (int32_t)idx.size();
+        for (size_t i = 0; i < idx.size(); ++i) {
+            u.index[i] = idx[i];
+            u.value[i] = c->pt[idx[i]];
+        }
+        e = kvq::launch_page_updates(dev, u, s);
+    } else {
+        size_t a = 0;
+        for (size_t i = 1; i <= idx.size() && e == hipSuccess; ++i) {
+            if (i < idx.size() && idx[i] <= idx[i - 1] + 64) continue;
+            const size_t n = idx[i - 1] + 1 - idx[a];
+            e = hipMemcpyAsync(dev + idx[a], c->pt.data() + idx[a], n * sizeof(uint32_t), hipMemcpyHostToDevice, s);
+            a = i;
+        }
+    }
+    return e == hipSuccess ? KVQ_OK : hip_fail(e, "uploading page lists");
+}
+
+void release_page(kvq_cache* c, uint32_t p) {
+    if (p == kvq::kNoPage) return;
+    if (--c->refs[p] == 0) c->free_pages.push_back(p);
+}
+
+uint32_t take_page(kvq_cache* c) {
+    const uint32_t p = c->free_pages.back();
+    c->free_pages.pop_back();
+    c->refs[p] = 1;
+    return p;
+}
+
+// Map every page an append writes into (tokens [len, len + n_new[s]) of each
+// sequence, in layers [layer, layer + n_layers)) that has no page yet, after
+// checking that the pool has enough free pages.
+kvq_status map_append_pages(kvq_cache* c, int32_t layer, int32_t n_layers, const int32_t* n_new, hipStream_t s) {
+    if (!c->paged) return KVQ_OK;
+    const int S = c->g.num_seqs;
+    size_t need = 0;
+    for (int l = layer; l < layer + n_layers; ++l)
+        for (int q = 0; q < S; ++q) {
+            if (!n_new[q]) continue;
+            const SeqEntry& e = c->entries[(size_t)l * S + q];
+            const int len = c->lens[(size_t)l * S + q];
+            for (int i = len >> e.page_shift; i <= (len + n_new[q] - 1) >> e.page_shift; ++i)
+                need += c->pt[(size_t)e.page_list + i] == kvq::kNoPage;
+        }
+    if (need > c->free_pages.size())
+        return fail(KVQ_ERR_CAPACITY, "page pool exhausted: the append needs %zu new pages, %zu are free", need,
+                    c->free_pages.size());
+    std::vector<uint32_t> changed;
+    for (int l = layer; l < layer + n_layers; ++l)
+        for (int q = 0; q < S; ++q) {
+            if (!n_new[q]) continue;
+            const SeqEntry& e = c->entries[(size_t)l * S + q];
+            const int len = c->lens[(size_t)l * S + q];
+            for (int i = len >> e.page_shift; i <= (len + n_new[q] - 1) >> e.page_shift; ++i) {
+                uint32_t& slot = c->pt[(size_t)e.page_list + i];
+                if (slot != kvq::kNoPage) continue;
+                slot = take_page(c);
+                changed.push_back(e.page_list + i);
+            }
+        }
+    return upload_pages(c, changed, s);
+}
+
 // Quantize-append of the same per-sequence counts into layers [layer, layer +
 // n_layers) in one launch (1 <= n_layers <= 64, checked by the callers).
 // k_new, v_new: [n_layers][sum n_new][kv_heads][head_dim].
@@ -463,8 +654,9 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
         a = kvq::TensorArgs{};
         a.src = srcs[t];
         a.codes = c->codes;
-        a.meta = c->meta;
+        a.meta = meta_pool(c);
         a.resid = c->resid;
+        a.pages = page_lists(c);
         a.table = entries;
         a.len_in = len_base + ((size_t)p * g.layers + layer) * S;
         a.len_out = t == 0 ? len_base + ((size_t)(1 - p) * g.layers + layer) * S : nullptr;
@@ -502,7 +694,7 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
     }
     if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");
     *max_new = max_n;
-    return KVQ_OK;
+    return map_append_pages(c, layer, n_layers, n_new, hs);
 }
 
 // The launch of a prepared append: quantize (and the full-precision window copy).
@@ -622,8 +814,9 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     a.ws_ml = (float*)workspace;
     a.ws_o = (float*)((uint8_t*)workspace + ml_bytes);
     a.codes = c->codes;
-    a.meta = c->meta;
+    a.meta = meta_pool(c);
     a.resid = c->resid;
+    a.pages = page_lists(c);
     a.table = (const SeqEntry*)c->table + (size_t)layer * S;
     a.len = (const int32_t*)(c->table + c->tl.len_off) + ((size_t)c->parity[layer] * g.layers + layer) * S;
     a.qscale = softmax_scale * 1.4426950408889634f;
@@ -842,8 +1035,9 @@ kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float*
         kvq::DequantArgs a{};
         a.out = outs[t];
         a.codes = c->codes;
-        a.meta = c->meta;
+        a.meta = meta_pool(c);
         a.resid = c->resid;
+        a.pages = page_lists(c);
         a.entry = c->entries[(size_t)layer * g.num_seqs + seq];
         a.tensor = t;
         a.len = len;
@@ -866,6 +1060,253 @@ kvq_status kvq_dequantize(const kvq_cache* c, int32_t layer, int32_t seq, float*
     return KVQ_OK;
 }
 
+kvq_status kvq_gather_sequences(kvq_cache* c, int32_t layer0, int32_t n_layers, const int32_t* src, void* stream) {
+    g_last_error.clear();
+    if (!c || !src) return fail(KVQ_ERR_ARG, "cache or src is NULL");
+    const kvq_geometry& g = c->g;
+    const int S = g.num_seqs;
+    if (n_layers < 1 || layer0 < 0 || layer0 > g.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    for (int q = 0; q < S; ++q) {
+        if (src[q] < 0 || src[q] >= S) return fail(KVQ_ERR_ARG, "src[%d] = %d out of range", q, src[q]);
+        const int o = src[q];
+        if (c->bits_k[q] != c->bits_k[o] || c->bits_v[q] != c->bits_v[o] || c->cap[q] != c->cap[o])
+            return fail(KVQ_ERR_ARG, "sequences %d and %d differ in bits or capacity", q, o);
+    }
+    // keeper[o]: the sequence that takes o's own regions and pages (o itself
+    // when it stays, else the first sequence copying it); -1: o is dropped
+    std::vector<int> keeper(S, -1);
+    for (int q = 0; q < S; ++q)
+        if (src[q] == q) keeper[q] = q;
+    for (int q = 0; q < S; ++q)
+        if (keeper[src[q]] < 0) keeper[src[q]] = q;
+    const int P = g.page_tokens;
+    auto partial_page = [&](int len) { return P && len % P ? len / P : -1; };  // index of a page still filling
+    if (c->paged) {  // enough free pages for the extra copies of incomplete pages, counting the call's releases
+        std::vector<uint32_t> refs = c->refs;
+        size_t freed = 0, need = 0;
+        for (int l = layer0; l < layer0 + n_layers; ++l) {
+            for (int q = 0; q < S; ++q) {
+                const SeqEntry& eo = c->entries[(size_t)l * S + src[q]];
+                const uint32_t used = pages_of(&g, c->lens[(size_t)l * S + src[q]]);
+                for (uint32_t i = 0; i < used; ++i)
+                    if (c->pt[(size_t)eo.page_list + i] != kvq::kNoPage) ++refs[c->pt[(size_t)eo.page_list + i]];
+                if (keeper[src[q]] != q && partial_page(c->lens[(size_t)l * S + src[q]]) >= 0) ++need;
+            }
+            for (int q = 0; q < S; ++q) {
+                const SeqEntry& e = c->entries[(size_t)l * S + q];
+                for (uint32_t i = 0; i < pages_of(&g, c->cap[q]); ++i) {
+                    const uint32_t p = c->pt[(size_t)e.page_list + i];
+                    if (p != kvq::kNoPage && --refs[p] == 0) ++freed;
+                }
+            }
+        }
+        if (need > c->free_pages.size() + freed)
+            return fail(KVQ_ERR_CAPACITY, "page pool exhausted: the gather needs %zu new pages, %zu are free", need,
+                        c->free_pages.size() + freed);
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    const uint64_t H = g.kv_heads, D = g.head_dim;
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const size_t base = (size_t)l * S;
+        // regions: a dropped sequence's slot goes to an extra copy of the same class
+        std::vector<int32_t> new_slot(S, -1);
+        std::vector<int> spare;  // dropped sequences, by class when taken
+        for (int o = 0; o < S; ++o)
+            if (keeper[o] < 0) spare.push_back(o);
+        std::vector<int> copies;  // sequences that receive a copy
+        for (int q = 0; q < S; ++q) {
+            if (keeper[src[q]] == q) {
+                new_slot[q] = c->slot[base + src[q]];
+                continue;
+            }
+            for (size_t i = 0; i < spare.size(); ++i) {
+                const int o = spare[i];
+                if (o >= 0 && c->bits_k[o] == c->bits_k[q] && c->bits_v[o] == c->bits_v[q] && c->cap[o] == c->cap[q]) {
+                    new_slot[q] = c->slot[base + o];
+                    spare[i] = -1;
+                    break;
+                }
+            }
+            if (new_slot[q] < 0) return fail(KVQ_ERR_ARG, "no region of sequence %d's class is free", q);  // unreachable
+            copies.push_back(q);
+        }
+        for (int q : copies) {
+            const int o = src[q];
+            const SeqEntry& from = c->slot_layout[base + c->slot[base + o]];
+            const SeqEntry& to = c->slot_layout[base + new_slot[q]];
+            const int len = c->lens[base + o];
+            for (int t = 0; t < 2; ++t) {
+                hipError_t e = hipSuccess;
+                if (from.resid_hs[t])
+                    e = hipMemcpyAsync(c->resid + to.resid[t], c->resid + from.resid[t], from.resid_hs[t] * H,
+                                       hipMemcpyDeviceToDevice, hs);
+                if (!c->paged && e == hipSuccess) {
+                    // the first len rows of codes and their metadata, every head
+                    const bool ch = (t == 0 ? g.axis_k : g.axis_v) == KVQ_AXIS_CHANNEL;
+                    const uint64_t G = t == 0 ? g.group_k : g.group_v, B = from.bits[t];
+                    const uint64_t rows = ch ? len / G * G : len;
+                    const uint64_t cb = rows * D * B / 8, mb = (ch ? len / G * D : (uint64_t)len * (D / G)) * 4;
+                    if (cb)
+                        e = hipMemcpy2DAsync(c->codes + to.codes[t], to.codes_hs[t], c->codes + from.codes[t],
+                                             from.codes_hs[t], cb, H, hipMemcpyDeviceToDevice, hs);
+                    if (mb && e == hipSuccess)
+                        e = hipMemcpy2DAsync(c->meta + to.meta[t], to.meta_hs[t], c->meta + from.meta[t],
+                                             from.meta_hs[t], mb, H, hipMemcpyDeviceToDevice, hs);
+                }
+                if (e != hipSuccess) return hip_fail(e, "copying a sequence");
+            }
+        }
+        std::vector<uint32_t> changed;
+        if (c->paged) {
+            // new lists: the source's pages up to its length, shared; an extra
+            // copy of a page still filling gets a page of its own
+            std::vector<std::vector<uint32_t>> nl(S);
+            for (int q = 0; q < S; ++q) {
+                const SeqEntry& eo = c->entries[base + src[q]];
+                const uint32_t n = pages_of(&g, c->cap[q]), used = pages_of(&g, c->lens[base + src[q]]);
+                nl[q].assign(n, kvq::kNoPage);
+                for (uint32_t i = 0; i < used; ++i) {
+                    nl[q][i] = c->pt[(size_t)eo.page_list + i];
+                    if (nl[q][i] != kvq::kNoPage) ++c->refs[nl[q][i]];
+                }
+            }
+            for (int q = 0; q < S; ++q) {
+                const SeqEntry& e = c->entries[base + q];
+                for (uint32_t i = 0; i < pages_of(&g, c->cap[q]); ++i) release_page(c, c->pt[(size_t)e.page_list + i]);
+            }
+            for (int q : copies) {
+                const int i = partial_page(c->lens[base + src[q]]);
+                if (i < 0 || nl[q][i] == kvq::kNoPage) continue;
+                const uint32_t p = nl[q][i], fresh = take_page(c);
+                --c->refs[p];  // still held by the keeper
+                nl[q][i] = fresh;
+                hipError_t e = hipMemcpyAsync(c->codes + (uint64_t)fresh * c->page_bytes,
+                                              c->codes + (uint64_t)p * c->page_bytes, c->page_bytes,
+                                              hipMemcpyDeviceToDevice, hs);
+                if (e != hipSuccess) return hip_fail(e, "copying a page");
+            }
+            for (int q = 0; q < S; ++q) {
+                const SeqEntry& e = c->entries[base + q];
+                for (uint32_t i = 0; i < nl[q].size(); ++i) {
+                    uint32_t& slot = c->pt[(size_t)e.page_list + i];
+                    if (slot != nl[q][i]) {
+                        slot = nl[q][i];
+                        changed.push_back(e.page_list + i);
+                    }
+                }
+            }
+        }
+        // entries and lengths
+        std::vector<SeqEntry> ne(S);
+        std::vector<int32_t> nlen(S);
+        for (int q = 0; q < S; ++q) {
+            ne[q] = c->slot_layout[base + new_slot[q]];
+            ne[q].page_list = c->entries[base + q].page_list;
+            ne[q].ring = c->entries[base + src[q]].ring;
+            nlen[q] = c->lens[base + src[q]];
+        }
+        for (int q = 0; q < S; ++q) {
+            c->entries[base + q] = ne[q];
+            c->slot[base + q] = new_slot[q];
+            c->lens[base + q] = nlen[q];
+        }
+        kvq_status st = upload_pages(c, changed, hs);
+        if (st == KVQ_OK) st = upload_layer(c, l, hs);
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_evict_tokens(kvq_cache* c, int32_t layer0, int32_t n_layers, int32_t seq, int32_t first, int32_t count,
+                            void* stream) {
+    g_last_error.clear();
+    if (!c) return fail(KVQ_ERR_ARG, "cache is NULL");
+    const kvq_geometry& g = c->g;
+    const int S = g.num_seqs;
+    if (n_layers < 1 || layer0 < 0 || layer0 > g.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    if (seq < 0 || seq >= S) return fail(KVQ_ERR_ARG, "seq %d out of range", seq);
+    if (!c->paged) return fail(KVQ_ERR_UNSUPPORTED, "eviction needs paged storage");
+    if (first < 0 || count < 0) return fail(KVQ_ERR_ARG, "first (%d) and count (%d) must be >= 0", first, count);
+    if (count == 0) return KVQ_OK;
+    const int P = g.page_tokens;
+    if (first % P || count % P) return fail(KVQ_ERR_ARG, "first and count must be multiples of page_tokens (%d)", P);
+    if (first < g.sinks) return fail(KVQ_ERR_ARG, "the sinks [0, %d) cannot be evicted", g.sinks);
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const int len = c->lens[(size_t)l * S + seq];
+        if ((long)first + count > (long)len / P * P)
+            return fail(KVQ_ERR_ARG, "layer %d: tokens [%d, %d) are not whole pages below length %d", l, first,
+                        first + count, len);
+        if (win_mode(g) && (long)first + count > (long)len - win_rows(g))
+            return fail(KVQ_ERR_ARG, "layer %d: tokens [%d, %d) reach the last window + block = %d tokens", l, first,
+                        first + count, win_rows(g));
+    }
+    hipStream_t hs = (hipStream_t)stream;
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const size_t i = (size_t)l * S + seq;
+        SeqEntry& e = c->entries[i];
+        uint32_t* list = &c->pt[e.page_list];
+        const uint32_t n = pages_of(&g, c->cap[seq]), i0 = first / P, k = count / P;
+        for (uint32_t j = i0; j < i0 + k; ++j) release_page(c, list[j]);
+        for (uint32_t j = i0; j < n; ++j) list[j] = j + k < n ? list[j + k] : kvq::kNoPage;
+        std::vector<uint32_t> changed;
+        for (uint32_t j = i0; j < n; ++j) changed.push_back(e.page_list + j);
+        c->lens[i] -= count;
+        if (win_mode(g)) e.ring = (int32_t)(((long)e.ring + count) % win_rows(g));
+        kvq_status st = upload_pages(c, changed, hs);
+        if (st == KVQ_OK) st = upload_layer(c, l, hs);
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_reset_sequence(kvq_cache* c, int32_t layer0, int32_t n_layers, int32_t seq, void* stream) {
+    g_last_error.clear();
+    if (!c) return fail(KVQ_ERR_ARG, "cache is NULL");
+    const kvq_geometry& g = c->g;
+    const int S = g.num_seqs;
+    if (n_layers < 1 || layer0 < 0 || layer0 > g.layers - n_layers)
+        return fail(KVQ_ERR_ARG, "layers [%d, %d + %d) out of range", layer0, layer0, n_layers);
+    if (seq < 0 || seq >= S) return fail(KVQ_ERR_ARG, "seq %d out of range", seq);
+    hipStream_t hs = (hipStream_t)stream;
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+        const size_t i = (size_t)l * S + seq;
+        SeqEntry& e = c->entries[i];
+        std::vector<uint32_t> changed;
+        if (c->paged) {
+            for (uint32_t j = 0; j < pages_of(&g, c->cap[seq]); ++j) {
+                uint32_t& p = c->pt[(size_t)e.page_list + j];
+                if (p == kvq::kNoPage) continue;
+                release_page(c, p);
+                p = kvq::kNoPage;
+                changed.push_back(e.page_list + j);
+            }
+        }
+        c->lens[i] = 0;
+        e.ring = 0;
+        kvq_status st = upload_pages(c, changed, hs);
+        if (st == KVQ_OK) st = upload_layer(c, l, hs);
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_page_list(const kvq_cache* c, int32_t layer, int32_t seq, uint32_t* out, int32_t max_out,
+                         int32_t* n_pages, int64_t* free_pages) {
+    g_last_error.clear();
+    if (!c || (!out && max_out > 0) || !n_pages) return fail(KVQ_ERR_ARG, "cache, out or n_pages is NULL");
+    if (layer < 0 || layer >= c->g.layers) return fail(KVQ_ERR_ARG, "layer %d out of range", layer);
+    if (seq < 0 || seq >= c->g.num_seqs) return fail(KVQ_ERR_ARG, "seq %d out of range", seq);
+    if (!c->paged) return fail(KVQ_ERR_UNSUPPORTED, "the cache has contiguous storage");
+    const SeqEntry& e = c->entries[(size_t)layer * c->g.num_seqs + seq];
+    const int32_t n = (int32_t)pages_of(&c->g, c->cap[seq]);
+    *n_pages = n;
+    for (int32_t i = 0; i < std::min(n, max_out); ++i) out[i] = c->pt[(size_t)e.page_list + i];
+    if (free_pages) *free_pages = (int64_t)c->free_pages.size();
+    return KVQ_OK;
+}
+
 kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* src, int32_t src_seq, int32_t layer0,
                              int32_t n_layers, void* stream) {
     g_last_error.clear();
@@ -875,7 +1316,8 @@ kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* s
                       gd.q_heads == gs.q_heads && gd.head_dim == gs.head_dim && gd.group_k == gs.group_k &&
                       gd.group_v == gs.group_v && gd.axis_k == gs.axis_k && gd.axis_v == gs.axis_v &&
                       gd.in_dtype == gs.in_dtype && gd.meta_dtype == gs.meta_dtype && gd.window == gs.window &&
-                      gd.sinks == gs.sinks && gd.rope_base == gs.rope_base;
+                      gd.sinks == gs.sinks && gd.rope_base == gs.rope_base && gd.page_tokens == gs.page_tokens &&
+                      gd.num_pages == gs.num_pages;
     if (!same) return fail(KVQ_ERR_ARG, "the caches' geometries differ");
     if (dst_seq < 0 || dst_seq >= gd.num_seqs || src_seq < 0 || src_seq >= gs.num_seqs)
         return fail(KVQ_ERR_ARG, "sequence index out of range");
@@ -885,6 +1327,13 @@ kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* s
     if (dst->bits_k[dst_seq] != src->bits_k[src_seq] || dst->bits_v[dst_seq] != src->bits_v[src_seq] ||
         dst->cap[dst_seq] != src->cap[src_seq])
         return fail(KVQ_ERR_ARG, "the sequences' bits or capacities differ");
+    if (dst->paged) {  // one cache: a gather that forks src_seq onto dst_seq
+        if (dst != src) return fail(KVQ_ERR_UNSUPPORTED, "paged storage copies sequences within one cache only");
+        std::vector<int32_t> map(gd.num_seqs);
+        for (int q = 0; q < gd.num_seqs; ++q) map[q] = q;
+        map[dst_seq] = src_seq;
+        return kvq_gather_sequences(dst, layer0, n_layers, map.data(), stream);
+    }
     hipStream_t hs = (hipStream_t)stream;
     const int S = gd.num_seqs;
     for (int l = layer0; l < layer0 + n_layers; ++l) {

@@ -41,12 +41,15 @@ __device__ __forceinline__ void token_axis_row(const TensorArgs& a, int r, int u
     const float s32 = (mx - mn) / L;
     const uint32_t sb = f32_to_f16_bits(s32), zb = f32_to_f16_bits(mn);
     const float s = f16_to_f32(sb), z = f16_to_f32(zb);
-    uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
-    if ((u & (UG - 1)) == 0) meta[(size_t)t * (D / G) + u / UG] = sb | (zb << 16);
+    const PageRow pr = page_row(a.pages, e, t);
+    uint32_t* meta = (uint32_t*)(a.meta + pr.base + e.meta[T] + (size_t)head * e.meta_hs[T]);
+    if ((u & (UG - 1)) == 0) meta[(size_t)pr.row * (D / G) + u / UG] = sb | (zb << 16);
     uint32_t c[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) c[j] = quant_code(x[j], s, z, L);
-    uint32_t* dst = (uint32_t*)(a.codes + e.codes[T] + (size_t)head * e.codes_hs[T] + (size_t)t * (D * B / 8)) + u * B;
+    uint32_t* dst =
+        (uint32_t*)(a.codes + pr.base + e.codes[T] + (size_t)head * e.codes_hs[T] + (size_t)pr.row * (D * B / 8)) +
+        u * B;
     store_codes_rt(B, c, dst);
 }
 
@@ -104,7 +107,7 @@ __device__ __forceinline__ void window_rows(const TensorArgs& k, const TensorArg
         const int j = idx / D, ch = idx % D;
         const int t = j < n1 ? len0 + j : s2 + (j - n1), i = t - len0;
         const size_t so = ((size_t)(row_start + i) * k.kv_heads + head) * D + ch;
-        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows) * D + ch;
+        const size_t dof = (size_t)window_row(t, k.sinks, k.win_rows, e.ring) * D + ch;
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
             const TensorArgs& x = T == 0 ? k : v;

@@ -424,11 +424,15 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     const int lng = __builtin_ctz(ngrp);
     const int tpg = lgv >= 4 ? 1 << (lgv - 4) : 1;          // 16-channel output tiles per value group
 
+    // head kvh's codes and metadata inside a page (pool offsets with contiguous
+    // storage); a 32-token tile lies in one page, at byte offset pb of the pool,
+    // whose first token is (t0 >> psh) << psh
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
-    const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
+    const uint8_t* km = a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0];
     const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
-    const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
+    const uint8_t* vm = a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1];
+    const int psh = e.page_shift;
 
     // ---- one tile of codes and metadata in registers
     uint32_t kw[2][KWL];    // key words: token rows 8(n>>2) + 4h + (n&3), lane group g's channels
@@ -441,16 +445,18 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         if constexpr (U >= 4) return 32 * (g * KU + c / 4) + 8 * (c % 4);
         else return 32 * (g >> 1) + 16 * (g & 1) + 8 * c;
     };
-    auto load_keys = [&](int t0) {
+    auto load_keys = [&](int t0, uint64_t pb) {
         const int wo = U >= 4 ? g * KU * BK : (g >> 1) * BK + (g & 1) * (BK / 2);
+        const int ps = (t0 >> psh) << psh;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), nqk - 1);
-            load_n<KWL, KALIGN>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + wo, kw[h]);
+            const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), nqk - 1) - ps;
+            load_n<KWL, KALIGN>((const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8)) + wo, kw[h]);
         }
     };
-    auto load_kmeta = [&](int t0) {
-        const uint32_t* src = km + (size_t)(t0 >> lgk) * D;
+    auto load_kmeta = [&](int t0, uint64_t pb) {
+        const int ps = (t0 >> psh) << psh;
+        const uint32_t* src = (const uint32_t*)(km + pb) + (size_t)((t0 - ps) >> lgk) * D;
 #pragma unroll
         for (int k = 0; k < NKP; ++k) {
             const int p = min(lane + 64 * k, D / 2 - 1), cb = (p >> 2) * 8, jj = p & 3;
@@ -462,14 +468,16 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
             kmw[2 * k + 1] = src[cb + c1];
         }
     };
-    auto load_values = [&](int t0) {
-        const int t = min(t0 + (lane >> 1), wb - 1);
-        load_n<VWL, VALIGN>((const uint32_t*)(vc + (size_t)t * VRB + (lane & 1) * (VRB / 2)), vw);
+    auto load_values = [&](int t0, uint64_t pb) {
+        const int ps = (t0 >> psh) << psh;
+        const int t = min(t0 + (lane >> 1), wb - 1) - ps;
+        load_n<VWL, VALIGN>((const uint32_t*)(vc + pb + (size_t)t * VRB + (lane & 1) * (VRB / 2)), vw);
+        const uint32_t* vmp = (const uint32_t*)(vm + pb);
 #pragma unroll
         for (int k = 0; k < NVML; ++k) {
             const int f = min(lane + 64 * k, 32 * ngrp - 1);
-            const int tt = min(t0 + (f >> lng), wb - 1);
-            vmw[k] = vm[(size_t)tt * ngrp + (f & (ngrp - 1))];
+            const int tt = min(t0 + (f >> lng), wb - 1) - ps;
+            vmw[k] = vmp[(size_t)tt * ngrp + (f & (ngrp - 1))];
         }
     };
 
@@ -480,11 +488,18 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     // so that every load of the main loop is unconditional and the compiler's
     // wait counts stay exact
     const int nqt = nqk > wa ? min(ntiles, (nqk - wa) >> 5) : 0;
+    // Lane k of pev holds the page of this wave's k-th tile of the loop below
+    // (tile wave + 4k, at most 64 of them: the host keeps splits within 8192
+    // tokens), so that the loop reads it with a lane read instead of a
+    // dependent memory load.
+    uint32_t pev = 0;
     if (wave < nqt) {
+        pev = a.pages[e.page_list + ((wa + 32 * min(wave + 4 * lane, nqt - 1)) >> psh)];
         const int t0 = wa + 32 * wave;
-        load_values(t0);
-        load_kmeta(t0);
-        load_keys(t0);
+        const uint64_t pb = (uint64_t)__builtin_amdgcn_readlane(pev, 0) * e.page_bytes;
+        load_values(t0, pb);
+        load_kmeta(t0, pb);
+        load_keys(t0, pb);
     }
     // ---- q' rows of this workgroup (rows >= RQ are 0), kept below 2^14 by
     // 2^-eqs: fp32 in natural channel order, and fp16 pairs in key-fragment order
@@ -611,7 +626,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         float p[8];
         const float mb = m - (float)kb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sc[j] - mb);
+        for (int j = 0; j < 8; ++j) p[j] = exp2_for_asm(sc[j] - mb);  // mul_split's asm reads them
         uint32_t pb[4];  // 2^kb p truncated to fp16 pairs
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) pb[jj] = pk_rtz(p[2 * jj], p[2 * jj + 1]);
@@ -662,14 +677,16 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 
     // ---- tiles with quantized keys: the next tile's words are requested as
     // soon as this tile's are consumed (the last tile re-requests itself)
-    for (int i = wave; i < nqt; i += 4) {
+    for (int i = wave, k = 0; i < nqt; i += 4, ++k) {
         const int t0 = wa + 32 * i;
-        const int tn = wa + 32 * (i + 4 < nqt ? i + 4 : i);
+        const bool more = i + 4 < nqt;
+        const int tn = wa + 32 * (more ? i + 4 : i);
+        const uint64_t pbn = (uint64_t)__builtin_amdgcn_readlane(pev, more ? k + 1 : k) * e.page_bytes;
         const int kb_tile = stage_values();
         const int fk = stage_kmeta();
         __builtin_amdgcn_sched_barrier(0);
-        load_values(tn);
-        load_kmeta(tn);
+        load_values(tn, pbn);
+        load_kmeta(tn, pbn);
         __builtin_amdgcn_sched_barrier(0);  // the requests go out before the arithmetic
         wave_lds_sync();
 
@@ -712,7 +729,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 c1 = mfma(a1f, bl, c1);
             });
             __builtin_amdgcn_sched_barrier(0);
-            load_keys(tn);
+            load_keys(tn, pbn);
             __builtin_amdgcn_sched_barrier(0);
             const float bias = col4_sum(bz) * __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
             const float cs = __builtin_amdgcn_ldexpf(1.0f, 16 + fk + eqs);
@@ -731,7 +748,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     for (int i = wave; i < ntiles; i += 4) {
         if (i < nqt) continue;
         const int t0 = wa + 32 * i;
-        load_values(t0);
+        load_values(t0, (uint64_t)a.pages[e.page_list + (t0 >> psh)] * e.page_bytes);
         const int kb_tile = stage_values();
         wave_lds_sync();
         // keys and queries both as fp16 hi + lo (three MFMAs)

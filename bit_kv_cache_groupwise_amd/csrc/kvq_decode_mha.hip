@@ -488,11 +488,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     const int nqk = a.win_mode ? te : (len >> lgk) << lgk;
     const int qend = min(wb, nqk);
 
+    // head kvh's codes and metadata inside a page (pool offsets with contiguous storage)
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
-    const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
+    const uint8_t* km = a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0];
     const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
-    const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
+    const uint8_t* vm = a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1];
     const int lgv = a.log2_group_v;
     const int vgpr = D >> lgv;           // value groups per row
     const int vg = (32 * cg) >> lgv;     // this lane's value group
@@ -523,19 +524,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     // loads exactly and keep the later stages in flight.
     const int tlast = qend - 1;
     const int blast = tlast >> lgk;
+    // Pages: a super-tile (64-aligned, pages hold a multiple of 64 tokens) lies
+    // in one page. Lane k of pev holds the page of this wave's k-th super-tile,
+    // clamped like the loads (the host keeps a split within 64 of them), so the
+    // loop reads it with a lane read instead of a dependent memory load.
+    const int st0 = wa + 64 * wave;
+    constexpr int STEP = NW * 64;
+    const int psh = e.page_shift;
+    uint32_t pev = 0;
+    if (st0 < qend) pev = a.pages[e.page_list + (min(st0 + STEP * lane, tlast) >> psh)];
     auto load_stage = [&](int st, St& r) {
+        const int sc0 = min(st, tlast);
+        const uint64_t pb = (uint64_t)__builtin_amdgcn_readlane(pev, min((st - st0) / STEP, 63)) * e.page_bytes;
+        const int ps = (sc0 >> psh) << psh;  // first token of the page
         const int t0 = st + ts;
 #pragma unroll
         for (int s = 0; s < UPR; ++s) {
-            const int t = min(t0 + s * TPW, tlast);
-            load_words<BK>((const uint32_t*)(kc + (size_t)t * (D * BK / 8)) + cg * BK, r.kw[s]);
-            load_words<BV>((const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + cg * BV, r.vw[s]);
-            r.vmw[s] = ld_stream(vm + (size_t)t * vgpr + vg);
+            const int t = min(t0 + s * TPW, tlast) - ps;
+            load_words<BK>((const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8)) + cg * BK, r.kw[s]);
+            load_words<BV>((const uint32_t*)(vc + pb + (size_t)t * (D * BV / 8)) + cg * BV, r.vw[s]);
+            r.vmw[s] = ld_stream((const uint32_t*)(vm + pb) + (size_t)t * vgpr + vg);
         }
-        const int b0 = min(st, tlast) >> lgk;
-        const int b1 = two_blocks ? min(b0 + 1, blast) : b0;
-        load_words_n<KPL>(km + (size_t)b0 * D + KPL * lane, r.kmw[0]);
-        load_words_n<KPL>(km + (size_t)b1 * D + KPL * lane, r.kmw[1]);
+        const int b0 = sc0 >> lgk;
+        const int b1 = (two_blocks ? min(b0 + 1, blast) : b0) - (ps >> lgk);
+        const uint32_t* kmp = (const uint32_t*)(km + pb);
+        load_words_n<KPL>(kmp + (size_t)(b0 - (ps >> lgk)) * D + KPL * lane, r.kmw[0]);
+        load_words_n<KPL>(kmp + (size_t)b1 * D + KPL * lane, r.kmw[1]);
     };
 
     // Online softmax over this lane's UPR scores (one per sub-tile), then the value rows.
@@ -559,7 +573,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 #pragma unroll
         for (int s = 0; s < UPR; ++s) {
             if (valid[s]) {
-                const float p = __builtin_amdgcn_exp2f(sc[s] - m24);
+                const float p = exp2_for_asm(sc[s] - m24);  // read by the mix asm below
                 lsum += p;
                 zacc = mix_hi(vmw[s], p, zacc);
                 ValueAxpy f{mix_lo(vmw[s], p, 0.f), acc};
@@ -641,10 +655,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 
     // ---- quantized keys: super-tiles of 64 tokens interleaved across waves,
     // a ring of NS register stages keeps NS-1 super-tiles in flight
-    if (wa + 64 * wave < qend) {
-        constexpr int STEP = NW * 64;
+    if (st0 < qend) {
         St rg[NS];
-        int st = wa + 64 * wave;
+        int st = st0;
 #pragma unroll
         for (int i = 0; i < NS - 1; ++i) load_stage(st + i * STEP, rg[i]);
         bool more = true;
@@ -675,8 +688,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
                 const int t = st + s * TPW + ts;
                 valid[s] = t < wb;
                 const int tc = valid[s] ? t : wb - 1;
-                load_words<BV>((const uint32_t*)(vc + (size_t)tc * (D * BV / 8)) + cg * BV, vw[s]);
-                vmw[s] = vm[(size_t)tc * vgpr + vg];
+                const PageRow pr = page_row(a.pages, e, tc);
+                load_words<BV>((const uint32_t*)(vc + pr.base + (size_t)pr.row * (D * BV / 8)) + cg * BV, vw[s]);
+                vmw[s] = ((const uint32_t*)(vm + pr.base))[(size_t)pr.row * vgpr + vg];
                 const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 32 * cg;
                 float x[32];
                 if (a.in_dtype == 0) load32<0>(kr, base, x);
@@ -713,7 +727,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
             for (int s = 0; s < UPR; ++s) {
                 const int i = st + s * TPW + ts;
                 valid[s] = i < nfp;
-                rows[s] = valid[s] ? window_row(fp_token(a, len, te, i), a.sinks, a.win_rows) : 0;
+                rows[s] = valid[s] ? window_row(fp_token(a, len, te, i), a.sinks, a.win_rows, e.ring) : 0;
                 float x[32];
                 row32(kwn, (size_t)rows[s] * D + 32 * cg, x);
                 float part = 0.f;

@@ -92,8 +92,33 @@ __device__ __forceinline__ int fp_token(const DecodeArgs& a, int len, int te, in
     const int rs = te > ns ? te : ns;
     return i < ns ? i : rs + (i - ns);
 }
-__device__ __forceinline__ int window_row(int t, int sinks, int win_rows) {
-    return t < sinks ? t : sinks + t % win_rows;
+// ring: the sequence's ring offset (tokens evicted before the window, mod win_rows)
+__device__ __forceinline__ int window_row(int t, int sinks, int win_rows, int ring) {
+    return t < sinks ? t : sinks + (t + ring) % win_rows;
+}
+
+// 2^x (v_exp_f32) for results that inline asm reads. On gfx940-class parts a
+// VALU instruction that reads the result of a transcendental one (exp, log,
+// rcp, ...) in the very next slot gets the old register contents; the
+// compiler inserts the wait state for its own instructions but does not look
+// inside asm blocks, so an asm consumer scheduled right after the exp read a
+// stale value. The wait state travels with the exp here, whatever follows it.
+__device__ __forceinline__ float exp2_for_asm(float x) {
+    float d;
+    asm("v_exp_f32 %0, %1\n\ts_nop 0" : "=v"(d) : "v"(x));
+    return d;
+}
+
+// Token t of a table entry: the byte offset of its page in the codes pool (the
+// metadata pool too with paged storage) and its row inside the page. Both
+// storages take the same path: a contiguous entry has one page at offset 0
+// (page_bytes 0) whose rows are the tokens themselves.
+struct PageRow {
+    uint64_t base;
+    int row;
+};
+__device__ __forceinline__ PageRow page_row(const uint32_t* pages, const SeqEntry& e, int t) {
+    return {(uint64_t)pages[e.page_list + (t >> e.page_shift)] * e.page_bytes, t & ((1 << e.page_shift) - 1)};
 }
 
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {

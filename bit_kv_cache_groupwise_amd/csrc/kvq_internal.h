@@ -16,6 +16,13 @@ constexpr uint64_t kAlign = 256;    // alignment of every head region and pool
 
 // One (layer, seq) entry of the device table. Byte offsets into the codes,
 // metadata and residual pools of head 0 of each tensor, and per-head strides.
+// Codes and metadata are addressed through pages: token t lies in physical
+// page pages[page_list + (t >> page_shift)], at byte pool offset page *
+// page_bytes, row t & (2^page_shift - 1) of the page; codes[] and meta[] are
+// offsets inside the page. Contiguous storage is the case of one page per
+// (layer, seq): page_shift 30, page_bytes 0 and a page list holding 0, so that
+// the offsets are pool offsets and the row is t.
+constexpr int kContiguousShift = 30;
 struct SeqEntry {
     uint64_t codes[2];        // [K, V]
     uint64_t meta[2];
@@ -23,11 +30,15 @@ struct SeqEntry {
     uint64_t codes_hs[2];
     uint64_t meta_hs[2];
     uint64_t resid_hs[2];
+    uint64_t page_bytes;      // stride of physical pages (0: contiguous)
     int32_t bits[2];
     int32_t cap;
-    int32_t pad_;
+    int32_t page_shift;       // log2 tokens per page
+    uint32_t page_list;       // first entry of this (layer, seq)'s page list
+    int32_t ring;             // window mode: token t >= sinks lives in ring row (t + ring) % win_rows
 };
-static_assert(sizeof(SeqEntry) == 112, "SeqEntry layout");
+static_assert(sizeof(SeqEntry) == 128, "SeqEntry layout");
+constexpr uint32_t kNoPage = 0xffffffffu;
 
 // Table buffer layout (bytes from d_table):
 //   [0, entries_bytes)                 SeqEntry[layers][num_seqs]
@@ -35,8 +46,9 @@ static_assert(sizeof(SeqEntry) == 112, "SeqEntry layout");
 //   [args_off, +2*num_seqs*4)          int32 call args: n_new[num_seqs], row_start[num_seqs]
 //   [ctr_off, +num_seqs*kv_heads*4)    int32 split counters of the decode merge (zero between calls)
 //   [pairs_off, +num_seqs*4)           int32 sequence indices grouped by (bits_k, bits_v) pair
+//   [pt_off, +page_entries*4)          uint32 page lists (contiguous storage: one entry, 0)
 struct TableLayout {
-    uint64_t entries_bytes, len_off, args_off, ctr_off, pairs_off, total;
+    uint64_t entries_bytes, len_off, args_off, ctr_off, pairs_off, pt_off, total;
 };
 
 // Per-launch description of one tensor (K = 0 or V = 1) of one layer.
@@ -66,6 +78,7 @@ struct TensorArgs {
     // into the window area of the head's residual region (window_store_kernel).
     int32_t win_mode, sinks, win_rows;  // win_rows = window + block (the recent ring)
     uint32_t win_off;           // byte offset of the window area inside a head's residual region
+    const uint32_t* pages;      // page lists (SeqEntry::page_list indexes them)
 };
 
 struct DecodeArgs {
@@ -115,6 +128,7 @@ struct DecodeArgs {
     // Keys cached before the rotary embedding (rope_base > 0; generic split
     // kernel): the reconstructed key of token t is rotated to position t.
     double rope_base;
+    const uint32_t* pages;      // page lists (SeqEntry::page_list indexes them)
 };
 
 struct DequantArgs {
@@ -126,6 +140,7 @@ struct DequantArgs {
     int32_t tensor, len, kv_heads, head_dim, group, axis, in_dtype;
     int32_t win_mode, window, sinks, tblock, win_rows;  // as in DecodeArgs
     uint32_t win_off;
+    const uint32_t* pages;      // page lists (SeqEntry::page_list indexes them)
 };
 
 // Work list of the query-group kernel when one launch covers every bit pair of
@@ -191,5 +206,15 @@ constexpr size_t kScratchBytes = 64ull << 20;
 hipError_t scratch_address(void** out);
 hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+
+// Scatter of page-list entries: pages[index[i]] = value[i], i < count, with the
+// pairs in the kernel arguments (no host staging).
+constexpr int kPageUpdateMax = 480;
+struct PageUpdates {
+    int32_t count;
+    uint32_t index[kPageUpdateMax];
+    uint32_t value[kPageUpdateMax];
+};
+hipError_t launch_page_updates(uint32_t* pages, const PageUpdates& u, hipStream_t s);
 
 }  // namespace kvq

@@ -111,10 +111,12 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
         const uint32_t sb0 = f32_to_f16_bits((mx0 - mn0) / L), zb0 = f32_to_f16_bits(mn0);
         const uint32_t sb1 = f32_to_f16_bits((mx1 - mn1) / L), zb1 = f32_to_f16_bits(mn1);
         const float s0 = f16_to_f32(sb0), z0 = f16_to_f32(zb0), s1 = f16_to_f32(sb1), z1 = f16_to_f32(zb1);
+        // the block's page (a block never straddles pages) and its first row there
+        const PageRow pr = page_row(a.pages, e, b * G);
         if (active && part == 0) {
-            uint32_t* meta = (uint32_t*)(a.meta + e.meta[T] + (size_t)head * e.meta_hs[T]);
-            meta[(size_t)b * D + c] = sb0 | (zb0 << 16);
-            if (CPT == 2) meta[(size_t)b * D + c + 1] = sb1 | (zb1 << 16);
+            uint32_t* meta = (uint32_t*)(a.meta + pr.base + e.meta[T] + (size_t)head * e.meta_hs[T]);
+            meta[(size_t)(pr.row / G) * D + c] = sb0 | (zb0 << 16);
+            if (CPT == 2) meta[(size_t)(pr.row / G) * D + c + 1] = sb1 | (zb1 << 16);
         }
         for (int i = 0; active && i < tpp; i += 2) {
             float x[4];
@@ -130,7 +132,7 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
             }
         }
         __syncthreads();
-        uint8_t* codes = a.codes + e.codes[T] + (size_t)head * e.codes_hs[T];
+        uint8_t* codes = a.codes + pr.base + e.codes[T] + (size_t)head * e.codes_hs[T];
         for (int idx = threadIdx.x; idx < G * UPR; idx += kThreads) {
             const int i = idx / UPR, u = idx % UPR;
             const uint32_t* src = smem + (i * D + 32 * u) / 4;
@@ -143,7 +145,7 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
                 cc[4 * k + 2] = (v >> 16) & 0xffu;
                 cc[4 * k + 3] = v >> 24;
             }
-            uint32_t* dst = (uint32_t*)(codes + (size_t)(b * G + i) * (D * B / 8)) + u * B;
+            uint32_t* dst = (uint32_t*)(codes + (size_t)(pr.row + i) * (D * B / 8)) + u * B;
             store_codes_rt(B, cc, dst);
         }
     }
@@ -226,15 +228,19 @@ __device__ __forceinline__ float key_score_token(const uint32_t* row, const uint
     return acc;
 }
 
+// vc, vm: head 0 offsets of the value codes and metadata inside a page (pool
+// offsets with contiguous storage); token t is found through the page list.
 template <int BV>
-__device__ __forceinline__ void value_pass(const uint8_t* vc, const uint32_t* vm, const float* sc, int t0, int t1,
-                                           int tl, int TL, int u, int D, int Gv, float (&acc)[32], float& zacc) {
+__device__ __forceinline__ void value_pass(const uint32_t* pages, const SeqEntry& e, const uint8_t* vc,
+                                           const uint8_t* vm, const float* sc, int t0, int t1, int tl, int TL, int u,
+                                           int D, int Gv, float (&acc)[32], float& zacc) {
     const int g = (32 * u) / Gv, gpr = D / Gv;
     for (int t = t0 + tl; t < t1; t += TL) {
         const float p = sc[t - t0];
-        const uint32_t w = vm[(size_t)t * gpr + g];
+        const PageRow pr = page_row(pages, e, t);
+        const uint32_t w = ((const uint32_t*)(vm + pr.base))[(size_t)pr.row * gpr + g];
         zacc = fmaf(p, f16_to_f32(w >> 16), zacc);
-        const uint32_t* unit = (const uint32_t*)(vc + (size_t)t * (D * BV / 8)) + u * BV;
+        const uint32_t* unit = (const uint32_t*)(vc + pr.base + (size_t)pr.row * (D * BV / 8)) + u * BV;
         axpy_unit<BV>(unit, p * f16_to_f32(w), acc);
     }
 }
@@ -314,11 +320,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     double* th = (double*)(red + 256 * 32);  // rotary frequencies [D/2] (rope_base > 0)
     const bool rope = a.rope_base > 0.0;
 
+    // head kvh's codes and metadata inside a page (pool offsets with contiguous storage)
     const uint8_t* kc = a.codes + e.codes[0] + (size_t)kvh * e.codes_hs[0];
-    const uint32_t* km = (const uint32_t*)(a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0]);
+    const uint8_t* kmp = a.meta + e.meta[0] + (size_t)kvh * e.meta_hs[0];
     const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
-    const uint32_t* vm = (const uint32_t*)(a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1]);
+    const uint8_t* vm = a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1];
+    // key code row of token t; key metadata of channel-axis block b (D words)
+    // or of token t (D / G words)
+    auto krow = [&](int t) -> const uint32_t* {
+        const PageRow pr = page_row(a.pages, e, t);
+        return (const uint32_t*)(kc + pr.base + (size_t)pr.row * (D * BK / 8));
+    };
+    auto kmeta_block = [&](int b) -> const uint32_t* {
+        const PageRow pr = page_row(a.pages, e, b * Gk);
+        return (const uint32_t*)(kmp + pr.base) + (size_t)(pr.row / Gk) * D;
+    };
+    auto kmeta_token = [&](int t) -> const uint32_t* {
+        const PageRow pr = page_row(a.pages, e, t);
+        return (const uint32_t*)(kmp + pr.base) + (size_t)pr.row * (D / Gk);
+    };
 
     for (int i = tid; i < R * D; i += kThreads) {
         const int r = i / D, ch = i % D;
@@ -336,8 +357,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
             // one thread per token: reconstruct, rotate to the token's position, score
             for (int t = t0 + tid; t < t1; t += kThreads) {
                 const bool quant = t < nqk;
-                const uint32_t* row = quant ? (const uint32_t*)(kc + (size_t)t * (D * BK / 8)) : nullptr;
-                const uint32_t* bm = km + (size_t)(t / Gk) * D;
+                const uint32_t* row = quant ? krow(t) : nullptr;
+                const uint32_t* bm = quant ? kmeta_block(t / Gk) : nullptr;
                 const uint8_t* rrow = kr + (size_t)(t % Gk) * D * IB;
                 float acc;
                 switch (BK) {
@@ -357,11 +378,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
                 const int nbl = (tile_end - tile0 + Gk - 1) / Gk;
                 for (int idx = tid; idx < nbl * D; idx += kThreads) {
                     const int bl = idx / D, ch = idx % D;
-                    qk[idx] = qr[ch] * f16_to_f32(km[(size_t)(b0 + bl) * D + ch]);
+                    qk[idx] = qr[ch] * f16_to_f32(kmeta_block(b0 + bl)[ch]);
                 }
                 for (int bl = wave; bl < nbl; bl += 4) {
                     float p = 0.f;
-                    for (int ch = lane; ch < D; ch += 64) p = fmaf(qr[ch], f16_to_f32(km[(size_t)(b0 + bl) * D + ch] >> 16), p);
+                    const uint32_t* bm = kmeta_block(b0 + bl);
+                    for (int ch = lane; ch < D; ch += 64) p = fmaf(qr[ch], f16_to_f32(bm[ch] >> 16), p);
                     p = wave_sum(p);
                     if (lane == 0) small[bl] = p;
                 }
@@ -369,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
                 const int t = tile0 + tid;
                 if (t < tile_end) {
                     const int bl = t / Gk - b0;
-                    const uint32_t* row = (const uint32_t*)(kc + (size_t)t * (D * BK / 8));
+                    const uint32_t* row = krow(t);
                     float acc = small[bl];
                     const float* qb = qk + bl * D;
                     switch (BK) {
@@ -400,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
             }
             __syncthreads();
             for (int t = t0 + tid; t < t1; t += kThreads) {
-                const uint32_t* row = (const uint32_t*)(kc + (size_t)t * (D * BK / 8));
-                const uint32_t* mrow = km + (size_t)t * (D / Gk);
+                const uint32_t* row = krow(t);
+                const uint32_t* mrow = kmeta_token(t);
                 float acc;
                 switch (BK) {
                     case 2: acc = key_score_token<2>(row, mrow, qr, small + 8, UPR, UG); break;
@@ -432,11 +454,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
         for (int j = 0; j < 32; ++j) acc[j] = 0.f;
         float zacc = 0.f;
         switch (BV) {
-            case 2: value_pass<2>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 3: value_pass<3>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 4: value_pass<4>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 6: value_pass<6>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            default: value_pass<8>(vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 2: value_pass<2>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 3: value_pass<3>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 4: value_pass<4>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            case 6: value_pass<6>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            default: value_pass<8>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
         }
 #pragma unroll
         for (int j = 0; j < 32; ++j) red[tl * D + 32 * u + j] = acc[j] + zacc;
@@ -598,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
         }
     }
     if (tid < kWinTokens)
-        row_s[tid] = tid < n ? window_row(fp_token(a, len, te, i0 + tid), a.sinks, a.win_rows) : 0;
+        row_s[tid] = tid < n ? window_row(fp_token(a, len, te, i0 + tid), a.sinks, a.win_rows, e.ring) : 0;
     __syncthreads();
 
     // ---- scores: thread = (token i, channel quarter p); the quarter's inputs come
@@ -733,16 +755,19 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a) {
         const int q = max(r > 0 ? r / a.tblock * a.tblock : 0, a.sinks);
         if (t < a.sinks || t >= q) {
             const uint8_t* wrow = a.resid + a.entry.resid[T] + (size_t)head * a.entry.resid_hs[T] + a.win_off +
-                                  (size_t)window_row(t, a.sinks, a.win_rows) * D * In<DT>::bytes;
+                                  (size_t)window_row(t, a.sinks, a.win_rows, a.entry.ring) * D * In<DT>::bytes;
             for (int j = 0; j < 32; ++j) out[j] = load_in<DT>(wrow, 32 * u + j);
             return;
         }
     }
     if (t < nq) {
-        const uint32_t* unit = (const uint32_t*)(a.codes + a.entry.codes[T] + (size_t)head * a.entry.codes_hs[T] +
-                                                 (size_t)t * (D * B / 8)) + u * B;
-        const uint32_t* meta = (const uint32_t*)(a.meta + a.entry.meta[T] + (size_t)head * a.entry.meta_hs[T]);
-        meta += ch ? (size_t)(t / G) * D + 32 * u : (size_t)t * (D / G) + (32 * u) / G;
+        const PageRow pr = page_row(a.pages, a.entry, t);
+        const uint32_t* unit = (const uint32_t*)(a.codes + pr.base + a.entry.codes[T] +
+                                                 (size_t)head * a.entry.codes_hs[T] + (size_t)pr.row * (D * B / 8)) +
+                               u * B;
+        const uint32_t* meta =
+            (const uint32_t*)(a.meta + pr.base + a.entry.meta[T] + (size_t)head * a.entry.meta_hs[T]);
+        meta += ch ? (size_t)(pr.row / G) * D + 32 * u : (size_t)pr.row * (D / G) + (32 * u) / G;
         float v[32];
         switch (B) {
             case 2: dequant_unit<2>(unit, meta, ch, v); break;
@@ -848,6 +873,20 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- page lists
+namespace {
+__global__ __launch_bounds__(kThreads) void page_update_kernel(uint32_t* pages, PageUpdates u) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < u.count) pages[u.index[i]] = u.value[i];
+}
+}  // namespace
+
+hipError_t launch_page_updates(uint32_t* pages, const PageUpdates& u, hipStream_t s) {
+    if (u.count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(page_update_kernel, dim3((u.count + kThreads - 1) / kThreads), dim3(kThreads), 0, s, pages, u);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- read probe
 // A plain streaming read (the measured HBM ceiling the decode kernels are

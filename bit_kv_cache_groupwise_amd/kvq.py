@@ -34,19 +34,21 @@ DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
             "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc")
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc",
+            "kvq_gather_sequences", "kvq_evict_tokens", "kvq_reset_sequence", "kvq_page_list")
 
 
 class kvq_geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "layers", "num_seqs", "kv_heads", "q_heads", "head_dim", "group_k", "group_v",
-        "axis_k", "axis_v", "in_dtype", "meta_dtype", "window", "sinks")] + [("rope_base", ctypes.c_double)]
+        "axis_k", "axis_v", "in_dtype", "meta_dtype", "window", "sinks")] + [("rope_base", ctypes.c_double)] + [
+        (n, ctypes.c_int32) for n in ("page_tokens", "num_pages")]
 
 
 class kvq_sizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "codes_bytes", "meta_bytes", "residual_bytes", "table_bytes",
-        "formula_codes_bytes", "formula_meta_bytes", "formula_residual_bytes")]
+        "formula_codes_bytes", "formula_meta_bytes", "formula_residual_bytes", "page_bytes", "num_pages")]
 
 
 class kvq_region(ctypes.Structure):
@@ -78,6 +80,12 @@ _lib.kvq_decode_attention_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_size_t, _P]
 _lib.kvq_dequantize.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
 _lib.kvq_seq_lengths.argtypes = [_P, ctypes.c_int32, _I32P]
+_lib.kvq_gather_sequences.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _I32P, _P]
+_lib.kvq_evict_tokens.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  _P]
+_lib.kvq_reset_sequence.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+_lib.kvq_page_list.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                               _I32P, ctypes.POINTER(ctypes.c_int64)]
 _lib.kvq_read_probe.argtypes = [_P, ctypes.c_uint64, _P, _P]
 _lib.kvq_get_region.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(kvq_region)]
 _lib.kvq_status_string.argtypes = [ctypes.c_int32]
@@ -88,7 +96,8 @@ _lib.kvq_version.argtypes = []
 _lib.kvq_version.restype = ctypes.c_char_p
 for _n in ("kvq_plan", "kvq_cache_create", "kvq_quantize_append", "kvq_decode_attention", "kvq_dequantize",
            "kvq_seq_lengths", "kvq_get_region", "kvq_read_probe", "kvq_decode_attention_layers",
-            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc"):
+            "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc",
+           "kvq_gather_sequences", "kvq_evict_tokens", "kvq_reset_sequence", "kvq_page_list"):
     getattr(_lib, _n).restype = ctypes.c_int32
 
 
@@ -127,9 +136,10 @@ def _stream(stream):
 
 def geometry(*, layers, num_seqs, kv_heads, q_heads, head_dim, group_k, group_v,
              axis_k=KVQ_AXIS_CHANNEL, axis_v=KVQ_AXIS_TOKEN, in_dtype="f16", meta_dtype=KVQ_F16,
-             window=0, sinks=0, rope_base=0.0):
+             window=0, sinks=0, rope_base=0.0, page_tokens=0, num_pages=0):
     return kvq_geometry(layers, num_seqs, kv_heads, q_heads, head_dim, group_k, group_v, axis_k, axis_v,
-                        DTYPE_CODE.get(in_dtype, in_dtype), meta_dtype, window, sinks, float(rope_base))
+                        DTYPE_CODE.get(in_dtype, in_dtype), meta_dtype, window, sinks, float(rope_base),
+                        page_tokens, num_pages)
 
 
 # ---------------------------------------------------------------------------
@@ -232,6 +242,28 @@ def kvq_decode_attention_layers(handle, layer0, n_layers, q, softmax_scale, out,
 def kvq_copy_sequence(dst_handle, dst_seq, src_handle, src_seq, layer0, n_layers, stream=None):
     _check(_lib.kvq_copy_sequence(dst_handle, dst_seq, src_handle, src_seq, layer0, n_layers, _stream(stream)),
            "kvq_copy_sequence")
+
+
+def kvq_gather_sequences(handle, layer0, n_layers, src, stream=None):
+    _check(_lib.kvq_gather_sequences(handle, layer0, n_layers, _i32(src), _stream(stream)), "kvq_gather_sequences")
+
+
+def kvq_evict_tokens(handle, layer0, n_layers, seq, first, count, stream=None):
+    _check(_lib.kvq_evict_tokens(handle, layer0, n_layers, seq, first, count, _stream(stream)), "kvq_evict_tokens")
+
+
+def kvq_reset_sequence(handle, layer0, n_layers, seq, stream=None):
+    _check(_lib.kvq_reset_sequence(handle, layer0, n_layers, seq, _stream(stream)), "kvq_reset_sequence")
+
+
+def kvq_page_list(handle, layer, seq):
+    """(physical page of each logical page, free pages of the pool)."""
+    n = ctypes.c_int32()
+    free = ctypes.c_int64()
+    _check(_lib.kvq_page_list(handle, layer, seq, None, 0, ctypes.byref(n), ctypes.byref(free)), "kvq_page_list")
+    out = (ctypes.c_uint32 * max(1, n.value))()
+    _check(_lib.kvq_page_list(handle, layer, seq, out, n.value, ctypes.byref(n), ctypes.byref(free)), "kvq_page_list")
+    return list(out)[:n.value], free.value
 
 
 def kvq_read_probe(buf, nbytes, sink, stream=None):
@@ -355,6 +387,22 @@ class Cache:
     def copy_sequence(self, dst_seq, src_cache, src_seq, layer0=0, n_layers=None, stream=None):
         n = self.geom.layers - layer0 if n_layers is None else n_layers
         kvq_copy_sequence(self.handle, dst_seq, src_cache.handle, src_seq, layer0, n, stream)
+
+    def gather(self, src, layer0=0, n_layers=None, stream=None):
+        """Sequence s takes what sequence src[s] held (beam reorder, forks)."""
+        n = self.geom.layers - layer0 if n_layers is None else n_layers
+        kvq_gather_sequences(self.handle, layer0, n, src, stream)
+
+    def evict(self, seq, first, count, layer0=0, n_layers=None, stream=None):
+        n = self.geom.layers - layer0 if n_layers is None else n_layers
+        kvq_evict_tokens(self.handle, layer0, n, seq, first, count, stream)
+
+    def reset(self, seq, layer0=0, n_layers=None, stream=None):
+        n = self.geom.layers - layer0 if n_layers is None else n_layers
+        kvq_reset_sequence(self.handle, layer0, n, seq, stream)
+
+    def page_list(self, layer, seq):
+        return kvq_page_list(self.handle, layer, seq)
 
     def lengths(self, layer):
         return kvq_seq_lengths(self.handle, layer, self.geom.num_seqs)

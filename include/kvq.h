@@ -51,6 +51,25 @@
  *   pools      four caller-owned device buffers (codes, metadata, residual,
  *              table) sized by kvq_plan; regions are ordered layer -> seq ->
  *              tensor (K, V) -> head, each head region 256-byte aligned.
+ *   pages      with kvq_geometry.page_tokens = P > 0 the codes and metadata
+ *              live in a shared pool of fixed-size pages instead (the codes
+ *              buffer; the metadata buffer is unused). A page holds P
+ *              consecutive tokens of one (layer, seq): K code rows [head][P],
+ *              V code rows [head][P], then the K and V metadata of those
+ *              tokens ([head][P/G][D] on the channel axis, [head][P][D/G] on
+ *              the token axis), each head region 256-byte aligned; the page
+ *              stride is the largest such size over the cache's bit pairs. A
+ *              per-(layer, seq) page list in the table maps logical page i
+ *              (tokens iP .. iP + P - 1) to a physical page. Since a key
+ *              block never straddles pages, a page carries the steps and
+ *              zeros of exactly the codes it holds ([N] "State quantized
+ *              cache harus tetap selaras dengan posisi": remapping logical to
+ *              physical positions must move the scales with their codes).
+ *              Pages are taken from the pool when an append first writes
+ *              into them and returned when no sequence refers to them; whole
+ *              pages are shared between sequences by reference count
+ *              (kvq_gather_sequences). Residual and window rows stay in the
+ *              residual pool, per (layer, seq).
  *
  * Conventions
  *   - Every call returns a kvq_status; nothing throws or aborts. On error
@@ -136,6 +155,14 @@ typedef struct kvq_geometry {
      * channel-axis keys, no window or sinks (else KVQ_ERR_UNSUPPORTED at
      * decode), computed by the generic split kernel. */
     double rope_base;
+    /* Paged storage (see "pages" above). 0: each (layer, seq) has contiguous
+     * regions sized for its capacity. Otherwise P tokens per page: a power of
+     * two, 64 <= P <= 65536, at least the key block, with sinks a multiple
+     * of P. */
+    int32_t page_tokens;
+    /* Physical pages in the pool (paged storage; 0: enough for every
+     * sequence of every layer at full capacity). At most 2^31 - 1. */
+    int32_t num_pages;
 } kvq_geometry;
 
 /* Byte counts. The pool sizes include 256-byte alignment of every head
@@ -152,10 +179,14 @@ typedef struct kvq_sizes {
     uint64_t formula_residual_bytes; /* G * D * in_bytes per channel-axis tensor head,
                                         plus (sinks + window + block) * D * in_bytes per
                                         tensor head with a window or sinks            */
+    uint64_t page_bytes;             /* paged storage: stride of a physical page (else 0) */
+    uint64_t num_pages;              /* paged storage: pages in the codes pool (else 0)   */
 } kvq_sizes;
 
 /* Byte offsets of one (layer, seq) in the pools, head 0, plus per-head
- * strides; for serialization, inspection and tests. */
+ * strides; for serialization, inspection and tests. With paged storage the
+ * codes and metadata offsets and strides are inside a page (kvq_page_list
+ * gives the pages); the residual offsets are pool offsets as before. */
 typedef struct kvq_region {
     uint64_t k_codes, v_codes, k_meta, v_meta, k_resid, v_resid;
     uint64_t k_codes_head_stride, v_codes_head_stride;
@@ -289,10 +320,56 @@ kvq_status kvq_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void*
  * src_seq). Requires equal geometry (every kvq_geometry field) and, for the
  * two sequences, equal bits_k, bits_v and capacity. Device-to-device copies
  * enqueued on `stream`; only the bytes of the first `length` tokens are
- * defined afterwards. Errors: KVQ_ERR_ARG (NULL cache, index out of range,
- * mismatch, same sequence), KVQ_ERR_HIP. */
+ * defined afterwards. Paged storage: dst must be src, and the copy is
+ * kvq_gather_sequences with src[dst_seq] = src_seq (shared pages). Errors:
+ * KVQ_ERR_ARG (NULL cache, index out of range, mismatch, same sequence),
+ * KVQ_ERR_UNSUPPORTED (paged storage across two caches), KVQ_ERR_CAPACITY
+ * (paged: no free page), KVQ_ERR_HIP. */
 kvq_status kvq_copy_sequence(kvq_cache* dst, int32_t dst_seq, const kvq_cache* src, int32_t src_seq, int32_t layer0,
                              int32_t n_layers, void* stream);
+
+/* Reorder and fork sequences ([N] "State quantized cache harus tetap selaras
+ * dengan posisi": beam operations and prefix reuse remap logical to physical
+ * slots, and the scales must move with the codes they describe): afterwards
+ * sequence s of each layer in [layer0, layer0 + n_layers) holds what sequence
+ * src[s] held before the call (codes, metadata, residual and window rows,
+ * length), for every s at once. src: host array of num_seqs indices; src[s]
+ * == s leaves s as it is, and an index may appear several times (beam
+ * search: surviving beams replace dropped ones; prefix sharing: one prompt's
+ * cache forked into several sequences). s and src[s] must have equal bits_k,
+ * bits_v and capacity. Paged storage: whole pages are shared by reference
+ * count, only the page holding a source's last incomplete page of tokens is
+ * copied, once per extra copy; contiguous storage: the regions of extra
+ * copies are copied into the regions of sequences no one refers to. Copies
+ * and table updates are enqueued on `stream`. Errors: KVQ_ERR_ARG (NULL,
+ * index out of range, mismatched bits or capacity), KVQ_ERR_CAPACITY (paged:
+ * not enough free pages; nothing changes), KVQ_ERR_HIP. */
+kvq_status kvq_gather_sequences(kvq_cache* cache, int32_t layer0, int32_t n_layers, const int32_t* src, void* stream);
+
+/* Evict tokens [first, first + count) of sequence `seq` in layers [layer0,
+ * layer0 + n_layers) ([N] "State quantized cache harus tetap selaras dengan
+ * posisi": eviction remaps logical positions; the pages go with their own
+ * steps and zeros). Paged storage only: first and count multiples of
+ * page_tokens, first >= sinks, first + count <= the sequence's whole pages
+ * and, with a window, <= length - (window + key block) (the window rows stay
+ * valid). The pages are released and later tokens move down by count
+ * (keys cached before the rotary embedding are then rotated to their new
+ * positions). count == 0 is a no-op. Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED
+ * (contiguous storage), KVQ_ERR_HIP. */
+kvq_status kvq_evict_tokens(kvq_cache* cache, int32_t layer0, int32_t n_layers, int32_t seq, int32_t first,
+                            int32_t count, void* stream);
+
+/* Empty sequence `seq` in layers [layer0, layer0 + n_layers): length 0, and
+ * with paged storage its pages released. Errors: KVQ_ERR_ARG, KVQ_ERR_HIP. */
+kvq_status kvq_reset_sequence(kvq_cache* cache, int32_t layer0, int32_t n_layers, int32_t seq, void* stream);
+
+/* Physical page of each logical page of (layer, seq), paged storage (host
+ * array of up to max_out entries; 0xFFFFFFFF = no page), and the number of
+ * logical pages the sequence's capacity spans in *n_pages. free_pages (may be
+ * NULL): pages of the pool no sequence refers to. Errors: KVQ_ERR_ARG,
+ * KVQ_ERR_UNSUPPORTED (contiguous storage). */
+kvq_status kvq_page_list(const kvq_cache* cache, int32_t layer, int32_t seq, uint32_t* out, int32_t max_out,
+                         int32_t* n_pages, int64_t* free_pages);
 
 /* Current cached lengths of `layer`: host array of num_seqs entries. */
 kvq_status kvq_seq_lengths(const kvq_cache* cache, int32_t layer, int32_t* out);

@@ -18,11 +18,12 @@ def kvq():
     return k
 
 
-def geom_of(w: W.Workload, layers=None, window=0, sinks=0, rope_base=0.0):
+def geom_of(w: W.Workload, layers=None, window=0, sinks=0, rope_base=0.0, page_tokens=0, num_pages=0):
     k = kvq()
     return k.geometry(layers=layers or w.layers, num_seqs=w.num_seqs, kv_heads=w.kv_heads, q_heads=w.q_heads,
                       head_dim=w.head_dim, group_k=w.group_k, group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v,
-                      in_dtype=w.in_dtype, window=window, sinks=sinks, rope_base=rope_base)
+                      in_dtype=w.in_dtype, window=window, sinks=sinks, rope_base=rope_base,
+                      page_tokens=page_tokens, num_pages=num_pages)
 
 
 def poison_(t):
@@ -75,10 +76,11 @@ def poison_cache(c):
     return c
 
 
-def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0, rope_base=0.0, poison=True):
+def make_cache(w: W.Workload, extra=0, layers=None, capacity=None, window=0, sinks=0, rope_base=0.0, poison=True,
+               page_tokens=0, num_pages=0):
     k = kvq()
     cap = capacity or [L + w.new_tokens + extra for L in w.lengths]
-    c = k.Cache(geom_of(w, layers, window, sinks, rope_base), cap, [b[0] for b in w.bits],
+    c = k.Cache(geom_of(w, layers, window, sinks, rope_base, page_tokens, num_pages), cap, [b[0] for b in w.bits],
                 [b[1] for b in w.bits])
     return poison_cache(c) if poison else c
 
@@ -141,12 +143,32 @@ def _u32(pool, off, nbytes):
     return pool[off:off + nbytes].cpu().numpy().view(np.uint32)
 
 
+def _paged_rows(pool_np, plist, P, page_bytes, off, rows, row_bytes, tokens_per_row=1):
+    """uint32 [rows][row_bytes/4] of a paged tensor: row i covers tokens
+    [i*tokens_per_row, (i+1)*tokens_per_row) and lives in page plist[token // P]
+    at byte off + (token % P) / tokens_per_row * row_bytes."""
+    out = np.empty((rows, row_bytes // 4), np.uint32)
+    for i in range(rows):
+        t = i * tokens_per_row
+        page = plist[t // P]
+        assert page != 0xFFFFFFFF, f"token {t} has no page"
+        b = page * page_bytes + off + (t % P) // tokens_per_row * row_bytes
+        out[i] = pool_np[b:b + row_bytes].view(np.uint32)
+    return out
+
+
 def read_head(cache, w: W.Workload, layer: int, seq: int, head: int) -> dict:
-    """Bytes of one (layer, seq, head) as stored in the device pools."""
+    """Bytes of one (layer, seq, head) as stored in the device pools (through
+    the page list with paged storage)."""
     r = cache.region(layer, seq)
     D, T = w.head_dim, r.length
     out = {}
     ib = 4 if w.in_dtype == "f32" else 2
+    P = cache.geom.page_tokens
+    if P:
+        plist, _ = cache.page_list(layer, seq)
+        pool = cache.codes.cpu().numpy()
+        pb = cache.sizes.page_bytes
     spec = (("k", w.axis_k, w.group_k, r.bits_k, r.k_codes, r.k_codes_head_stride, r.k_meta, r.k_meta_head_stride,
              r.k_resid, r.k_resid_head_stride),
             ("v", w.axis_v, w.group_v, r.bits_v, r.v_codes, r.v_codes_head_stride, r.v_meta, r.v_meta_head_stride,
@@ -154,13 +176,21 @@ def read_head(cache, w: W.Workload, layer: int, seq: int, head: int) -> dict:
     for name, axis, G, bits, co, chs, mo, mhs, ro, rhs in spec:
         rows = (T // G) * G if axis == o.AXIS_CHANNEL else T
         wpr = D * bits // 32
-        out[name + "_words"] = _u32(cache.codes, co + head * chs, rows * wpr * 4).reshape(rows, wpr)
+        if P:
+            out[name + "_words"] = _paged_rows(pool, plist, P, pb, co + head * chs, rows, wpr * 4)
+            if axis == o.AXIS_CHANNEL:
+                out[name + "_meta"] = _paged_rows(pool, plist, P, pb, mo + head * mhs, T // G, D * 4, G)
+            else:
+                out[name + "_meta"] = _paged_rows(pool, plist, P, pb, mo + head * mhs, T, (D // G) * 4)
+        else:
+            out[name + "_words"] = _u32(cache.codes, co + head * chs, rows * wpr * 4).reshape(rows, wpr)
         if axis == o.AXIS_CHANNEL:
-            out[name + "_meta"] = _u32(cache.meta, mo + head * mhs, (T // G) * D * 4).reshape(T // G, D)
+            if not P:
+                out[name + "_meta"] = _u32(cache.meta, mo + head * mhs, (T // G) * D * 4).reshape(T // G, D)
             raw = cache.resid[ro + head * rhs: ro + head * rhs + G * D * ib].cpu()
             raw = raw.view(torch.int32 if ib == 4 else torch.int16).numpy().reshape(G, D)
             out[name + "_resid_raw"] = np.stack([raw[t % G] for t in range(rows, T)]) if T > rows else raw[:0]
-        else:
+        elif not P:
             out[name + "_meta"] = _u32(cache.meta, mo + head * mhs, T * (D // G) * 4).reshape(T, D // G)
     return out
 

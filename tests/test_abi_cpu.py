@@ -116,7 +116,53 @@ def test_geometry_struct_layout():
     import re
     names = re.findall(r"^\s*(?:int32_t|double)\s+(\w+);", body, flags=re.M)
     assert [f[0] for f in kvq.kvq_geometry._fields_] == names
-    assert kvq.kvq_geometry.rope_base.offset == 56 and ctypes.sizeof(kvq.kvq_geometry) == 64
+    assert kvq.kvq_geometry.rope_base.offset == 56 and kvq.kvq_geometry.page_tokens.offset == 64
+    assert ctypes.sizeof(kvq.kvq_geometry) == 72
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_tokens=64), 0), (dict(page_tokens=4096), 0), (dict(page_tokens=65536), 0),
+    (dict(page_tokens=32), -1), (dict(page_tokens=96), -1), (dict(page_tokens=131072), -1), (dict(page_tokens=-64), -1),
+    (dict(page_tokens=64, group_k=128), -1), (dict(page_tokens=128, group_k=128), 0),
+    (dict(page_tokens=64, sinks=32, window=16), -1), (dict(page_tokens=64, sinks=64, window=16), 0),
+    (dict(page_tokens=64, num_pages=-1), -1), (dict(page_tokens=64, num_pages=5), 0),
+])
+def test_plan_paged_geometry(kw, status):
+    """Pages hold a power of two of at least 64 tokens, at least the key block,
+    and the sinks fill whole pages."""
+    assert kvq.kvq_plan_status(_geom(**kw), [100] * 3, [2] * 3, [2] * 3) == status
+    if status:
+        assert kvq.kvq_last_error()
+
+
+def test_plan_paged_sizes():
+    """Paged storage: a page holds P tokens of K and V codes of every head and
+    their metadata (each head region 256-byte aligned); the page stride is the
+    largest over the bit pairs; the pool holds every sequence's pages at full
+    capacity unless num_pages says otherwise; the table grows by one uint32 per
+    logical page; the closed-form byte counts do not change."""
+    D, H, P = 128, 3, 64
+    g = kvq.geometry(layers=2, num_seqs=3, kv_heads=H, q_heads=H, head_dim=D, group_k=32, group_v=32)
+    gp = kvq.geometry(layers=2, num_seqs=3, kv_heads=H, q_heads=H, head_dim=D, group_k=32, group_v=32, page_tokens=P)
+    cap, bk, bv = [100, 64, 1000], [2, 4, 6], [2, 8, 4]
+    plain, paged = kvq.kvq_plan(g, cap, bk, bv), kvq.kvq_plan(gp, cap, bk, bv)
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    def page(b_k, b_v):
+        return H * (a256(P * D * b_k // 8) + a256(P * D * b_v // 8) + a256(P // 32 * D * 4) + a256(P * (D // 32) * 4))
+
+    assert paged.page_bytes == max(page(2, 2), page(4, 8), page(6, 4))
+    pages = 2 * sum((c + P - 1) // P for c in cap)
+    assert paged.num_pages == pages and paged.codes_bytes == pages * paged.page_bytes
+    assert paged.table_bytes >= plain.table_bytes + 4 * pages - 255
+    for f in ("formula_codes_bytes", "formula_meta_bytes", "formula_residual_bytes", "residual_bytes"):
+        assert getattr(paged, f) == getattr(plain, f), f
+    assert plain.page_bytes == 0 and plain.num_pages == 0
+    small = kvq.kvq_plan(kvq.geometry(layers=2, num_seqs=3, kv_heads=H, q_heads=H, head_dim=D, group_k=32, group_v=32,
+                                      page_tokens=P, num_pages=7), cap, bk, bv)
+    assert small.num_pages == 7 and small.codes_bytes == 7 * paged.page_bytes
 
 
 def test_plan_gpt2_effective_bits():
@@ -172,6 +218,11 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.kvq_quantize_append_layers(None, 0, 1, None, None, None, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_attention_layers(None, 0, 1, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_copy_sequence(None, 0, None, 1, 0, 1, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_gather_sequences(None, 0, 1, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_evict_tokens(None, 0, 1, 0, 0, 64, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_reset_sequence(None, 0, 1, 0, None) == kvq.KVQ_ERR_ARG
+    n = ctypes.c_int32()
+    assert lib.kvq_page_list(None, 0, 0, None, 0, ctypes.byref(n), None) == kvq.KVQ_ERR_ARG
 
 
 def test_read_probe_validates_before_launching():
