@@ -492,11 +492,14 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     // (tile wave + 4k, at most 64 of them: the host keeps splits within 8192
     // tokens), so that the loop reads it with a lane read instead of a
     // dependent memory load.
+    // Contiguous storage (page stride 0) skips the load, so that the first
+    // tile's loads do not wait for it.
+    const bool paged = e.page_bytes != 0;
     uint32_t pev = 0;
     if (wave < nqt) {
-        pev = a.pages[e.page_list + ((wa + 32 * min(wave + 4 * lane, nqt - 1)) >> psh)];
+        if (paged) pev = a.pages[e.page_list + ((wa + 32 * min(wave + 4 * lane, nqt - 1)) >> psh)];
         const int t0 = wa + 32 * wave;
-        const uint64_t pb = (uint64_t)__builtin_amdgcn_readlane(pev, 0) * e.page_bytes;
+        const uint64_t pb = paged ? (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pev, 0) * e.page_bytes : 0;
         load_values(t0, pb);
         load_kmeta(t0, pb);
         load_keys(t0, pb);
@@ -681,7 +684,8 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         const int t0 = wa + 32 * i;
         const bool more = i + 4 < nqt;
         const int tn = wa + 32 * (more ? i + 4 : i);
-        const uint64_t pbn = (uint64_t)__builtin_amdgcn_readlane(pev, more ? k + 1 : k) * e.page_bytes;
+        const uint64_t pbn =
+            paged ? (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pev, more ? k + 1 : k) * e.page_bytes : 0;
         const int kb_tile = stage_values();
         const int fk = stage_kmeta();
         __builtin_amdgcn_sched_barrier(0);

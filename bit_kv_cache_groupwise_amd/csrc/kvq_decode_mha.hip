@@ -531,11 +531,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     const int st0 = wa + 64 * wave;
     constexpr int STEP = NW * 64;
     const int psh = e.page_shift;
+    // (contiguous storage, page stride 0, skips the load: the first loads do not wait for it)
+    const bool paged = e.page_bytes != 0;
     uint32_t pev = 0;
-    if (st0 < qend) pev = a.pages[e.page_list + (min(st0 + STEP * lane, tlast) >> psh)];
+    if (paged && st0 < qend) pev = a.pages[e.page_list + (min(st0 + STEP * lane, tlast) >> psh)];
     auto load_stage = [&](int st, St& r) {
         const int sc0 = min(st, tlast);
-        const uint64_t pb = (uint64_t)__builtin_amdgcn_readlane(pev, min((st - st0) / STEP, 63)) * e.page_bytes;
+        const uint64_t pb =
+            paged ? (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pev, min((st - st0) / STEP, 63)) * e.page_bytes : 0;
         const int ps = (sc0 >> psh) << psh;  // first token of the page
         const int t0 = st + ts;
 #pragma unroll
