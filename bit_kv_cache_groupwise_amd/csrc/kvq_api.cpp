@@ -773,8 +773,8 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const kvq_geometry& g = c->g;
     if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
     const bool rope = g.rope_base > 0.0;
-    if (rope && (g.axis_k != KVQ_AXIS_CHANNEL || win_mode(g)))
-        return fail(KVQ_ERR_UNSUPPORTED, "rotary keys need channel-axis keys and no window or sinks in this build");
+    if (rope && g.axis_k != KVQ_AXIS_CHANNEL)
+        return fail(KVQ_ERR_UNSUPPORTED, "rotary keys need channel-axis keys in this build");
     if (!(softmax_scale == softmax_scale)) return fail(KVQ_ERR_ARG, "softmax_scale is NaN");
     if (!aligned(q, in_bytes(g.in_dtype)) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "q or out misaligned");
     const int S = g.num_seqs;

@@ -605,6 +605,11 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
     float* ml_s = p_s + R * kWinTokens;    // [R][2]
     float* red = ml_s + 2 * R;             // [TP][R][D] partial outputs (TP > 1)
     int* row_s = (int*)(red + (TP > 1 ? TP * R * D : 0));  // [kWinTokens]: window row of each token
+    int* pos_s = row_s + kWinTokens;                      // [kWinTokens]: position of each token
+    double* th = (double*)(((uintptr_t)(pos_s + kWinTokens) + 7) & ~(uintptr_t)7);  // rotary frequencies [D/2]
+    const bool rope = a.rope_base > 0.0;
+    if (rope)
+        for (int i = tid; i < D / 2; i += kThreads) th[i] = pow(a.rope_base, -2.0 * i / D);
     {
         // the R query rows: every load issued before the first use. Loads are
         // unconditional, from clamped (valid) addresses: a load under a branch
@@ -619,8 +624,11 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
             if (i < R * D) q_s[i] = qv[k] * a.qscale;
         }
     }
-    if (tid < kWinTokens)
-        row_s[tid] = tid < n ? window_row(fp_token(a, len, te, i0 + tid), a.sinks, a.win_rows, e.ring) : 0;
+    if (tid < kWinTokens) {
+        const int t = tid < n ? fp_token(a, len, te, i0 + tid) : 0;
+        row_s[tid] = tid < n ? window_row(t, a.sinks, a.win_rows, e.ring) : 0;
+        pos_s[tid] = t;
+    }
     __syncthreads();
 
     // ---- scores: thread = (token i, channel quarter p); the quarter's inputs come
@@ -636,6 +644,20 @@ __global__ __launch_bounds__(kThreads) void decode_window_kernel(DecodeArgs a0) 
             load8<DT>(kw, base + j, y);
 #pragma unroll
             for (int u = 0; u < 8; ++u) x[j + u] = i < n ? y[u] : 0.f;
+        }
+        if (rope) {
+            // keys cached before the rotary embedding: rotate to the token's
+            // position; channel pair (c, c + D/2) is split between quarters p
+            // and p ^ 2 of the same token (threads tid and tid ^ 2)
+            const int t = pos_s[i];
+#pragma unroll
+            for (int j = 0; j < DQ; ++j) {
+                const float other = __shfl_xor(x[j], 2);
+                const int pair = (p & 1) * DQ + j;
+                float c, sn;
+                rope_cs(t, th[pair], c, sn);
+                x[j] = p < 2 ? x[j] * c - other * sn : other * sn + x[j] * c;
+            }
         }
         // one query head per iteration, not unrolled: the code stays small
         // (it runs once per workgroup, so its instruction fetches are cold)
@@ -852,7 +874,7 @@ hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s) {
     const int TP = kThreads / a.head_dim;
     const size_t lds = sizeof(float) * ((size_t)R * a.head_dim + (size_t)R * kWinTokens + 2 * R +
                                         (TP > 1 ? (size_t)TP * R * a.head_dim : 0)) +
-                       sizeof(int) * kWinTokens;
+                       sizeof(int) * 2 * kWinTokens + 8 + sizeof(double) * (a.head_dim / 2);
     switch (a.in_dtype) {
         case 0: window_d<0>(a, grid, lds, s); break;
         case 1: window_d<1>(a, grid, lds, s); break;

@@ -151,9 +151,10 @@ typedef struct kvq_geometry {
      * taken as un-rotated, and the decode attention rotates the reconstructed
      * key of token t to position t: channel pair (i, i + head_dim/2) turns by
      * t * rope_base^(-2i/head_dim); q must be given rotated to its own
-     * position. kvq_dequantize returns the un-rotated keys. This build:
-     * channel-axis keys, no window or sinks (else KVQ_ERR_UNSUPPORTED at
-     * decode), computed by the generic split kernel. */
+     * position. kvq_dequantize returns the un-rotated keys. With a window or
+     * sinks the full-precision rows are rotated to their positions too. This
+     * build: channel-axis keys (else KVQ_ERR_UNSUPPORTED at decode), computed
+     * by the generic split kernel and the window kernel. */
     double rope_base;
     /* Paged storage (see "pages" above). 0: each (layer, seq) has contiguous
      * regions sized for its capacity. Otherwise P tokens per page: a power of

@@ -96,19 +96,58 @@ def test_rope_decode_step_and_layers():
     cb.close()
 
 
+# (workload, base, window, sinks): the full-precision rows are rotated too
+WINDOW_CASES = {
+    "llama": (W.llama2_7b().scaled(num_seqs=3, kv_heads=2, q_heads=2, lengths=(3000, 150, 20),
+                                   bits=((2, 2), (4, 4), (3, 3))), 10000.0, 100, 32),
+    "gqa": (W.long_gqa().scaled(lengths=(4000,)), 500000.0, 128, 64),
+    "mixed": (W.mixed_batch().scaled(num_seqs=5, lengths=(10, 100, 700, 1500, 33), bits=tuple(W.BIT_PAIRS_MIXED)),
+              10000.0, 64, 0),
+    "sinks_only": (W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=2, lengths=(900, 40), bits=((2, 2),) * 2),
+                   10000.0, 0, 64),
+    "d96": (W.tiny().scaled(head_dim=96, lengths=(300,), bits=((3, 4),), group_k=64), 10000.0, 40, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(WINDOW_CASES))
+def test_rope_with_window_and_sinks(name):
+    """Rotary keys with a full-precision window and sinks ([U] "O Que Fazer Com
+    Isso": keys before the rotation and a full-precision window, used together):
+    the quantized keys and the full-precision rows are both rotated to their
+    positions; attention within 2e-3 of the fp64 oracle that rotates the
+    windowed reconstruction; dequantize returns the unrotated rows."""
+    w, base, window, sinks = WINDOW_CASES[name]
+    _note(f"[rope window] case={name} base={base} R={window} S={sinks} lens={w.lengths}")
+    cache = H.make_cache(w, rope_base=base, window=window, sinks=sinks)
+    prefix, new = H.history(w, 0)
+    H.append_chunks(cache, 0, prefix[0], prefix[1], prefix[2])
+    H.append_chunks(cache, 0, new[0], new[1], new[2])
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    R = w.q_heads // w.kv_heads
+    worst = 0.0
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        kd, _ = cache.dequantize(0, s)
+        torch.cuda.synchronize()
+        for h in range(w.kv_heads):
+            enc = H.encode_window(w, k, v, s, h, window, sinks)
+            np.testing.assert_array_equal(kd[h].cpu().numpy(), enc["k_hat"].astype(np.float32))
+            qs = q[s, h * R:(h + 1) * R].double().numpy()
+            ref = o.attend_rope(qs, enc["k_hat"], enc["v_hat"], w.softmax_scale, base)
+            err = H.row_rel_err(out[s, h * R:(h + 1) * R], ref)
+            worst = max(worst, float(err.max()))
+            assert np.all(err <= H.ATTN_TOL), (name, s, h, float(err.max()))
+    _note(f"[rope window] case={name} worst row rel err {worst:.3e}")
+    cache.close()
+
+
 def test_rope_unsupported_combinations():
-    """Rotary keys with a window, or with per-token keys, are rejected at decode
-    before anything is launched; a base in (0, 1] is rejected at plan time."""
+    """Rotary keys with per-token keys are rejected at decode before anything
+    is launched; a base in (0, 1] is rejected at plan time."""
     kvq = H.kvq()
     w, base = CASES["llama"]
     w = w.scaled(lengths=(40, 40, 40))
-    for kw in (dict(window=64), dict(sinks=32)):
-        cache = H.make_cache(w, rope_base=base, **kw)
-        q = W.draw_q(w, 0).cuda()
-        with pytest.raises(kvq.KVQError) as e:
-            cache.decode(0, q, w.softmax_scale)
-        assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
-        cache.close()
     wt = w.scaled(axis_k=o.AXIS_TOKEN)
     cache = H.make_cache(wt, rope_base=base)
     with pytest.raises(kvq.KVQError) as e:
