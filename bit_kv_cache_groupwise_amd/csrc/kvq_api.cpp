@@ -771,7 +771,6 @@ struct StepOpts {
 kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, const void* q, float softmax_scale,
                          float* out, void* workspace, size_t workspace_bytes, void* stream, const StepOpts& opt = {}) {
     const kvq_geometry& g = c->g;
-    if (g.axis_v != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "decode reads token-axis values only");
     const bool rope = g.rope_base > 0.0;
     if (rope && g.axis_k != KVQ_AXIS_CHANNEL)
         return fail(KVQ_ERR_UNSUPPORTED, "rotary keys need channel-axis keys in this build");
@@ -787,8 +786,11 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     }
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     // rotary keys: the generic split kernel
-    const bool mha = !rope && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
-    bool gqa = !rope && group_size(c) > 1 && g.axis_k == KVQ_AXIS_CHANNEL && kvq::mha_supported(g.head_dim);
+    // the single-query and query-group kernels: per-channel keys, per-token values
+    const bool fast = !rope && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
+                      kvq::mha_supported(g.head_dim);
+    const bool mha = fast && group_size(c) == 1;
+    bool gqa = fast && group_size(c) > 1;
     for (const auto& pr : c->pairs)  // head_dim 64: a lane group's half unit of key codes must be whole words
         gqa = gqa && (g.head_dim >= 128 || pr.bk % 2 == 0);
     if (!mha && !gqa && group_size(c) > kvq::kMaxQueryGroup)

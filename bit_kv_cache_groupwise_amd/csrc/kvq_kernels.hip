@@ -245,6 +245,35 @@ __device__ __forceinline__ void value_pass(const uint32_t* pages, const SeqEntry
     }
 }
 
+// Values grouped along tokens like keys (one step and zero per channel per
+// block of G tokens): x_hat = fma(code, s_bc, z_bc) per element, added with
+// weight p; tokens past the last whole block are read from the residual rows
+// vr (row t mod G, input dtype). nqv: tokens with quantized values.
+template <int DT, int BV>
+__device__ __forceinline__ void value_pass_channel(const uint32_t* pages, const SeqEntry& e, const uint8_t* vc,
+                                                   const uint8_t* vm, const uint8_t* vr, const float* sc, int t0,
+                                                   int t1, int nqv, int tl, int TL, int u, int D, int Gv,
+                                                   float (&acc)[32]) {
+    for (int t = t0 + tl; t < t1; t += TL) {
+        const float p = sc[t - t0];
+        if (t < nqv) {
+            const PageRow pr = page_row(pages, e, t);
+            uint32_t w[BV];
+            load_unit<BV>((const uint32_t*)(vc + pr.base + (size_t)pr.row * (D * BV / 8)) + u * BV, w);
+            const uint32_t* meta = (const uint32_t*)(vm + pr.base) + (size_t)(pr.row / Gv) * D + 32 * u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t m = meta[j];
+                acc[j] = fmaf(p, fmaf((float)code_at<BV>(w, j), f16_to_f32(m), f16_to_f32(m >> 16)), acc[j]);
+            }
+        } else {
+            const uint8_t* row = vr + (size_t)(t % Gv) * D * In<DT>::bytes;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) acc[j] = fmaf(p, load_in<DT>(row, 32 * u + j), acc[j]);
+        }
+    }
+}
+
 // Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
 // Complicam as Chaves"): cos and sin of the angle t * theta, reduced modulo
 // 2 pi in float64 (t * theta reaches 1e5-1e8 radians at long context, where a
@@ -326,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
     const uint8_t* kr = a.resid + e.resid[0] + (size_t)kvh * e.resid_hs[0];
     const uint8_t* vc = a.codes + e.codes[1] + (size_t)kvh * e.codes_hs[1];
     const uint8_t* vm = a.meta + e.meta[1] + (size_t)kvh * e.meta_hs[1];
+    const uint8_t* vr = a.resid + e.resid[1] + (size_t)kvh * e.resid_hs[1];  // per-channel values' residual rows
     // key code row of token t; key metadata of channel-axis block b (D words)
     // or of token t (D / G words)
     auto krow = [&](int t) -> const uint32_t* {
@@ -453,12 +483,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
 #pragma unroll
         for (int j = 0; j < 32; ++j) acc[j] = 0.f;
         float zacc = 0.f;
-        switch (BV) {
-            case 2: value_pass<2>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 3: value_pass<3>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 4: value_pass<4>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            case 6: value_pass<6>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
-            default: value_pass<8>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+        if (a.axis_v == 0) {  // per-channel values (windowed tokens all lie in whole blocks)
+            const int nqv = a.win_mode ? te : (len / Gv) * Gv;
+            switch (BV) {
+                case 2: value_pass_channel<DT, 2>(a.pages, e, vc, vm, vr, sc, t0, t1, nqv, tl, TL, u, D, Gv, acc); break;
+                case 3: value_pass_channel<DT, 3>(a.pages, e, vc, vm, vr, sc, t0, t1, nqv, tl, TL, u, D, Gv, acc); break;
+                case 4: value_pass_channel<DT, 4>(a.pages, e, vc, vm, vr, sc, t0, t1, nqv, tl, TL, u, D, Gv, acc); break;
+                case 6: value_pass_channel<DT, 6>(a.pages, e, vc, vm, vr, sc, t0, t1, nqv, tl, TL, u, D, Gv, acc); break;
+                default: value_pass_channel<DT, 8>(a.pages, e, vc, vm, vr, sc, t0, t1, nqv, tl, TL, u, D, Gv, acc); break;
+            }
+        } else {
+            switch (BV) {
+                case 2: value_pass<2>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+                case 3: value_pass<3>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+                case 4: value_pass<4>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+                case 6: value_pass<6>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+                default: value_pass<8>(a.pages, e, vc, vm, sc, t0, t1, tl, TL, u, D, Gv, acc, zacc); break;
+            }
         }
 #pragma unroll
         for (int j = 0; j < 32; ++j) red[tl * D + 32 * u + j] = acc[j] + zacc;

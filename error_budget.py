@@ -84,30 +84,36 @@ def recent_queries(k, S, T, H, D, gen):
     return kk + torch.randn(kk.shape, generator=gen, device=k.device)
 
 
-def run_config(w, device="cuda", window=0, sinks=0, q_recent=False):
+def run_config(w, device="cuda", window=0, sinks=0, q_recent=False, whole_vector=False):
     """Quantize w's cache on the GPU, read it back and decode; return the error
     metrics. With a window or sinks, the reconstruction read back is the one the
     attention reads (those tokens unquantized). q_recent: queries from
-    recent_queries instead of N(0,1)."""
+    recent_queries instead of N(0,1). whole_vector: groups that span every kv
+    head of a token (token axis, group = kv_heads * head_dim): the cache is
+    built as one head of kv_heads * head_dim channels (the same [T][H][D] rows),
+    and its reconstruction is split back into heads for the attention; no fused
+    decode (it would attend over the merged head)."""
     import torch
 
     from bit_kv_cache_groupwise_amd import kvq
     from bit_kv_cache_groupwise_amd import workloads as W
 
     S, H, D, T = w.num_seqs, w.kv_heads, w.head_dim, w.lengths[0]
-    geom = kvq.geometry(layers=1, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D, group_k=w.group_k,
-                        group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype,
-                        window=window, sinks=sinks)
+    Hc, Dc = (1, H * D) if whole_vector else (H, D)
+    geom = kvq.geometry(layers=1, num_seqs=S, kv_heads=Hc, q_heads=Hc if whole_vector else w.q_heads, head_dim=Dc,
+                        group_k=Dc if whole_vector else w.group_k, group_v=Dc if whole_vector else w.group_v,
+                        axis_k=TOK if whole_vector else w.axis_k, axis_v=TOK if whole_vector else w.axis_v,
+                        in_dtype=w.in_dtype, window=window, sinks=sinks)
     cache = kvq.Cache(geom, list(w.lengths), [b[0] for b in w.bits], [b[1] for b in w.bits], device=device)
     k, v = W.draw_kv(w, 0, w.lengths, device=device, stream=0)
-    cache.append(0, k, v, list(w.lengths))
+    cache.append(0, k.reshape(-1, Hc, Dc), v.reshape(-1, Hc, Dc), list(w.lengths))
     q = W.draw_q(w, 0, device=device)
     if q_recent:
         gen = torch.Generator(device=device)
         gen.manual_seed(4242)
         q = recent_queries(k, S, T, H, D, gen).to(q.dtype)
     fused = None
-    if w.axis_v == TOK:  # the fused decode reads token-axis values
+    if not whole_vector:
         fused = cache.decode(0, q, w.softmax_scale).double().cpu().numpy()
     torch.cuda.synchronize()
     kx = k.double().cpu().numpy().reshape(S, T, H, D).transpose(0, 2, 1, 3)  # [S][H][T][D]
@@ -118,8 +124,9 @@ def run_config(w, device="cuda", window=0, sinks=0, q_recent=False):
     kn2 = kd2 = vn2 = vd2 = 0.0
     for s in range(S):
         kd, vd = cache.dequantize(0, s)
-        kd = kd.double().cpu().numpy()
-        vd = vd.double().cpu().numpy()
+        # [Hc][T][Dc] -> [H][T][D] (a no-op unless whole_vector)
+        kd = kd.double().cpu().numpy().reshape(Hc, T, Dc).transpose(1, 0, 2).reshape(T, H, D).transpose(1, 0, 2)
+        vd = vd.double().cpu().numpy().reshape(Hc, T, Dc).transpose(1, 0, 2).reshape(T, H, D).transpose(1, 0, 2)
         kn2 += float(np.sum(kx[s] ** 2))
         kd2 += float(np.sum((kd - kx[s]) ** 2))
         vn2 += float(np.sum(vx[s] ** 2))
@@ -138,7 +145,8 @@ def run_config(w, device="cuda", window=0, sinks=0, q_recent=False):
         acc["top5_mass"].append(top_mass(w_ref))
     cache.close()
     return {
-        "axis_k": AXIS_NAME[w.axis_k], "axis_v": AXIS_NAME[w.axis_v], "group_k": w.group_k, "group_v": w.group_v,
+        "axis_k": AXIS_NAME[TOK if whole_vector else w.axis_k], "axis_v": AXIS_NAME[TOK if whole_vector else w.axis_v],
+        "group_k": "vector" if whole_vector else w.group_k, "group_v": "vector" if whole_vector else w.group_v,
         "bits": list(w.bits[0]), "v_dist": w.v_dist, "window": window, "sinks": sinks,
         "queries": "recent" if q_recent else "normal",
         "k_recon_rel": math.sqrt(kd2 / kn2), "v_recon_rel": math.sqrt(vd2 / vn2),
@@ -166,16 +174,35 @@ def configs(T=2048):
         for G in (64, 128):
             out.append(base.scaled(group_k=G, group_v=G, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
         out.append(base.scaled(group_k=256, group_v=128, bits=((bits, bits),) * 4, v_dist="token_lognormal"))
-    return [(x, 0, 0, False) for x in out] + window_configs(base)
+    return [(x, 0, 0, False, False) for x in out] + window_configs(base) + granularity_configs(T)
+
+
+def granularity_configs(T=2048):
+    """Scales per whole vector, per head, per 64 and per 32 channels ([H]
+    "Granularita jako jediné univerzální doporučení"; [H] "Výchozí zjištění na
+    GPT-2": per-head against whole-vector scaling): keys and values both grouped
+    along the channels of a token, 3 and 4 bits, two kv heads of 128 channels
+    (a 256-channel vector)."""
+    from bit_kv_cache_groupwise_amd import workloads as W
+
+    base = W.llama2_7b().scaled(name="granularity", num_seqs=4, kv_heads=2, q_heads=2, lengths=(T,) * 4,
+                                axis_k=TOK, axis_v=TOK, v_dist="token_lognormal")
+    rows = []
+    for bits in (3, 4):
+        wb = base.scaled(bits=((bits, bits),) * 4)
+        rows.append((wb.scaled(group_k=128, group_v=128), 0, 0, False, True))  # whole vector
+        for G in (128, 64, 32):  # per head, then finer
+            rows.append((wb.scaled(group_k=G, group_v=G), 0, 0, False, False))
+    return rows
 
 
 def window_configs(base):
     """Full-precision recent window and sinks at 2 bits (keys per channel,
     values per token, groups of 32): (workload, window, sinks)."""
     w2 = base.scaled(group_k=32, group_v=32, bits=((2, 2),) * 4, v_dist="token_lognormal")
-    rows = [(w2, win, snk, False) for win, snk in ((32, 0), (128, 0), (512, 0), (128, 32), (0, 64))]
+    rows = [(w2, win, snk, False, False) for win, snk in ((32, 0), (128, 0), (512, 0), (128, 32), (0, 64))]
     # queries that attend to the most recent tokens
-    return rows + [(w2, win, snk, True) for win, snk in ((0, 0), (32, 0), (128, 0), (128, 32))]
+    return rows + [(w2, win, snk, True, False) for win, snk in ((0, 0), (32, 0), (128, 0), (128, 32))]
 
 
 def table(rows):
@@ -198,8 +225,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=2048)
     args = ap.parse_args()
     rows = []
-    for w, window, sinks, q_recent in configs(args.tokens):
-        r = run_config(w, window=window, sinks=sinks, q_recent=q_recent)
+    for w, window, sinks, q_recent, whole in configs(args.tokens):
+        r = run_config(w, window=window, sinks=sinks, q_recent=q_recent, whole_vector=whole)
         rows.append(r)
         print(json.dumps(r), flush=True)
     print(table(rows), flush=True)

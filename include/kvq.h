@@ -239,8 +239,11 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
  * once per generated token). out[s][h] = sum_t softmax_t(scale * q.k_hat_t) *
  * v_hat_t, keys in the residual taken as stored. q: device, in_dtype,
  * [num_seqs][q_heads][head_dim]; out: device float32, same shape; a sequence
- * of length 0 gets zeros. This build: K on either axis, V on the token axis,
- * q_heads/kv_heads <= 16 (else KVQ_ERR_UNSUPPORTED). */
+ * of length 0 gets zeros. K and V on either axis. Per-channel keys with
+ * per-token values and head_dim 64, 128 or 256 take the single-query or
+ * query-group kernel (any q_heads/kv_heads); other caches (per-token keys,
+ * per-channel values, rotary keys, other head_dims) take the generic split
+ * kernel, which needs q_heads/kv_heads <= 16 (else KVQ_ERR_UNSUPPORTED). */
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 

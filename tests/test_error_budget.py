@@ -72,7 +72,37 @@ def test_gpu_metrics_match_the_oracle(axes, window, sinks):
     assert r["k_recon_rel"] == pytest.approx(math.sqrt(kd2 / kn2), rel=1e-9)
     assert r["v_recon_rel"] == pytest.approx(math.sqrt(vd2 / vn2), rel=1e-9)
     assert r["out_rel_dequant"] == pytest.approx(float(np.mean(outs)), rel=1e-9)
-    if av == eb.TOK:  # the fused decode sits within its tolerance of the dequantized attention
-        assert abs(r["out_rel_fused"] - r["out_rel_dequant"]) <= 2e-3
-    else:
-        assert r["out_rel_fused"] is None
+    # the fused decode (per-channel values: the generic split kernel) sits within
+    # its tolerance of the dequantized attention
+    assert abs(r["out_rel_fused"] - r["out_rel_dequant"]) <= 2e-3
+
+
+@pytest.mark.gpu
+def test_whole_vector_groups_match_the_oracle():
+    """Whole-vector granularity (one step per token over every kv head's
+    channels): the reconstruction the workload measures is the oracle's token-axis
+    quantization of the concatenated heads, split back into heads."""
+    import torch  # noqa: F401
+
+    from bit_kv_cache_groupwise_amd import workloads as W
+    from oracle import kvq_oracle as o
+
+    w = W.llama2_7b().scaled(name="granularity", num_seqs=2, kv_heads=2, q_heads=2, lengths=(64, 64),
+                             axis_k=eb.TOK, axis_v=eb.TOK, bits=((3, 3),) * 2, v_dist="token_lognormal")
+    r = eb.run_config(w, whole_vector=True)
+    k, v = W.draw_kv(w, 0, w.lengths, device="cuda", stream=0)
+    k = k.float().cpu().numpy()
+    v = v.float().cpu().numpy()
+    T, HD = 64, 2 * w.head_dim
+    kn2 = kd2 = vn2 = vd2 = 0.0
+    for s in range(2):
+        ks, vs = k[s * T:(s + 1) * T].reshape(T, HD), v[s * T:(s + 1) * T].reshape(T, HD)
+        e = o.encode_head(ks, vs, group_k=HD, group_v=HD, axis_k=o.AXIS_TOKEN, axis_v=o.AXIS_TOKEN, bits_k=3,
+                          bits_v=3)
+        kn2 += np.sum(ks.astype(np.float64) ** 2)
+        kd2 += np.sum((e["k_hat"] - ks) ** 2)
+        vn2 += np.sum(vs.astype(np.float64) ** 2)
+        vd2 += np.sum((e["v_hat"] - vs) ** 2)
+    assert r["k_recon_rel"] == pytest.approx(math.sqrt(kd2 / kn2), rel=1e-9)
+    assert r["v_recon_rel"] == pytest.approx(math.sqrt(vd2 / vn2), rel=1e-9)
+    assert r["group_k"] == "vector" and r["out_rel_fused"] is None

@@ -214,12 +214,63 @@ def test_error_paths_leave_the_cache_untouched():
         k.kvq_decode_attention(cache.handle, 0, q, w.softmax_scale, out, ws, 16)
     assert ei.value.status == k.KVQ_ERR_WORKSPACE
     cache.close()
-    vch = W.mixed_batch().scaled(num_seqs=1, lengths=(10,), bits=((2, 2),), axis_v=o.AXIS_CHANNEL)
-    c2 = H.make_cache(vch)
+    # the generic split kernel (here: per-channel values) takes at most 16 query heads per kv head
+    wide = W.mixed_batch().scaled(num_seqs=1, kv_heads=2, q_heads=64, lengths=(10,), bits=((2, 2),),
+                                  axis_v=o.AXIS_CHANNEL)
+    c2 = H.make_cache(wide)
     with pytest.raises(k.KVQError) as ei:
-        c2.decode(0, torch.zeros((1, vch.q_heads, 128), dtype=torch.float16, device="cuda"), 0.1)
+        c2.decode(0, torch.zeros((1, wide.q_heads, 128), dtype=torch.float16, device="cuda"), 0.1)
     assert ei.value.status == k.KVQ_ERR_UNSUPPORTED
     c2.close()
+
+
+# per-channel values ([U] "Valores: Onde a Intuicao Quebra": the pages compare
+# value grouping along channels with grouping along tokens)
+VCHAN_CASES = {
+    "llama": (W.llama2_7b().scaled(num_seqs=3, kv_heads=2, q_heads=2, lengths=(700, 31, 64), bits=((2, 2), (4, 8),
+                                   (3, 6)), axis_v=o.AXIS_CHANNEL), 0, 0, 0),
+    "mixed": (W.mixed_batch().scaled(num_seqs=5, lengths=(0, 33, 300, 1000, 129), bits=tuple(W.BIT_PAIRS_MIXED),
+                                     axis_v=o.AXIS_CHANNEL, group_v=64), 0, 0, 0),
+    "both_token_keys": (W.gpt2_small().scaled(num_seqs=2, layers=1, kv_heads=2, q_heads=2, lengths=(300, 70),
+                                              bits=((6, 4),) * 2, axis_k=o.AXIS_TOKEN, axis_v=o.AXIS_CHANNEL), 0, 0,
+                        0),
+    "window": (W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=4, lengths=(900, 100), bits=((2, 2),) * 2,
+                                    axis_v=o.AXIS_CHANNEL, group_v=128), 64, 128, 0),
+    "paged": (W.mixed_batch().scaled(num_seqs=3, lengths=(500, 77, 1200), bits=((4, 4), (2, 8), (3, 3)),
+                                     axis_v=o.AXIS_CHANNEL), 0, 0, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(VCHAN_CASES))
+def test_per_channel_values_decode(name):
+    """Values quantized per channel (one step and zero per channel per block of
+    G tokens, the last len mod G rows in the residual) decode through the generic
+    split kernel: stored bytes and dequantize bit-exact, attention within 2e-3 of
+    the fp64 oracle; with a window the full-precision rows are read as stored."""
+    w, window, sinks, P = VCHAN_CASES[name]
+    _note(f"[vchan] case={name} lens={w.lengths} R={window} S={sinks} P={P}")
+    cache = H.make_cache(w, window=window, sinks=sinks, page_tokens=P)
+    prefix, new = H.history(w, 0)
+    H.append_chunks(cache, 0, prefix[0], prefix[1], prefix[2], [37, 5])
+    H.append_chunks(cache, 0, new[0], new[1], new[2])
+    q = W.draw_q(w, 0)
+    out = cache.decode(0, q.cuda(), w.softmax_scale).cpu().numpy()
+    worst = 0.0
+    for s in range(w.num_seqs):
+        k, v = H.full_seq(prefix, new, s)
+        encs = []
+        for h in range(w.kv_heads):
+            H.assert_head_bytes(cache, w, 0, s, h, k, v)
+            encs.append(H.encode_window(w, k, v, s, h, window, sinks) if (window or sinks) else H.encode(w, k, v, s, h))
+        kd, vd = cache.dequantize(0, s)
+        torch.cuda.synchronize()
+        for h in range(w.kv_heads):
+            np.testing.assert_array_equal(vd[h].cpu().numpy(), encs[h]["v_hat"].astype(np.float32))
+        err = H.row_rel_err(out[s], H.attn_ref(w, q[s].float().numpy(), encs))
+        worst = max(worst, float(err.max()))
+        assert np.all(err <= H.ATTN_TOL), (name, s, float(err.max()))
+    _note(f"[vchan] case={name} worst row rel err {worst:.3e}")
+    cache.close()
 
 
 @pytest.mark.parametrize("q_heads,head_dim", [(64, 128), (48, 256), (40, 64)])
