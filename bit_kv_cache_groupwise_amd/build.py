@@ -69,6 +69,23 @@ def link() -> str:
     return LIB
 
 
+def build_host_sanitized(out_dir: str) -> str:
+    """libkvq with its host code (argument checks, layout, page management)
+    built by g++ under AddressSanitizer and UndefinedBehaviorSanitizer, linked
+    with this build's device objects (which must exist: build() first). For the
+    CPU tests of the C ABI; load it with libasan preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, "kvq_api_sanitized.o")
+    lib = os.path.join(out_dir, "libkvq_sanitized.so")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", *san, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+          "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "kvq_api.cpp"), "-o", obj])
+    devobjs = [os.path.join(BUILD, u[1]) for u in units() if u[3]]
+    _run(["g++", "-shared", *san, "-o", lib, obj, *devobjs, "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"])
+    return lib
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
