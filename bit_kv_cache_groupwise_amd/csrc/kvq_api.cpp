@@ -47,7 +47,6 @@ struct kvq_cache {
     std::vector<uint32_t> pt;
     std::vector<int32_t> lens;      // host mirror of the current lengths [layers][num_seqs]
     std::vector<uint8_t> parity;    // which length buffer is current, per layer
-    std::vector<int32_t> args;      // staging for the call-argument area
     struct Pair { int bk, bv, offset, count; };
     std::vector<Pair> pairs;        // distinct (bits_k, bits_v) pairs and their slice of the table's seq list
     std::vector<int32_t> pair_list; // host copy of that seq list
@@ -432,7 +431,6 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
     }
     c->lens.assign((size_t)g->layers * g->num_seqs, 0);
     c->parity.assign(g->layers, 0);
-    c->args.assign(2 * (size_t)g->num_seqs, 0);
     c->max_cap = *std::max_element(cap, cap + g->num_seqs);
     std::vector<uint8_t> img(c->tl.total, 0);
     std::memcpy(img.data(), c->entries.data(), c->entries.size() * sizeof(SeqEntry));
@@ -631,13 +629,26 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
     const int32_t* d_start = nullptr;
     int32_t* args_dev = (int32_t*)(c->table + c->tl.args_off);
     if (!uniform) {
+        // the counts and row offsets travel in the arguments of a small scatter
+        // kernel (a host-to-device copy from pageable memory would make the host
+        // wait for the stream)
+        kvq::PageUpdates u;
+        u.count = 0;
         int32_t acc = 0;
-        for (int s = 0; s < S; ++s) {
-            c->args[s] = n_new[s];
-            c->args[S + s] = acc;
+        hipError_t e = hipSuccess;
+        for (int s = 0; s < S && e == hipSuccess; ++s) {
+            const int32_t vals[2] = {n_new[s], acc};
             acc += n_new[s];
+            for (int k = 0; k < 2; ++k) {
+                u.index[u.count] = (uint32_t)(k * S + s);
+                u.value[u.count] = (uint32_t)vals[k];
+                if (++u.count == kvq::kPageUpdateMax) {
+                    e = kvq::launch_page_updates((uint32_t*)args_dev, u, hs);
+                    u.count = 0;
+                }
+            }
         }
-        hipError_t e = hipMemcpyAsync(args_dev, c->args.data(), sizeof(int32_t) * 2 * S, hipMemcpyHostToDevice, hs);
+        if (e == hipSuccess) e = kvq::launch_page_updates((uint32_t*)args_dev, u, hs);
         if (e != hipSuccess) return hip_fail(e, "uploading append counts");
         d_n = args_dev;
         d_start = args_dev + S;
@@ -684,12 +695,14 @@ kvq_status prepare_append(kvq_cache* c, int32_t layer, int32_t n_layers, const v
         if (axes[t] == KVQ_AXIS_TOKEN) {
             gx[t] = std::max(1, (max_n + a.rows_per_block - 1) / a.rows_per_block);
         } else {
-            gx[t] = 1;
+            gx[t] = 1;  // completed blocks per (seq, head), at most
             for (int l = layer; l < layer + n_layers; ++l)
                 for (int s = 0; s < S; ++s) {
                     const int len = c->lens[(size_t)l * S + s];
                     gx[t] = std::max(gx[t], (len + n_new[s]) / groups[t] - len / groups[t]);
                 }
+            if (kvq::quant_wave_path(groups[t], g.head_dim, g.in_dtype))  // four blocks per workgroup
+                gx[t] = (gx[t] + kvq::kQuantBlocksPerGroup - 1) / kvq::kQuantBlocksPerGroup;
         }
     }
     if ((long)gx[0] + gx[1] > INT32_MAX / 2) return fail(KVQ_ERR_ARG, "append too large for one launch");

@@ -158,6 +158,15 @@ struct GqaList {
 constexpr int kWinTokens = 64;  // full-precision tokens per decode_window_kernel workgroup
 constexpr int kWinHeads = 4;    // query heads per decode_window_kernel workgroup
 
+// Channel-axis quantization by one wave per block (four blocks per workgroup),
+// with the block's inputs held in registers (one channel pair per lane): blocks
+// of 32 tokens, head_dim <= 128. Other blocks take one workgroup per block, two
+// passes over the inputs.
+constexpr int kQuantBlocksPerGroup = 4;
+constexpr bool quant_wave_path(int group, int head_dim, int in_dtype) {
+    return group == 32 && head_dim <= 128 && in_dtype >= 0;
+}
+
 // Keys and values of one append in one launch: gx_k workgroups per (head, seq)
 // for the keys, then gx_v for the values, then (window mode) the copy of the
 // rows the full-precision window keeps (max_new: most tokens a sequence appends).
@@ -207,8 +216,9 @@ hipError_t scratch_address(void** out);
 hipError_t launch_decode_window(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
-// Scatter of page-list entries: pages[index[i]] = value[i], i < count, with the
-// pairs in the kernel arguments (no host staging).
+// Scatter of 32-bit words: base[index[i]] = value[i], i < count, with the pairs
+// in the kernel arguments (no host staging): page-list entries and the
+// per-sequence counts of an append.
 constexpr int kPageUpdateMax = 480;
 struct PageUpdates {
     int32_t count;

@@ -155,6 +155,115 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     }
 }
 
+// Quantize, channel axis, one wave per block of G tokens (G = 32 or 64), four
+// blocks per workgroup: lane l holds channel pairs (2p, 2p + 1), p = l + 64q,
+// of every token of the block in registers (one coalesced read of each token
+// row, no second pass); min, max, step, zero and codes per channel in
+// registers; the codes go through a wave-private LDS tile [G][D] bytes to be
+// packed per 32-channel unit. The wave of the append's first block also copies
+// the rows past the last complete block into the residual, after its own reads
+// of the old residual rows. Same arithmetic and results as channel_axis_part.
+template <int DT, int G, int PPL>
+__device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item, int head, int seq, uint8_t* smem) {
+    constexpr int IB = In<DT>::bytes, NW = IB == 4 ? 2 : 1;  // 32-bit words per channel pair
+    const int D = a.head_dim, UPR = D >> 5;
+    const int len0 = a.len_in[seq];
+    const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
+    const int len1 = len0 + n;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (a.len_out && item == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len1;
+    const int b_first = len0 / G, b_end = len1 / G, nb = b_end - b_first;
+    const int k = item * kQuantBlocksPerGroup + wave;  // block of this append
+    if (k >= (nb > 0 ? nb : 1)) return;
+    const int row_start = a.row_start ? a.row_start[seq] : seq * a.n_uniform;
+    const SeqEntry& e = a.table[seq];
+    const int T = a.tensor, B = e.bits[T];
+    const uint8_t* resid = a.resid + e.resid[T] + (size_t)head * e.resid_hs[T];
+    if (k < nb) {
+        const int b = b_first + k;
+        const float L = (float)((1 << B) - 1);
+        uint32_t raw[G][PPL][NW];
+        // all loads first (pairs past D read channel 0 and are not used)
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int t = b * G + i;
+            const uint8_t* row = t < len0 ? resid + (size_t)(t % G) * D * IB
+                                          : (const uint8_t*)a.src + ((size_t)(row_start + t - len0) * a.kv_heads + head) * D * IB;
+#pragma unroll
+            for (int q = 0; q < PPL; ++q) {
+                const int c = 2 * (lane + 64 * q);
+                const uint32_t* w = (const uint32_t*)(row + (size_t)(c < D ? c : 0) * IB);
+#pragma unroll
+                for (int h = 0; h < NW; ++h) raw[i][q][h] = w[h];
+            }
+        }
+        auto val = [&](int i, int q, int h) -> float {  // channel 2p + h of token i
+            if constexpr (IB == 4) return __uint_as_float(raw[i][q][h]);
+            else return half_to_f32<DT>(h ? raw[i][q][0] >> 16 : raw[i][q][0]);
+        };
+        const PageRow pr = page_row(a.pages, e, b * G);
+        uint32_t* meta = (uint32_t*)(a.meta + pr.base + e.meta[T] + (size_t)head * e.meta_hs[T]) + (size_t)(pr.row / G) * D;
+        uint8_t* tile = smem + (size_t)wave * G * D;
+#pragma unroll
+        for (int q = 0; q < PPL; ++q) {
+            const int c = 2 * (lane + 64 * q);
+            float mn[2], mx[2], sf[2], zf[2];
+            uint32_t sb[2], zb[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                mn[h] = INFINITY, mx[h] = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < G; ++i) mn[h] = fminf(mn[h], val(i, q, h)), mx[h] = fmaxf(mx[h], val(i, q, h));
+                sb[h] = f32_to_f16_bits((mx[h] - mn[h]) / L);
+                zb[h] = f32_to_f16_bits(mn[h]);
+                sf[h] = f16_to_f32(sb[h]);
+                zf[h] = f16_to_f32(zb[h]);
+            }
+            if (c < D) {
+                meta[c] = sb[0] | (zb[0] << 16);
+                meta[c + 1] = sb[1] | (zb[1] << 16);
+#pragma unroll
+                for (int i = 0; i < G; ++i)
+                    *(uint16_t*)&tile[i * D + c] =
+                        (uint16_t)(quant_code(val(i, q, 0), sf[0], zf[0], L) | (quant_code(val(i, q, 1), sf[1], zf[1], L) << 8));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint8_t* codes = a.codes + pr.base + e.codes[T] + (size_t)head * e.codes_hs[T];
+        for (int idx = lane; idx < G * UPR; idx += 64) {
+            const int i = idx / UPR, u = idx - i * UPR;
+            const uint4* src = (const uint4*)(tile + i * D + 32 * u);
+            uint32_t cc[32];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 v4 = src[h];
+                const uint32_t v[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    cc[16 * h + 4 * m + 0] = v[m] & 0xffu;
+                    cc[16 * h + 4 * m + 1] = (v[m] >> 8) & 0xffu;
+                    cc[16 * h + 4 * m + 2] = (v[m] >> 16) & 0xffu;
+                    cc[16 * h + 4 * m + 3] = v[m] >> 24;
+                }
+            }
+            store_codes_rt(B, cc, (uint32_t*)(codes + (size_t)(pr.row + i) * (D * B / 8)) + u * B);
+        }
+    }
+    if (k == 0)  // the first block's reads of the old residual rows are done (their values were used above)
+        residual_rows<DT>(a, head, seq, b_end * G > len0 ? b_end * G : len0, len0, len1, 64);
+}
+
+template <int DT>
+__device__ __forceinline__ void channel_axis_any(const TensorArgs& a, int item, int head, int seq, uint32_t* smem) {
+    if (quant_wave_path(a.group, a.head_dim, a.in_dtype)) {
+        channel_axis_wave<DT, 32, 1>(a, item, head, seq, (uint8_t*)smem);
+    } else {
+        channel_axis_part<DT>(a, item, head, seq, smem);
+    }
+}
+
 // One launch quantizes and appends both tensors: workgroups [0, gx_k) take the
 // keys, [gx_k, gx_kv) the values, each with its own axis, and with a
 // full-precision window [gx_kv, gridDim.x) copy the rows the window keeps.
@@ -171,11 +280,11 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, T
         window_rows<DT>(k, v, seq, head, (int)blockIdx.x - gx_kv, (int)gridDim.x - gx_kv, kThreads);
     } else if ((int)blockIdx.x < gx_k) {
         if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
-        else channel_axis_part<DT>(k, blockIdx.x, head, seq, smem);
+        else channel_axis_any<DT>(k, blockIdx.x, head, seq, smem);
     } else {
         const int item = (int)blockIdx.x - gx_k;
         if (v.axis == 1) token_axis_part<DT>(v, item, head, seq);
-        else channel_axis_part<DT>(v, item, head, seq, smem);
+        else channel_axis_any<DT>(v, item, head, seq, smem);
     }
 }
 
@@ -868,7 +977,10 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
     dim3 grid(gx_kv + gx_w, k.kv_heads, k.num_seqs * k.n_layers);
     size_t lds = 0;
     for (const TensorArgs* t : {&k, &v})
-        if (t->axis == 0) lds = std::max(lds, std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));
+        if (t->axis == 0)
+            lds = std::max(lds, quant_wave_path(t->group, t->head_dim, t->in_dtype)
+                                    ? (size_t)kQuantBlocksPerGroup * t->group * t->head_dim
+                                    : std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));
     switch (k.in_dtype) {
         case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
         case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
