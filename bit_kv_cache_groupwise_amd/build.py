@@ -47,6 +47,8 @@ def units():
             ("kvq_scratch.hip", "kvq_scratch.o", [], True),
             *[("kvq_decode_mha.hip", f"kvq_decode_mha_d{d}.o", [f"-DKVQ_MHA_HEAD_DIM={d}"], True)
               for d in MHA_HEAD_DIMS],
+            *[("kvq_decode_mha.hip", f"kvq_decode_mha_rope_d{d}.o", [f"-DKVQ_MHA_HEAD_DIM={d}", "-DKVQ_MHA_ROPE=1"], True)
+              for d in MHA_HEAD_DIMS],
             *[("kvq_decode_gqa.hip", f"kvq_decode_gqa_d{d}.o", [f"-DKVQ_GQA_HEAD_DIM={d}"], True)
               for d in MHA_HEAD_DIMS],
             ("kvq_api.cpp", "kvq_api.o", [], False)]

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -170,6 +171,26 @@ uint32_t pages_of(const kvq_geometry* g, int cap) {
 // head regions; the page stride is the largest over the sequences), residual
 // regions as with contiguous storage. Fails when the pool would not be
 // addressable (page lists or page indices beyond 32 bits).
+// Rotary tables of a cache with rope_base > 0 (device copy in the table
+// buffer): theta_i = base^(-2i/D) for the D/2 pairs (i, i + D/2) as doubles,
+// then (cos, sin)(u theta_i) as floats for u = 0..kRopeRows-1, row-major
+// [u][i] ([U] "Embebedos Rotatorios Complicam as Chaves").
+uint64_t rope_table_bytes(int head_dim) {
+    return (uint64_t)head_dim / 2 * 8 + (uint64_t)kvq::kRopeRows * head_dim / 2 * 8;
+}
+void fill_rope_tables(const kvq_geometry& g, uint8_t* dst) {
+    const int P = g.head_dim / 2;
+    double* theta = (double*)dst;
+    float* tab = (float*)(dst + (size_t)P * 8);
+    for (int i = 0; i < P; ++i) theta[i] = std::pow(g.rope_base, -2.0 * i / g.head_dim);
+    for (int u = 0; u < kvq::kRopeRows; ++u)
+        for (int i = 0; i < P; ++i) {
+            const double ang = u * theta[i];
+            tab[2 * ((size_t)u * P + i)] = (float)std::cos(ang);
+            tab[2 * ((size_t)u * P + i) + 1] = (float)std::sin(ang);
+        }
+}
+
 kvq_status layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, const uint8_t* bv,
                   std::vector<SeqEntry>* entries, kvq_sizes* sz, kvq::TableLayout* tl) {
     const uint64_t D = g->head_dim, H = g->kv_heads, ib = in_bytes(g->in_dtype);
@@ -247,7 +268,8 @@ kvq_status layout(const kvq_geometry* g, const int32_t* cap, const uint8_t* bk, 
     tl->ctr_off = tl->args_off + align_up(2 * (uint64_t)g->num_seqs * 4, kvq::kAlign);
     tl->pairs_off = tl->ctr_off + align_up((uint64_t)g->num_seqs * g->kv_heads * 4, kvq::kAlign);
     tl->pt_off = tl->pairs_off + align_up((uint64_t)g->num_seqs * 4, kvq::kAlign);
-    tl->total = tl->pt_off + align_up(std::max<uint64_t>(plist, 1) * 4, kvq::kAlign);
+    tl->rope_off = tl->pt_off + align_up(std::max<uint64_t>(plist, 1) * 4, kvq::kAlign);
+    tl->total = tl->rope_off + (g->rope_base > 0.0 ? align_up(rope_table_bytes(g->head_dim), kvq::kAlign) : 0);
     sz->codes_bytes = std::max<uint64_t>(oc, kvq::kAlign);
     sz->meta_bytes = std::max<uint64_t>(om, kvq::kAlign);
     sz->residual_bytes = std::max<uint64_t>(orr, kvq::kAlign);
@@ -435,6 +457,7 @@ kvq_status kvq_cache_create(const kvq_geometry* g, const int32_t* cap, const uin
     std::vector<uint8_t> img(c->tl.total, 0);
     std::memcpy(img.data(), c->entries.data(), c->entries.size() * sizeof(SeqEntry));
     std::memcpy(img.data() + c->tl.pt_off, c->pt.data(), c->pt.size() * sizeof(uint32_t));
+    if (g->rope_base > 0.0) fill_rope_tables(*g, img.data() + c->tl.rope_off);
     {
         int32_t* list = (int32_t*)(img.data() + c->tl.pairs_off);
         int n = 0;
@@ -800,10 +823,10 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     // rotary keys: the generic split kernel
     // the single-query and query-group kernels: per-channel keys, per-token values
-    const bool fast = !rope && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
-                      kvq::mha_supported(g.head_dim);
+    // (rotary keys: the single-query kernel's rotary instantiations, else the generic kernel)
+    const bool fast = g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN && kvq::mha_supported(g.head_dim);
     const bool mha = fast && group_size(c) == 1;
-    bool gqa = fast && group_size(c) > 1;
+    bool gqa = fast && !rope && group_size(c) > 1;
     for (const auto& pr : c->pairs)  // head_dim 64: a lane group's half unit of key codes must be whole words
         gqa = gqa && (g.head_dim >= 128 || pr.bk % 2 == 0);
     if (!mha && !gqa && group_size(c) > kvq::kMaxQueryGroup)
@@ -857,6 +880,10 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     a.log2_group_v = __builtin_ctz((unsigned)g.group_v);
     a.split_floor = mha ? 1 : 0;
     a.rope_base = g.rope_base;
+    if (rope) {
+        a.rope_theta = (const double*)(c->table + c->tl.rope_off);
+        a.rope_tab = (const float*)(c->table + c->tl.rope_off + (size_t)g.head_dim / 2 * 8);
+    }
     if (win_mode(g)) {
         a.win_mode = 1;
         a.window = g.window;
@@ -882,7 +909,8 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         }
         for (const auto& pr : c->pairs) {
             a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
-            hipError_t e = kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
+            hipError_t e = rope ? kvq::launch_decode_mha_rope(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream)
+                                : kvq::launch_decode_mha(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "launching decode attention");
         }
         if (max_chunks > 1) {

@@ -71,15 +71,6 @@ __device__ __forceinline__ f32x4 mfma(const Frag& a, const Frag& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.h, b.h, c, 0, 0, 0);
 }
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // v_fma_mix_f32 with the first operand an fp16 half of a word: exact product
 // of an fp16 and an fp32 value, one rounding.
 __device__ __forceinline__ float mix_lo(uint32_t m, float b, float c) {

@@ -29,6 +29,18 @@
 // into the key vector; on the value side the softmax weights carry 2^24 (the
 // reference maximum is lowered by 24) and the code shifts are undone at the end.
 //
+// Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
+// Complicam as Chaves": rotate after dequantization). The rotary
+// instantiations (KVQ_MHA_ROPE, objects of their own) give a lane 16 whole
+// channel pairs (i, i + D/2) of its token instead of a 32-channel unit: run A =
+// channels 16cg..16cg+15, run B = their partners. With the query rotated to
+// the position t0 of a 32-token half, Q = R(-t0) q, the score of the token at
+// t0 + u is sum_i C_ui (Q_a k_a + Q_b k_b) + S_ui (Q_b k_a - Q_a k_b), where
+// (C, S)_ui = (cos, sin)(u theta_i) comes from a table of the cache. With
+// k = z + s code, each pair's two sums take four products of its two codes
+// with weights built once per half and pair, so a code costs 3 VALU (1 on the
+// plain path).
+//
 // Softmax: online in the log2 domain with a lazily moved reference maximum
 // (moved only when a score exceeds it by more than 2^8), so rescaling is
 // rare. Splits of one (seq, head) are merged by merge_kernel; a sequence that
@@ -36,6 +48,10 @@
 #include "kvq_append.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
+
+#ifndef KVQ_MHA_ROPE
+#define KVQ_MHA_ROPE 0
+#endif
 
 namespace kvq {
 namespace {
@@ -274,6 +290,96 @@ struct KeyDot2 {
     }
 };
 
+// Rotary layout: the words of a 16-code run (a run of 3-bit codes starts on
+// a half word when cg is odd: two words, aligned at use).
+template <int B>
+__host__ __device__ constexpr int run_words() { return B == 3 ? 2 : B / 2; }
+
+// Visit the 16 code pairs of runs A and B (same token): f.pair2<JL, JH>(mA, mB)
+// gets run A's and run B's words masked to codes JL (low half) and JH (high
+// half), each at bit code_shift(J) of its half; f.one2<J>(cA, cB) the codes
+// themselves. `sh` is the run's bit offset in its first word (0, or 16 for
+// 3-bit runs of odd cg).
+template <int B, class F>
+__device__ __forceinline__ void visit_runs(const uint32_t* w, int sh, F& f) {
+    constexpr int RW = run_words<B>();
+    if constexpr (B == 2) {
+        Unit<2>::word2<0>(w[0], w[RW], f);
+    } else if constexpr (B == 4) {
+        Unit<4>::word2<0>(w[0], w[RW], f);
+        Unit<4>::word2<1>(w[1], w[RW + 1], f);
+    } else if constexpr (B == 8) {
+        static_for<4>([&](auto Q) { Unit<8>::word2<Q>(w[Q], w[RW + Q], f); });
+    } else {
+        uint32_t a[RW], b[RW];
+        if constexpr (B == 3) {
+            a[0] = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+            a[1] = w[1] >> sh;
+            b[0] = __builtin_amdgcn_alignbit(w[3], w[2], sh);
+            b[1] = w[3] >> sh;
+        } else {
+#pragma unroll
+            for (int k = 0; k < RW; ++k) a[k] = w[k], b[k] = w[RW + k];
+        }
+        static_for<16>([&](auto J) {
+            constexpr int j = J;
+            f.template one2<j>(UnitStraddle<B>::template code<j>(a), UnitStraddle<B>::template code<j>(b));
+        });
+    }
+}
+
+// Rotary score of one token over the lane's 16 pairs J: w4[J] = {Q_a s_a,
+// Q_b s_b, Q_a z_a + Q_b z_b, Q_b s_a}, w2[J] = {-Q_a s_b, Q_b z_a - Q_a z_b}
+// (steps with the 2^(24 - code_shift(J)) factor of the code halves), cs[J] =
+// (C, S) of the token's offset: a0 = sum C A, a1 = sum S B.
+struct RopeDot {
+    const float4* w4;
+    const float2* w2;
+    const float2* cs;
+    float a0, a1;
+    template <int J, bool HI>
+    __device__ __forceinline__ void pair_j(uint32_t mA, uint32_t mB) {
+        const float4 w = w4[J];
+        const float2 v = w2[J];
+        const float2 c = cs[J];
+        float A, Bs;
+        if constexpr (HI) {
+            A = mix_hi(mB, w.y, mix_hi(mA, w.x, w.z));
+            Bs = mix_hi(mB, v.x, mix_hi(mA, w.w, v.y));
+        } else {
+            A = mix_lo(mB, w.y, mix_lo(mA, w.x, w.z));
+            Bs = mix_lo(mB, v.x, mix_lo(mA, w.w, v.y));
+        }
+        a0 = fmaf(c.x, A, a0);
+        a1 = fmaf(c.y, Bs, a1);
+    }
+    template <int JL, int JH>
+    __device__ __forceinline__ void pair2(uint32_t mA, uint32_t mB) {
+        pair_j<JL, false>(mA, mB);
+        pair_j<JH, true>(mA, mB);
+    }
+    template <int J>
+    __device__ __forceinline__ void one2(uint32_t cA, uint32_t cB) {
+        pair_j<J, false>(cA, cB);
+    }
+};
+
+// Full-precision rotary score over the lane's 16 pairs: q4[J] = {Q_a, Q_b}
+// of the token's anchor (x, y or z, w: `second`), rows xa (run A) and xb (run B).
+__device__ __forceinline__ float rope_row_score(const float4* q4, bool second, const float2* cs, const float (&xa)[16],
+                                                const float (&xb)[16]) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float4 q = q4[j];
+        const float qa = second ? q.z : q.x, qb = second ? q.w : q.y;
+        const float2 c = cs[j];
+        a0 = fmaf(c.x, fmaf(qa, xa[j], qb * xb[j]), a0);
+        a1 = fmaf(c.y, fmaf(qb, xa[j], -(qa * xb[j])), a1);
+    }
+    return a0 + a1;
+}
+
 // acc[j] += w * code_j * 2^code_shift(j)  (w carries the 2^24 factor).
 struct ValueAxpy {
     float w;
@@ -326,6 +432,27 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t* w) {
     }
 }
 
+// The words of a 16-code run of the rotary layout, starting at word p.
+template <int B>
+__device__ __forceinline__ void load_run(const uint32_t* p, uint32_t* w) {
+    if constexpr (B == 2) {
+        w[0] = ld_stream(p);
+    } else if constexpr (B == 4) {
+        const uint2 v = ld_stream2(p);
+        w[0] = v.x;
+        w[1] = v.y;
+    } else if constexpr (B == 8) {
+        const uint4 v = ld_stream4(p);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    } else {  // 3 and 6 bits: runs start on any word
+#pragma unroll
+        for (int k = 0; k < run_words<B>(); ++k) w[k] = ld_stream(p + k);
+    }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
@@ -358,19 +485,29 @@ __device__ __forceinline__ float load_in_rt(const void* p, size_t i, int dt) {
     return load_in<2>(p, i);
 }
 
+__device__ __forceinline__ void load16_rt(const void* p, size_t off, int dt, float (&x)[16]) {
+    if (dt == 0) load16<0>(p, off, x);
+    else if (dt == 1) load16<1>(p, off, x);
+    else load16<2>(p, off, x);
+}
+
 constexpr float kTwo24 = 16777216.0f;
 
 constexpr float kRescale = 8.0f;  // log2-domain slack before the reference maximum moves
 
 // Registers of one 64-token super-tile: the lane's key and value unit words,
 // value metadata, and the key metadata of the super-tile's blocks.
-template <int D, int BK, int BV>
+// Rotary instantiations: runs A and B of the lane's 16 pairs per token, and
+// the key metadata of channels p and p + D/2 of the lane's prologue pairs p.
+template <int D, int BK, int BV, bool ROPE>
 struct Stage {
-    static constexpr int UPR = D / 32, KPL = D / 64;
-    uint32_t kw[UPR][BK];
+    static constexpr int UPR = D / 32;
+    static constexpr int KW = ROPE ? 2 * run_words<BK>() : BK;
+    static constexpr int KM = ROPE ? 2 * (D >= 128 ? D / 128 : 1) : D / 64;
+    uint32_t kw[UPR][KW];
     uint32_t vw[UPR][BV];
     uint32_t vmw[UPR];
-    uint32_t kmw[2][KPL];
+    uint32_t kmw[2][KM];
 };
 
 template <int N>
@@ -436,15 +573,23 @@ __device__ __forceinline__ void fused_append(const DecodeArgs& a, int head, int 
 
 // FUSED: the instantiation of the fused decode step (the append prologue is
 // compiled only there, so the attention loop of the plain call is unchanged).
-template <int D, int BK, int BV, int NW, int NS, bool FUSED>
-__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
+// ROPE: keys cached before the rotary embedding.
+// The rotary object keeps two waves per SIMD (the plain kernel fits there by itself).
+#if KVQ_MHA_ROPE
+#define KVQ_MHA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2, 2)))
+#else
+#define KVQ_MHA_OCCUPANCY
+#endif
+template <int D, int BK, int BV, int NW, int NS, bool FUSED, bool ROPE>
+__global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(DecodeArgs a0) {
     int z = blockIdx.z;
     const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
     constexpr int UPR = D / 32;   // units per row = lanes per token
     constexpr int TPW = 64 / UPR; // tokens per sub-tile
     constexpr int KPL = D / 64;   // channels per lane in the per-block prologue
     constexpr int HALF = UPR / 2; // sub-tiles per 32 tokens
-    using St = Stage<D, BK, BV>;
+    using St = Stage<D, BK, BV, ROPE>;
+    static_assert(!(FUSED && ROPE), "the fused step has no rotary instantiation");
 
     __shared__ float q_lds[D];
     constexpr int QSP = 36;         // padded floats per unit row of the key vector (bank spread)
@@ -453,6 +598,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
     __shared__ float mrg_o[NW][D];
     __shared__ float mrg_ml[NW][2];
     constexpr int NT = NW * 64;  // threads
+    // Rotary keys: the (cos, sin) table [u][pair] of the cache (rows padded by
+    // 4 floats, so that the 16 offsets a wave reads at once spread over the
+    // banks); per wave and 32-token half the weights of the D/2 pairs (slot
+    // p + p / 16: a lane's 16 pairs are contiguous, groups one slot apart), or
+    // in the full-precision loops the rotated query pairs of two anchors.
+    constexpr int RTS = D + 4;
+    constexpr int NPS = D / 2 + D / 32;
+    constexpr int KPP = D >= 128 ? D / 128 : 1;  // prologue pairs per lane (p = lane + 64k < D/2)
+    __shared__ __align__(16) float rt_lds[ROPE ? kRopeRows * RTS : 1];
+    __shared__ float4 pw4_lds[ROPE ? NW : 1][2][ROPE ? NPS : 1];
+    __shared__ float2 pw2_lds[ROPE ? NW : 1][2][ROPE ? NPS : 1];
 
     const int seq = a.seq_list ? a.seq_list[z] : z;
     const int kvh = blockIdx.y, split = blockIdx.x;
@@ -500,6 +656,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 
     for (int c = tid; c < D; c += NT)
         q_lds[c] = load_in_rt(a.q, ((size_t)seq * a.q_heads + kvh) * D + c, a.in_dtype) * a.qscale;
+    double th[KPP];  // rotary frequencies of the lane's prologue pairs
+    if constexpr (ROPE) {
+        for (int i = tid; i < kRopeRows * (D / 2); i += NT) {
+            const int u = i / (D / 2), pp = i - u * (D / 2);
+            *(float2*)&rt_lds[u * RTS + 2 * pp] = ((const float2*)a.rope_tab)[i];
+        }
+#pragma unroll
+        for (int k = 0; k < KPP; ++k) th[k] = a.rope_theta[min(lane + 64 * k, D / 2 - 1)];
+    }
     __syncthreads();
 
     // per-lane constants of the per-block prologue: q_c and q_c * 2^(24 - shift(c))
@@ -544,15 +709,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 #pragma unroll
         for (int s = 0; s < UPR; ++s) {
             const int t = min(t0 + s * TPW, tlast) - ps;
-            load_words<BK>((const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8)) + cg * BK, r.kw[s]);
+            const uint32_t* krow = (const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8));
+            if constexpr (ROPE) {
+                load_run<BK>(krow + ((16 * BK * cg) >> 5), r.kw[s]);
+                load_run<BK>(krow + ((16 * BK * cg) >> 5) + D * BK / 64, r.kw[s] + run_words<BK>());
+            } else {
+                load_words<BK>(krow + cg * BK, r.kw[s]);
+            }
             load_words<BV>((const uint32_t*)(vc + pb + (size_t)t * (D * BV / 8)) + cg * BV, r.vw[s]);
             r.vmw[s] = ld_stream((const uint32_t*)(vm + pb) + (size_t)t * vgpr + vg);
         }
         const int b0 = sc0 >> lgk;
         const int b1 = (two_blocks ? min(b0 + 1, blast) : b0) - (ps >> lgk);
         const uint32_t* kmp = (const uint32_t*)(km + pb);
-        load_words_n<KPL>(kmp + (size_t)(b0 - (ps >> lgk)) * D + KPL * lane, r.kmw[0]);
-        load_words_n<KPL>(kmp + (size_t)b1 * D + KPL * lane, r.kmw[1]);
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int k = 0; k < KPP; ++k) {
+                const int pp = min(lane + 64 * k, D / 2 - 1);
+                r.kmw[0][2 * k] = ld_stream(kmp + (size_t)(b0 - (ps >> lgk)) * D + pp);
+                r.kmw[0][2 * k + 1] = ld_stream(kmp + (size_t)(b0 - (ps >> lgk)) * D + pp + D / 2);
+                r.kmw[1][2 * k] = ld_stream(kmp + (size_t)b1 * D + pp);
+                r.kmw[1][2 * k + 1] = ld_stream(kmp + (size_t)b1 * D + pp + D / 2);
+            }
+        } else {
+            load_words_n<KPL>(kmp + (size_t)(b0 - (ps >> lgk)) * D + KPL * lane, r.kmw[0]);
+            load_words_n<KPL>(kmp + (size_t)b1 * D + KPL * lane, r.kmw[1]);
+        }
     };
 
     // Online softmax over this lane's UPR scores (one per sub-tile), then the value rows.
@@ -645,10 +827,89 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
         wave_sync_lds();  // qs_lds is rewritten by the next super-tile
     };
 
+    // Rotary keys: per 32-token half h, the weights of the lane's prologue
+    // pairs from the query rotated to the half's first position st + 32h (the
+    // second half's angle is the first's plus the table's row 32).
+    auto key_scores_rope = [&](int st, const St& r, float (&sc)[UPR], bool (&valid)[UPR]) {
+        float ca[KPP], sa[KPP];
+#pragma unroll
+        for (int k = 0; k < KPP; ++k) rope_cs(st, th[k], ca[k], sa[k]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int bl = two_blocks ? h : 0;
+#pragma unroll
+            for (int k = 0; k < KPP; ++k) {
+                const int pp = lane + 64 * k;
+                if (h == 1) {
+                    const float2 r32 = *(const float2*)&rt_lds[32 * RTS + 2 * min(pp, D / 2 - 1)];
+                    const float c1 = fmaf(ca[k], r32.x, -(sa[k] * r32.y));
+                    sa[k] = fmaf(sa[k], r32.x, ca[k] * r32.y);
+                    ca[k] = c1;
+                }
+                if (pp < D / 2) {
+                    const float qa = q_lds[pp], qb = q_lds[pp + D / 2];
+                    const float Qa = fmaf(ca[k], qa, sa[k] * qb), Qb = fmaf(ca[k], qb, -(sa[k] * qa));
+                    const uint32_t ma = r.kmw[bl][2 * k], mb = r.kmw[bl][2 * k + 1];
+                    const float f = (float)(1 << (24 - code_shift<BK>(pp & 15)));
+                    const float s_a = f16_to_f32(ma & 0xffffu) * f, z_a = f16_to_f32(ma >> 16);
+                    const float s_b = f16_to_f32(mb & 0xffffu) * f, z_b = f16_to_f32(mb >> 16);
+                    const int slot = pp + (pp >> 4);
+                    pw4_lds[wave][h][slot] = make_float4(Qa * s_a, Qb * s_b, fmaf(Qa, z_a, Qb * z_b), Qb * s_a);
+                    pw2_lds[wave][h][slot] = make_float2(-(Qa * s_b), fmaf(Qb, z_a, -(Qa * z_b)));
+                }
+            }
+        }
+        wave_sync_lds();
+#pragma unroll
+        for (int s = 0; s < UPR; ++s) {
+            const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
+            valid[s] = st + s * TPW + ts < qend;
+            RopeDot f{&pw4_lds[wave][h][17 * cg], &pw2_lds[wave][h][17 * cg],
+                      (const float2*)&rt_lds[u * RTS + 32 * cg], 0.f, 0.f};
+            visit_runs<BK>(r.kw[s], (16 * BK * cg) & 31, f);
+            const float part = group_sum<UPR>(f.a0 + f.a1);
+            sc[s] = valid[s] ? part : -INFINITY;
+            __builtin_amdgcn_sched_barrier(0);  // one token's weights live at a time
+        }
+        wave_sync_lds();  // the weights are rewritten by the next super-tile
+    };
+
+    // Rotary full-precision rows: per half h, the query pairs rotated to the
+    // anchors t0 + 32h (x, y) and t0 + off + 32h (z, w).
+    auto rope_queries = [&](int t0, int off) {
+#pragma unroll
+        for (int k = 0; k < KPP; ++k) {
+            const int pp = lane + 64 * k;
+            float c0, s0, c1, s1;
+            rope_cs(t0, th[k], c0, s0);
+            rope_cs(t0 + off, th[k], c1, s1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h == 1) {
+                    const float2 r32 = *(const float2*)&rt_lds[32 * RTS + 2 * min(pp, D / 2 - 1)];
+                    float t = fmaf(c0, r32.x, -(s0 * r32.y));
+                    s0 = fmaf(s0, r32.x, c0 * r32.y);
+                    c0 = t;
+                    t = fmaf(c1, r32.x, -(s1 * r32.y));
+                    s1 = fmaf(s1, r32.x, c1 * r32.y);
+                    c1 = t;
+                }
+                if (pp < D / 2) {
+                    const float qa = q_lds[pp], qb = q_lds[pp + D / 2];
+                    pw4_lds[wave][h][pp + (pp >> 4)] = make_float4(fmaf(c0, qa, s0 * qb), fmaf(c0, qb, -(s0 * qa)),
+                                                                   fmaf(c1, qa, s1 * qb), fmaf(c1, qb, -(s1 * qa)));
+                }
+            }
+        }
+        wave_sync_lds();
+    };
+
     auto compute_stage = [&](int st, const St& r) {
         float sc[UPR];
         bool valid[UPR];
-        if (st + 64 <= qend) {
+        if constexpr (ROPE) {
+            key_scores_rope(st, r, sc, valid);
+        } else if (st + 64 <= qend) {
             key_scores(st, r, true, sc, valid);
         } else {
             key_scores(st, r, false, sc, valid);
@@ -684,6 +945,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
             uint32_t vw[UPR][BV], vmw[UPR];
             float sc[UPR];
             bool valid[UPR];
+            if constexpr (ROPE) rope_queries(st, 0);
             // loads are unconditional, from the clamped token (a load under a
             // branch waits on its own), so they can be issued ahead of the sums
 #pragma unroll
@@ -694,18 +956,29 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
                 const PageRow pr = page_row(a.pages, e, tc);
                 load_words<BV>((const uint32_t*)(vc + pr.base + (size_t)pr.row * (D * BV / 8)) + cg * BV, vw[s]);
                 vmw[s] = ((const uint32_t*)(vm + pr.base))[(size_t)pr.row * vgpr + vg];
-                const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 32 * cg;
-                float x[32];
-                if (a.in_dtype == 0) load32<0>(kr, base, x);
-                else if (a.in_dtype == 1) load32<1>(kr, base, x);
-                else load32<2>(kr, base, x);
                 float part = 0.f;
+                if constexpr (ROPE) {
+                    const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 16 * cg;
+                    float xa[16], xb[16];
+                    load16_rt(kr, base, a.in_dtype, xa);
+                    load16_rt(kr, base + D / 2, a.in_dtype, xb);
+                    const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
+                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], false, (const float2*)&rt_lds[u * RTS + 32 * cg],
+                                          xa, xb);
+                } else {
+                    const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 32 * cg;
+                    float x[32];
+                    if (a.in_dtype == 0) load32<0>(kr, base, x);
+                    else if (a.in_dtype == 1) load32<1>(kr, base, x);
+                    else load32<2>(kr, base, x);
 #pragma unroll
-                for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                    for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                }
                 part = group_sum<UPR>(part);
                 sc[s] = valid[s] ? part : -INFINITY;
             }
             softmax_and_values(sc, vw, vmw, valid);
+            if constexpr (ROPE) wave_sync_lds();  // the next tile rewrites the rotated queries
         }
     }
 
@@ -722,20 +995,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
             else if (a.in_dtype == 1) load32<1>(base, off, x);
             else load32<2>(base, off, x);
         };
+        // rotary positions: i for the sinks (i < ns), i + rs - ns after them
+        const int ns = min(len, a.sinks), rs = max(te, ns);
         for (int st = 64 * wave; st < nfp; st += 64 * NW) {
             float sc[UPR];
             bool valid[UPR];
             int rows[UPR];
+            if constexpr (ROPE) rope_queries(st, rs - ns);
 #pragma unroll
             for (int s = 0; s < UPR; ++s) {
                 const int i = st + s * TPW + ts;
                 valid[s] = i < nfp;
                 rows[s] = valid[s] ? window_row(fp_token(a, len, te, i), a.sinks, a.win_rows, e.ring) : 0;
-                float x[32];
-                row32(kwn, (size_t)rows[s] * D + 32 * cg, x);
                 float part = 0.f;
+                if constexpr (ROPE) {
+                    float xa[16], xb[16];
+                    load16_rt(kwn, (size_t)rows[s] * D + 16 * cg, a.in_dtype, xa);
+                    load16_rt(kwn, (size_t)rows[s] * D + D / 2 + 16 * cg, a.in_dtype, xb);
+                    const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
+                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], i >= ns, (const float2*)&rt_lds[u * RTS + 32 * cg],
+                                          xa, xb);
+                } else {
+                    float x[32];
+                    row32(kwn, (size_t)rows[s] * D + 32 * cg, x);
 #pragma unroll
-                for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                    for (int j = 0; j < 32; ++j) part = fmaf(q_lds[32 * cg + j], x[j], part);
+                }
                 part = group_sum<UPR>(part);
                 sc[s] = valid[s] ? part : -INFINITY;
             }
@@ -764,6 +1049,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
                         acc[j] = fmaf(p * ((float)(1 << code_shift<BV>(j)) * (1.0f / 16777216.0f)), v[j], acc[j]);
                 }
             }
+            if constexpr (ROPE) wave_sync_lds();  // the next tile rewrites the rotated queries
         }
     }
 
@@ -813,6 +1099,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(DecodeArgs a0) {
 
 // 4 waves per workgroup with a 3-stage register ring measured fastest on the
 // Llama-2-7B-shaped step (6 waves with 2 stages was ~20% slower).
+#if !KVQ_MHA_ROPE
 // Whether the fused instantiation (a few more registers) keeps the plain
 // one's resident workgroups per compute unit; asked once per bit pair.
 template <int D, int BK, int BV>
@@ -820,11 +1107,12 @@ bool fused_keeps_occupancy() {
     static int cached = -1;  // racing first calls compute the same value
     if (cached < 0) {
         int plain = 0, fused = 0;
-        const bool ok =
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, false>,
-                                                         4 * 64, 0) == hipSuccess &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&fused, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, true>,
-                                                         4 * 64, 0) == hipSuccess;
+        const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &plain, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, false, false>, 4 * 64, 0) ==
+                            hipSuccess &&
+                        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &fused, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, true, false>, 4 * 64, 0) ==
+                            hipSuccess;
         cached = ok && fused >= plain ? 1 : 0;
     }
     return cached == 1;
@@ -843,10 +1131,21 @@ bool fused_ok_bv(int bv) {
 
 template <int D, int BK, int BV>
 hipError_t launch_nw(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    if (a.append_fused) hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, true>), grid, dim3(4 * 64), 0, s, a);
-    else hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, false>), grid, dim3(4 * 64), 0, s, a);
+    if (a.append_fused)
+        hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, true, false>), grid, dim3(4 * 64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, false, false>), grid, dim3(4 * 64), 0, s, a);
     return hipGetLastError();
 }
+#else
+#ifndef KVQ_ROPE_NS
+#define KVQ_ROPE_NS 2
+#endif
+template <int D, int BK, int BV>
+hipError_t launch_nw(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, KVQ_ROPE_NS, false, true>), grid, dim3(4 * 64), 0, s, a);
+    return hipGetLastError();
+}
+#endif
 
 template <int D, int BK>
 hipError_t launch_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
@@ -872,9 +1171,11 @@ hipError_t launch_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t
 
 }  // namespace
 
-// This file is compiled once per head_dim (KVQ_MHA_HEAD_DIM = 64, 128, 256).
+// This file is compiled once per head_dim (KVQ_MHA_HEAD_DIM = 64, 128, 256),
+// plain and with KVQ_MHA_ROPE = 1 (the rotary instantiations).
 #define KVQ_CAT2(a, b) a##b
 #define KVQ_CAT(a, b) KVQ_CAT2(a, b)
+#if !KVQ_MHA_ROPE
 bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
     constexpr int D = KVQ_MHA_HEAD_DIM;
     switch (bits_k) {
@@ -885,9 +1186,12 @@ bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
         default: return fused_ok_bv<D, 8>(bits_v);
     }
 }
+#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)
+#else
+#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_rope_d, KVQ_MHA_HEAD_DIM)
+#endif
 
-hipError_t KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
-                                                          hipStream_t s) {
+hipError_t KVQ_MHA_LAUNCH(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     // x: the quantized splits only (the workspace's full-precision slots have no
     // workgroups here: empty ones would leave the busy ones on a few XCDs)
     dim3 grid(a.max_chunks - a.win_splits, a.kv_heads, nseqs * a.n_layers);

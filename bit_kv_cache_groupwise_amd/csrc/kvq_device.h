@@ -3,10 +3,22 @@
 
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace dev {
+
+// f(integral_constant<int, I>) for I = 0..N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Streaming loads of the quantized cache, which a decode step reads exactly
 // once: the non-temporal hint keeps them from displacing reused lines and
@@ -152,6 +164,23 @@ template <int DT>
 __device__ __forceinline__ float half_to_f32(uint32_t h) {
     if constexpr (DT == 1) return f16_to_f32(h);
     else return bf16_to_f32(h);
+}
+
+// Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
+// Complicam as Chaves"): cos and sin of the angle t * theta, reduced modulo
+// 2 pi in float64 (t * theta reaches 1e5-1e8 radians at long context, where a
+// float32 product would be off by 1e-2 rad), then evaluated in float32.
+__device__ __forceinline__ void rope_cs(int t, double theta, float& c, float& s) {
+    const double ang = (double)t * theta;
+    const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    sincosf((float)r, &s, &c);
+}
+
+// 16 consecutive input elements starting at element `off`.
+template <int DT>
+__device__ __forceinline__ void load16(const void* base, size_t off, float (&x)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = load_in<DT>(base, off + j);
 }
 
 // 32 consecutive input elements starting at element `off` (16-byte aligned).

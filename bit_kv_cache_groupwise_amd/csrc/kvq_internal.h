@@ -48,7 +48,7 @@ constexpr uint32_t kNoPage = 0xffffffffu;
 //   [pairs_off, +num_seqs*4)           int32 sequence indices grouped by (bits_k, bits_v) pair
 //   [pt_off, +page_entries*4)          uint32 page lists (contiguous storage: one entry, 0)
 struct TableLayout {
-    uint64_t entries_bytes, len_off, args_off, ctr_off, pairs_off, pt_off, total;
+    uint64_t entries_bytes, len_off, args_off, ctr_off, pairs_off, pt_off, rope_off, total;
 };
 
 // Per-launch description of one tensor (K = 0 or V = 1) of one layer.
@@ -125,9 +125,14 @@ struct DecodeArgs {
     uint32_t win_off[2];        // byte offset of the window area inside a head's residual region [K, V]
     float ws_scale;             // factor the quantized kernel's partial l and o carry (2^24: single query)
     int32_t win_splits;         // grid x of decode_window_kernel (full-precision splits at most)
-    // Keys cached before the rotary embedding (rope_base > 0; generic split
-    // kernel): the reconstructed key of token t is rotated to position t.
+    // Keys cached before the rotary embedding (rope_base > 0): the
+    // reconstructed key of token t is rotated to position t.
     double rope_base;
+    // Rotary tables of the cache (rope_base > 0): theta_i = base^(-2i/D) for
+    // the D/2 pairs (i, i + D/2), and (cos, sin)(u theta_i) for the in-tile
+    // offsets u = 0..kRopeRows-1, row-major [u][i] as float pairs.
+    const double* rope_theta;
+    const float* rope_tab;
     const uint32_t* pages;      // page lists (SeqEntry::page_list indexes them)
 };
 
@@ -147,6 +152,10 @@ struct DequantArgs {
 // a call: entry k = one (layer, seq) with start[k] its first workgroup; the
 // entries are ordered by bit pair and start[count] is the total. Passed by
 // value in the kernel arguments.
+// Rows of the rotary (cos, sin) table: in-tile offsets 0..31 and the step 32
+// between the two 32-token halves of a 64-token tile.
+constexpr int kRopeRows = 33;
+
 constexpr int kGqaListMax = 256;
 struct GqaList {
     int32_t count;
@@ -207,6 +216,16 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
     return a.head_dim == 64    ? launch_decode_mha_d64(a, bits_k, bits_v, nseqs, s)
            : a.head_dim == 128 ? launch_decode_mha_d128(a, bits_k, bits_v, nseqs, s)
                                : launch_decode_mha_d256(a, bits_k, bits_v, nseqs, s);
+}
+// Keys cached before the rotary embedding on the single-query kernel (its
+// rotary instantiations, one object per head_dim).
+hipError_t launch_decode_mha_rope_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_mha_rope_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_mha_rope_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+inline hipError_t launch_decode_mha_rope(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
+    return a.head_dim == 64    ? launch_decode_mha_rope_d64(a, bits_k, bits_v, nseqs, s)
+           : a.head_dim == 128 ? launch_decode_mha_rope_d128(a, bits_k, bits_v, nseqs, s)
+                               : launch_decode_mha_rope_d256(a, bits_k, bits_v, nseqs, s);
 }
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 // The library's fixed device scratch (kvq_scratch.hip): its address on the

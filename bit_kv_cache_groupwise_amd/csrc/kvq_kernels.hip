@@ -383,16 +383,6 @@ __device__ __forceinline__ void value_pass_channel(const uint32_t* pages, const 
     }
 }
 
-// Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
-// Complicam as Chaves"): cos and sin of the angle t * theta, reduced modulo
-// 2 pi in float64 (t * theta reaches 1e5-1e8 radians at long context, where a
-// float32 product would be off by 1e-2 rad), then evaluated in float32.
-__device__ __forceinline__ void rope_cs(int t, double theta, float& c, float& s) {
-    const double ang = (double)t * theta;
-    const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
-    sincosf((float)r, &s, &c);
-}
-
 template <int B>
 __device__ __forceinline__ uint32_t code_of(const uint32_t* row, int ch) {
     const uint32_t* unit = row + (ch >> 5) * B;
