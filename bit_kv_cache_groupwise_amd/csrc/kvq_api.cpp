@@ -1010,11 +1010,14 @@ kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k_new, const
     // adds residual key rows (no key block completes) and at most one
     // workgroup's worth of value rows per sequence.
     const int32_t* lens = &c->lens[(size_t)layer * S];
+    const bool rope = g.rope_base > 0.0;
     bool fuse = !empty && group_size(c) == 1 && g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN &&
-                kvq::mha_supported(g.head_dim) && !(g.rope_base > 0.0);
+                kvq::mha_supported(g.head_dim);
     for (int s = 0; fuse && s < S; ++s)
         fuse = (lens[s] + n_new[s]) / g.group_k == lens[s] / g.group_k && n_new[s] <= 256 / (g.head_dim / 32);
-    for (const auto& pr : c->pairs) fuse = fuse && kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv);
+    for (const auto& pr : c->pairs)
+        fuse = fuse && (rope ? kvq::mha_rope_fused_ok(g.head_dim, pr.bk, pr.bv)
+                             : kvq::mha_fused_ok(g.head_dim, pr.bk, pr.bv));
     opt.dry_run = false;
     if (fuse) {
         opt.fused = ta;

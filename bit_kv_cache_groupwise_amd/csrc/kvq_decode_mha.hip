@@ -328,20 +328,88 @@ __device__ __forceinline__ void visit_runs(const uint32_t* w, int sh, F& f) {
     }
 }
 
+// LDS layout of the rotary (cos, sin) table: pair-major, [pair][u] as float
+// pairs, 68 floats per pair (33 offsets and 2 spare), a group of 16 pairs 16
+// floats after the previous one. The 16 lanes of a quarter wave (4 offsets x
+// 4 pair groups) then read 8-byte words on 16 distinct bank pairs.
+constexpr int kRopePairStride = 68;
+__host__ __device__ constexpr int rope_lds_off(int pair, int u) { return kRopePairStride * pair + 8 * (pair >> 4) + 2 * u; }
+
+// The same for two tokens of one 32-token half (w0, w1), which share the
+// pair weights: f.pair4<JL, JH>(mA0, mB0, mA1, mB1), f.one4<J>(cA0, cB0, cA1, cB1).
+template <int JL, int JH, class F>
+__device__ __forceinline__ void mask4(F& f, uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1, uint32_t m) {
+    f.template pair4<JL, JH>(a0 & m, b0 & m, a1 & m, b1 & m);
+}
+template <int B, class F>
+__device__ __forceinline__ void visit_runs2(const uint32_t* w0, const uint32_t* w1, int sh, F& f) {
+    constexpr int RW = run_words<B>();
+    if constexpr (B == 2) {  // the masks of Unit<2>::word
+        const uint32_t a0 = w0[0], b0 = w0[RW], a1 = w1[0], b1 = w1[RW];
+        mask4<0, 8>(f, a0, b0, a1, b1, 0x00030003u);
+        mask4<1, 9>(f, a0, b0, a1, b1, 0x000c000cu);
+        mask4<2, 10>(f, a0, b0, a1, b1, 0x00300030u);
+        mask4<3, 11>(f, a0, b0, a1, b1, 0x00c000c0u);
+        mask4<4, 12>(f, a0, b0, a1, b1, 0x03000300u);
+        const uint32_t c0 = a0 >> 10, d0 = b0 >> 10, c1 = a1 >> 10, d1 = b1 >> 10;
+        mask4<5, 13>(f, c0, d0, c1, d1, 0x00030003u);
+        mask4<6, 14>(f, c0, d0, c1, d1, 0x000c000cu);
+        mask4<7, 15>(f, c0, d0, c1, d1, 0x00300030u);
+    } else if constexpr (B == 4) {  // Unit<4>::word
+        static_for<2>([&](auto Q) {
+            constexpr int J = 8 * Q;
+            const uint32_t a0 = w0[Q], b0 = w0[RW + Q], a1 = w1[Q], b1 = w1[RW + Q];
+            mask4<J + 0, J + 4>(f, a0, b0, a1, b1, 0x000f000fu);
+            mask4<J + 1, J + 5>(f, a0, b0, a1, b1, 0x00f000f0u);
+            mask4<J + 2, J + 6>(f, a0 >> 8, b0 >> 8, a1 >> 8, b1 >> 8, 0x000f000fu);
+            mask4<J + 3, J + 7>(f, a0 >> 8, b0 >> 8, a1 >> 8, b1 >> 8, 0x00f000f0u);
+        });
+    } else if constexpr (B == 8) {  // Unit<8>::word
+        static_for<4>([&](auto Q) {
+            constexpr int J = 4 * Q;
+            const uint32_t a0 = w0[Q], b0 = w0[RW + Q], a1 = w1[Q], b1 = w1[RW + Q];
+            mask4<J + 0, J + 2>(f, a0, b0, a1, b1, 0x00ff00ffu);
+            f.template pair4<J + 1, J + 3>(
+                __builtin_amdgcn_perm(a0, a0, 0x0c070c05u), __builtin_amdgcn_perm(b0, b0, 0x0c070c05u),
+                __builtin_amdgcn_perm(a1, a1, 0x0c070c05u), __builtin_amdgcn_perm(b1, b1, 0x0c070c05u));
+        });
+    } else {
+        uint32_t a[2][RW], b[2][RW];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t* w = t ? w1 : w0;
+            if constexpr (B == 3) {
+                a[t][0] = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+                a[t][1] = w[1] >> sh;
+                b[t][0] = __builtin_amdgcn_alignbit(w[3], w[2], sh);
+                b[t][1] = w[3] >> sh;
+            } else {
+#pragma unroll
+                for (int k = 0; k < RW; ++k) a[t][k] = w[k], b[t][k] = w[RW + k];
+            }
+        }
+        static_for<16>([&](auto J) {
+            constexpr int j = J;
+            f.template one4<j>(UnitStraddle<B>::template code<j>(a[0]), UnitStraddle<B>::template code<j>(b[0]),
+                               UnitStraddle<B>::template code<j>(a[1]), UnitStraddle<B>::template code<j>(b[1]));
+        });
+    }
+}
+
 // Rotary score of one token over the lane's 16 pairs J: w4[J] = {Q_a s_a,
 // Q_b s_b, Q_a z_a + Q_b z_b, Q_b s_a}, w2[J] = {-Q_a s_b, Q_b z_a - Q_a z_b}
-// (steps with the 2^(24 - code_shift(J)) factor of the code halves), cs[J] =
+// (steps with the 2^(24 - code_shift(J)) factor of the code halves), cs[kRopePairStride J] =
 // (C, S) of the token's offset: a0 = sum C A, a1 = sum S B.
 struct RopeDot {
     const float4* w4;
     const float2* w2;
-    const float2* cs;
+    const float* cs;
     float a0, a1;
     template <int J, bool HI>
     __device__ __forceinline__ void pair_j(uint32_t mA, uint32_t mB) {
         const float4 w = w4[J];
         const float2 v = w2[J];
-        const float2 c = cs[J];
+        const float2 c = *(const float2*)&cs[kRopePairStride * J];
         float A, Bs;
         if constexpr (HI) {
             A = mix_hi(mB, w.y, mix_hi(mA, w.x, w.z));
@@ -364,16 +432,56 @@ struct RopeDot {
     }
 };
 
+// Two tokens of one half (offsets cs0, cs1), one load of the pair weights.
+struct RopeDot2 {
+    const float4* w4;
+    const float2* w2;
+    const float* cs0;
+    const float* cs1;
+    float a0, a1, b0, b1;  // token 0: sum C A, sum S B; token 1: the same
+    template <int J, bool HI>
+    __device__ __forceinline__ void pair_j(uint32_t mA0, uint32_t mB0, uint32_t mA1, uint32_t mB1) {
+        const float4 w = w4[J];
+        const float2 v = w2[J];
+        const float2 c = *(const float2*)&cs0[kRopePairStride * J], d = *(const float2*)&cs1[kRopePairStride * J];
+        float A0, B0, A1, B1;
+        if constexpr (HI) {
+            A0 = mix_hi(mB0, w.y, mix_hi(mA0, w.x, w.z));
+            B0 = mix_hi(mB0, v.x, mix_hi(mA0, w.w, v.y));
+            A1 = mix_hi(mB1, w.y, mix_hi(mA1, w.x, w.z));
+            B1 = mix_hi(mB1, v.x, mix_hi(mA1, w.w, v.y));
+        } else {
+            A0 = mix_lo(mB0, w.y, mix_lo(mA0, w.x, w.z));
+            B0 = mix_lo(mB0, v.x, mix_lo(mA0, w.w, v.y));
+            A1 = mix_lo(mB1, w.y, mix_lo(mA1, w.x, w.z));
+            B1 = mix_lo(mB1, v.x, mix_lo(mA1, w.w, v.y));
+        }
+        a0 = fmaf(c.x, A0, a0);
+        a1 = fmaf(c.y, B0, a1);
+        b0 = fmaf(d.x, A1, b0);
+        b1 = fmaf(d.y, B1, b1);
+    }
+    template <int JL, int JH>
+    __device__ __forceinline__ void pair4(uint32_t mA0, uint32_t mB0, uint32_t mA1, uint32_t mB1) {
+        pair_j<JL, false>(mA0, mB0, mA1, mB1);
+        pair_j<JH, true>(mA0, mB0, mA1, mB1);
+    }
+    template <int J>
+    __device__ __forceinline__ void one4(uint32_t cA0, uint32_t cB0, uint32_t cA1, uint32_t cB1) {
+        pair_j<J, false>(cA0, cB0, cA1, cB1);
+    }
+};
+
 // Full-precision rotary score over the lane's 16 pairs: q4[J] = {Q_a, Q_b}
 // of the token's anchor (x, y or z, w: `second`), rows xa (run A) and xb (run B).
-__device__ __forceinline__ float rope_row_score(const float4* q4, bool second, const float2* cs, const float (&xa)[16],
+__device__ __forceinline__ float rope_row_score(const float4* q4, bool second, const float* cs, const float (&xa)[16],
                                                 const float (&xb)[16]) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float4 q = q4[j];
         const float qa = second ? q.z : q.x, qb = second ? q.w : q.y;
-        const float2 c = cs[j];
+        const float2 c = *(const float2*)&cs[kRopePairStride * j];
         a0 = fmaf(c.x, fmaf(qa, xa[j], qb * xb[j]), a0);
         a1 = fmaf(c.y, fmaf(qb, xa[j], -(qa * xb[j])), a1);
     }
@@ -589,7 +697,6 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
     constexpr int KPL = D / 64;   // channels per lane in the per-block prologue
     constexpr int HALF = UPR / 2; // sub-tiles per 32 tokens
     using St = Stage<D, BK, BV, ROPE>;
-    static_assert(!(FUSED && ROPE), "the fused step has no rotary instantiation");
 
     __shared__ float q_lds[D];
     constexpr int QSP = 36;         // padded floats per unit row of the key vector (bank spread)
@@ -598,15 +705,13 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
     __shared__ float mrg_o[NW][D];
     __shared__ float mrg_ml[NW][2];
     constexpr int NT = NW * 64;  // threads
-    // Rotary keys: the (cos, sin) table [u][pair] of the cache (rows padded by
-    // 4 floats, so that the 16 offsets a wave reads at once spread over the
-    // banks); per wave and 32-token half the weights of the D/2 pairs (slot
+    // Rotary keys: the (cos, sin) table of the cache (rope_lds_off layout);
+    // per wave and 32-token half the weights of the D/2 pairs (slot
     // p + p / 16: a lane's 16 pairs are contiguous, groups one slot apart), or
     // in the full-precision loops the rotated query pairs of two anchors.
-    constexpr int RTS = D + 4;
     constexpr int NPS = D / 2 + D / 32;
     constexpr int KPP = D >= 128 ? D / 128 : 1;  // prologue pairs per lane (p = lane + 64k < D/2)
-    __shared__ __align__(16) float rt_lds[ROPE ? kRopeRows * RTS : 1];
+    __shared__ __align__(16) float rt_lds[ROPE ? rope_lds_off(D / 2, 0) : 1];
     __shared__ float4 pw4_lds[ROPE ? NW : 1][2][ROPE ? NPS : 1];
     __shared__ float2 pw2_lds[ROPE ? NW : 1][2][ROPE ? NPS : 1];
 
@@ -660,7 +765,7 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
     if constexpr (ROPE) {
         for (int i = tid; i < kRopeRows * (D / 2); i += NT) {
             const int u = i / (D / 2), pp = i - u * (D / 2);
-            *(float2*)&rt_lds[u * RTS + 2 * pp] = ((const float2*)a.rope_tab)[i];
+            *(float2*)&rt_lds[rope_lds_off(pp, u)] = ((const float2*)a.rope_tab)[i];
         }
 #pragma unroll
         for (int k = 0; k < KPP; ++k) th[k] = a.rope_theta[min(lane + 64 * k, D / 2 - 1)];
@@ -841,7 +946,7 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
             for (int k = 0; k < KPP; ++k) {
                 const int pp = lane + 64 * k;
                 if (h == 1) {
-                    const float2 r32 = *(const float2*)&rt_lds[32 * RTS + 2 * min(pp, D / 2 - 1)];
+                    const float2 r32 = *(const float2*)&rt_lds[rope_lds_off(min(pp, D / 2 - 1), 32)];
                     const float c1 = fmaf(ca[k], r32.x, -(sa[k] * r32.y));
                     sa[k] = fmaf(sa[k], r32.x, ca[k] * r32.y);
                     ca[k] = c1;
@@ -861,15 +966,31 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
         }
         wave_sync_lds();
 #pragma unroll
-        for (int s = 0; s < UPR; ++s) {
-            const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
-            valid[s] = st + s * TPW + ts < qend;
-            RopeDot f{&pw4_lds[wave][h][17 * cg], &pw2_lds[wave][h][17 * cg],
-                      (const float2*)&rt_lds[u * RTS + 32 * cg], 0.f, 0.f};
-            visit_runs<BK>(r.kw[s], (16 * BK * cg) & 31, f);
-            const float part = group_sum<UPR>(f.a0 + f.a1);
-            sc[s] = valid[s] ? part : -INFINITY;
-            __builtin_amdgcn_sched_barrier(0);  // one token's weights live at a time
+        for (int s = 0; s < UPR; ++s) valid[s] = st + s * TPW + ts < qend;
+        if constexpr (HALF >= 2) {  // the two tokens s, s + 1 of a half share the pair weights
+#pragma unroll
+            for (int s = 0; s < UPR; s += 2) {
+                const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
+                RopeDot2 f{&pw4_lds[wave][h][17 * cg], &pw2_lds[wave][h][17 * cg],
+                           &rt_lds[rope_lds_off(16 * cg, u)], &rt_lds[rope_lds_off(16 * cg, u + TPW)],
+                           0.f, 0.f, 0.f, 0.f};
+                visit_runs2<BK>(r.kw[s], r.kw[s + 1], (16 * BK * cg) & 31, f);
+                const float p0 = group_sum<UPR>(f.a0 + f.a1), p1 = group_sum<UPR>(f.b0 + f.b1);
+                sc[s] = valid[s] ? p0 : -INFINITY;
+                sc[s + 1] = valid[s + 1] ? p1 : -INFINITY;
+                __builtin_amdgcn_sched_barrier(0);  // one token pair's weights live at a time
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < UPR; ++s) {
+                const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
+                RopeDot f{&pw4_lds[wave][h][17 * cg], &pw2_lds[wave][h][17 * cg],
+                          &rt_lds[rope_lds_off(16 * cg, u)], 0.f, 0.f};
+                visit_runs<BK>(r.kw[s], (16 * BK * cg) & 31, f);
+                const float part = group_sum<UPR>(f.a0 + f.a1);
+                sc[s] = valid[s] ? part : -INFINITY;
+                __builtin_amdgcn_sched_barrier(0);  // one token's weights live at a time
+            }
         }
         wave_sync_lds();  // the weights are rewritten by the next super-tile
     };
@@ -886,7 +1007,7 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h == 1) {
-                    const float2 r32 = *(const float2*)&rt_lds[32 * RTS + 2 * min(pp, D / 2 - 1)];
+                    const float2 r32 = *(const float2*)&rt_lds[rope_lds_off(min(pp, D / 2 - 1), 32)];
                     float t = fmaf(c0, r32.x, -(s0 * r32.y));
                     s0 = fmaf(s0, r32.x, c0 * r32.y);
                     c0 = t;
@@ -963,7 +1084,7 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
                     load16_rt(kr, base, a.in_dtype, xa);
                     load16_rt(kr, base + D / 2, a.in_dtype, xb);
                     const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
-                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], false, (const float2*)&rt_lds[u * RTS + 32 * cg],
+                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], false, &rt_lds[rope_lds_off(16 * cg, u)],
                                           xa, xb);
                 } else {
                     const size_t base = (size_t)(tc & ((1 << lgk) - 1)) * D + 32 * cg;
@@ -1013,7 +1134,7 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
                     load16_rt(kwn, (size_t)rows[s] * D + 16 * cg, a.in_dtype, xa);
                     load16_rt(kwn, (size_t)rows[s] * D + D / 2 + 16 * cg, a.in_dtype, xb);
                     const int h = s / HALF, u = (s - h * HALF) * TPW + ts;
-                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], i >= ns, (const float2*)&rt_lds[u * RTS + 32 * cg],
+                    part = rope_row_score(&pw4_lds[wave][h][17 * cg], i >= ns, &rt_lds[rope_lds_off(16 * cg, u)],
                                           xa, xb);
                 } else {
                     float x[32];
@@ -1098,8 +1219,16 @@ __global__ __launch_bounds__(NW * 64) KVQ_MHA_OCCUPANCY void decode_mha_kernel(D
 }
 
 // 4 waves per workgroup with a 3-stage register ring measured fastest on the
-// Llama-2-7B-shaped step (6 waves with 2 stages was ~20% slower).
-#if !KVQ_MHA_ROPE
+// Llama-2-7B-shaped step (6 waves with 2 stages was ~20% slower); the rotary
+// instantiations keep 2 stages (3 measured slower and spill at 8 bits).
+#if KVQ_MHA_ROPE
+constexpr bool kRope = true;
+constexpr int kStages = 2;
+#else
+constexpr bool kRope = false;
+constexpr int kStages = 3;
+#endif
+
 // Whether the fused instantiation (a few more registers) keeps the plain
 // one's resident workgroups per compute unit; asked once per bit pair.
 template <int D, int BK, int BV>
@@ -1108,10 +1237,10 @@ bool fused_keeps_occupancy() {
     if (cached < 0) {
         int plain = 0, fused = 0;
         const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            &plain, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, false, false>, 4 * 64, 0) ==
+                            &plain, (const void*)decode_mha_kernel<D, BK, BV, 4, kStages, false, kRope>, 4 * 64, 0) ==
                             hipSuccess &&
                         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                            &fused, (const void*)decode_mha_kernel<D, BK, BV, 4, 3, true, false>, 4 * 64, 0) ==
+                            &fused, (const void*)decode_mha_kernel<D, BK, BV, 4, kStages, true, kRope>, 4 * 64, 0) ==
                             hipSuccess;
         cached = ok && fused >= plain ? 1 : 0;
     }
@@ -1132,20 +1261,10 @@ bool fused_ok_bv(int bv) {
 template <int D, int BK, int BV>
 hipError_t launch_nw(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     if (a.append_fused)
-        hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, true, false>), grid, dim3(4 * 64), 0, s, a);
-    else hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, 3, false, false>), grid, dim3(4 * 64), 0, s, a);
+        hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, kStages, true, kRope>), grid, dim3(4 * 64), 0, s, a);
+    else hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, kStages, false, kRope>), grid, dim3(4 * 64), 0, s, a);
     return hipGetLastError();
 }
-#else
-#ifndef KVQ_ROPE_NS
-#define KVQ_ROPE_NS 2
-#endif
-template <int D, int BK, int BV>
-hipError_t launch_nw(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((decode_mha_kernel<D, BK, BV, 4, KVQ_ROPE_NS, false, true>), grid, dim3(4 * 64), 0, s, a);
-    return hipGetLastError();
-}
-#endif
 
 template <int D, int BK>
 hipError_t launch_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
@@ -1176,7 +1295,13 @@ hipError_t launch_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t
 #define KVQ_CAT2(a, b) a##b
 #define KVQ_CAT(a, b) KVQ_CAT2(a, b)
 #if !KVQ_MHA_ROPE
-bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
+#define KVQ_MHA_FUSED_OK KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)
+#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)
+#else
+#define KVQ_MHA_FUSED_OK KVQ_CAT(mha_rope_fused_ok_d, KVQ_MHA_HEAD_DIM)
+#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_rope_d, KVQ_MHA_HEAD_DIM)
+#endif
+bool KVQ_MHA_FUSED_OK(int bits_k, int bits_v) {
     constexpr int D = KVQ_MHA_HEAD_DIM;
     switch (bits_k) {
         case 2: return fused_ok_bv<D, 2>(bits_v);
@@ -1186,10 +1311,6 @@ bool KVQ_CAT(mha_fused_ok_d, KVQ_MHA_HEAD_DIM)(int bits_k, int bits_v) {
         default: return fused_ok_bv<D, 8>(bits_v);
     }
 }
-#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_d, KVQ_MHA_HEAD_DIM)
-#else
-#define KVQ_MHA_LAUNCH KVQ_CAT(launch_decode_mha_rope_d, KVQ_MHA_HEAD_DIM)
-#endif
 
 hipError_t KVQ_MHA_LAUNCH(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     // x: the quantized splits only (the workspace's full-precision slots have no

@@ -222,6 +222,14 @@ inline hipError_t launch_decode_mha(const DecodeArgs& a, int bits_k, int bits_v,
 hipError_t launch_decode_mha_rope_d64(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_mha_rope_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
 hipError_t launch_decode_mha_rope_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+bool mha_rope_fused_ok_d64(int bits_k, int bits_v);
+bool mha_rope_fused_ok_d128(int bits_k, int bits_v);
+bool mha_rope_fused_ok_d256(int bits_k, int bits_v);
+inline bool mha_rope_fused_ok(int head_dim, int bits_k, int bits_v) {
+    return head_dim == 64    ? mha_rope_fused_ok_d64(bits_k, bits_v)
+           : head_dim == 128 ? mha_rope_fused_ok_d128(bits_k, bits_v)
+                             : mha_rope_fused_ok_d256(bits_k, bits_v);
+}
 inline hipError_t launch_decode_mha_rope(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     return a.head_dim == 64    ? launch_decode_mha_rope_d64(a, bits_k, bits_v, nseqs, s)
            : a.head_dim == 128 ? launch_decode_mha_rope_d128(a, bits_k, bits_v, nseqs, s)
