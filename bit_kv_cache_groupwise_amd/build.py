@@ -25,6 +25,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 MHA_HEAD_DIMS = (64, 128, 256)
+GQA_ROPE_HEAD_DIMS = (128, 256)  # rotary keys on the query-group kernel
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -51,6 +52,8 @@ def units():
               for d in MHA_HEAD_DIMS],
             *[("kvq_decode_gqa.hip", f"kvq_decode_gqa_d{d}.o", [f"-DKVQ_GQA_HEAD_DIM={d}"], True)
               for d in MHA_HEAD_DIMS],
+            *[("kvq_decode_gqa.hip", f"kvq_decode_gqa_rope_d{d}.o", [f"-DKVQ_GQA_HEAD_DIM={d}", "-DKVQ_GQA_ROPE=1"], True)
+              for d in GQA_ROPE_HEAD_DIMS],
             ("kvq_api.cpp", "kvq_api.o", [], False)]
 
 

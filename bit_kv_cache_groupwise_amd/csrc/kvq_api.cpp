@@ -823,10 +823,11 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
     // rotary keys: the generic split kernel
     // the single-query and query-group kernels: per-channel keys, per-token values
-    // (rotary keys: the single-query kernel's rotary instantiations, else the generic kernel)
+    // (rotary keys: their instantiations of both kernels; the query-group one
+    // for head_dim 128 and 256)
     const bool fast = g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN && kvq::mha_supported(g.head_dim);
     const bool mha = fast && group_size(c) == 1;
-    bool gqa = fast && !rope && group_size(c) > 1;
+    bool gqa = fast && group_size(c) > 1 && (!rope || kvq::gqa_rope_supported(g.head_dim));
     for (const auto& pr : c->pairs)  // head_dim 64: a lane group's half unit of key codes must be whole words
         gqa = gqa && (g.head_dim >= 128 || pr.bk % 2 == 0);
     if (!mha && !gqa && group_size(c) > kvq::kMaxQueryGroup)
@@ -953,13 +954,18 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
                     }
             list.start[list.count] = items;
             if (items > 0) {
-                hipError_t e = kvq::launch_decode_gqa_list(a, list, items, (hipStream_t)stream);
+                hipError_t e = !rope                  ? kvq::launch_decode_gqa_list(a, list, items, (hipStream_t)stream)
+                               : g.head_dim == 128 ? kvq::launch_decode_gqa_rope_list_d128(a, list, items, (hipStream_t)stream)
+                                                   : kvq::launch_decode_gqa_rope_list_d256(a, list, items, (hipStream_t)stream);
                 if (e != hipSuccess) return hip_fail(e, "launching decode attention");
             }
         } else {
             for (const auto& pr : c->pairs) {
                 a.seq_list = c->pairs.size() == 1 ? nullptr : (const int32_t*)(c->table + c->tl.pairs_off) + pr.offset;
-                hipError_t e = kvq::launch_decode_gqa(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
+                hipError_t e =
+                    !rope               ? kvq::launch_decode_gqa(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream)
+                    : g.head_dim == 128 ? kvq::launch_decode_gqa_rope_d128(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream)
+                                        : kvq::launch_decode_gqa_rope_d256(a, pr.bk, pr.bv, pr.count, (hipStream_t)stream);
                 if (e != hipSuccess) return hip_fail(e, "launching decode attention");
             }
         }

@@ -45,6 +45,17 @@
 // weights q' s of a block whose steps would push them past 2^15 are scaled by
 // 2^-f. Splits are merged by merge_kernel.
 //
+// Keys cached before the rotary embedding ([U] "Embebedos Rotatorios
+// Complicam as Chaves": rotate after dequantization; objects built with
+// KVQ_GQA_ROPE): lane group g holds D/8 whole channel pairs (i, i + D/2), a
+// run of codes and its partner run. Per tile and pair the lane reconstructs
+// its token's two key values (one v_fma_mix each from the code halves), rotates
+// them by the token's offset u in the tile ((cos, sin)(u theta_i) held in
+// registers: the lane's offsets never change), and splits them into fp16
+// hi + lo parts: A. B is q' rotated back to the tile's first position, also
+// hi + lo, so the score takes three MFMAs per chunk (hi hi, hi lo, lo hi).
+// The zero points are inside the reconstructed keys (no bias term).
+//
 // Pipeline: one tile of codes and metadata in registers per wave: the value and
 // metadata words of tile i + 4 are requested as soon as tile i's are staged in
 // LDS, its key words as soon as tile i's key products are issued.
@@ -52,6 +63,10 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+
+#ifndef KVQ_GQA_ROPE
+#define KVQ_GQA_ROPE 0
+#endif
 
 namespace kvq {
 namespace {
@@ -180,12 +195,51 @@ struct KeyFrag<8> {
     }
 };
 
+// Rotary layout: the words of a run of N codes (N = D/8 = 16 or 32); a run of
+// 16 3-bit codes starts on a half word when g is odd (two words, aligned at use).
+template <int B, int N>
+__host__ __device__ constexpr int rope_run_words() { return N == 32 ? B : (B == 3 ? 2 : B / 2); }
+// Bit at which pair jj (0..3) of a chunk sits in its fp16 half after extraction.
+template <int B>
+__host__ __device__ constexpr int rope_code_shift(int jj) { return B == 2 ? 2 * jj : B == 4 ? 4 * (jj & 1) : 0; }
+
 // Code j (0..31) of one packed 32-channel unit (little-endian bitstream).
 template <int B, int J>
 __device__ __forceinline__ uint32_t unit_code(const uint32_t* w) {
     constexpr int pos = J * B, wi = pos >> 5, sh = pos & 31;
     if constexpr (sh + B <= 32) return (w[wi] >> sh) & ((1u << B) - 1u);
     else return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << B) - 1u);
+}
+
+// Codes 4C + jj (jj = 0..3) of run A (wa) and run B (wb) as the words
+// (a | b << 16) << rope_code_shift(jj): fp16 halves (code << sh) 2^-24.
+template <int B, int C>
+__device__ __forceinline__ void rope_chunk_codes(const uint32_t* wa, const uint32_t* wb, uint32_t (&ab)[4]) {
+    // v_perm selector: byte k of run A to byte 0, byte k of run B to byte 2
+    auto sel = [](uint32_t k) { return k | 0x0c00u | ((4u + k) << 16) | 0x0c000000u; };
+    if constexpr (B == 8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ab[jj] = __builtin_amdgcn_perm(wb[C], wa[C], sel(jj));
+    } else if constexpr (B == 4) {
+        constexpr uint32_t b0 = 2 * (C % 2);  // the byte of codes 4C, 4C + 1
+        const uint32_t lo = __builtin_amdgcn_perm(wb[C / 2], wa[C / 2], sel(b0));
+        const uint32_t hi = __builtin_amdgcn_perm(wb[C / 2], wa[C / 2], sel(b0 + 1));
+        ab[0] = lo & 0x000f000fu;
+        ab[1] = lo & 0x00f000f0u;
+        ab[2] = hi & 0x000f000fu;
+        ab[3] = hi & 0x00f000f0u;
+    } else if constexpr (B == 2) {
+        const uint32_t v = __builtin_amdgcn_perm(wb[C / 4], wa[C / 4], sel(C % 4));
+        ab[0] = v & 0x00030003u;
+        ab[1] = v & 0x000c000cu;
+        ab[2] = v & 0x00300030u;
+        ab[3] = v & 0x00c000c0u;
+    } else {  // 3 and 6 bits: one extract per code
+        static_for<4>([&](auto JJ) {
+            constexpr int j = 4 * C + JJ;
+            ab[JJ] = unit_code<B, j>(wa) | (unit_code<B, j>(wb) << 16);
+        });
+    }
 }
 
 // 3- and 6-bit codes straddle words: one bit-field extract per code.
@@ -334,7 +388,7 @@ constexpr float kFarBelow = -1.0e30f;  // initial maximum: exp2(score - kFarBelo
 // value code bytes [token][position], value steps [group][token] and the
 // zero-point fragment rows [row][token]. After the loop the same bytes hold the
 // four waves' output rows and their (m, l) for the merge.
-template <int D>
+template <int D, bool ROPE = false>
 struct Lds {
     static constexpr int U = D / 32;
     static constexpr int VROW = D + 16;  // bytes per token row of the value tile (padded)
@@ -344,25 +398,38 @@ struct Lds {
     static constexpr int QFS = D + 4;      // floats per q' row
     static constexpr int QHS = D / 2 + 4;  // fp16 pairs per q' row
     static constexpr int QF = 0;
-    static constexpr int QH = QF + 16 * QFS * 4;
-    static constexpr int RED = QH + 16 * QHS * 4;  // 4 ints: per-wave exponent maxima
-    static constexpr int WAVE0 = RED + 16;
+    static constexpr int QH = QF + 16 * QFS * 4;  // (rotary keys: no fp16 copy of q')
+    static constexpr int RED = QH + (ROPE ? 0 : 16 * QHS * 4);  // 4 ints: per-wave exponent maxima
+    // rotary keys, head_dim <= 128: the (cos, sin) table of the tile offsets,
+    // row n + 16h = offset 8(n>>2) + 4h + (n&3) (the rows of lane n), D + 4
+    // floats per row (a quarter wave's 16 rows spread over the banks)
+    static constexpr bool TABLE = ROPE && D <= 128;
+    static constexpr int TB = RED + 16;
+    static constexpr int WAVE0 = TB + (TABLE ? 32 * (D + 4) * 4 : 0);
     static constexpr int SROW = 40;      // halves per row of the value steps (padded; cols 32.. take spare writes)
-    // key step / zero-point pairs: D / 2 words plus 4 spare words for lanes without a pair
-    static constexpr int SP = 0, ZP = SP + D * 2 + 16, VT = ZP + D * 2 + 16, ST = VT + 32 * VROW,
+    // key step / zero-point pairs: D / 2 words plus 4 spare words for lanes without a pair.
+    // Rotary keys instead: per pair slot p + p / (D/8) a float4 of the block's
+    // (s_a, s_b, z_a, z_b) (RM) and the (cos, sin) of the tile's anchors (AC:
+    // float2 slots p + 2 (p / (D/8)), or float4 of two anchors for head_dim 256)
+    static constexpr int PPG = D / 8;
+    static constexpr int ACE = D <= 128 ? 2 : 4;  // floats per anchor slot
+    static constexpr int RM = 0, AC = RM + (D / 2 + 8) * 16;
+    static constexpr int SP = 0, ZP = SP + D * 2 + 16,
+                         VT = ROPE ? AC + (D / 2 + 16) * ACE * 4 : ZP + D * 2 + 16, ST = VT + 32 * VROW,
                          ZT = ST + U * SROW * 2;
     static constexpr int WAVE = ZT + 16 * ZROW * 2;
     static constexpr int LOOP = WAVE0 + 4 * WAVE;
     static constexpr int MO = 0, ML = 4 * 16 * D * 4;
     static constexpr int MERGE = ML + 4 * 16 * 2 * 4;
     static constexpr int BYTES = LOOP > MERGE ? LOOP : MERGE;
-    static_assert(WAVE % 16 == 0 && WAVE0 % 16 == 0 && VT % 16 == 0 && ST % 16 == 0 && ZT % 16 == 0 && ZP % 16 == 0,
+    static_assert(WAVE % 16 == 0 && WAVE0 % 16 == 0 && VT % 16 == 0 && ST % 16 == 0 && ZT % 16 == 0 && ZP % 16 == 0 &&
+                      AC % 16 == 0,
                   "LDS alignment");
 };
 
 // One workgroup's work: split `split` of the quantized tokens of (seq, kv head
 // hy / nqg, query rows 16 (hy % nqg) ..), with the layer's arguments `a`.
-template <int D, int BK, int BV>
+template <int D, int BK, int BV, bool ROPE>
 __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int seq, int hy, int split) {
     constexpr int U = D / 32;                      // 32-channel units per row
     constexpr int KU = U >= 4 ? U / 4 : 1;         // key units per lane group (head_dim 64: half a unit)
@@ -380,8 +447,18 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     constexpr int KALIGN = min_align(pow2_align(D * BK / 8), pow2_align(KLOFF));
     constexpr int VALIGN = pow2_align(VRB / 2);
     using KF = KeyFrag<BK>;
-    using L = Lds<D>;
+    using L = Lds<D, ROPE>;
     static_assert(U >= 4 || BK % 2 == 0, "head_dim 64 needs even key bits (half a unit per lane group)");
+    // rotary keys: lane group g's PPG pairs, runs of PPG codes (RW words, run A
+    // from word RWO of the row, run B D*BK/64 words later), the (cos, sin) of its
+    // token offsets for CSH of its two token rows (head_dim 256: the first only;
+    // the second row's offset, 4 more, goes into a second query anchor)
+    constexpr int PPG = D / 8;
+    constexpr int RW = rope_run_words<BK, PPG>();
+    constexpr int CSH = D <= 128 ? 2 : 1;
+    constexpr int RALIGN =
+        (BK == 3 && PPG == 16) ? 4 : min_align(pow2_align(PPG * BK / 8), min_align(pow2_align(D * BK / 16), KALIGN));
+    static_assert(!ROPE || D >= 128, "rotary keys on the query-group kernel: head_dim 128 or 256");
 
     float* qf_lds = (float*)(smem + L::QF);
     uint32_t* qh_lds = (uint32_t*)(smem + L::QH);
@@ -426,7 +503,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     const int psh = e.page_shift;
 
     // ---- one tile of codes and metadata in registers
-    uint32_t kw[2][KWL];    // key words: token rows 8(n>>2) + 4h + (n&3), lane group g's channels
+    uint32_t kw[2][ROPE ? 2 * RW : KWL];  // key words: token rows 8(n>>2) + 4h + (n&3), lane group g's channels
     uint32_t kmw[2 * NKP];  // key (step, zero) words of the lane's fragment pairs
     uint32_t vw[VWL];       // value words: token row lane >> 1, half lane & 1
     uint32_t vmw[NVML];     // value (step, zero) words
@@ -442,12 +519,27 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), nqk - 1) - ps;
-            load_n<KWL, KALIGN>((const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8)) + wo, kw[h]);
+            const uint32_t* row = (const uint32_t*)(kc + pb + (size_t)t * (D * BK / 8));
+            if constexpr (ROPE) {
+                load_n<RW, RALIGN>(row + ((PPG * BK * g) >> 5), kw[h]);
+                load_n<RW, RALIGN>(row + ((PPG * BK * g) >> 5) + D * BK / 64, kw[h] + RW);
+            } else {
+                load_n<KWL, KALIGN>(row + wo, kw[h]);
+            }
         }
     };
     auto load_kmeta = [&](int t0, uint64_t pb) {
         const int ps = (t0 >> psh) << psh;
         const uint32_t* src = (const uint32_t*)(km + pb) + (size_t)((t0 - ps) >> lgk) * D;
+        if constexpr (ROPE) {  // channels p and p + D/2 of the lane's staging pairs p = lane + 64k
+#pragma unroll
+            for (int k = 0; k < NKP; ++k) {
+                const int pp = min(lane + 64 * k, D / 2 - 1);
+                kmw[2 * k] = src[pp];
+                kmw[2 * k + 1] = src[pp + D / 2];
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < NKP; ++k) {
             const int p = min(lane + 64 * k, D / 2 - 1), cb = (p >> 2) * 8, jj = p & 3;
@@ -495,12 +587,42 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         load_kmeta(t0, pb);
         load_keys(t0, pb);
     }
+    // rotary keys: per lane the frequencies of its staging pairs (and the
+    // rotation by 4 positions, head_dim 256), and the (cos, sin) of its token
+    // offsets u = 8(n>>2) + 4h + (n&3) for its PPG pairs from the cache's table:
+    // in LDS (head_dim 128), or in registers (head_dim 256: the first row only)
+    double th[NKP];
+    float2 r4[NKP];
+    float2 csr[L::TABLE ? 1 : CSH][L::TABLE ? 1 : PPG];
+    float* tb_lds = (float*)(smem + L::TB);
+    if constexpr (ROPE) {
+        const float2* tab = (const float2*)a.rope_tab;
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+            const int pp = min(lane + 64 * k, D / 2 - 1);
+            th[k] = a.rope_theta[pp];
+            r4[k] = tab[4 * (D / 2) + pp];
+        }
+        if constexpr (L::TABLE) {  // visible after the barrier below
+            for (int i = tid; i < 32 * (D / 2); i += 256) {
+                const int row = i / (D / 2), pp = i - row * (D / 2);
+                const int u = 8 * ((row & 15) >> 2) + 4 * (row >> 4) + (row & 3);
+                *(float2*)&tb_lds[row * (D + 4) + 2 * pp] = tab[u * (D / 2) + pp];
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < CSH; ++h)
+#pragma unroll
+                for (int j = 0; j < PPG; ++j)
+                    csr[h][j] = tab[(8 * (n >> 2) + 4 * h + (n & 3)) * (D / 2) + PPG * g + j];
+        }
+    }
     // ---- q' rows of this workgroup (rows >= RQ are 0), kept below 2^14 by
     // 2^-eqs: fp32 in natural channel order, and fp16 pairs in key-fragment order
     // (8-channel block cb: pair jj = channels cb + PERM[2jj], cb + PERM[2jj + 1])
     int eqs, eq;
     {
-        const float qs = a.qscale * ((float)(1 << 8) / (float)(1 << KSH));
+        const float qs = ROPE ? a.qscale : a.qscale * ((float)(1 << 8) / (float)(1 << KSH));
         const size_t qrow0 = ((size_t)seq * a.q_heads + kvh * R + q0) * D;
         float qm = 0.f;
         for (int i = tid; i < 16 * D; i += 256) {
@@ -521,10 +643,12 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
             for (int i = tid; i < 16 * D; i += 256) qf_lds[(i / D) * L::QFS + i % D] *= f;
             __syncthreads();
         }
-        for (int i = tid; i < 16 * D / 2; i += 256) {
-            const int r = i / (D / 2), p = i % (D / 2), cb = (p >> 2) * 8, jj = p & 3;
-            const float* qr = qf_lds + r * L::QFS + cb;
-            qh_lds[r * L::QHS + p] = pk_rtz(qr[KF::PERM[2 * jj]], qr[KF::PERM[2 * jj + 1]]);
+        if constexpr (!ROPE) {
+            for (int i = tid; i < 16 * D / 2; i += 256) {
+                const int r = i / (D / 2), p = i % (D / 2), cb = (p >> 2) * 8, jj = p & 3;
+                const float* qr = qf_lds + r * L::QFS + cb;
+                qh_lds[r * L::QHS + p] = pk_rtz(qr[KF::PERM[2 * jj]], qr[KF::PERM[2 * jj + 1]]);
+            }
         }
     }
     // constant rows of the zero-point fragment: 1.0 in row ngrp, 0 below it
@@ -669,6 +793,139 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         });
     };
 
+    // ---- rotary keys: staging of the block's metadata and the tile's anchors,
+    // query and key fragments
+    float* rm_lds = (float*)(wbase + L::RM);  // float4 (s_a, s_b, z_a, z_b) per pair slot
+    float* ac_lds = (float*)(wbase + L::AC);  // (cos, sin) of the anchors per pair slot
+    auto rslot = [](int p) { return p + p / PPG; };
+    auto aslot = [](int p) { return p + (L::ACE == 2 ? 2 : 1) * (p / PPG); };
+    auto stage_anchors = [&](int t0) {
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+            const int pp = lane + 64 * k;
+            if (pp < D / 2) {
+                float c0, s0;
+                rope_cs(t0, th[k], c0, s0);
+                if constexpr (L::ACE == 2) {
+                    *(float2*)&ac_lds[2 * aslot(pp)] = make_float2(c0, s0);
+                } else {  // and the anchor t0 + 4 of the second token row
+                    *(float4*)&ac_lds[4 * aslot(pp)] = make_float4(c0, s0, fmaf(c0, r4[k].x, -(s0 * r4[k].y)),
+                                                                   fmaf(s0, r4[k].x, c0 * r4[k].y));
+                }
+            }
+        }
+    };
+    // returns fa: the reconstructed keys (|k| <= max(|z|, |z + s (2^BK - 1)|))
+    // are scaled by 2^-fa to stay below 2^14 (their rotations below 2^14.5)
+    auto stage_rope = [&](int t0) -> int {
+        constexpr float cmax = (float)((1 << BK) - 1);
+        float sv[2 * NKP], zv[2 * NKP];
+        uint32_t emx = 0;
+#pragma unroll
+        for (int k = 0; k < 2 * NKP; ++k) {
+            sv[k] = f16_to_f32(kmw[k] & 0xffffu);
+            zv[k] = f16_to_f32(kmw[k] >> 16);
+            const float m = fmaxf(fabsf(zv[k]), fabsf(fmaf(sv[k], cmax, zv[k])));
+            emx = max(emx, (__float_as_uint(m) >> 23) & 0xffu);
+        }
+        const int fa =
+            __builtin_amdgcn_ballot_w64((int)emx > 140) ? max(0, wave_max_field<8>((int)emx) - 140) : 0;
+        const float fs = __builtin_amdgcn_ldexpf(1.0f, -fa);
+#pragma unroll
+        for (int k = 0; k < NKP; ++k) {
+            const int pp = lane + 64 * k;
+            if (pp < D / 2) {
+                const float f = __builtin_amdgcn_ldexpf(fs, 24 - rope_code_shift<BK>(pp & 3));
+                *(float4*)&rm_lds[4 * rslot(pp)] =
+                    make_float4(sv[2 * k] * f, sv[2 * k + 1] * f, zv[2 * k] * fs, zv[2 * k + 1] * fs);
+            }
+        }
+        stage_anchors(t0);
+        return fa;
+    };
+    // B of chunk pairs cb..cb+3: q' rotated back to anchor hh, fp16 hi + lo
+    auto rope_b = [&](int cb, int hh, Frag& bh, Frag& bl) {
+        const float4 qa4 = *(const float4*)&qf_lds[n * L::QFS + cb];
+        const float4 qb4 = *(const float4*)&qf_lds[n * L::QFS + cb + D / 2];
+        const float qa[4] = {qa4.x, qa4.y, qa4.z, qa4.w}, qb[4] = {qb4.x, qb4.y, qb4.z, qb4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            float c, sn;
+            if constexpr (L::ACE == 2) {
+                const float2 v = *(const float2*)&ac_lds[2 * aslot(cb + jj)];
+                c = v.x, sn = v.y;
+            } else {
+                const float4 v = *(const float4*)&ac_lds[4 * aslot(cb + jj)];
+                c = hh ? v.z : v.x, sn = hh ? v.w : v.y;
+            }
+            split2(fmaf(c, qa[jj], sn * qb[jj]), fmaf(c, qb[jj], -(sn * qa[jj])), bh.u[jj], bl.u[jj]);
+        }
+    };
+    // A of one token row: the pair values (xa, xb) rotated by the row's offset, fp16 hi + lo
+    auto rope_a = [&](const float (&xa)[4], const float (&xb)[4], int h, int c, Frag& ah, Frag& al) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            float2 r;
+            if constexpr (L::TABLE) r = *(const float2*)&tb_lds[(n + 16 * h) * (D + 4) + 2 * (PPG * g + 4 * c + jj)];
+            else r = csr[CSH == 2 ? h : 0][4 * c + jj];
+            split2(fmaf(r.x, xa[jj], -(r.y * xb[jj])), fmaf(r.y, xa[jj], r.x * xb[jj]), ah.u[jj], al.u[jj]);
+        }
+    };
+    // scores of a tile with quantized keys (metadata and anchors staged)
+    auto rope_scores = [&](float* sc, int fa) {
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+        uint32_t ra[2][RW], rb[2][RW];  // runs A and B of the two token rows, bit-aligned
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (BK == 3 && PPG == 16) {
+                const int sh = (PPG * BK * g) & 31;
+                ra[h][0] = __builtin_amdgcn_alignbit(kw[h][1], kw[h][0], sh);
+                ra[h][1] = kw[h][1] >> sh;
+                rb[h][0] = __builtin_amdgcn_alignbit(kw[h][3], kw[h][2], sh);
+                rb[h][1] = kw[h][3] >> sh;
+            } else {
+#pragma unroll
+                for (int k = 0; k < RW; ++k) ra[h][k] = kw[h][k], rb[h][k] = kw[h][RW + k];
+            }
+        }
+        static_for<NCH>([&](auto C) {
+            constexpr int c = C;
+            const int cb = PPG * g + 4 * c;
+            Frag bh[3 - CSH], bl[3 - CSH];
+            rope_b(cb, 0, bh[0], bl[0]);
+            if constexpr (CSH == 1) rope_b(cb, 1, bh[1], bl[1]);
+            float4 m4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) m4[jj] = *(const float4*)&rm_lds[4 * rslot(cb + jj)];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t ab[4];
+                rope_chunk_codes<BK, c>(ra[h], rb[h], ab);
+                float xa[4], xb[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    xa[jj] = mix_lo(ab[jj], m4[jj].x, m4[jj].z);
+                    xb[jj] = mix_hi(ab[jj], m4[jj].y, m4[jj].w);
+                }
+                Frag ah, al;
+                rope_a(xa, xb, h, c, ah, al);
+                const int bi = CSH == 2 ? 0 : h;
+                f32x4 acc2 = h ? c1 : c0;
+                acc2 = mfma(ah, bh[bi], acc2);
+                acc2 = mfma(ah, bl[bi], acc2);
+                acc2 = mfma(al, bh[bi], acc2);
+                if (h) c1 = acc2;
+                else c0 = acc2;
+            }
+        });
+        const float cs = __builtin_amdgcn_ldexpf(1.0f, eqs + fa);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            sc[k] = c0[k] * cs;
+            sc[4 + k] = c1[k] * cs;
+        }
+    };
+
     // ---- tiles with quantized keys: the next tile's words are requested as
     // soon as this tile's are consumed (the last tile re-requests itself)
     for (int i = wave, k = 0; i < nqt; i += 4, ++k) {
@@ -678,7 +935,9 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         const uint64_t pbn =
             paged ? (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pev, more ? k + 1 : k) * e.page_bytes : 0;
         const int kb_tile = stage_values();
-        const int fk = stage_kmeta();
+        int fk;
+        if constexpr (ROPE) fk = stage_rope(t0);
+        else fk = stage_kmeta();
         __builtin_amdgcn_sched_barrier(0);
         load_values(tn, pbn);
         load_kmeta(tn, pbn);
@@ -687,7 +946,12 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 
         // key scores: sc[j] for query n, token t0 + 8g + j
         float sc[8];
-        {
+        if constexpr (ROPE) {
+            rope_scores(sc, fk);
+            __builtin_amdgcn_sched_barrier(0);
+            load_keys(tn, pbn);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
             f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
             float bz = 0.f;
             const uint32_t fpair = f16_pow2_neg(fk) * 0x10001u;
@@ -745,7 +1009,42 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         const int t0 = wa + 32 * i;
         load_values(t0, (uint64_t)a.pages[e.page_list + (t0 >> psh)] * e.page_bytes);
         const int kb_tile = stage_values();
+        if constexpr (ROPE) stage_anchors(t0);
         wave_lds_sync();
+        float sc[8];
+        if constexpr (ROPE) {  // input rows rotated by their offsets, q' rotated back to the tile's anchors
+            f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            static_for<NCH>([&](auto C) {
+                constexpr int cc = C;
+                const int cb = PPG * g + 4 * cc;
+                Frag bh[3 - CSH], bl[3 - CSH];
+                rope_b(cb, 0, bh[0], bl[0]);
+                if constexpr (CSH == 1) rope_b(cb, 1, bh[1], bl[1]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
+                    const size_t base = (size_t)(t & (Gk - 1)) * D + cb;
+                    float xa[4], xb[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        xa[jj] = load_in_rt(kr, base + jj, a.in_dtype);
+                        xb[jj] = load_in_rt(kr, base + D / 2 + jj, a.in_dtype);
+                    }
+                    Frag ah, al;
+                    rope_a(xa, xb, h, cc, ah, al);
+                    const int bi = CSH == 2 ? 0 : h;
+                    c[h] = mfma(ah, bh[bi], c[h]);
+                    c[h] = mfma(ah, bl[bi], c[h]);
+                    c[h] = mfma(al, bh[bi], c[h]);
+                }
+            });
+            const float cs = __builtin_amdgcn_ldexpf(1.0f, eqs);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sc[k] = c[0][k] * cs;
+                sc[4 + k] = c[1][k] * cs;
+            }
+        } else {
         // keys and queries both as fp16 hi + lo (three MFMAs)
         f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         static_for<NCH>([&](auto C) {
@@ -771,12 +1070,12 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 c[h] = mfma(al, bh, c[h]);
             }
         });
-        float sc[8];
         const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             sc[k] = c[0][k] * cs;
             sc[4 + k] = c[1][k] * cs;
+        }
         }
         attend(sc, t0, kb_tile);
         wave_lds_sync();
@@ -824,34 +1123,52 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     }
 }
 
+// Keys cached before the rotary embedding: the instantiations of the objects
+// built with KVQ_GQA_ROPE (fewer waves per SIMD: the rotated fragments, and at
+// head_dim 256 the lane's (cos, sin), need the registers).
+#if KVQ_GQA_ROPE
+constexpr bool kRope = true;
+#if KVQ_GQA_HEAD_DIM > 128  // head_dim 256 keeps its (cos, sin) in registers: one wave per SIMD
+#define KVQ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(1, 1)))
+#else
+#define KVQ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2, 2)))
+#endif
+#else
+constexpr bool kRope = false;
+#if KVQ_GQA_HEAD_DIM > 128  // the LDS of a head_dim 256 workgroup leaves room for two per compute unit
+#define KVQ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2, 2)))
+#else
+#define KVQ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3, 3)))
+#endif
+#endif
+
 // One launch per (bits_k, bits_v) pair: grid = (split, kv head x query group,
 // the pair's sequences x layers).
-template <int D, int BK, int BV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_gqa_kernel(DecodeArgs a0) {
-    __shared__ __align__(16) uint8_t smem[Lds<D>::BYTES];
+template <int D, int BK, int BV, bool ROPE>
+__global__ __launch_bounds__(256) KVQ_GQA_OCCUPANCY void decode_gqa_kernel(DecodeArgs a0) {
+    __shared__ __align__(16) uint8_t smem[Lds<D, ROPE>::BYTES];
     int z = blockIdx.z;
     const DecodeArgs a = layer_args(a0, z, gridDim.z / a0.n_layers);
-    gqa_body<D, BK, BV>(a, smem, a.seq_list ? a.seq_list[z] : z, blockIdx.y, blockIdx.x);
+    gqa_body<D, BK, BV, ROPE>(a, smem, a.seq_list ? a.seq_list[z] : z, blockIdx.y, blockIdx.x);
 }
 
-template <int D, int BK>
+template <int D, int BK, bool ROPE>
 __device__ __forceinline__ void gqa_list_bv(int bv, const DecodeArgs& a, uint8_t* smem, int seq, int hy, int split) {
     switch (bv) {
-        case 2: gqa_body<D, BK, 2>(a, smem, seq, hy, split); break;
-        case 3: gqa_body<D, BK, 3>(a, smem, seq, hy, split); break;
-        case 4: gqa_body<D, BK, 4>(a, smem, seq, hy, split); break;
-        case 6: gqa_body<D, BK, 6>(a, smem, seq, hy, split); break;
-        default: gqa_body<D, BK, 8>(a, smem, seq, hy, split); break;
+        case 2: gqa_body<D, BK, 2, ROPE>(a, smem, seq, hy, split); break;
+        case 3: gqa_body<D, BK, 3, ROPE>(a, smem, seq, hy, split); break;
+        case 4: gqa_body<D, BK, 4, ROPE>(a, smem, seq, hy, split); break;
+        case 6: gqa_body<D, BK, 6, ROPE>(a, smem, seq, hy, split); break;
+        default: gqa_body<D, BK, 8, ROPE>(a, smem, seq, hy, split); break;
     }
 }
 
 // Every bit pair of the call in one launch: workgroup f takes the f-th active
 // (layer, seq, split, kv head x query group) item of a list ordered by bit
 // pair, found by binary search over the list's per-(layer, seq) starts.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_gqa_list_kernel(DecodeArgs a0,
-                                                                                                        GqaList list) {
-    __shared__ __align__(16) uint8_t smem[Lds<D>::BYTES];
+template <int D, bool ROPE>
+__global__ __launch_bounds__(256) KVQ_GQA_OCCUPANCY void decode_gqa_list_kernel(DecodeArgs a0, GqaList list) {
+    __shared__ __align__(16) uint8_t smem[Lds<D, ROPE>::BYTES];
     const int f = blockIdx.x;
     int lo = 0, hi = list.count - 1;
     while (lo < hi) {
@@ -868,13 +1185,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const SeqEntry& e = a.table[seq];
     const int bk = e.bits[0], bv = e.bits[1];
     switch (bk) {
-        case 2: gqa_list_bv<D, 2>(bv, a, smem, seq, r % nh, r / nh); break;
+        case 2: gqa_list_bv<D, 2, ROPE>(bv, a, smem, seq, r % nh, r / nh); break;
         case 3:
-            if constexpr (D >= 128) gqa_list_bv<D, 3>(bv, a, smem, seq, r % nh, r / nh);
+            if constexpr (D >= 128) gqa_list_bv<D, 3, ROPE>(bv, a, smem, seq, r % nh, r / nh);
             break;
-        case 4: gqa_list_bv<D, 4>(bv, a, smem, seq, r % nh, r / nh); break;
-        case 6: gqa_list_bv<D, 6>(bv, a, smem, seq, r % nh, r / nh); break;
-        default: gqa_list_bv<D, 8>(bv, a, smem, seq, r % nh, r / nh); break;
+        case 4: gqa_list_bv<D, 4, ROPE>(bv, a, smem, seq, r % nh, r / nh); break;
+        case 6: gqa_list_bv<D, 6, ROPE>(bv, a, smem, seq, r % nh, r / nh); break;
+        default: gqa_list_bv<D, 8, ROPE>(bv, a, smem, seq, r % nh, r / nh); break;
     }
 }
 
@@ -882,11 +1199,11 @@ template <int D, int BK>
 hipError_t gqa_bv(const DecodeArgs& a, int bv, dim3 grid, hipStream_t s) {
     const dim3 block(256);
     switch (bv) {
-        case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 2>), grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 3>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 4>), grid, block, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 6>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 8>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 2, kRope>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 3, kRope>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 4, kRope>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 6, kRope>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_gqa_kernel<D, BK, 8, kRope>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }
@@ -906,17 +1223,23 @@ hipError_t gqa_bk(const DecodeArgs& a, int bk, int bv, dim3 grid, hipStream_t s)
 
 }  // namespace
 
-// Compiled once per head_dim (KVQ_GQA_HEAD_DIM = 64, 128, 256).
+// Compiled once per head_dim (KVQ_GQA_HEAD_DIM = 64, 128, 256), and with
+// KVQ_GQA_ROPE = 1 for head_dim 128 and 256 (the rotary instantiations).
 #define KVQ_GCAT2(a, b) a##b
 #define KVQ_GCAT(a, b) KVQ_GCAT2(a, b)
-hipError_t KVQ_GCAT(launch_decode_gqa_list_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, const GqaList& list, int items,
-                                                                hipStream_t s) {
-    hipLaunchKernelGGL((decode_gqa_list_kernel<KVQ_GQA_HEAD_DIM>), dim3(items), dim3(256), 0, s, a, list);
+#if KVQ_GQA_ROPE
+#define KVQ_GQA_LIST KVQ_GCAT(launch_decode_gqa_rope_list_d, KVQ_GQA_HEAD_DIM)
+#define KVQ_GQA_LAUNCH KVQ_GCAT(launch_decode_gqa_rope_d, KVQ_GQA_HEAD_DIM)
+#else
+#define KVQ_GQA_LIST KVQ_GCAT(launch_decode_gqa_list_d, KVQ_GQA_HEAD_DIM)
+#define KVQ_GQA_LAUNCH KVQ_GCAT(launch_decode_gqa_d, KVQ_GQA_HEAD_DIM)
+#endif
+hipError_t KVQ_GQA_LIST(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s) {
+    hipLaunchKernelGGL((decode_gqa_list_kernel<KVQ_GQA_HEAD_DIM, kRope>), dim3(items), dim3(256), 0, s, a, list);
     return hipGetLastError();
 }
 
-hipError_t KVQ_GCAT(launch_decode_gqa_d, KVQ_GQA_HEAD_DIM)(const DecodeArgs& a, int bits_k, int bits_v, int nseqs,
-                                                           hipStream_t s) {
+hipError_t KVQ_GQA_LAUNCH(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s) {
     // x: the quantized splits only (the workspace's full-precision slots have no
     // workgroups here: empty ones would leave the busy ones on a few XCDs);
     // y: kv heads x groups of 16 query heads

@@ -202,6 +202,12 @@ inline hipError_t launch_decode_gqa(const DecodeArgs& a, int bits_k, int bits_v,
            : a.head_dim == 128 ? launch_decode_gqa_d128(a, bits_k, bits_v, nseqs, s)
                                : launch_decode_gqa_d256(a, bits_k, bits_v, nseqs, s);
 }
+// Keys cached before the rotary embedding on the query-group kernel (head_dim 128 and 256).
+hipError_t launch_decode_gqa_rope_list_d128(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s);
+hipError_t launch_decode_gqa_rope_list_d256(const DecodeArgs& a, const GqaList& list, int items, hipStream_t s);
+hipError_t launch_decode_gqa_rope_d128(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+hipError_t launch_decode_gqa_rope_d256(const DecodeArgs& a, int bits_k, int bits_v, int nseqs, hipStream_t s);
+inline bool gqa_rope_supported(int head_dim) { return head_dim == 128 || head_dim == 256; }
 inline bool mha_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 bool mha_fused_ok_d64(int bits_k, int bits_v);
 bool mha_fused_ok_d128(int bits_k, int bits_v);

@@ -620,15 +620,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a0) {
 // Merge the splits of one (seq, q head): m* = max m_i, l* = sum l_i 2^(m_i - m*),
 // out = sum o_i 2^(m_i - m*) / l*. A sequence of length 0 gets zeros.
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
-    // grid = (ceil(q_heads / 4), num_seqs x layers): one wave per (seq, query
-    // head). Every lane computes the same maximum and denominator over the
-    // splits (lane-strided, then wave reductions); lane l owns channels
-    // l, l + 64, ... and sums the splits in order.
+    // grid = (q_heads x ceil(D / 64), num_seqs x layers): one workgroup per
+    // (seq, query head, 64-channel slice). Every wave computes the same maximum
+    // and denominator over the splits (lane-strided, then wave reductions);
+    // wave w sums the splits w, w + 4, ... of channel slice + lane, and the four
+    // partial sums are added in a fixed order.
+    __shared__ float part[kThreads];
     int y = blockIdx.y;
     const DecodeArgs a = layer_args(a0, y, gridDim.y / a0.n_layers);
-    const int lane = threadIdx.x & 63;
-    const int hq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6), seq = y, D = a.head_dim;
-    if (hq >= a.q_heads) return;
+    const int D = a.head_dim, nsl = (D + 63) >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hq = blockIdx.x / nsl, c = (blockIdx.x - hq * nsl) * 64 + lane, seq = y;
     const int len = a.len[seq];
     float* out = a.out + ((size_t)seq * a.q_heads + hq) * D;
     int nch;
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
         nch = a.split_floor ? len / a.chunk : (len + a.chunk - 1) / a.chunk;
     }
     if (nch == 0) {
-        for (int c = lane; c < D; c += 64) out[c] = 0.f;
+        if (wave == 0 && c < D) out[c] = 0.f;
         return;
     }
     const size_t base = ((size_t)seq * a.q_heads + hq) * a.max_chunks;
@@ -661,24 +663,24 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a0) {
     float L = 0.f;
     for (int i = lane; i < nch; i += 64) L += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
     L = wave_sum(L);
-    const float inv = 1.0f / L;
     const float* src = a.ws_o + base * D;
-    for (int c = lane; c < D; c += 64) {
-        // 8 splits' loads in flight at a time (clamped indices, zero weights past the end)
-        float o = 0.f;
-        for (int i0 = 0; i0 < nch; i0 += 8) {
-            float v[8], wgt[8];
+    const int cc = min(c, D - 1);
+    float o = 0.f;
+    // 8 of the wave's splits in flight at a time (clamped indices, zero weights past the end)
+    for (int i0 = wave; i0 < nch; i0 += 32) {
+        float v[8], wgt[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int i = min(i0 + k, nch - 1);
-                v[k] = src[(size_t)i * D + c];
-                wgt[k] = i0 + k < nch ? exp2f(ml[2 * i] - M) : 0.f;
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) o = fmaf(v[k], wgt[k], o);
+        for (int k = 0; k < 8; ++k) {
+            const int i = min(i0 + 4 * k, nch - 1);
+            v[k] = src[(size_t)i * D + cc];
+            wgt[k] = i0 + 4 * k < nch ? exp2f(ml[2 * i] - M) : 0.f;
         }
-        out[c] = o * inv;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o = fmaf(v[k], wgt[k], o);
     }
+    part[threadIdx.x] = o;
+    __syncthreads();
+    if (wave == 0 && c < D) out[c] = (((part[lane] + part[64 + lane]) + part[128 + lane]) + part[192 + lane]) * (1.0f / L);
 }
 
 // ---------------------------------------------------------------------------
@@ -980,7 +982,7 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3((a.q_heads + kThreads / 64 - 1) / (kThreads / 64), a.num_seqs * a.n_layers),
+    hipLaunchKernelGGL(merge_kernel, dim3(a.q_heads * ((a.head_dim + 63) / 64), a.num_seqs * a.n_layers),
                        dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

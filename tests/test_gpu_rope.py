@@ -52,6 +52,19 @@ CASES = {
     # positions to 100k: angles of 1e5 rad reduced in float64
     "long_positions": (W.llama2_7b().scaled(num_seqs=1, kv_heads=1, q_heads=1, lengths=(100000,), bits=((2, 2),)),
                        10000.0),
+    # query groups: the query-group kernel's rotary instantiations, every bit
+    # pair at head_dim 128 (8 query heads per kv head, fp16) and 256 (16, bf16)
+    "gqa_d128_pairs": (W.mixed_batch().scaled(num_seqs=25, kv_heads=2, q_heads=16, lengths=_PAIR_LENS, bits=ALL_PAIRS),
+                       10000.0),
+    "gqa_d256_pairs": (W.long_gqa().scaled(num_seqs=25, lengths=_PAIR_LENS, bits=ALL_PAIRS), 500000.0),
+    # 4 query heads per kv head (12 zero rows), and 24 (two query groups)
+    "gqa_r4": (W.mixed_batch().scaled(num_seqs=3, kv_heads=2, q_heads=8, lengths=(3000, 100, 33),
+                                      bits=((2, 2), (3, 3), (6, 4))), 10000.0),
+    "gqa_r24": (W.mixed_batch().scaled(num_seqs=2, kv_heads=2, q_heads=48, lengths=(1500, 70), bits=((4, 8), (2, 2))),
+                10000.0),
+    # 64-token key blocks on the query-group kernel
+    "gqa_g64": (W.mixed_batch().scaled(num_seqs=2, kv_heads=2, q_heads=16, group_k=64, lengths=(2000, 130),
+                                       bits=((4, 4), (8, 6))), 10000.0),
 }
 
 
