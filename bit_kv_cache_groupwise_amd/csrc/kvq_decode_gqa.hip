@@ -1045,37 +1045,37 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 sc[4 + k] = c[1][k] * cs;
             }
         } else {
-        // keys and queries both as fp16 hi + lo (three MFMAs)
-        f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        static_for<NCH>([&](auto C) {
-            constexpr int cc = C;
-            const int cb = cbase(cc);
-            const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
-            const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
-            Frag bh, bl;
-            split2(qa.x, qa.y, bh.u[0], bl.u[0]);
-            split2(qa.z, qa.w, bh.u[1], bl.u[1]);
-            split2(qb.x, qb.y, bh.u[2], bl.u[2]);
-            split2(qb.z, qb.w, bh.u[3], bl.u[3]);
+            // keys and queries both as fp16 hi + lo (three MFMAs)
+            f32x4 c[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            static_for<NCH>([&](auto C) {
+                constexpr int cc = C;
+                const int cb = cbase(cc);
+                const float4 qa = *(const float4*)&qf_lds[n * L::QFS + cb];
+                const float4 qb = *(const float4*)&qf_lds[n * L::QFS + cb + 4];
+                Frag bh, bl;
+                split2(qa.x, qa.y, bh.u[0], bl.u[0]);
+                split2(qa.z, qa.w, bh.u[1], bl.u[1]);
+                split2(qb.x, qb.y, bh.u[2], bl.u[2]);
+                split2(qb.z, qb.w, bh.u[3], bl.u[3]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
-                float kv[8];
-                load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
-                Frag ah, al;
+                for (int h = 0; h < 2; ++h) {
+                    const int t = min(t0 + 8 * (n >> 2) + 4 * h + (n & 3), wb - 1);
+                    float kv[8];
+                    load8_rt(kr, (size_t)(t & (Gk - 1)) * D + cb, a.in_dtype, kv);
+                    Frag ah, al;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
-                c[h] = mfma(ah, bh, c[h]);
-                c[h] = mfma(ah, bl, c[h]);
-                c[h] = mfma(al, bh, c[h]);
+                    for (int jj = 0; jj < 4; ++jj) split2(kv[2 * jj], kv[2 * jj + 1], ah.u[jj], al.u[jj]);
+                    c[h] = mfma(ah, bh, c[h]);
+                    c[h] = mfma(ah, bl, c[h]);
+                    c[h] = mfma(al, bh, c[h]);
+                }
+            });
+            const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                sc[k] = c[0][k] * cs;
+                sc[4 + k] = c[1][k] * cs;
             }
-        });
-        const float cs = __builtin_amdgcn_ldexpf(1.0f, KSH - 8 + eqs);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sc[k] = c[0][k] * cs;
-            sc[4 + k] = c[1][k] * cs;
-        }
         }
         attend(sc, t0, kb_tile);
         wave_lds_sync();

@@ -153,8 +153,10 @@ typedef struct kvq_geometry {
      * t * rope_base^(-2i/head_dim); q must be given rotated to its own
      * position. kvq_dequantize returns the un-rotated keys. With a window or
      * sinks the full-precision rows are rotated to their positions too. This
-     * build: channel-axis keys (else KVQ_ERR_UNSUPPORTED at decode), computed
-     * by the generic split kernel and the window kernel. */
+     * build: channel-axis keys (else KVQ_ERR_UNSUPPORTED at decode); the
+     * single-query kernel (head_dim 64, 128, 256) and the query-group kernel
+     * (head_dim 128, 256) have rotary instantiations, other caches take the
+     * generic split kernel. */
     double rope_base;
     /* Paged storage (see "pages" above). 0: each (layer, seq) has contiguous
      * regions sized for its capacity. Otherwise P tokens per page: a power of
@@ -241,9 +243,10 @@ size_t kvq_decode_workspace_size(const kvq_cache* cache);
  * [num_seqs][q_heads][head_dim]; out: device float32, same shape; a sequence
  * of length 0 gets zeros. K and V on either axis. Per-channel keys with
  * per-token values and head_dim 64, 128 or 256 take the single-query or
- * query-group kernel (any q_heads/kv_heads); other caches (per-token keys,
- * per-channel values, rotary keys, other head_dims) take the generic split
- * kernel, which needs q_heads/kv_heads <= 16 (else KVQ_ERR_UNSUPPORTED). */
+ * query-group kernel (any q_heads/kv_heads; rotary keys: the query-group
+ * kernel at head_dim 128 and 256 only); other caches (per-token keys,
+ * per-channel values, other head_dims) take the generic split kernel, which
+ * needs q_heads/kv_heads <= 16 (else KVQ_ERR_UNSUPPORTED). */
 kvq_status kvq_decode_attention(const kvq_cache* cache, int32_t layer, const void* q, float softmax_scale,
                                 float* out, void* workspace, size_t workspace_bytes, void* stream);
 
