@@ -39,9 +39,11 @@
 //
 // Softmax: online in the log2 domain with the exact running maximum, so weights
 // are <= 1. They enter the fp16 operands pre-scaled by powers of two: 2^kb for
-// p * s (kb <= BV + 2, lowered per tile when large value steps would push
-// 2^kb p s past 2^15; the accumulators are rescaled exactly), 2^KZ for the zero
-// points. q' is kept below 2^14 by a power of two per workgroup, and the key
+// p * s (kb per query row, from BV + 2: lowered per tile when large value
+// steps would push 2^kb p s past 2^15, and set from the row's largest p s over
+// the tile, up to 15, when a small step would take its products below fp16's
+// normal range; the row's accumulators are rescaled exactly), 2^KZ for the
+// zero points. q' is kept below 2^14 by a power of two per workgroup, and the key
 // weights q' s of a block whose steps would push them past 2^15 are scaled by
 // 2^-f. Splits are merged by merge_kernel.
 //
@@ -124,6 +126,7 @@ __device__ __forceinline__ float mix3_hi(float a, uint32_t b, uint32_t c) {
     return d;
 }
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
 }
@@ -663,12 +666,23 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     for (int o = 0; o < NOT; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 cz = {0.f, 0.f, 0.f, 0.f};  // C[query 4g+k][column n]: zero-point sums (n < ngrp), denominator (n == ngrp)
     float m = kFarBelow;              // running maximum of query n
-    int kb = KB;                      // value-product exponent (wave-uniform, never rises)
+    // the value-product exponent kb of query n (rows weight different tokens),
+    // held as mb = m - kb (the weights 2^kb p = 2^(score - mb)) and zsc = 2^(KZ - kb)
+    float mb = kFarBelow;
+    float zsc = __builtin_amdgcn_ldexpf(1.0f, KZ - KB);
+    int kb_lo = KB, kb_hi = KB;       // smallest kb of the rows < RQ, largest of all rows (wave-uniform)
+    auto kb_of = [&]() { return KZ + 127 - (int)(__float_as_uint(zsc) >> 23); };
 
     // ---- staging of a tile's value codes (bytes), value metadata and key
     // metadata in LDS, branch-free (lanes without an item write spare slots);
-    // returns the exponent the tile's value steps allow (kb_tile)
-    auto stage_values = [&]() -> int {
+    // returns the value-product exponent the tile's steps allow, and whether a
+    // nonzero step is so small that 2^kb s < 2^-7 for some query row's kb (its
+    // products would leave fp16's normal range, keeping few bits)
+    struct TileSteps {
+        int kb;     // the largest with 2^kb p s < 2^15 for every step s and p <= 1 (wave-uniform)
+        bool tiny;  // wave-uniform
+    };
+    auto stage_values = [&]() -> TileSteps {
 #pragma unroll
         for (int u = 0; u < VUL; ++u) {
             uint32_t by[8];
@@ -677,7 +691,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
             ((uint4*)dst)[0] = make_uint4(by[0], by[1], by[2], by[3]);
             ((uint4*)dst)[1] = make_uint4(by[4], by[5], by[6], by[7]);
         }
-        uint32_t smx = 0;  // largest fp16 value step of the tile (steps are >= 0: bit order = value order)
+        uint32_t smx = 0, smn1 = ~0u;  // largest step, smallest nonzero step - 1 (fp16 bits: >= 0, ordered)
 #pragma unroll
         for (int k = 0; k < NVML; ++k) {
             const int f = lane + 64 * k;
@@ -685,13 +699,20 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
             const int tt = f >> lng, gg = f & (ngrp - 1);
             st_lds[ok ? gg * L::SROW + tt : 32] = (uint16_t)(vmw[k] & 0xffffu);
             zt_lds[ok ? gg * L::ZROW + tt : 15 * L::ZROW + 32] = (uint16_t)(vmw[k] >> 16);
-            smx = max(smx, ok ? vmw[k] & 0x7fffu : 0u);
+            const uint32_t sb = vmw[k] & 0x7fffu;
+            smx = max(smx, ok ? sb : 0u);
+            smn1 = min(smn1, ok ? sb - 1u : ~0u);
         }
         // s < 2^(e - 14) for biased fp16 exponent e: 2^kb p s < 2^15 with kb = 29 - e
         // (one ballot in the common case that no step needs kb below KB)
-        return __builtin_amdgcn_ballot_w64((int)(smx >> 10) > 29 - KB)
-                   ? min(KB, 29 - wave_max_field<5>((int)(smx >> 10)))
-                   : KB;
+        const int kbt = __builtin_amdgcn_ballot_w64((int)(smx >> 10) > 29 - KB)
+                            ? min(KB, 29 - wave_max_field<5>((int)(smx >> 10)))
+                            : KB;
+        // tiny: 0 < s < 2^et, et = -7 - min(kb_lo, kbt) >= -22; thr = fp16 bits of 2^et (inf above 2^15)
+        const int et = -7 - min(kb_lo, kbt);
+        const uint32_t thr = et > 15 ? 0x7c00u : et >= -14 ? (uint32_t)(et + 15) << 10 : 1u << (et + 24);
+        const bool tiny = __builtin_amdgcn_ballot_w64(smn1 < thr - 1u);
+        return TileSteps{kbt, tiny};
     };
     // returns fk: the key weights q' s are scaled by 2^-fk to stay in fp16 range
     auto stage_kmeta = [&]() -> int {
@@ -711,7 +732,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     };
 
     // ---- masked scores of tile t0 -> online softmax -> zero points and the value products
-    auto attend = [&](float* sc, int t0, int kb_tile) {
+    auto attend = [&](float* sc, int t0, TileSteps ts) {
         if (t0 + 32 > wb) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -733,16 +754,53 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
                 for (int o = 0; o < NOT; ++o) acc[o][k] *= ak;
                 cz[k] *= ak;
             }
+            mb = mnew - (float)kb_of();
             m = mnew;
         }
-        if (kb_tile < kb) {  // a tile with larger value steps: lower the exponent (exact rescale)
-            const float f = __builtin_amdgcn_ldexpf(1.0f, kb_tile - kb);
+        // query n's value-product exponent: lowered when the tile's steps are
+        // larger; where a step is tiny at the rows' exponents, taken from the
+        // row's largest weighted step over the tile, max p s (p <= 1 against the
+        // row's running maximum), up to 15 (2^kb p stays an fp16 value): a row
+        // whose weight sits on tokens with small steps next to tokens with large
+        // ones, or on a tile whose steps are all small, keeps the products'
+        // precision. Exact rescale of the row's accumulators.
+        if (ts.kb < kb_hi || ts.tiny) {
+          const int kb = kb_of();
+          int kbt = min(kb, ts.kb);
+          if (ts.tiny) {
+            float pm = 0.f;
 #pragma unroll
-            for (int o = 0; o < NOT; ++o) acc[o] *= f;
-            kb = kb_tile;
+            for (int jj = 0; jj < 4; ++jj) {  // tokens 8g + 2jj, 8g + 2jj + 1: largest step over the groups
+                u16x2_t sm = {};
+                for (int gg = 0; gg < ngrp; ++gg)
+                    sm = __builtin_elementwise_max(
+                        sm, *(const u16x2_t*)&st_lds[gg * L::SROW + 8 * g + 2 * jj]);
+                pm = fmaxf(pm, fmaxf(__builtin_amdgcn_exp2f(sc[2 * jj] - m) * f16_to_f32(sm[0]),
+                                     __builtin_amdgcn_exp2f(sc[2 * jj + 1] - m) * f16_to_f32(sm[1])));
+            }
+            pm = col4_max(pm);  // over the row's 32 tokens
+            // pm < 2^(e - 126) for biased fp32 exponent e: 2^kb p s < 2^15 with kb = 141 - e
+            const int e = (int)(__float_as_uint(pm) >> 23);
+            if (e > 0) kbt = min(15, 141 - e);  // kbt >= -113
+            kb_lo = 15 - wave_max_field<8>(n < RQ ? 15 - kbt : 0);
+            kb_hi = wave_max_field<8>(kbt + 114) - 114;
+          } else {
+            kb_lo = min(kb_lo, ts.kb);
+            kb_hi = ts.kb;
+          }
+          if (__builtin_amdgcn_ballot_w64(kbt != kb)) {
+            const float f = __builtin_amdgcn_ldexpf(1.0f, kbt - kb);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float fk = __shfl(f, 4 * g + k);
+#pragma unroll
+                for (int o = 0; o < NOT; ++o) acc[o][k] *= fk;
+            }
+            zsc = __builtin_amdgcn_ldexpf(1.0f, KZ - kbt);
+            mb = m - (float)kbt;
+          }
         }
         float p[8];
-        const float mb = m - (float)kb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) p[j] = exp2_for_asm(sc[j] - mb);  // mul_split's asm reads them
         uint32_t pb[4];  // 2^kb p truncated to fp16 pairs
@@ -752,9 +810,8 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         // zero points and denominator
         {
             Frag ph, pl, zf;
-            const float zscale = __builtin_amdgcn_ldexpf(1.0f, KZ - kb);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj] * zscale, p[2 * jj + 1] * zscale, ph.u[jj], pl.u[jj]);
+            for (int jj = 0; jj < 4; ++jj) split2(p[2 * jj] * zsc, p[2 * jj + 1] * zsc, ph.u[jj], pl.u[jj]);
             const uint4 z4 = *(const uint4*)&zt_lds[n * L::ZROW + 8 * g];
             zf.u[0] = z4.x, zf.u[1] = z4.y, zf.u[2] = z4.z, zf.u[3] = z4.w;
             cz = mfma(ph, zf, cz);
@@ -934,7 +991,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         const int tn = wa + 32 * (more ? i + 4 : i);
         const uint64_t pbn =
             paged ? (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pev, more ? k + 1 : k) * e.page_bytes : 0;
-        const int kb_tile = stage_values();
+        const TileSteps kb_tile = stage_values();
         int fk;
         if constexpr (ROPE) fk = stage_rope(t0);
         else fk = stage_kmeta();
@@ -1008,7 +1065,7 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
         if (i < nqt) continue;
         const int t0 = wa + 32 * i;
         load_values(t0, (uint64_t)a.pages[e.page_list + (t0 >> psh)] * e.page_bytes);
-        const int kb_tile = stage_values();
+        const TileSteps kb_tile = stage_values();
         if constexpr (ROPE) stage_anchors(t0);
         wave_lds_sync();
         float sc[8];
@@ -1086,16 +1143,17 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
     float* ml = (float*)(smem + L::ML);  // [wave][row][m, l]
     wg_lds_barrier();                    // every wave is done with the loop areas
     {
-        const float oscale = __builtin_amdgcn_ldexpf(1.0f, 24 - kb - VSH);
+        const float oscale = zsc * (float)(1 << (24 - VSH - KZ));  // 2^(24 - kb - VSH) of query n
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int r = 4 * g + k;
+            const float osk = __shfl(oscale, r);
 #pragma unroll
             for (int o = 0; o < NOT; ++o) {
                 const int gg = (32 * (o >> 1)) >> lgv;
                 const float zs = __shfl(cz[k], 16 * g + gg) * (1.0f / (float)(1 << KZ));
                 const int ch = 32 * (o >> 1) + val_chan<BV>(16 * (o & 1) + n);
-                mo[(wave * 16 + r) * D + ch] = fmaf(acc[o][k], oscale, zs);
+                mo[(wave * 16 + r) * D + ch] = fmaf(acc[o][k], osk, zs);
             }
             if (n == ngrp) ml[(wave * 16 + r) * 2 + 1] = cz[k] * (1.0f / (float)(1 << KZ));
         }

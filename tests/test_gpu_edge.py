@@ -2,7 +2,8 @@
 oracle: every bit width B in {2,3,4,6,8}, both grouping axes for both tensors,
 fp32, fp16 and bf16 inputs. The groups (tests/edge_inputs.py) are constant,
 have fp16-subnormal steps whose rounding makes the top clamp, steps that
-underflow to 0, exact ties t = k + 1/2, fp32 minima that fp16 rounds above the
+underflow to 0, exact ties t = k + 1/2, near ties (t a few float32 ulps
+from k + 1/2, step with no exact reciprocal), fp32 minima that fp16 rounds above the
 group, magnitudes below fp16's normal range and near 65504, and a 7000x
 outlier ([U] "O Que o Erro de Quantizacao E Realmente Feito": nearest step,
 half-step bound; [N] "Scale menentukan sistem koordinat kuantisasi": clamp).
@@ -114,4 +115,58 @@ def test_edge_groups_decode(dtype, q_heads):
         worst = max(worst, float(err.max()))
         assert np.all(err <= H.ATTN_TOL), (dtype, q_heads, s, w.bits[s], float(err.max()))
     _note(f"[edge decode] dtype={dtype} q_heads={q_heads} worst row rel err {worst:.3e}")
+    cache.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_tiny_value_steps_next_to_large(dtype):
+    """Query groups whose rows weight tokens of very different value scales.
+
+    Per bit width B, two sequences of one kv head and four query heads (the
+    query-group kernel). In the first, query row 0 puts all of its weight on
+    token 37, whose values are tiny (1e-6, 1e-5, 1e-4 times U(1, 3) at B = 2, 4,
+    8: nonzero value steps below fp16's normal range), inside a 32-token tile of
+    tokens with values up to 6e4 (steps ~4e4 at B = 2); rows 1-3 are orthogonal
+    to row 0 and spread their weight over every token. In the second, every
+    value is that small. Each row's output must meet the 2e-3 bar relative to
+    its own magnitude (~1e-6 for row 0, ~1e4 for rows 1-3), which a single
+    power-of-two scale shared by the rows of a tile cannot give."""
+    bits = (2, 4, 8)
+    w = W.tiny().scaled(num_seqs=2 * len(bits), kv_heads=1, q_heads=4, head_dim=128, in_dtype=dtype,
+                        group_k=E.G, group_v=E.G, axis_k=o.AXIS_CHANNEL, axis_v=o.AXIS_TOKEN,
+                        bits=tuple((b, b) for b in bits for _ in range(2)), lengths=(T,) * (2 * len(bits)),
+                        new_tokens=0)
+    _note(f"[edge tiny steps] dtype={dtype} bits={bits}")
+    rng = np.random.Generator(np.random.PCG64(77))
+    S, D, hot = w.num_seqs, w.head_dim, 37
+    tiny = {2: 1.0e-6, 4: 1.0e-5, 8: 1.0e-4}
+    q = rng.normal(0.0, 1.0, (S, 4, D))
+    for s in range(S):  # rows 1-3 orthogonal to row 0
+        q0 = q[s, 0] / np.linalg.norm(q[s, 0])
+        for r in range(1, 4):
+            q[s, r] -= (q[s, r] @ q0) * q0
+    q = E.to_dtype(q, dtype)
+    k = np.zeros((S, T, 1, D), np.float32)
+    v = np.zeros((S, T, 1, D), np.float32)
+    for s in range(S):
+        if s % 2 == 0:
+            # row 0's logit at the hot token is ~60 above every other one
+            c = 60.0 / (float(q[s, 0].astype(np.float64) @ q[s, 0]) * w.softmax_scale)
+            k[s, hot, 0] = E.to_dtype(c * q[s, 0], dtype)
+            v[s, :, 0] = E.to_dtype(rng.uniform(-6.0e4, 6.0e4, (T, D)), dtype)
+            v[s, hot, 0] = E.to_dtype(tiny[w.bits[s][1]] * rng.uniform(1.0, 3.0, D), dtype)
+        else:
+            k[s, :, 0] = E.to_dtype(rng.normal(0.0, 1.0, (T, D)), dtype)
+            v[s, :, 0] = E.to_dtype(tiny[w.bits[s][1]] * rng.uniform(-2.0, 2.0, (T, D)), dtype)
+    cache = _fill(w, k, v)
+    qt = torch.from_numpy(np.ascontiguousarray(q)).to(E.TORCH[dtype])
+    out = cache.decode(0, qt.cuda(), w.softmax_scale)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for s in range(S):
+        enc = H.assert_head_bytes(cache, w, 0, s, 0, k[s], v[s])
+        ref = H.attn_ref(w, qt[s].float().numpy(), [enc])
+        err = H.row_rel_err(out[s], ref)
+        _note(f"[edge tiny steps] s{s} B{w.bits[s]} |ref| {np.abs(ref).max(axis=-1)} row err {err}")
+        assert np.all(err <= H.ATTN_TOL), (dtype, s, w.bits[s], err)
     cache.close()
