@@ -12,7 +12,9 @@ stored in fp16):
 
   constant groups (stored step 0), fp16-subnormal steps whose rounding makes
   the top of the group clamp, steps that underflow to 0 in fp16, exact ties
-  t = k + 1/2 against a power-of-two step, minima that fp16 rounds above the
+  t = k + 1/2 against a power-of-two step, near ties (t a few float32 ulps
+  from k + 1/2) against a step with no exact reciprocal, minima that fp16
+  rounds above the
   group (negative t, clamped to 0), bf16 and fp32 magnitudes below fp16's
   normal range (and below its smallest subnormal), magnitudes near +-65504,
   a 7000x outlier among small values, and plain normal draws.
@@ -61,6 +63,46 @@ def _ties(bits, dtype, z0, s0, rng):
     return _fill([z0, z0 + L * s0, *keep], rng)
 
 
+def _step_units(x: float, dtype: str, j: int) -> float:
+    """The value j units in the last place of the dtype away from x (x nonzero,
+    representable; the step keeps the sign of x)."""
+    if dtype == "f32":
+        u = np.array([x], np.float32).view(np.int32)
+        return float((u + np.int32(j)).view(np.float32)[0])
+    t = torch.tensor([x], dtype=TORCH[dtype]).view(torch.int16)
+    return float((t + j).view(TORCH[dtype]).float()[0])
+
+
+def _near_ties(bits, dtype, m, e, rng):
+    """Values a few units in the dtype's last place either side of the tie
+    points z0 + (k + 1/2)*s0, and ones 2^-14..2^-12 steps from them, for a
+    step s0 = m * 2^e (m odd, so s0 is not a power of two and has no exact
+    reciprocal) that the group stores exactly: z0 and z0 + L*s0, the minimum
+    and maximum, are both held by the dtype and by fp16. Where the dtype
+    allows it (fp32), the quotient t then lands within a few float32 ulps of
+    k + 1/2, on both sides."""
+    L = (1 << bits) - 1
+    s0 = m * 2.0 ** e
+    z_opts = [0.0] + [-(L * m - 2 ** p) * 2.0 ** e for p in range(24) if 2 ** p < L * m]
+    z0 = next(z for z in z_opts if representable([z, z + L * s0], dtype) and representable([z], "f16"))
+    top = z0 + L * s0
+    cand = set()
+    for k in range(L):
+        p = z0 + (k + 0.5) * s0
+        base = float(to_dtype([p], dtype)[0])
+        pts = [base] + [float(to_dtype([p + d * s0], dtype)[0])
+                        for d in (2.0 ** -14, -2.0 ** -14, 2.0 ** -13, -2.0 ** -13, 2.0 ** -12, -2.0 ** -12)]
+        for b in pts:
+            for j in (-2, -1, 0, 1, 2):
+                v = _step_units(b, dtype, j) if b != 0.0 else b
+                if z0 < v < top and (v > 0) == (b > 0):
+                    cand.add(v)
+    cand = sorted(cand)
+    if len(cand) > G - 2:
+        cand = list(rng.choice(cand, G - 2, replace=False))
+    return _fill([z0, top, *cand], rng)
+
+
 def groups(bits: int, dtype: str, seed: int = 0):
     """(name, float32[32]) adversarial groups for a bit width and input dtype."""
     rng = np.random.Generator(np.random.PCG64([seed, bits, {"f32": 0, "f16": 1, "bf16": 2}[dtype]]))
@@ -74,6 +116,8 @@ def groups(bits: int, dtype: str, seed: int = 0):
         ("ties_unit", _ties(bits, dtype, -2.0, 1.0 / 8, rng)),
         ("ties_small", _ties(bits, dtype, 0.25 if dtype != "bf16" else 0.0, 2.0 ** -12, rng)),
         ("ties_neg", _ties(bits, dtype, -40.0, 0.5, rng)),
+        ("neartie_m3", _near_ties(bits, dtype, 3, -8, rng)),
+        ("neartie_m5", _near_ties(bits, dtype, 5, -4, rng)),
     ]
     # fp16-subnormal steps: range M * 2^-24 with M a little above L, so the
     # stored step rounds down and the top of the group clamps

@@ -570,8 +570,8 @@ def r16(fr):
 
 
 def check_edge_groups_exact(o):
-    """Constant groups, fp16-subnormal and underflowing steps, exact ties,
-    clamping after the fp16 rounding of the step or the zero, magnitudes below
+    """Constant groups, fp16-subnormal and underflowing steps, exact ties and
+    near ties (t within 2^-13 of k + 1/2 but not on it), clamping after the fp16 rounding of the step or the zero, magnitudes below
     fp16's range and near 65504: step, zero, codes and reconstruction of the
     oracle equal the definition evaluated in exact rationals with every float32
     and fp16 rounding written out (zero = min, step = fp32(fp32(max - min) /
@@ -611,9 +611,13 @@ def check_edge_groups_exact(o):
                     seen.add("zero_above_min" if z > mn else "zero_below")
                 if s == 0 and mx > mn:
                     seen.add("step_underflow")
+                if name.startswith("neartie") and s != 0 and any(
+                        0 < abs(abs(r32(r32(x - z) / s) - round_half_even(r32(r32(x - z) / s))) - Fraction(1, 2))
+                        < Fraction(1, 2 ** 13) for x in xs):
+                    seen.add("near_tie_band")
     # the cases exercise what they are named for
-    for need in ("const", "ties", "substep", "underflow", "tiny", "big", "clamp_top", "zero_above_min",
-                 "step_underflow"):
+    for need in ("const", "ties", "neartie", "substep", "underflow", "tiny", "big", "clamp_top", "zero_above_min",
+                 "step_underflow", "near_tie_band"):
         assert need in seen, need
 
 
