@@ -155,7 +155,7 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     }
 }
 
-// Quantize, channel axis, one wave per block of G tokens (G = 32 or 64), four
+// Quantize, channel axis, one wave per block of G = 32 tokens, four
 // blocks per workgroup: lane l holds channel pairs (2p, 2p + 1), p = l + 64q,
 // of every token of the block in registers (one coalesced read of each token
 // row, no second pass); min, max, step, zero and codes per channel in
@@ -255,12 +255,19 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
         residual_rows<DT>(a, head, seq, b_end * G > len0 ? b_end * G : len0, len0, len1, 64);
 }
 
-template <int DT>
+// WIDE: the instantiation that also holds the wave path's larger tile (head_dim
+// 256: two channel pairs per lane), which needs about twice the registers;
+// launched only for appends that use it, so the others keep their occupancy.
+// (64-token blocks stay on channel_axis_part: at head_dim 64 a wave-per-block
+// tile leaves half the lanes without a channel pair, and measured slower.)
+template <int DT, bool WIDE>
 __device__ __forceinline__ void channel_axis_any(const TensorArgs& a, int item, int head, int seq, uint32_t* smem) {
-    if (quant_wave_path(a.group, a.head_dim, a.in_dtype)) {
-        channel_axis_wave<DT, 32, 1>(a, item, head, seq, (uint8_t*)smem);
-    } else {
+    if (!quant_wave_path(a.group, a.head_dim, a.in_dtype)) {
         channel_axis_part<DT>(a, item, head, seq, smem);
+    } else if (!quant_wave_wide(a.group, a.head_dim)) {
+        channel_axis_wave<DT, 32, 1>(a, item, head, seq, (uint8_t*)smem);
+    } else if constexpr (WIDE && In<DT>::bytes == 2) {
+        channel_axis_wave<DT, 32, 2>(a, item, head, seq, (uint8_t*)smem);
     }
 }
 
@@ -268,7 +275,7 @@ __device__ __forceinline__ void channel_axis_any(const TensorArgs& a, int item, 
 // keys, [gx_k, gx_kv) the values, each with its own axis, and with a
 // full-precision window [gx_kv, gridDim.x) copy the rows the window keeps.
 // grid = (gx_kv + window workgroups, kv_heads, num_seqs x layers)
-template <int DT>
+template <int DT, bool WIDE>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, TensorArgs v0, int gx_k, int gx_kv) {
     extern __shared__ uint32_t quant_smem[];
     int z = blockIdx.z, zv = blockIdx.z;
@@ -280,11 +287,11 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(TensorArgs k0, T
         window_rows<DT>(k, v, seq, head, (int)blockIdx.x - gx_kv, (int)gridDim.x - gx_kv, kThreads);
     } else if ((int)blockIdx.x < gx_k) {
         if (k.axis == 1) token_axis_part<DT>(k, blockIdx.x, head, seq);
-        else channel_axis_any<DT>(k, blockIdx.x, head, seq, smem);
+        else channel_axis_any<DT, WIDE>(k, blockIdx.x, head, seq, smem);
     } else {
         const int item = (int)blockIdx.x - gx_k;
         if (v.axis == 1) token_axis_part<DT>(v, item, head, seq);
-        else channel_axis_any<DT>(v, item, head, seq, smem);
+        else channel_axis_any<DT, WIDE>(v, item, head, seq, smem);
     }
 }
 
@@ -973,10 +980,19 @@ hipError_t launch_quant_append(const TensorArgs& k, const TensorArgs& v, int gx_
             lds = std::max(lds, quant_wave_path(t->group, t->head_dim, t->in_dtype)
                                     ? (size_t)kQuantBlocksPerGroup * t->group * t->head_dim
                                     : std::max((size_t)t->group * t->head_dim, (size_t)2 * 2 * kThreads * sizeof(float)));
+    bool wide = false;
+    for (const TensorArgs* t : {&k, &v})
+        wide |= t->axis == 0 && quant_wave_path(t->group, t->head_dim, t->in_dtype) && quant_wave_wide(t->group, t->head_dim);
     switch (k.in_dtype) {
-        case 0: hipLaunchKernelGGL(quant_append_kernel<0>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
-        case 1: hipLaunchKernelGGL(quant_append_kernel<1>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
-        default: hipLaunchKernelGGL(quant_append_kernel<2>, grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
+        case 0: hipLaunchKernelGGL((quant_append_kernel<0, false>), grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv); break;
+        case 1:
+            if (wide) hipLaunchKernelGGL((quant_append_kernel<1, true>), grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv);
+            else hipLaunchKernelGGL((quant_append_kernel<1, false>), grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv);
+            break;
+        default:
+            if (wide) hipLaunchKernelGGL((quant_append_kernel<2, true>), grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv);
+            else hipLaunchKernelGGL((quant_append_kernel<2, false>), grid, dim3(kThreads), lds, s, k, v, gx_k, gx_kv);
+            break;
     }
     return hipGetLastError();
 }
