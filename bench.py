@@ -151,7 +151,9 @@ def main():
     # ---- bulk prefill = quantize-append into an empty cache (timed: quantize GB/s).
     # The append kernel runs once on a small scratch cache first (its first launch
     # in a process also loads the code); the first layer's prefill is timed three
-    # times, emptied in between (kvq_reset_sequence), the median reported.
+    # times, emptied in between (kvq_reset_sequence), the median reported. A
+    # multi-layer model (the 12-layer GPT-2 shape) prefills all of its layers in
+    # one kvq_quantize_append_layers call, the shape of its decode step.
     qz_ms = []
     ev = lambda: torch.cuda.Event(enable_timing=True)
     warm = kvq.Cache(kvq.geometry(layers=1, num_seqs=S, kv_heads=H, q_heads=w.q_heads, head_dim=D,
@@ -163,22 +165,32 @@ def main():
     torch.cuda.synchronize()
     warm.close()
     del warm, wk, wv
-    for l in range(layers):
-        k, v = W.draw_kv(w, l % model_layers if rot == 1 else l, w.lengths, device=dev, stream=0)
-        for rep in range(3 if l == 0 else 1):
+    for l0 in range(0, layers, model_layers):
+        kv = [W.draw_kv(w, l % model_layers if rot == 1 else l, w.lengths, device=dev, stream=0)
+              for l in range(l0, l0 + model_layers)]
+        if model_layers > 1:
+            k, v = torch.stack([x[0] for x in kv]), torch.stack([x[1] for x in kv])
+        else:
+            k, v = kv[0]
+        del kv
+        for rep in range(3 if l0 == 0 else 1):
             if rep:
                 for s_ in range(S):
-                    cache.reset(s_, l, 1)
+                    cache.reset(s_, l0, model_layers)
             torch.cuda.synchronize()
             e0, e1 = ev(), ev()
             e0.record()
-            cache.append(l, k, v, list(w.lengths))
+            if model_layers > 1:
+                cache.append_layers(l0, k, v, list(w.lengths))
+            else:
+                cache.append(l0, k, v, list(w.lengths))
             e1.record()
             torch.cuda.synchronize()
             qz_ms.append(e0.elapsed_time(e1))
         del k, v
-    prefill_tokens = sum(w.lengths)
-    qz_bytes = sum(H * append_head_bytes(0, T, D, w, bk, bv, ib) for T, (bk, bv) in zip(w.lengths, w.bits))
+    prefill_tokens = sum(w.lengths) * model_layers
+    qz_bytes = model_layers * sum(H * append_head_bytes(0, T, D, w, bk, bv, ib)
+                                  for T, (bk, bv) in zip(w.lengths, w.bits))
     quantize_gbps = qz_bytes / (np.median(qz_ms) * 1e-3) / 1e9
 
     # ---- calibration copy: a plain device-to-device copy of known size whose
@@ -379,6 +391,7 @@ def main():
         "quantize_GBps": round(quantize_gbps, 2),
         "quantize_prefill_us": round(float(np.median(qz_ms)) * 1e3, 2),
         "prefill_tokens": prefill_tokens,
+        "quantize_layers_per_call": model_layers,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name + (f"_window{args.window}_sinks{args.sinks}"
