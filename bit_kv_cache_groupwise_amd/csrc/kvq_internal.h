@@ -172,11 +172,13 @@ constexpr int kWinHeads = 4;    // query heads per decode_window_kernel workgrou
 // of 32 tokens, head_dim <= 128. Other blocks take one workgroup per block, two
 // passes over the inputs.
 constexpr int kQuantBlocksPerGroup = 4;
-// Channel-axis blocks of 32 tokens quantized by one wave each (the block's
-// 32 x D tile read once into registers: D / 2 input words per lane): head_dim
-// <= 128 for every input type, head_dim <= 256 for 2-byte inputs.
+// Channel-axis blocks quantized by one wave each (the block's G x D tile read
+// once into registers, G * D / 64 input values per lane): 32-token blocks at
+// head_dim <= 128 for every input type; for 2-byte inputs also 32-token blocks
+// at head_dim <= 256 and 64-token blocks at head_dim <= 64.
 constexpr bool quant_wave_path(int group, int head_dim, int in_dtype) {
-    return group == 32 && (head_dim <= 128 || (in_dtype != 0 && head_dim <= 256));
+    return (group == 32 && head_dim <= 128) ||
+           (in_dtype != 0 && ((group == 32 && head_dim <= 256) || (group == 64 && head_dim <= 64)));
 }
 // the wave path's larger tile (two channel pairs per lane)
 constexpr bool quant_wave_wide(int group, int head_dim) { return group == 32 && head_dim > 128; }

@@ -155,22 +155,25 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
     }
 }
 
-// Quantize, channel axis, one wave per block of G = 32 tokens, four
-// blocks per workgroup: lane l holds channel pairs (2p, 2p + 1), p = l + 64q,
-// of every token of the block in registers (one coalesced read of each token
-// row, no second pass); min, max, step, zero and codes per channel in
+// Quantize, channel axis, one wave per block of G tokens, four blocks per
+// workgroup: lane l holds channel pairs (2p, 2p + 1), p = l % (64 / HS) +
+// (64 / HS) q, of G / HS tokens of the block in registers (HS = 2: lanes l and
+// l + 32 hold the two halves of the block, their min and max combined by one
+// swap), one coalesced read of each token row, no second pass; min, max, step, zero and codes per channel in
 // registers; the codes go through a wave-private LDS tile [G][D] bytes to be
 // packed per 32-channel unit. The wave of the append's first block also copies
 // the rows past the last complete block into the residual, after its own reads
 // of the old residual rows. Same arithmetic and results as channel_axis_part.
-template <int DT, int G, int PPL>
+template <int DT, int G, int PPL, int HS>
 __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item, int head, int seq, uint8_t* smem) {
     constexpr int IB = In<DT>::bytes, NW = IB == 4 ? 2 : 1;  // 32-bit words per channel pair
+    constexpr int GL = G / HS, PW = 64 / HS;                 // tokens per lane, pair slots per half
     const int D = a.head_dim, UPR = D >> 5;
     const int len0 = a.len_in[seq];
     const int n = a.n_new ? a.n_new[seq] : a.n_uniform;
     const int len1 = len0 + n;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lp = lane % PW, t0 = (lane / PW) * GL;  // pair slot, first token of the lane's half
     if (a.len_out && item == 0 && head == 0 && threadIdx.x == 0) a.len_out[seq] = len1;
     const int b_first = len0 / G, b_end = len1 / G, nb = b_end - b_first;
     const int k = item * kQuantBlocksPerGroup + wave;  // block of this append
@@ -182,16 +185,16 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
     if (k < nb) {
         const int b = b_first + k;
         const float L = (float)((1 << B) - 1);
-        uint32_t raw[G][PPL][NW];
+        uint32_t raw[GL][PPL][NW];
         // all loads first (pairs past D read channel 0 and are not used)
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int t = b * G + i;
+        for (int i = 0; i < GL; ++i) {
+            const int t = b * G + t0 + i;
             const uint8_t* row = t < len0 ? resid + (size_t)(t % G) * D * IB
                                           : (const uint8_t*)a.src + ((size_t)(row_start + t - len0) * a.kv_heads + head) * D * IB;
 #pragma unroll
             for (int q = 0; q < PPL; ++q) {
-                const int c = 2 * (lane + 64 * q);
+                const int c = 2 * (lp + PW * q);
                 const uint32_t* w = (const uint32_t*)(row + (size_t)(c < D ? c : 0) * IB);
 #pragma unroll
                 for (int h = 0; h < NW; ++h) raw[i][q][h] = w[h];
@@ -206,25 +209,31 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
         uint8_t* tile = smem + (size_t)wave * G * D;
 #pragma unroll
         for (int q = 0; q < PPL; ++q) {
-            const int c = 2 * (lane + 64 * q);
+            const int c = 2 * (lp + PW * q);
             float mn[2], mx[2], sf[2], zf[2];
             uint32_t sb[2], zb[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 mn[h] = INFINITY, mx[h] = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < G; ++i) mn[h] = fminf(mn[h], val(i, q, h)), mx[h] = fmaxf(mx[h], val(i, q, h));
+                for (int i = 0; i < GL; ++i) mn[h] = fminf(mn[h], val(i, q, h)), mx[h] = fmaxf(mx[h], val(i, q, h));
+                if constexpr (HS == 2) {  // the other half of the block: lane l ^ 32
+                    mn[h] = fminf(mn[h], __shfl_xor(mn[h], 32));
+                    mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], 32));
+                }
                 sb[h] = f32_to_f16_bits((mx[h] - mn[h]) / L);
                 zb[h] = f32_to_f16_bits(mn[h]);
                 sf[h] = f16_to_f32(sb[h]);
                 zf[h] = f16_to_f32(zb[h]);
             }
             if (c < D) {
-                meta[c] = sb[0] | (zb[0] << 16);
-                meta[c + 1] = sb[1] | (zb[1] << 16);
+                if (t0 == 0) {
+                    meta[c] = sb[0] | (zb[0] << 16);
+                    meta[c + 1] = sb[1] | (zb[1] << 16);
+                }
 #pragma unroll
-                for (int i = 0; i < G; ++i)
-                    *(uint16_t*)&tile[i * D + c] =
+                for (int i = 0; i < GL; ++i)
+                    *(uint16_t*)&tile[(t0 + i) * D + c] =
                         (uint16_t)(quant_code(val(i, q, 0), sf[0], zf[0], L) | (quant_code(val(i, q, 1), sf[1], zf[1], L) << 8));
             }
         }
@@ -258,16 +267,17 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
 // WIDE: the instantiation that also holds the wave path's larger tile (head_dim
 // 256: two channel pairs per lane), which needs about twice the registers;
 // launched only for appends that use it, so the others keep their occupancy.
-// (64-token blocks stay on channel_axis_part: at head_dim 64 a wave-per-block
-// tile leaves half the lanes without a channel pair, and measured slower.)
+// 64-token blocks at head_dim <= 64 split the block's tokens between the two
+// halves of the wave (32 input words per lane, as for 32-token blocks).
 template <int DT, bool WIDE>
 __device__ __forceinline__ void channel_axis_any(const TensorArgs& a, int item, int head, int seq, uint32_t* smem) {
     if (!quant_wave_path(a.group, a.head_dim, a.in_dtype)) {
         channel_axis_part<DT>(a, item, head, seq, smem);
-    } else if (!quant_wave_wide(a.group, a.head_dim)) {
-        channel_axis_wave<DT, 32, 1>(a, item, head, seq, (uint8_t*)smem);
-    } else if constexpr (WIDE && In<DT>::bytes == 2) {
-        channel_axis_wave<DT, 32, 2>(a, item, head, seq, (uint8_t*)smem);
+    } else if (a.group == 32 && a.head_dim <= 128) {
+        channel_axis_wave<DT, 32, 1, 1>(a, item, head, seq, (uint8_t*)smem);
+    } else if constexpr (In<DT>::bytes == 2) {
+        if (a.group == 64) channel_axis_wave<DT, 64, 1, 2>(a, item, head, seq, (uint8_t*)smem);
+        else if constexpr (WIDE) channel_axis_wave<DT, 32, 2, 1>(a, item, head, seq, (uint8_t*)smem);
     }
 }
 
