@@ -44,9 +44,10 @@ __device__ __forceinline__ void token_axis_row(const TensorArgs& a, int r, int u
     const PageRow pr = page_row(a.pages, e, t);
     uint32_t* meta = (uint32_t*)(a.meta + pr.base + e.meta[T] + (size_t)head * e.meta_hs[T]);
     if ((u & (UG - 1)) == 0) meta[(size_t)pr.row * (D / G) + u / UG] = sb | (zb << 16);
+    const float rs = quant_rcp(s);
     uint32_t c[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) c[j] = quant_code(x[j], s, z, L);
+    for (int j = 0; j < 32; ++j) c[j] = quant_code(x[j], rs, s, z, L);
     uint32_t* dst =
         (uint32_t*)(a.codes + pr.base + e.codes[T] + (size_t)head * e.codes_hs[T] + (size_t)pr.row * (D * B / 8)) +
         u * B;

@@ -211,18 +211,22 @@ __device__ __forceinline__ void load32(const void* base, size_t off, float (&x)[
     }
 }
 
+// The reciprocal quant_code takes for a stored step s, once per group: 0 for
+// a zero step, whose codes are all 0 (every product is then 0).
+__device__ __forceinline__ float quant_rcp(float s) { return s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s); }
+
 // Code of one value against the stored grid (step s, zero z), L = 2^B - 1:
 // clamp(rint((x - z) / s), 0, L) with the correctly rounded fp32 quotient and
-// ties to even. The quotient is taken as (x - z) * rcp(s), within 2^-21 of it
-// relative (reciprocal and product roundings, the quotient's own), clamped,
-// and rounded to an integer by the fp32 adder (t + 2^23 keeps the integer
-// part, ties to even). For t <= 255 the two can round apart only when the
-// product lies within 2^-13 of a half-integer; there the quotient is divided
-// out (about 2 elements in 10^4).
-__device__ __forceinline__ uint32_t quant_code(float x, float s, float z, float L) {
-    if (s == 0.0f) return 0u;
+// ties to even, 0 where s = 0. The quotient is taken as (x - z) * r, r =
+// quant_rcp(s), within 2^-21 of it relative (reciprocal and product roundings,
+// the quotient's own), clamped, and rounded to an integer by the fp32 adder
+// (t + 2^23 keeps the integer part, ties to even). For t <= 255 the two can
+// round apart only when the product lies within 2^-13 of a half-integer;
+// there the quotient is divided out (about 2 elements in 10^4; never for s =
+// 0, where t = 0).
+__device__ __forceinline__ uint32_t quant_code(float x, float r, float s, float z, float L) {
     const float a = x - z;
-    const float t = __builtin_amdgcn_fmed3f(a * __builtin_amdgcn_rcpf(s), 0.0f, L);
+    const float t = __builtin_amdgcn_fmed3f(a * r, 0.0f, L);
     const float m = t + 8388608.0f;
     if (fabsf(fabsf(t - (m - 8388608.0f)) - 0.5f) < 0x1p-13f)
         return (uint32_t)__builtin_amdgcn_fmed3f(rintf(a / s), 0.0f, L);

@@ -111,6 +111,7 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
         const uint32_t sb0 = f32_to_f16_bits((mx0 - mn0) / L), zb0 = f32_to_f16_bits(mn0);
         const uint32_t sb1 = f32_to_f16_bits((mx1 - mn1) / L), zb1 = f32_to_f16_bits(mn1);
         const float s0 = f16_to_f32(sb0), z0 = f16_to_f32(zb0), s1 = f16_to_f32(sb1), z1 = f16_to_f32(zb1);
+        const float r0 = quant_rcp(s0), r1 = quant_rcp(s1);
         // the block's page (a block never straddles pages) and its first row there
         const PageRow pr = page_row(a.pages, e, b * G);
         if (active && part == 0) {
@@ -124,11 +125,11 @@ __device__ __forceinline__ void channel_axis_part(const TensorArgs& a, int item,
             chan_pair<DT>(a, resid, t0 + i + 1, len0, row_start, head, c, x[2], x[3]);
             const int r = part * tpp + i;
             if constexpr (CPT == 2) {
-                *(uint16_t*)&lds_codes[r * D + c] = (uint16_t)(quant_code(x[0], s0, z0, L) | (quant_code(x[1], s1, z1, L) << 8));
-                *(uint16_t*)&lds_codes[(r + 1) * D + c] = (uint16_t)(quant_code(x[2], s0, z0, L) | (quant_code(x[3], s1, z1, L) << 8));
+                *(uint16_t*)&lds_codes[r * D + c] = (uint16_t)(quant_code(x[0], r0, s0, z0, L) | (quant_code(x[1], r1, s1, z1, L) << 8));
+                *(uint16_t*)&lds_codes[(r + 1) * D + c] = (uint16_t)(quant_code(x[2], r0, s0, z0, L) | (quant_code(x[3], r1, s1, z1, L) << 8));
             } else {
-                lds_codes[r * D + c] = (uint8_t)quant_code(x[0], s0, z0, L);
-                lds_codes[(r + 1) * D + c] = (uint8_t)quant_code(x[2], s0, z0, L);
+                lds_codes[r * D + c] = (uint8_t)quant_code(x[0], r0, s0, z0, L);
+                lds_codes[(r + 1) * D + c] = (uint8_t)quant_code(x[2], r0, s0, z0, L);
             }
         }
         __syncthreads();
@@ -210,7 +211,7 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
 #pragma unroll
         for (int q = 0; q < PPL; ++q) {
             const int c = 2 * (lp + PW * q);
-            float mn[2], mx[2], sf[2], zf[2];
+            float mn[2], mx[2], sf[2], zf[2], rf[2];
             uint32_t sb[2], zb[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -225,6 +226,7 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
                 zb[h] = f32_to_f16_bits(mn[h]);
                 sf[h] = f16_to_f32(sb[h]);
                 zf[h] = f16_to_f32(zb[h]);
+                rf[h] = quant_rcp(sf[h]);
             }
             if (c < D) {
                 if (t0 == 0) {
@@ -234,7 +236,7 @@ __device__ __forceinline__ void channel_axis_wave(const TensorArgs& a, int item,
 #pragma unroll
                 for (int i = 0; i < GL; ++i)
                     *(uint16_t*)&tile[(t0 + i) * D + c] =
-                        (uint16_t)(quant_code(val(i, q, 0), sf[0], zf[0], L) | (quant_code(val(i, q, 1), sf[1], zf[1], L) << 8));
+                        (uint16_t)(quant_code(val(i, q, 0), rf[0], sf[0], zf[0], L) | (quant_code(val(i, q, 1), rf[1], sf[1], zf[1], L) << 8));
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
