@@ -333,7 +333,7 @@ int choose_split_mha(const kvq_cache* c, int max_len, int n_layers) {
 // 512). One launch over every bit pair (one per pair for batches beyond the
 // work list's size); a launch runs its workgroups
 // in rounds of the resident count (4-wave workgroups, one wave per SIMD each;
-// three per compute unit, two for head_dim 256). The choice minimises sum over launches of rounds *
+// gqa_resident_per_cu per compute unit). The choice minimises sum over launches of rounds *
 // (tokens per workgroup + a fixed per-workgroup cost of 512 tokens: loading
 // the queries, merging the waves and writing a split partial that the merge
 // reads back).
@@ -345,7 +345,7 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
         // (paged storage: at most 8192, 64 of a wave's tiles, whose page entries the kernel keeps in one register)
         if (v >= 128 && v % 128 == 0 && v <= (c->paged ? 8192 : (1 << 24))) return v;
     }
-    const long slots = 256L * (g.head_dim >= 256 ? 2 : 3);
+    const long slots = 256L * kvq::gqa_resident_per_cu(g.head_dim, g.rope_base > 0.0);
     const bool one_launch = (long)n_layers * g.num_seqs <= kvq::kGqaListMax;
     long best_cost = -1;
     int best = 512;

@@ -1183,7 +1183,8 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a, uint8_t* smem, int
 
 // Keys cached before the rotary embedding: the instantiations of the objects
 // built with KVQ_GQA_ROPE (fewer waves per SIMD: the rotated fragments, and at
-// head_dim 256 the lane's (cos, sin), need the registers).
+// head_dim 256 the lane's (cos, sin), need the registers). The split choice
+// assumes these bounds (gqa_resident_per_cu).
 #if KVQ_GQA_ROPE
 constexpr bool kRope = true;
 #if KVQ_GQA_HEAD_DIM > 128  // head_dim 256 keeps its (cos, sin) in registers: one wave per SIMD

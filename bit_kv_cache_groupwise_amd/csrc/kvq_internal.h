@@ -180,6 +180,14 @@ constexpr bool quant_wave_path(int group, int head_dim, int in_dtype) {
     return (group == 32 && head_dim <= 128) ||
            (in_dtype != 0 && ((group == 32 && head_dim <= 256) || (group == 64 && head_dim <= 64)));
 }
+// Resident workgroups per compute unit of the query-group kernel (4 waves, one
+// per SIMD each): the waves-per-SIMD bound each of its objects is built with
+// (KVQ_GQA_OCCUPANCY: 3 below head_dim 256, 2 at 256; rotary keys 2 and 1).
+// The split choice runs its workgroups in rounds of this count.
+constexpr int gqa_resident_per_cu(int head_dim, bool rope) {
+    return rope ? (head_dim >= 256 ? 1 : 2) : (head_dim >= 256 ? 2 : 3);
+}
+
 // the wave path's larger tile (two channel pairs per lane)
 constexpr bool quant_wave_wide(int group, int head_dim) { return group == 32 && head_dim > 128; }
 
