@@ -41,6 +41,13 @@ def _cases():
                                              bits=((6, 4),) * 2, axis_k=o.AXIS_TOKEN),
         # head_dim 32 (one unit per row), 3-bit, fp32 input, groups of 32
         "d32": W.tiny().scaled(head_dim=32, lengths=(95,), bits=((3, 3),)),
+        # the quantizer's one-wave key tiles on 2-byte inputs: 64-token blocks split over the wave's two halves
+        # (a bf16 GPT-2 shape; head_dim 32), two channel pairs per lane at head_dim 256 (fp16)
+        "gpt2_bf16": W.gpt2_small().scaled(num_seqs=2, layers=1, kv_heads=2, q_heads=2, lengths=(300, 129),
+                                           bits=((6, 4), (3, 8)), in_dtype="bf16"),
+        "d32_g64": W.tiny().scaled(num_seqs=2, head_dim=32, group_k=64, in_dtype="f16", lengths=(200, 70),
+                                   bits=((4, 2), (8, 3))),
+        "gqa_f16": W.long_gqa().scaled(lengths=(3001,), in_dtype="f16"),
         # groups of 128 and 256 tokens on the channel axis, G=128 channels on the token axis
         "bigG": W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=4, lengths=(700, 256), group_k=256,
                                      group_v=128, bits=((4, 6), (8, 3))),
