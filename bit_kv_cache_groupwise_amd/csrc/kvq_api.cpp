@@ -366,6 +366,23 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
     return best;
 }
 
+// The decode kernel every call on a cache takes: the single-query and
+// query-group kernels for per-channel keys with per-token values at head_dim
+// 64, 128 and 256 (rotary keys: the query-group one at head_dim 128 and 256;
+// head_dim 64: even key bit widths only, a lane group's half unit of key codes
+// being whole words), the generic split kernel otherwise.
+int32_t decode_route(const kvq_cache* c) {
+    const kvq_geometry& g = c->g;
+    const bool rope = g.rope_base > 0.0;
+    if (g.axis_k != KVQ_AXIS_CHANNEL || g.axis_v != KVQ_AXIS_TOKEN || !kvq::mha_supported(g.head_dim))
+        return KVQ_DECODE_GENERIC;
+    if (group_size(c) == 1) return KVQ_DECODE_SINGLE_QUERY;
+    if (rope && !kvq::gqa_rope_supported(g.head_dim)) return KVQ_DECODE_GENERIC;
+    for (const auto& pr : c->pairs)
+        if (g.head_dim < 128 && pr.bk % 2 != 0) return KVQ_DECODE_GENERIC;
+    return KVQ_DECODE_QUERY_GROUP;
+}
+
 int min_chunk(const kvq_cache* c) {
     return c->g.axis_k == KVQ_AXIS_CHANNEL ? std::max(64, c->g.group_k) : 64;
 }
@@ -782,6 +799,18 @@ kvq_status kvq_quantize_append_layers(kvq_cache* c, int32_t layer0, int32_t n_la
     return append_layers(c, layer0, n_layers, k_new, v_new, n_new, stream);
 }
 
+kvq_status kvq_decode_kernel(const kvq_cache* c, int32_t* kernel) {
+    if (!c || !kernel) return fail(KVQ_ERR_ARG, "cache or kernel is NULL");
+    const int32_t route = decode_route(c);
+    if (route == KVQ_DECODE_GENERIC && group_size(c) > kvq::kMaxQueryGroup)
+        return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d on the generic decode kernel",
+                    group_size(c), kvq::kMaxQueryGroup);
+    if (c->g.rope_base > 0.0 && c->g.axis_k != KVQ_AXIS_CHANNEL)
+        return fail(KVQ_ERR_UNSUPPORTED, "rotary keys need channel-axis keys in this build");
+    *kernel = route;
+    return KVQ_OK;
+}
+
 size_t kvq_decode_workspace_size(const kvq_cache* c) {
     if (!c) return 0;
     const kvq_geometry& g = c->g;
@@ -821,15 +850,9 @@ kvq_status decode_layers(const kvq_cache* c, int32_t layer, int32_t n_layers, co
         lens = step_lens.data();
     }
     const int max_len = *std::max_element(lens, lens + (size_t)S * n_layers);
-    // rotary keys: the generic split kernel
-    // the single-query and query-group kernels: per-channel keys, per-token values
-    // (rotary keys: their instantiations of both kernels; the query-group one
-    // for head_dim 128 and 256)
-    const bool fast = g.axis_k == KVQ_AXIS_CHANNEL && g.axis_v == KVQ_AXIS_TOKEN && kvq::mha_supported(g.head_dim);
-    const bool mha = fast && group_size(c) == 1;
-    bool gqa = fast && group_size(c) > 1 && (!rope || kvq::gqa_rope_supported(g.head_dim));
-    for (const auto& pr : c->pairs)  // head_dim 64: a lane group's half unit of key codes must be whole words
-        gqa = gqa && (g.head_dim >= 128 || pr.bk % 2 == 0);
+    const int32_t route = decode_route(c);
+    const bool mha = route == KVQ_DECODE_SINGLE_QUERY;
+    const bool gqa = route == KVQ_DECODE_QUERY_GROUP;
     if (!mha && !gqa && group_size(c) > kvq::kMaxQueryGroup)
         return fail(KVQ_ERR_UNSUPPORTED, "q_heads / kv_heads = %d exceeds %d on the generic decode kernel",
                     group_size(c), kvq::kMaxQueryGroup);

@@ -29,13 +29,14 @@ KVQ_ERR_HIP = -6
 KVQ_AXIS_CHANNEL = 0
 KVQ_AXIS_TOKEN = 1
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
+KVQ_DECODE_SINGLE_QUERY, KVQ_DECODE_QUERY_GROUP, KVQ_DECODE_GENERIC = 1, 2, 3
 DTYPE_CODE = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 
 EXPORTED = ("kvq_plan", "kvq_cache_create", "kvq_cache_destroy", "kvq_quantize_append",
             "kvq_decode_workspace_size", "kvq_decode_attention", "kvq_dequantize", "kvq_seq_lengths",
             "kvq_get_region", "kvq_status_string", "kvq_last_error", "kvq_version", "kvq_read_probe", "kvq_decode_attention_layers",
             "kvq_quantize_append_layers", "kvq_decode_step", "kvq_copy_sequence", "kvq_decode_attention_noalloc",
-            "kvq_gather_sequences", "kvq_evict_tokens", "kvq_reset_sequence", "kvq_page_list")
+            "kvq_gather_sequences", "kvq_evict_tokens", "kvq_reset_sequence", "kvq_page_list", "kvq_decode_kernel")
 
 
 class kvq_geometry(ctypes.Structure):
@@ -72,6 +73,7 @@ _lib.kvq_quantize_append.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_copy_sequence.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
 _lib.kvq_quantize_append_layers.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _I32P, _P]
 _lib.kvq_decode_step.argtypes = [_P, ctypes.c_int32, _P, _P, _I32P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.kvq_decode_kernel.argtypes = [_P, _I32P]
 _lib.kvq_decode_workspace_size.argtypes = [_P]
 _lib.kvq_decode_workspace_size.restype = ctypes.c_size_t
 _lib.kvq_decode_attention.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
@@ -212,6 +214,13 @@ def kvq_decode_step(handle, layer, k_new, v_new, n_new, q, softmax_scale, out, w
     _check(_lib.kvq_decode_step(handle, layer, _ptr(k_new), _ptr(v_new), _i32(n_new), _ptr(q),
                                 ctypes.c_float(softmax_scale), _ptr(out), _ptr(workspace), workspace_bytes,
                                 _stream(stream)), "kvq_decode_step")
+
+
+def kvq_decode_kernel(handle) -> int:
+    """KVQ_DECODE_SINGLE_QUERY, KVQ_DECODE_QUERY_GROUP or KVQ_DECODE_GENERIC."""
+    out = (ctypes.c_int32 * 1)()
+    _check(_lib.kvq_decode_kernel(handle, out), "kvq_decode_kernel")
+    return int(out[0])
 
 
 def kvq_decode_workspace_size(handle) -> int:
@@ -403,6 +412,9 @@ class Cache:
 
     def page_list(self, layer, seq):
         return kvq_page_list(self.handle, layer, seq)
+
+    def decode_kernel(self):
+        return kvq_decode_kernel(self.handle)
 
     def lengths(self, layer):
         return kvq_seq_lengths(self.handle, layer, self.geom.num_seqs)

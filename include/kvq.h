@@ -233,6 +233,22 @@ kvq_status kvq_quantize_append(kvq_cache* cache, int32_t layer, const void* k_ne
  * length up to capacity (split partials; caller-owned, 256-byte aligned). */
 size_t kvq_decode_workspace_size(const kvq_cache* cache);
 
+/* Which decode kernel every decode call on this cache runs (host only; the
+ * choice depends on the geometry and the cache's bit pairs, never on the
+ * lengths), so that a cache that falls to the generic kernel is visible
+ * before it is timed:
+ *   KVQ_DECODE_SINGLE_QUERY: one query per kv head (per-channel keys,
+ *     per-token values, head_dim 64, 128 or 256);
+ *   KVQ_DECODE_QUERY_GROUP: 2 or more query heads per kv head, same caches
+ *     (rotary keys: head_dim 128 and 256; head_dim 64: even key bit widths);
+ *   KVQ_DECODE_GENERIC: the generic split kernel (every other cache), much
+ *     slower.
+ * Errors: KVQ_ERR_ARG for a NULL argument; KVQ_ERR_UNSUPPORTED where decode
+ * itself fails with it (the generic kernel with more than 16 query heads per
+ * kv head, rotary keys on the token axis). */
+enum { KVQ_DECODE_SINGLE_QUERY = 1, KVQ_DECODE_QUERY_GROUP = 2, KVQ_DECODE_GENERIC = 3 };
+kvq_status kvq_decode_kernel(const kvq_cache* cache, int32_t* kernel);
+
 /* Decode-step attention of one query per sequence and query head over every
  * cached token of `layer`, reading the packed codes and fp16 metadata and
  * dequantizing in registers ([N] "Kuantisasi dapat memindahkan pekerjaan ke

@@ -212,6 +212,7 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.kvq_decode_attention(None, 0, None, ctypes.c_float(1.0), None, None, 0, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_dequantize(None, 0, 0, None, None, None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_decode_workspace_size(None) == 0
+    assert lib.kvq_decode_kernel(None, None) == kvq.KVQ_ERR_ARG
     lib.kvq_cache_destroy(None)
     f = ctypes.c_float(1.0)
     assert lib.kvq_decode_step(None, 0, None, None, None, None, f, None, None, 0, None) == kvq.KVQ_ERR_ARG

@@ -571,3 +571,35 @@ def test_decode_step_equals_append_then_decode(name, counts):
     assert ca.lengths(0) == before
     ca.close()
     cb.close()
+
+
+def test_decode_kernel_routing():
+    """kvq_decode_kernel names the kernel decode calls take: single-query for
+    one query per kv head, query-group for more (per-channel keys, per-token
+    values, head_dim 64/128/256; rotary keys at 128/256; head_dim 64 with even
+    key widths), generic otherwise; decode's own KVQ_ERR_UNSUPPORTED where the
+    generic kernel would need more than 16 query heads per kv head."""
+    kvq = H.kvq()
+    llama = W.llama2_7b().scaled(num_seqs=2, kv_heads=2, q_heads=2, lengths=(64, 40), bits=((2, 2), (4, 8)))
+    tiny = W.tiny().scaled(num_seqs=1, q_heads=4, lengths=(64,))
+    cases = [
+        (llama, {}, kvq.KVQ_DECODE_SINGLE_QUERY),
+        (llama.scaled(q_heads=16), {}, kvq.KVQ_DECODE_QUERY_GROUP),
+        (llama.scaled(q_heads=16), {"rope_base": 10000.0}, kvq.KVQ_DECODE_QUERY_GROUP),
+        (llama, {"rope_base": 10000.0}, kvq.KVQ_DECODE_SINGLE_QUERY),
+        (llama.scaled(axis_k=o.AXIS_TOKEN, q_heads=8), {}, kvq.KVQ_DECODE_GENERIC),
+        (llama.scaled(axis_v=o.AXIS_CHANNEL), {}, kvq.KVQ_DECODE_GENERIC),
+        (tiny.scaled(bits=((2, 3),)), {}, kvq.KVQ_DECODE_QUERY_GROUP),
+        (tiny.scaled(bits=((3, 2),)), {}, kvq.KVQ_DECODE_GENERIC),
+        (tiny.scaled(bits=((2, 2),)), {"rope_base": 10000.0}, kvq.KVQ_DECODE_GENERIC),
+        (tiny.scaled(head_dim=96, q_heads=2), {}, kvq.KVQ_DECODE_GENERIC),
+    ]
+    for w, kw, want in cases:
+        cache = H.make_cache(w, **kw)
+        assert cache.decode_kernel() == want, (w.head_dim, w.q_heads, w.axis_k, w.axis_v, w.bits, kw)
+        cache.close()
+    cache = H.make_cache(llama.scaled(axis_k=o.AXIS_TOKEN, kv_heads=1, q_heads=32))
+    with pytest.raises(kvq.KVQError) as e:
+        cache.decode_kernel()
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+    cache.close()
