@@ -331,12 +331,14 @@ int choose_split_mha(const kvq_cache* c, int max_len, int n_layers) {
 
 // Tokens per workgroup of the query-group kernel (a multiple of 128, at least
 // 512). One launch over every bit pair (one per pair for batches beyond the
-// work list's size); a launch runs its workgroups
-// in rounds of the resident count (4-wave workgroups, one wave per SIMD each;
-// gqa_resident_per_cu per compute unit). The choice minimises sum over launches of rounds *
-// (tokens per workgroup + a fixed per-workgroup cost of 512 tokens: loading
-// the queries, merging the waves and writing a split partial that the merge
-// reads back).
+// work list's size). A launch holds gqa_resident_per_cu workgroups per compute
+// unit (4 waves each, one per SIMD) and dispatches the rest as slots free up.
+// Each workgroup costs its tokens plus a fixed 512 (loading the queries,
+// merging the waves, writing a split partial that the merge reads back). A
+// launch whose workgroups all fit at once takes its longest one; a larger one
+// takes its total cost over the slots plus half its longest workgroup (the
+// tail), so a ragged batch is not charged full rounds for its short splits.
+// The choice minimises the sum over launches.
 // lens: [n_layers][num_seqs], the layers of one launch.
 int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
     const kvq_geometry& g = c->g;
@@ -345,23 +347,35 @@ int choose_split_gqa(const kvq_cache* c, const int32_t* lens, int n_layers) {
         // (paged storage: at most 8192, 64 of a wave's tiles, whose page entries the kernel keeps in one register)
         if (v >= 128 && v % 128 == 0 && v <= (c->paged ? 8192 : (1 << 24))) return v;
     }
-    const long slots = 256L * kvq::gqa_resident_per_cu(g.head_dim, g.rope_base > 0.0);
+    const double slots = 256.0 * kvq::gqa_resident_per_cu(g.head_dim, g.rope_base > 0.0);
     const bool one_launch = (long)n_layers * g.num_seqs <= kvq::kGqaListMax;
-    long best_cost = -1;
+    const long rows = (long)g.kv_heads * ((group_size(c) + 15) / 16);  // workgroups per split of a sequence
+    constexpr double kFixed = 512.0;  // per-workgroup cost in tokens (queries, wave merge, the partial)
+    // a launch's time in tokens: all of its workgroups resident at once, the
+    // longest; else its work spread over the resident slots (dynamic dispatch)
+    // plus half the longest workgroup for the tail
+    auto launch = [&](double wgs, double work, double longest) {
+        return wgs <= slots ? longest : work / slots + 0.5 * longest;
+    };
+    double best_cost = -1.0;
     int best = 512;
     for (int cw : {512, 640, 768, 896, 1024, 1280, 1536, 2048, 2560, 3072, 4096, 6144, 8192}) {
-        long cost = 0, all = 0;
+        double cost = 0.0, all_wgs = 0.0, all_work = 0.0, all_longest = 0.0;
         for (const auto& pr : c->pairs) {
-            long wgs = 0;
+            double wgs = 0.0, work = 0.0, longest = 0.0;
             for (int l = 0; l < n_layers; ++l)
-                for (int i = 0; i < pr.count; ++i)
-                    wgs += (lens[(size_t)l * g.num_seqs + c->pair_list[pr.offset + i]] + cw - 1) / cw;
-            wgs *= (long)g.kv_heads * ((group_size(c) + 15) / 16);
-            cost += (wgs + slots - 1) / slots * (cw + 512);
-            all += wgs;
+                for (int i = 0; i < pr.count; ++i) {
+                    const long len = lens[(size_t)l * g.num_seqs + c->pair_list[pr.offset + i]];
+                    const long n = (len + cw - 1) / cw;
+                    wgs += (double)(n * rows);
+                    work += (double)((len + n * (long)kFixed) * rows);
+                    if (n) longest = std::max(longest, (double)std::min<long>(len, cw) + kFixed);
+                }
+            cost += wgs ? launch(wgs, work, longest) : 0.0;
+            all_wgs += wgs, all_work += work, all_longest = std::max(all_longest, longest);
         }
-        if (one_launch) cost = (all + slots - 1) / slots * (cw + 512);
-        if (best_cost < 0 || cost < best_cost) best_cost = cost, best = cw;
+        if (one_launch) cost = all_wgs ? launch(all_wgs, all_work, all_longest) : 0.0;
+        if (best_cost < 0.0 || cost < best_cost) best_cost = cost, best = cw;
     }
     return best;
 }
