@@ -147,6 +147,8 @@ def main():
                         group_v=w.group_v, axis_k=w.axis_k, axis_v=w.axis_v, in_dtype=w.in_dtype,
                         window=args.window, sinks=args.sinks, rope_base=args.rope_base)
     cache = kvq.Cache(geom, cap, [b[0] for b in w.bits], [b[1] for b in w.bits], device=dev)
+    decode_kernel = {kvq.KVQ_DECODE_SINGLE_QUERY: "single_query", kvq.KVQ_DECODE_QUERY_GROUP: "query_group",
+                     kvq.KVQ_DECODE_GENERIC: "generic"}[cache.decode_kernel()]
 
     # ---- bulk prefill = quantize-append into an empty cache (timed: quantize GB/s).
     # The append kernel runs once on a small scratch cache first (its first launch
@@ -378,6 +380,7 @@ def main():
                    "layers_per_step": model_layers, "decode_calls_per_step": dec_per_step,
                    "bits_kv": sorted(set(w.bits)), "group": [w.group_k, w.group_v],
                    "input_dtype": w.in_dtype, "rotated_layer_caches": rot, "parallelism": "single-gpu",
+                   "decode_kernel": decode_kernel,
                    **({"full_precision_window": args.window, "sinks": args.sinks} if args.window or args.sinks
                       else {}), **({"rope_base": args.rope_base} if args.rope_base else {})},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
